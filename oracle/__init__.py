@@ -1,0 +1,192 @@
+"""CPU oracle for exact categorical sampling (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library in
+``decode_exact_categorical_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``fs_oracle.c`` (plain C, float64, OpenMP over the
+vocabulary); this module only marshals numpy arrays into it.  What each C
+function computes, and which passage of the source pages it follows, is stated
+in the header of ``fs_oracle.c``.  Statistical helpers used by the pins
+(Poisson intervals, chi-square) live in ``oracle/stats.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fs_oracle.c")
+_LIB = os.path.join(_HERE, "libfs_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile fs_oracle.c into libfs_oracle.so (gcc, -O2, OpenMP, strict IEEE)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, u64, u32, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
+        lib.oracle_num_threads.restype = i32
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [i32]
+        lib.oracle_philox_words.restype = None
+        lib.oracle_philox_words.argtypes = [u64, u64, P, i64, i64, P]
+        lib.oracle_philox_block.restype = None
+        lib.oracle_philox_block.argtypes = [P, u32, u32, P]
+        lib.oracle_noise_at.restype = None
+        lib.oracle_noise_at.argtypes = [u64, u64, u32, i64, i32, P, P, P]
+        lib.oracle_noise_of_uniform.restype = None
+        lib.oracle_noise_of_uniform.argtypes = [ctypes.c_double, P, P]
+        lib.oracle_logits.restype = None
+        lib.oracle_logits.argtypes = [P, P, i64, i64, i64, P]
+        lib.oracle_sample_fused.restype = None
+        lib.oracle_sample_fused.argtypes = [P, P, i64, i64, i64, P, P, u64, u64, P,
+                                            i32, P, P, P]
+        lib.oracle_sample_logits.restype = None
+        lib.oracle_sample_logits.argtypes = [P, i64, i64, P, u64, u64, P, i32, P, P, P]
+        lib.oracle_sample_repeated_row.restype = None
+        lib.oracle_sample_repeated_row.argtypes = [P, i64, ctypes.c_float, u64, u64, P,
+                                                   i64, i32, P]
+        _lib = lib
+        return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bf16_bits(x) -> np.ndarray:
+    """Accept a numpy uint16 array of bf16 bit patterns or a torch bfloat16 tensor."""
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint16
+        return np.ascontiguousarray(x)
+    import torch  # local: only the tests pass torch tensors
+    assert x.dtype == torch.bfloat16
+    return np.ascontiguousarray(x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def _u32_or_none(row_ids, B):
+    if row_ids is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(row_ids, dtype=np.uint32))
+    assert a.shape == (B,)
+    return a
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+def philox_words(seed: int, offset: int, row_ids, B: int, n_ctr: int) -> np.ndarray:
+    """uint32[B, n_ctr, 4]: Philox4x32-10 words of counters (j, row, offset)."""
+    out = np.zeros((B, n_ctr, 4), dtype=np.uint32)
+    rid = _u32_or_none(row_ids, B)
+    _load().oracle_philox_words(seed, offset, _ptr(rid), B, n_ctr, _ptr(out))
+    return out
+
+
+def philox_block(ctr, key) -> np.ndarray:
+    """The raw Philox4x32-10 bijection of counter ctr[4] under key (k0, k1)."""
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    out = np.zeros(4, dtype=np.uint32)
+    _load().oracle_philox_block(_ptr(c), int(key[0]), int(key[1]), _ptr(out))
+    return out
+
+
+def noise_at(seed: int, offset: int, row_id: int, i: int, fp64: bool):
+    """(u, E, g) of vocabulary index i in logical row row_id."""
+    u, E, g = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _load().oracle_noise_at(seed, offset, row_id, i, int(fp64),
+                            ctypes.byref(u), ctypes.byref(E), ctypes.byref(g))
+    return u.value, E.value, g.value
+
+
+def noise_of_uniform(u: float):
+    """(E, g) for a uniform value u."""
+    E, g = ctypes.c_double(), ctypes.c_double()
+    _load().oracle_noise_of_uniform(float(u), ctypes.byref(E), ctypes.byref(g))
+    return E.value, g.value
+
+
+def logits(H, W) -> np.ndarray:
+    """float64[B, V] = H @ W.T with H[B,D], W[V,D] given as bf16."""
+    h, w = _bf16_bits(H), _bf16_bits(W)
+    B, D = h.shape
+    V, D2 = w.shape
+    assert D == D2
+    Y = np.zeros((B, V), dtype=np.float64)
+    _load().oracle_logits(_ptr(h), _ptr(w), B, D, V, _ptr(Y))
+    return Y
+
+
+def sample_fused(H, W, temp, bias=None, *, seed: int, offset: int, row_ids=None,
+                 fp64_noise: bool = False):
+    """(idx int64[B], gap float64[B], best float64[B]) for the fused definition."""
+    h, w = _bf16_bits(H), _bf16_bits(W)
+    B, D = h.shape
+    V = w.shape[0]
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    bb = None
+    if bias is not None:
+        bb = np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+        assert bb.shape == (B, V)
+    rid = _u32_or_none(row_ids, B)
+    idx = np.zeros(B, dtype=np.int64)
+    gap = np.zeros(B, dtype=np.float64)
+    best = np.zeros(B, dtype=np.float64)
+    _load().oracle_sample_fused(_ptr(h), _ptr(w), B, D, V, _ptr(t), _ptr(bb), seed, offset,
+                                _ptr(rid), int(fp64_noise), _ptr(idx), _ptr(gap), _ptr(best))
+    return idx, gap, best
+
+
+def sample_logits(logits_f32, temp, *, seed: int, offset: int, row_ids=None,
+                  fp64_noise: bool = False):
+    """(idx, gap, best) for the standalone sampler over float32 logits[B,V]."""
+    x = np.ascontiguousarray(np.asarray(logits_f32, dtype=np.float32))
+    B, V = x.shape
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    rid = _u32_or_none(row_ids, B)
+    idx = np.zeros(B, dtype=np.int64)
+    gap = np.zeros(B, dtype=np.float64)
+    best = np.zeros(B, dtype=np.float64)
+    _load().oracle_sample_logits(_ptr(x), B, V, _ptr(t), seed, offset, _ptr(rid),
+                                 int(fp64_noise), _ptr(idx), _ptr(gap), _ptr(best))
+    return idx, gap, best
+
+
+def sample_repeated_row(row_f32, temp: float, *, seed: int, offset: int, row_ids,
+                        fp64_noise: bool = False) -> np.ndarray:
+    """Sampled indices of many logical rows that all carry the logits row_f32[V]."""
+    x = np.ascontiguousarray(np.asarray(row_f32, dtype=np.float32).reshape(-1))
+    rid = np.ascontiguousarray(np.asarray(row_ids, dtype=np.uint32).reshape(-1))
+    out = np.zeros(rid.shape[0], dtype=np.int64)
+    _load().oracle_sample_repeated_row(_ptr(x), x.shape[0], float(temp), seed, offset,
+                                       _ptr(rid), rid.shape[0], int(fp64_noise), _ptr(out))
+    return out

@@ -1,0 +1,334 @@
+/*
+ * fs_oracle.c -- CPU oracle for exact categorical sampling fused into an
+ * LM head (FlashSampling) and for the standalone Gumbel / exponential-race
+ * sampler over materialised logits.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this library.  The product path
+ * (the HIP library and its Python binding) never calls into it, and the two
+ * share no source: this file includes nothing from the HIP tree and the HIP
+ * tree includes nothing from here.
+ *
+ * Everything is plain, slow and in float64.  Every function below names the
+ * passage of the source pages it follows:
+ *   [FS]  "FlashSampling: fast and memory-efficient exact sampling" (paper
+ *         summary page): prerequisites (Gumbel-max trick), method, and the
+ *         algorithm-details section (Stage 1 steps (1)-(6), Stage 2).
+ *   [MG]  Megatron-LM pull request "fp64 sampling noise": sections
+ *         "Problem" (race argmax p/E with E = -log U), "The change" (two
+ *         Philox words -> 52-bit midpoint uniform, keyed by request seed,
+ *         position and vocabulary index) and "Tests".
+ *   [SK]  "Write Triton Sampling Kernel" skill page: "Required reasoning
+ *         process" items 3-4 (greedy short-circuit; bias before temperature)
+ *         and "Correctness requirements" (smallest-index tie-break).
+ *   [PH]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
+ *         1, 2, 3", SC'11, section 4 (the Philox-4x32 bijection, 10 rounds).
+ *
+ * Definition computed (per batch row b, logical row id r = row_ids[b] or b):
+ *   y_i   = sum_d H[b,d] * W[i,d]           float64, d ascending   [FS (1)]
+ *   if t = temp[b] > 0:  yt_i = (y_i + bias[b,i]) / t               [SK 4]
+ *   else (greedy):       yt_i =  y_i + bias[b,i],  g_i = 0          [SK 3]
+ *   Philox4x32-10, key (seed lo, seed hi),
+ *     counter (j, r, offset lo, offset hi), j = i>>2 (fp32 noise) or i>>1
+ *     (fp64 noise) -> words x[0..3]                         [PH; MG change]
+ *   fp32 noise: k = x[i&3] >> 9          (23 bits), u = (2k+1) / 2^24
+ *   fp64 noise: k = top 52 bits of x[2(i&1)] : x[2(i&1)+1], u = (2k+1) / 2^53
+ *   E_i = -log(u) (computed as -log1p(u-1) when u >= 1/2), g_i = -log(E_i)
+ *                                                       [MG problem; FS (3)]
+ *   s_i = yt_i + g_i                                                [FS (4)]
+ *   out = smallest i attaining max s_i over the i whose s_i is neither NaN nor
+ *         -inf; -1 if there is none.                  [FS (5), Stage 2; SK]
+ *   gap = s_(1) - s_(2), the top-2 gap of those scores (+inf if only one).
+ *
+ * Parity pins (tests marked "not gpu"): the Philox words against an
+ * independent engine (the one PyTorch ships as a header); the uniform, E and
+ * g values against 60-digit decimal arithmetic; the logits against exact
+ * rational sums; the sampled law against softmax by chi-square, by a
+ * Poisson tail count with the closed-form miss probability, and by exact
+ * enumeration of the noise grid for two-token rows; greedy against numpy's
+ * argmax; masks, NaN and empty rows against the rule above.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 [PH].                                                 */
+/* One round multiplies counter words 0 and 2 by the two round          */
+/* multipliers, keeps both halves of each 64-bit product, and mixes the */
+/* high halves with the other two counter words and the key.  The key   */
+/* is bumped by the two Weyl constants between rounds.                  */
+/* ------------------------------------------------------------------ */
+static void philox4x32_10(const uint32_t ctr[4], uint32_t k0, uint32_t k1,
+                          uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c1 ^ k0;
+        uint32_t n1 = lo1;
+        uint32_t n2 = hi0 ^ c3 ^ k1;
+        uint32_t n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Words for counter (j, r, offset), key = seed [MG change: keyed by request
+ * seed, absolute position and vocabulary index]. */
+static void words_for(uint64_t seed, uint64_t offset, uint32_t r, uint32_t j,
+                      uint32_t out[4])
+{
+    uint32_t ctr[4];
+    ctr[0] = j;
+    ctr[1] = r;
+    ctr[2] = (uint32_t)(offset & 0xFFFFFFFFu);
+    ctr[3] = (uint32_t)(offset >> 32);
+    philox4x32_10(ctr, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), out);
+}
+
+/* Uniform on the midpoint grid for vocabulary index i.
+ * fp32 noise: one 32-bit word per index, its top 23 bits k, u = (k + 1/2)/2^23.
+ * fp64 noise: two words per index, the top 52 bits k of their 64-bit
+ * concatenation, u = (k + 1/2)/2^52 [MG change].  Both are exact in double. */
+static double uniform_for(uint64_t seed, uint64_t offset, uint32_t r, int64_t i,
+                          int fp64)
+{
+    uint32_t x[4];
+    if (!fp64) {
+        words_for(seed, offset, r, (uint32_t)(i >> 2), x);
+        uint32_t k = x[i & 3] >> 9;
+        return ((double)k + 0.5) / 8388608.0;               /* 2^23 */
+    }
+    words_for(seed, offset, r, (uint32_t)(i >> 1), x);
+    uint64_t a = x[2 * (i & 1)], b = x[2 * (i & 1) + 1];
+    uint64_t k = ((a << 32) | b) >> 12;                      /* top 52 bits */
+    return ((double)k + 0.5) / 4503599627370496.0;           /* 2^52 */
+}
+
+/* E = -log u is a standard exponential; g = -log E is a standard Gumbel
+ * [MG problem; FS (3)].  Near u = 1 the log1p form keeps E's relative
+ * accuracy, which is what decides the deep tail. */
+static double exponential_of(double u)
+{
+    return (u >= 0.5) ? -log1p(u - 1.0) : -log(u);
+}
+
+static double gumbel_of(double u) { return -log(exponential_of(u)); }
+
+/* bf16 bit pattern -> double (exact). */
+static double bf16_to_double(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------ */
+/* Exported helpers.                                                    */
+/* ------------------------------------------------------------------ */
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Philox words for counters j = 0..n_ctr-1 of each row: out[B][n_ctr][4]. */
+void oracle_philox_words(uint64_t seed, uint64_t offset, const uint32_t *row_ids,
+                         int64_t B, int64_t n_ctr, uint32_t *out)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        for (int64_t j = 0; j < n_ctr; ++j)
+            words_for(seed, offset, r, (uint32_t)j, out + (b * n_ctr + j) * 4);
+    }
+}
+
+/* Raw Philox block on an arbitrary counter and key (for the engine pin). */
+void oracle_philox_block(const uint32_t ctr[4], uint32_t k0, uint32_t k1,
+                         uint32_t out[4])
+{
+    philox4x32_10(ctr, k0, k1, out);
+}
+
+/* u, E and g of vocabulary index i of logical row r. */
+void oracle_noise_at(uint64_t seed, uint64_t offset, uint32_t r, int64_t i,
+                     int fp64, double *u, double *E, double *g)
+{
+    double uu = uniform_for(seed, offset, r, i, fp64);
+    double ee = exponential_of(uu);
+    *u = uu;
+    *E = ee;
+    *g = -log(ee);
+}
+
+/* Noise transforms of a given uniform (for the decimal-arithmetic pin). */
+void oracle_noise_of_uniform(double u, double *E, double *g)
+{
+    *E = exponential_of(u);
+    *g = gumbel_of(u);
+}
+
+/* Logits Y[b,i] = sum_d H[b,d] W[i,d], float64, d ascending [FS (1)].
+ * H[B,D] and W[V,D] are bf16 bit patterns, row-major. */
+void oracle_logits(const uint16_t *H, const uint16_t *W, int64_t B, int64_t D,
+                   int64_t V, double *Y)
+{
+    double *hrow = (double *)malloc((size_t)D * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t d = 0; d < D; ++d) hrow[d] = bf16_to_double(H[b * D + d]);
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i) {
+            const uint16_t *w = W + i * D;
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc += hrow[d] * bf16_to_double(w[d]);
+            Y[b * V + i] = acc;
+        }
+    }
+    free(hrow);
+}
+
+/* Perturbed score of one element [FS (2)-(4); SK 3-4].  y is the logit, beta
+ * the additive bias (NULL bias means 0), t the row temperature. */
+static double score_of(double y, double beta, double t, uint64_t seed,
+                       uint64_t offset, uint32_t r, int64_t i, int fp64)
+{
+    if (!(t > 0.0)) return y + beta;                 /* greedy: no noise */
+    double yt = (y + beta) / t;
+    return yt + gumbel_of(uniform_for(seed, offset, r, i, fp64));
+}
+
+/* Smallest-index argmax over valid scores plus the top-2 gap [FS (5), Stage 2;
+ * SK tie-break].  Valid means neither NaN nor -inf. */
+static void select_row(const double *s, int64_t V, int64_t *idx, double *gap,
+                       double *best)
+{
+    int64_t bi = -1;
+    double b1 = -INFINITY, b2 = -INFINITY;
+    int64_t nvalid = 0;
+    for (int64_t i = 0; i < V; ++i) {
+        double v = s[i];
+        if (isnan(v) || v == -INFINITY) continue;
+        ++nvalid;
+        if (bi < 0) {                 /* first valid score */
+            b1 = v;
+            bi = i;
+        } else if (v > b1) {          /* strictly larger: new leader */
+            b2 = b1;
+            b1 = v;
+            bi = i;
+        } else if (v > b2) {          /* v <= b1; an equal score keeps the
+                                         smaller index and makes the gap 0 */
+            b2 = v;
+        }
+    }
+    *idx = bi;
+    if (bi < 0) {
+        *gap = NAN;
+        *best = -INFINITY;
+    } else {
+        *gap = (nvalid == 1) ? INFINITY : b1 - b2;
+        *best = b1;
+    }
+}
+
+/* Fused path: logits from H and W, then transform, noise and selection.
+ * temp[B]; bias[B,V] or NULL; row_ids[B] or NULL.  Outputs per row: the
+ * sampled index, the top-2 perturbed-score gap and the winning score. */
+void oracle_sample_fused(const uint16_t *H, const uint16_t *W, int64_t B,
+                         int64_t D, int64_t V, const float *temp,
+                         const float *bias, uint64_t seed, uint64_t offset,
+                         const uint32_t *row_ids, int fp64_noise,
+                         int64_t *out_idx, double *out_gap, double *out_best)
+{
+    double *s = (double *)malloc((size_t)V * sizeof(double));
+    double *hrow = (double *)malloc((size_t)D * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        double t = (double)temp[b];
+        for (int64_t d = 0; d < D; ++d) hrow[d] = bf16_to_double(H[b * D + d]);
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i) {
+            const uint16_t *w = W + i * D;
+            double y = 0.0;
+            for (int64_t d = 0; d < D; ++d) y += hrow[d] * bf16_to_double(w[d]);
+            double beta = bias ? (double)bias[b * V + i] : 0.0;
+            s[i] = score_of(y, beta, t, seed, offset, r, i, fp64_noise);
+        }
+        select_row(s, V, &out_idx[b], &out_gap[b], &out_best[b]);
+    }
+    free(hrow);
+    free(s);
+}
+
+/* Standalone sampler over materialised float32 logits[B,V]: the same
+ * transform, noise and selection with y_i = logits[b,i] [MG problem;
+ * FS prerequisites]. */
+void oracle_sample_logits(const float *logits, int64_t B, int64_t V,
+                          const float *temp, uint64_t seed, uint64_t offset,
+                          const uint32_t *row_ids, int fp64_noise,
+                          int64_t *out_idx, double *out_gap, double *out_best)
+{
+    double *s = (double *)malloc((size_t)V * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        double t = (double)temp[b];
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i)
+            s[i] = score_of((double)logits[b * V + i], 0.0, t, seed, offset, r, i,
+                            fp64_noise);
+        select_row(s, V, &out_idx[b], &out_gap[b], &out_best[b]);
+    }
+    free(s);
+}
+
+/* Many logical rows that share one logits row: row k of the batch has
+ * logical id row_ids[k] and the logits of `logits[0..V)`.  This is the same
+ * computation as oracle_sample_logits with the row repeated, without
+ * materialising the repeats (used by the tail-rate and chi-square tests,
+ * whose rows are identical by construction). */
+void oracle_sample_repeated_row(const float *logits, int64_t V, float temp,
+                                uint64_t seed, uint64_t offset,
+                                const uint32_t *row_ids, int64_t n_rows,
+                                int fp64_noise, int64_t *out_idx)
+{
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)V * sizeof(double));
+        #pragma omp for schedule(static)
+        for (int64_t k = 0; k < n_rows; ++k) {
+            double gap, best;
+            for (int64_t i = 0; i < V; ++i)
+                s[i] = score_of((double)logits[i], 0.0, (double)temp, seed, offset,
+                                row_ids[k], i, fp64_noise);
+            select_row(s, V, &out_idx[k], &gap, &best);
+        }
+        free(s);
+    }
+}

@@ -1,0 +1,77 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds no arithmetic of the sampling method: it only draws the
+tensors the method consumes, with the shapes and distributions of the LM-head
+workloads on the FlashSampling page (D = 4096, V = 151936 Qwen3-8B-shaped head;
+D = 4096, V = 128256 Llama-3-shaped head; D = 8192 wide head) and of the
+Megatron-LM tail-rate and chi-square tests.  Every draw uses a CPU
+``torch.Generator`` with a fixed seed, so the oracle and the GPU path see
+identical bits.  Seeds: W = 0, H = 1, temperatures = 2, bias/mask = 3,
+chi-square row = 4.  Reading of "N(0, s)": s is the standard deviation.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+SEED_W, SEED_H, SEED_T, SEED_BIAS, SEED_CHI2 = 0, 1, 2, 3, 4
+
+
+def _gen(seed: int) -> torch.Generator:
+    return torch.Generator(device="cpu").manual_seed(int(seed))
+
+
+def weight(V: int, D: int, std: float, seed: int = SEED_W, chunk_rows: int = 8192) -> torch.Tensor:
+    """W[V, D] bf16 ~ N(0, std^2), drawn in row chunks so large heads fit in host memory."""
+    W = torch.empty((V, D), dtype=torch.bfloat16)
+    g = _gen(seed)
+    for r0 in range(0, V, chunk_rows):
+        r1 = min(V, r0 + chunk_rows)
+        W[r0:r1] = (torch.randn((r1 - r0, D), generator=g) * std).to(torch.bfloat16)
+    return W
+
+
+def hidden(B: int, D: int, std: float = 1.0, seed: int = SEED_H) -> torch.Tensor:
+    """H[B, D] bf16 ~ N(0, std^2)."""
+    return (torch.randn((B, D), generator=_gen(seed)) * std).to(torch.bfloat16)
+
+
+def temperatures(B: int, lo: float = 0.5, hi: float = 1.2, seed: int = SEED_T) -> torch.Tensor:
+    """temp[B] fp32 ~ U[lo, hi]."""
+    return (torch.rand((B,), generator=_gen(seed), dtype=torch.float64) * (hi - lo) + lo).float()
+
+
+def bias_with_mask(B: int, V: int, p_mask: float = 0.1, seed: int = SEED_BIAS) -> torch.Tensor:
+    """bias[B, V] fp32: N(0, 1) values with Bernoulli(p_mask) entries set to -inf."""
+    g = _gen(seed)
+    out = torch.empty((B, V), dtype=torch.float32)
+    for b in range(B):
+        vals = torch.randn((V,), generator=g)
+        mask = torch.rand((V,), generator=g) < p_mask
+        vals[mask] = float("-inf")
+        out[b] = vals
+    return out
+
+
+def chi2_row(n: int = 16, std: float = 2.0, seed: int = SEED_CHI2) -> torch.Tensor:
+    """A row of n logits ~ N(0, std^2), fp32."""
+    return (torch.randn((n,), generator=_gen(seed)) * std).float()
+
+
+def tail_depth(r: float) -> float:
+    """D = fl32(-ln r): the depth of the tail tokens, rounded to float32."""
+    return float(np.float32(-math.log(r)))
+
+
+def tail_row(V: int, r: float) -> torch.Tensor:
+    """The row [0, -D, ..., -D] of V float32 logits with D = fl32(-ln r)."""
+    row = torch.full((V,), -tail_depth(r), dtype=torch.float32)
+    row[0] = 0.0
+    return row
+
+
+def row_ids(B: int, start: int = 0) -> torch.Tensor:
+    """Logical row ids start..start+B-1 as int32 (bit pattern of uint32)."""
+    return torch.arange(start, start + B, dtype=torch.int64).to(torch.int32)
