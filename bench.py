@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LM-head + exact-sampling decode step on one MI355X.
+
+Workload (the FlashSampling page's main micro-benchmark shape, "reproduction"):
+a Qwen3-8B-shaped LM head, H [B, 4096] bf16 ~ N(0, 1), W [151936, 4096] bf16 ~
+N(0, 0.02), per-row temperature ~ U[0.5, 1.2], seeded per row, exact
+sampling with float32 noise (no filtering); B = 64 is the headline, B = 1, 8, 32 are reported
+beside it.  Inputs are synthetic and already resident in HBM when timing starts.
+
+One step = one fs_sample_fused call (Stage 1 + Stage 2), offset advancing each
+step.  Prints one JSON line: `value` is microseconds per decode step at B = 64;
+`roofline` prices the Stage 1 kernel's algorithmic HBM bytes against its own
+average duration, read from HIP events the library records around it on the
+stream it runs on, over the same timed region; `cpu_baseline` is the float64 CPU
+oracle computing the same step on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("µs/decode-step & achieved HBM GB/s (fused LM-head+sample), "
+          "D=4096 V=151936 B=1–64")
+D_MODEL, VOCAB = 4096, 151936
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_stage1_qwen3_8b_b64_traffic.txt")
+KERNEL_SOURCES = ["decode_exact_categorical_amd/csrc/fs_fused.hip",
+                  "decode_exact_categorical_amd/csrc/fs_device.hpp",
+                  "decode_exact_categorical_amd/csrc/fs_launch.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per Stage 1 launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source (else None)."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    vals = {}
+    with open(PROFILE_TRAFFIC) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def fused_tiles(V: int, cus: int) -> int:
+    """Vocabulary tiles of the fused Stage 1 (two workgroups per CU, 16-row blocks)."""
+    return max(1, min((V + 15) // 16, 2 * cus))
+
+
+def stage1_alg_bytes(B: int, D: int, V: int, n_tiles: int, bias: bool = False) -> int:
+    """What Stage 1 must move: W once, H once, temperatures, [bias], candidates out."""
+    return V * D * 2 + B * D * 2 + 4 * B + (4 * B * V if bias else 0) + 8 * B * n_tiles
+
+
+def step_alg_bytes(B: int, D: int, V: int, n_tiles: int) -> int:
+    """One decode step (Stage 1 + Stage 2): candidates written and read once, out written."""
+    return V * D * 2 + B * D * 2 + 4 * B + 2 * 8 * B * n_tiles + 8 * B
+
+
+def time_fused(fs, torch, H, W, temp, steps, warmup, offset0=0):
+    """(ms per step over `steps` timed calls, mean Stage 1 ms, mean Stage 2 ms)."""
+    for s in range(warmup):
+        fs.sample_fused(H, W, temp, seed=1234, offset=offset0 + s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with fs.KernelTimer() as kt:
+        e0.record()
+        for s in range(steps):
+            fs.sample_fused(H, W, temp, seed=1234, offset=offset0 + warmup + s)
+        e1.record()
+        torch.cuda.synchronize()
+    total = e0.elapsed_time(e1)
+    n = max(1, kt.calls)
+    return total / steps, kt.stage1_ms / n, kt.stage2_ms / n
+
+
+def time_region(torch, fn, steps, warmup):
+    for s in range(warmup):
+        fn(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        fn(warmup + s)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--sweep", default="1,8,32", help="extra batch sizes reported beside B")
+    ap.add_argument("--only-fused", action="store_true",
+                    help="time the fused step only (no sweep, baselines or CPU oracle)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
+              "(sharding the vocabulary across GPUs is not built).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import decode_exact_categorical_amd as fs
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    B = args.batch
+    sweep = [int(x) for x in args.sweep.split(",") if x] if not args.only_fused else []
+    Bmax = max([B] + sweep)
+
+    log(f"device {props.name} ({cus} CUs); generating W [{VOCAB}, {D_MODEL}] bf16 on the host")
+    W_h = synthetic.weight(VOCAB, D_MODEL, std=0.02)
+    H_h = synthetic.hidden(Bmax, D_MODEL)
+    T_h = synthetic.temperatures(Bmax)
+    W = W_h.to(dev)
+    H = H_h.to(dev)
+    temp = T_h.to(dev)
+    torch.cuda.synchronize()
+
+    nT = fused_tiles(VOCAB, cus)
+    log(f"timing fused step B={B}: {args.warmup} warmup + {args.steps} timed steps")
+    t0 = time.perf_counter()
+    ms_step, s1_ms, s2_ms = time_fused(fs, torch, H[:B].contiguous(), W, temp[:B].contiguous(),
+                                       args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    us_step = ms_step * 1e3
+    step_bytes = step_alg_bytes(B, D_MODEL, VOCAB, nT)
+    s1_bytes = stage1_alg_bytes(B, D_MODEL, VOCAB, nT)
+    s1_gbs = s1_bytes / (s1_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(us_step, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) H, N(0,0.02) W, U[0.5,1.2] temperatures)",
+        "config": {
+            "workload": "fused LM-head matmul + exact Gumbel-max sampling, one decode step",
+            "global_batch": B, "D": D_MODEL, "V": VOCAB, "noise": "fp32 (23-bit Philox uniforms)",
+            "temperature": "per row U[0.5,1.2]", "bias": None, "seed": 1234,
+            "offset": "advances every step",
+        },
+        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "hbm_gbs_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "fused_stage1_kernel (matmul + transform + noise + tile argmax)",
+            "bound": "hbm",
+            "achieved": round(s1_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(s1_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": s1_bytes,
+            "avg_launch_us": round(s1_ms * 1e3, 2),
+        },
+        "stage2_avg_us": round(s2_ms * 1e3, 2),
+        "timed_wall_s": round(wall, 3),
+    }
+
+    if not args.only_fused:
+        per = {}
+        for b in sweep:
+            ms, a1, a2 = time_fused(fs, torch, H[:b].contiguous(), W, temp[:b].contiguous(),
+                                    max(20, args.steps // 2), args.warmup, offset0=10**6)
+            per[str(b)] = {"us_per_step": round(ms * 1e3, 2),
+                           "stage1_us": round(a1 * 1e3, 2),
+                           "stage1_gbs": round(stage1_alg_bytes(b, D_MODEL, VOCAB, nT) / (a1 * 1e-3) / 1e9, 1),
+                           "tokens_per_s": round(b / (ms * 1e-3), 1)}
+            log(f"  B={b}: {per[str(b)]}")
+        result["batch_sweep"] = per
+
+        # Baselines on the same data: (1) unfused: rocBLAS/hipBLASLt GEMM writes bf16
+        # logits to HBM, then the standalone sampler; (2) softmax + multinomial.
+        Hb, Tb = H[:B].contiguous(), temp[:B].contiguous()
+        log("timing unfused baselines")
+
+        def unfused(s):
+            y = torch.matmul(Hb, W.t())
+            return fs.sample_logits(y.float(), Tb, seed=1234, offset=s)
+
+        def conventional(s):
+            y = torch.matmul(Hb, W.t()).float()
+            p = torch.softmax(y / Tb[:, None], dim=-1)
+            return torch.multinomial(p, 1)
+
+        def gemm_only(s):
+            return torch.matmul(Hb, W.t())
+
+        n_base = max(20, args.steps // 2)
+        base = {
+            "gemm_plus_fs_sample_logits_us": round(time_region(torch, unfused, n_base, 10) * 1e3, 2),
+            "gemm_softmax_multinomial_us": round(time_region(torch, conventional, n_base, 10) * 1e3, 2),
+            "gemm_only_us": round(time_region(torch, gemm_only, n_base, 10) * 1e3, 2),
+        }
+        base["fused_speedup_vs_gemm_plus_sampler"] = round(base["gemm_plus_fs_sample_logits_us"] / us_step, 3)
+        base["fused_speedup_vs_softmax_multinomial"] = round(base["gemm_softmax_multinomial_us"] / us_step, 3)
+        result["baselines"] = base
+        log(f"  {base}")
+
+    if not args.only_fused and not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.num_threads()
+        log(f"CPU oracle: one full decode step B={B} on {threads} threads")
+        offset = 4242
+        got = fs.sample_fused(H[:B].contiguous(), W, temp[:B].contiguous(), seed=1234, offset=offset)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ref, gap, _ = oracle.sample_fused(H_h[:B], W_h, T_h[:B].numpy(), seed=1234, offset=offset)
+        cpu_s = time.perf_counter() - t0
+        got = got.cpu().numpy()
+        decided = gap > 1e-3
+        result["cpu_baseline"] = {
+            "value": round(cpu_s * 1e6, 1),
+            "unit": "us/step",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"one full decode step: B={B}, D={D_MODEL}, V={VOCAB}, all rows, float64",
+        }
+        result["step_parity_vs_oracle"] = {
+            "decided_rows": int(decided.sum()),
+            "decided_rows_equal": int((got[decided] == ref[decided]).sum()),
+            "near_tie_rows": int((~decided).sum()),
+        }
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

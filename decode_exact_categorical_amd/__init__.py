@@ -1,0 +1,233 @@
+"""Exact categorical sampling fused into the LM head, for AMD MI355X (gfx950).
+
+Thin Python binding over ``libfsample.so`` (C ABI in ``include/fsample.h``).
+Every step of the sampling path runs in the library's HIP kernels; this module
+only checks tensor arguments, finds the current HIP stream, keeps a workspace
+per (device, stream), and passes raw pointers.  PyTorch provides device memory
+and streams.  If the library has not been built, every call raises.
+
+    tok = sample_fused(H, W, temp, bias=None, seed=1234, offset=step)   # [B] int64
+    tok = sample_logits(logits, temp, seed=1234, offset=step, fp64_noise=True)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "FS_FP64_NOISE", "FSampleError", "sample_fused", "sample_logits", "workspace_bytes",
+    "debug_philox_words", "debug_logits", "library_path", "load_library", "KernelTimer",
+]
+
+FS_FP64_NOISE = 0x1
+_STATUS = {0: "FS_OK", 1: "FS_ERR_INVALID_ARG", 2: "FS_ERR_UNSUPPORTED", 3: "FS_ERR_WORKSPACE",
+           4: "FS_ERR_HIP"}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfsample.so")
+_lib = None
+_lock = threading.Lock()
+_workspaces: dict = {}
+
+
+class FSampleError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {detail}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfsample.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built: run `python __graft_entry__.py` "
+                               "or decode_exact_categorical_amd.build.build()")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, i64, u64, u32, sz, i32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                     ctypes.c_uint32, ctypes.c_size_t, ctypes.c_int)
+        lib.fs_workspace_bytes.restype = sz
+        lib.fs_workspace_bytes.argtypes = [i64, i64, u32]
+        lib.fs_sample_fused.restype = i32
+        lib.fs_sample_fused.argtypes = [P, P, i64, i64, i64, P, P, u64, u64, P, P, u32, P, sz, P]
+        lib.fs_sample_logits.restype = i32
+        lib.fs_sample_logits.argtypes = [P, i64, i64, P, u64, u64, i32, P, P, P, sz, P]
+        lib.fs_status_string.restype = ctypes.c_char_p
+        lib.fs_status_string.argtypes = [i32]
+        lib.fs_last_error.restype = ctypes.c_char_p
+        lib.fs_last_error.argtypes = []
+        lib.fs_debug_philox_words.restype = i32
+        lib.fs_debug_philox_words.argtypes = [u64, u64, P, i64, i64, P, P]
+        lib.fs_profile_begin.restype = i32
+        lib.fs_profile_begin.argtypes = []
+        lib.fs_profile_end.restype = i32
+        lib.fs_profile_end.argtypes = [P, P, P]
+        lib.fs_debug_logits.restype = i32
+        lib.fs_debug_logits.argtypes = [P, P, i64, i64, i64, P, P]
+        _lib = lib
+        return lib
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        detail = load_library().fs_last_error().decode(errors="replace")
+        raise FSampleError(status, fn, detail)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _temp_tensor(temp, B: int, device) -> torch.Tensor:
+    if isinstance(temp, (int, float)):
+        return torch.full((B,), float(temp), dtype=torch.float32, device=device)
+    _need(temp, "temp", torch.float32, device, (B,))
+    return temp
+
+
+def _row_ids(row_ids, B: int, device):
+    if row_ids is None:
+        return None
+    if row_ids.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise TypeError("row_ids must be int32 (read as uint32)")
+    _need(row_ids, "row_ids", row_ids.dtype, device, (B,))
+    return row_ids
+
+
+def workspace_bytes(B: int, V: int, fp64_noise: bool = False) -> int:
+    return int(load_library().fs_workspace_bytes(B, V, FS_FP64_NOISE if fp64_noise else 0))
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A cached uint8 workspace for the current stream of `device` (stream-ordered reuse)."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def sample_fused(H: torch.Tensor, W: torch.Tensor, temp, bias: torch.Tensor | None = None, *,
+                 seed: int, offset: int, row_ids: torch.Tensor | None = None,
+                 fp64_noise: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One exact draw per row from softmax((H W^T + bias) / temp); [B] int64 (-1: no token)."""
+    lib = load_library()
+    dev = H.device
+    if dev.type != "cuda":
+        raise ValueError("H must be a GPU tensor")
+    if H.dim() != 2 or W.dim() != 2:
+        raise ValueError("H must be [B, D] and W [V, D]")
+    B, D = H.shape
+    V = W.shape[0]
+    _need(H, "H", torch.bfloat16, dev, (B, D))
+    _need(W, "W", torch.bfloat16, dev, (V, D))
+    t = _temp_tensor(temp, B, dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (B, V))
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B,))
+    flags = FS_FP64_NOISE if fp64_noise else 0
+    need = int(lib.fs_workspace_bytes(B, V, flags)) if V > 0 else 0
+    ws = _workspace(dev, need)
+    st = lib.fs_sample_fused(_ptr(H), _ptr(W), B, D, V, _ptr(t), _ptr(bias), seed, offset,
+                             _ptr(out), _ptr(rid), flags, _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "fs_sample_fused")
+    return out
+
+
+def sample_logits(logits: torch.Tensor, temp, *, seed: int, offset: int,
+                  row_ids: torch.Tensor | None = None, fp64_noise: bool = False,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """One exact draw per row from softmax(logits / temp) over float32 logits [B, V]."""
+    lib = load_library()
+    dev = logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    B, V = logits.shape
+    _need(logits, "logits", torch.float32, dev, (B, V))
+    t = _temp_tensor(temp, B, dev)
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B,))
+    need = int(lib.fs_workspace_bytes(B, V, FS_FP64_NOISE if fp64_noise else 0)) if V > 0 else 0
+    ws = _workspace(dev, need)
+    st = lib.fs_sample_logits(_ptr(logits), B, V, _ptr(t), seed, offset, int(bool(fp64_noise)),
+                              _ptr(out), _ptr(rid), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "fs_sample_logits")
+    return out
+
+
+class KernelTimer:
+    """Context manager: summed Stage 1 / Stage 2 kernel milliseconds of the sampling
+    calls made inside it, from HIP events the library records on each call's stream."""
+
+    def __enter__(self):
+        _check(load_library().fs_profile_begin(), "fs_profile_begin")
+        self.stage1_ms = self.stage2_ms = 0.0
+        self.calls = 0
+        return self
+
+    def __exit__(self, *exc):
+        a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+        _check(load_library().fs_profile_end(ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)),
+               "fs_profile_end")
+        self.stage1_ms, self.stage2_ms, self.calls = a.value, b.value, n.value
+        return False
+
+
+def debug_philox_words(seed: int, offset: int, B: int, n_ctr: int, *,
+                       row_ids: torch.Tensor | None = None, device="cuda") -> torch.Tensor:
+    """int32 view of the uint32 words [B, n_ctr, 4] the samplers draw from (test hook)."""
+    lib = load_library()
+    dev = torch.device(device)
+    rid = _row_ids(row_ids, B, dev)
+    out = torch.empty((B, n_ctr, 4), dtype=torch.int32, device=dev)
+    _check(lib.fs_debug_philox_words(seed, offset, _ptr(rid), B, n_ctr, _ptr(out), _stream(dev)),
+           "fs_debug_philox_words")
+    return out
+
+
+def debug_logits(H: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
+    """float32 [B, V] logits from the fused path's matmul code (test hook)."""
+    lib = load_library()
+    dev = H.device
+    B, D = H.shape
+    V = W.shape[0]
+    _need(H, "H", torch.bfloat16, dev, (B, D))
+    _need(W, "W", torch.bfloat16, dev, (V, D))
+    Y = torch.empty((B, V), dtype=torch.float32, device=dev)
+    _check(lib.fs_debug_logits(_ptr(H), _ptr(W), B, D, V, _ptr(Y), _stream(dev)),
+           "fs_debug_logits")
+    return Y

@@ -1,0 +1,296 @@
+// fs_api.hip -- the C ABI of libfsample.so (declared and documented in
+// include/fsample.h): argument checks on the host, workspace sizing, and the
+// Stage 1 + Stage 2 launches on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "fs_launch.hpp"
+#include "fsample.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fs_status fail(fs_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fs_status hip_fail(hipError_t e, const char* what) {
+  return fail(FS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxV = (int64_t)1 << 31;  // indices are int32 inside the kernels
+constexpr int kMaxDevices = 64;
+constexpr int kAssumedCUs = 256;  // MI355X; sizes the workspace without a device query
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxFusedB = (int64_t)1 << 22;  // 65536 batch tiles of 64 along grid y
+
+// ---- kernel timing (fs_profile_begin / fs_profile_end) ----
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;  // 3 events per timed call
+  size_t used = 0;               // calls recorded since begin
+  static constexpr size_t kMaxCalls = 4096;
+};
+Profiler g_prof;
+
+// Events (start, after stage 1, after stage 2) for one call, or null if not timing.
+hipEvent_t* prof_slot() {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (!g_prof.on || g_prof.used >= Profiler::kMaxCalls) return nullptr;
+  const size_t need = 3 * (g_prof.used + 1);
+  while (g_prof.pool.size() < need) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_prof.pool.push_back(e);
+  }
+  hipEvent_t* slot = &g_prof.pool[3 * g_prof.used];
+  ++g_prof.used;
+  return slot;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t cand_bytes(uint32_t flags) { return (flags & FS_FP64_NOISE) ? 16 : 8; }
+
+int logits_tiles(int64_t V) { return (int)((V + fs::kLogitsChunk - 1) / fs::kLogitsChunk); }
+
+// Compute units of the current device, cached per device (first call queries).
+fs_status device_cus(int* cus) {
+  static int cached[kMaxDevices] = {0};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FS_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    if (n > kAssumedCUs) n = kAssumedCUs;  // workspace is sized for this many
+    cached[dev] = n > 0 ? n : 1;
+  }
+  *cus = cached[dev];
+  return FS_OK;
+}
+
+fs_status check_sizes(int64_t B, int64_t V) {
+  if (B < 0) return fail(FS_ERR_INVALID_ARG, "B = %lld is negative", (long long)B);
+  if (V < 1 || V >= kMaxV) return fail(FS_ERR_INVALID_ARG, "V = %lld outside [1, 2^31)", (long long)V);
+  if (B > ((int64_t)1 << 31) / 1) return fail(FS_ERR_INVALID_ARG, "B = %lld too large", (long long)B);
+  return FS_OK;
+}
+
+fs_status check_workspace(void* ws, size_t have, int64_t B, int64_t V, uint32_t flags) {
+  const size_t need = fs_workspace_bytes(B, V, flags);
+  if (ws == nullptr || have < need)
+    return fail(FS_ERR_WORKSPACE, "workspace %p of %zu bytes, need %zu", ws, have, need);
+  if (((uintptr_t)ws & 15u) != 0) return fail(FS_ERR_WORKSPACE, "workspace not 16-byte aligned");
+  return FS_OK;
+}
+
+fs_status check_fused(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D, int64_t V) {
+  fs_status s = check_sizes(B, V);
+  if (s != FS_OK) return s;
+  if (B > kMaxFusedB) return fail(FS_ERR_UNSUPPORTED, "B = %lld > 2^22", (long long)B);
+  if (D < 1) return fail(FS_ERR_INVALID_ARG, "D = %lld must be positive", (long long)D);
+  if (D % 8 != 0) return fail(FS_ERR_UNSUPPORTED, "D = %lld is not a multiple of 8", (long long)D);
+  if (D > ((int64_t)1 << 24)) return fail(FS_ERR_UNSUPPORTED, "D = %lld too large", (long long)D);
+  if (B > 0 && (H == nullptr || W == nullptr)) return fail(FS_ERR_INVALID_ARG, "H or W is null");
+  if (B > 0 && (!aligned16(H) || !aligned16(W)))
+    return fail(FS_ERR_UNSUPPORTED, "H and W must be 16-byte aligned");
+  return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fs_workspace_bytes(int64_t B, int64_t V, uint32_t flags) {
+  if (B < 0 || V < 1 || V >= kMaxV) return 0;
+  int64_t tiles = fs::fused_num_tiles(V, kAssumedCUs);
+  const int64_t lt = logits_tiles(V);
+  if (lt > tiles) tiles = lt;
+  const size_t bytes = (size_t)B * (size_t)tiles * cand_bytes(flags);
+  return (bytes + kAlign - 1) / kAlign * kAlign + kAlign;
+}
+
+const char* fs_status_string(fs_status status) {
+  switch (status) {
+    case FS_OK: return "FS_OK";
+    case FS_ERR_INVALID_ARG: return "FS_ERR_INVALID_ARG: invalid argument";
+    case FS_ERR_UNSUPPORTED: return "FS_ERR_UNSUPPORTED: unsupported size or alignment";
+    case FS_ERR_WORKSPACE: return "FS_ERR_WORKSPACE: workspace missing or too small";
+    case FS_ERR_HIP: return "FS_ERR_HIP: HIP runtime error";
+  }
+  return "unknown fs_status";
+}
+
+const char* fs_last_error(void) { return g_last_error; }
+
+fs_status fs_sample_fused(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D, int64_t V,
+                          const float* temp, const float* bias, uint64_t seed, uint64_t offset,
+                          int64_t* out_idx, const uint32_t* row_ids, uint32_t flags,
+                          void* workspace, size_t workspace_bytes, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_fused(H, W, B, D, V);
+  if (s != FS_OK) return s;
+  if (flags & ~FS_FP64_NOISE) return fail(FS_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (B == 0) return FS_OK;
+  if (temp == nullptr || out_idx == nullptr) return fail(FS_ERR_INVALID_ARG, "temp or out_idx is null");
+  s = check_workspace(workspace, workspace_bytes, B, V, flags);
+  if (s != FS_OK) return s;
+
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != FS_OK) return s;
+  const bool fp64 = (flags & FS_FP64_NOISE) != 0;
+  fs::FusedArgs a;
+  a.H = H;
+  a.W = W;
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.temp = temp;
+  a.bias = bias;
+  a.row_ids = row_ids;
+  a.key = fs::make_key(seed, offset);
+  a.cand = workspace;
+  a.nT = fs::fused_num_tiles(V, cus);
+  a.Y = nullptr;
+  a.bias_vec4 = bias != nullptr && aligned16(bias) && (V % 4 == 0);
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  if (ev) (void)hipEventRecord(ev[0], st);
+  hipError_t e = fs::launch_fused_stage1(a, fp64 ? fs::kEpiSample64 : fs::kEpiSample32, st);
+  if (e != hipSuccess) return hip_fail(e, "fused stage 1 launch");
+  if (ev) (void)hipEventRecord(ev[1], st);
+  e = fs::launch_stage2(workspace, B, a.nT, fp64, out_idx, st);
+  if (e != hipSuccess) return hip_fail(e, "stage 2 launch");
+  if (ev) (void)hipEventRecord(ev[2], st);
+  return FS_OK;
+}
+
+fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const float* temp,
+                           uint64_t seed, uint64_t offset, int fp64_noise, int64_t* out_idx,
+                           const uint32_t* row_ids, void* workspace, size_t workspace_bytes,
+                           fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_sizes(B, V);
+  if (s != FS_OK) return s;
+  if (B == 0) return FS_OK;
+  if (logits == nullptr || temp == nullptr || out_idx == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "logits, temp or out_idx is null");
+  if (((uintptr_t)logits & 3u) != 0) return fail(FS_ERR_UNSUPPORTED, "logits not 4-byte aligned");
+  const int nT = logits_tiles(V);
+  if ((int64_t)B * nT >= ((int64_t)1 << 31))
+    return fail(FS_ERR_INVALID_ARG, "B * ceil(V / %d) exceeds 2^31", fs::kLogitsChunk);
+  const uint32_t flags = fp64_noise ? FS_FP64_NOISE : 0u;
+  s = check_workspace(workspace, workspace_bytes, B, V, flags);
+  if (s != FS_OK) return s;
+
+  fs::LogitsArgs a;
+  a.X = logits;
+  a.B = B;
+  a.V = V;
+  a.temp = temp;
+  a.row_ids = row_ids;
+  a.key = fs::make_key(seed, offset);
+  a.cand = workspace;
+  a.nT = nT;
+  a.vec4 = aligned16(logits) && (V % 4 == 0);
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  if (ev) (void)hipEventRecord(ev[0], st);
+  hipError_t e = fs::launch_logits_stage1(a, fp64_noise != 0, st);
+  if (e != hipSuccess) return hip_fail(e, "logits stage 1 launch");
+  if (ev) (void)hipEventRecord(ev[1], st);
+  e = fs::launch_stage2(workspace, B, nT, fp64_noise != 0, out_idx, st);
+  if (e != hipSuccess) return hip_fail(e, "stage 2 launch");
+  if (ev) (void)hipEventRecord(ev[2], st);
+  return FS_OK;
+}
+
+fs_status fs_profile_begin(void) {
+  g_last_error[0] = 0;
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  g_prof.on = true;
+  g_prof.used = 0;
+  return FS_OK;
+}
+
+fs_status fs_profile_end(double* stage1_ms, double* stage2_ms, int64_t* calls) {
+  g_last_error[0] = 0;
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  double t1 = 0.0, t2 = 0.0;
+  fs_status status = FS_OK;
+  for (size_t c = 0; c < g_prof.used; ++c) {
+    hipEvent_t* ev = &g_prof.pool[3 * c];
+    float a = 0.f, b = 0.f;
+    hipError_t e = hipEventSynchronize(ev[2]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&a, ev[0], ev[1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&b, ev[1], ev[2]);
+    if (e != hipSuccess) {
+      status = hip_fail(e, "profile events");
+      break;
+    }
+    t1 += a;
+    t2 += b;
+  }
+  if (stage1_ms) *stage1_ms = t1;
+  if (stage2_ms) *stage2_ms = t2;
+  if (calls) *calls = (int64_t)g_prof.used;
+  g_prof.on = false;
+  g_prof.used = 0;
+  return status;
+}
+
+fs_status fs_debug_philox_words(uint64_t seed, uint64_t offset, const uint32_t* row_ids,
+                                int64_t B, int64_t n_ctr, uint32_t* out, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  if (B < 0 || n_ctr < 0) return fail(FS_ERR_INVALID_ARG, "negative size");
+  if (B == 0 || n_ctr == 0) return FS_OK;
+  if (B > (((int64_t)1 << 31) - 1) / n_ctr) return fail(FS_ERR_INVALID_ARG, "B * n_ctr >= 2^31");
+  if (out == nullptr) return fail(FS_ERR_INVALID_ARG, "out is null");
+  if (!aligned16(out)) return fail(FS_ERR_UNSUPPORTED, "out not 16-byte aligned");
+  hipError_t e = fs::launch_philox_words(fs::make_key(seed, offset), row_ids, B, n_ctr, out,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "philox words launch");
+  return FS_OK;
+}
+
+fs_status fs_debug_logits(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D, int64_t V,
+                          float* Y, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_fused(H, W, B, D, V);
+  if (s != FS_OK) return s;
+  if (B == 0) return FS_OK;
+  if (Y == nullptr) return fail(FS_ERR_INVALID_ARG, "Y is null");
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != FS_OK) return s;
+  fs::FusedArgs a;
+  memset(&a, 0, sizeof a);
+  a.H = H;
+  a.W = W;
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.nT = fs::fused_num_tiles(V, cus);
+  a.Y = Y;
+  hipError_t e = fs::launch_fused_stage1(a, fs::kEpiStore, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fused logits launch");
+  return FS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// fs_launch.hpp -- host-side launch entry points of the gfx950 kernels (internal;
+// the public C ABI is include/fsample.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fs_device.hpp"
+
+namespace fs {
+
+// Fused Stage 1 (matmul + transform + noise + per-tile argmax) and its
+// logits-store twin.
+struct FusedArgs {
+  const uint16_t* H;  // [B, D] bf16
+  const uint16_t* W;  // [V, D] bf16
+  int64_t B, D, V;
+  const float* temp;       // [B]
+  const float* bias;       // [B, V] or null
+  const uint32_t* row_ids;  // [B] or null
+  NoiseKey key;
+  void* cand;  // [B, nT] candidates
+  int nT;      // vocabulary tiles = workgroups along x
+  float* Y;    // [B, V] (store epilogue only)
+  int bias_vec4;  // bias rows are 16-byte aligned
+};
+
+enum FusedEpilogue { kEpiSample32 = 0, kEpiSample64 = 1, kEpiStore = 2 };
+
+// Number of vocabulary tiles (workgroups along x) the fused kernel uses.
+int fused_num_tiles(int64_t V, int num_cus);
+hipError_t launch_fused_stage1(const FusedArgs& a, int epilogue, hipStream_t stream);
+
+// Standalone Stage 1 over float32 logits.
+constexpr int kLogitsChunk = 2048;  // logits per workgroup
+struct LogitsArgs {
+  const float* X;  // [B, V]
+  int64_t B, V;
+  const float* temp;
+  const uint32_t* row_ids;
+  NoiseKey key;
+  void* cand;  // [B, nT]
+  int nT;      // ceil(V / kLogitsChunk)
+  int vec4;    // rows 16-byte aligned
+};
+hipError_t launch_logits_stage1(const LogitsArgs& a, bool fp64, hipStream_t stream);
+
+// Stage 2: per row, the best of its nT candidates -> out_idx.
+hipError_t launch_stage2(const void* cand, int64_t B, int nT, bool fp64, int64_t* out,
+                         hipStream_t stream);
+
+// Test hook: Philox words.
+hipError_t launch_philox_words(NoiseKey key, const uint32_t* row_ids, int64_t B,
+                               int64_t n_ctr, uint32_t* out, hipStream_t stream);
+
+}  // namespace fs

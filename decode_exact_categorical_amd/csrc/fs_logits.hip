@@ -1,0 +1,100 @@
+// fs_logits.hip -- standalone exact sampler over materialised float32 logits,
+// Stage 1, for gfx950.
+//
+// The Megatron-LM "fp64 sampling noise" page ("Cost") notes that its sampler
+// materialises the noise and the ratio p/E in HBM, and that one program per
+// row is latency-bound at small batch.  Here the noise is generated in
+// registers and each row is split over ceil(V / 2048) workgroups, each
+// reducing 2048 logits to one (score, index) candidate; Stage 2
+// (fs_reduce.hip) picks each row's winner.  Same transform, noise stream
+// and tie rule as the fused path, so equal y + bias gives equal draws.
+#include <type_traits>
+
+#include "fs_launch.hpp"
+
+namespace fs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kIters = kLogitsChunk / (4 * kThreads);  // float4 groups per thread
+
+template <bool FP64>
+__global__ __launch_bounds__(kThreads) void logits_stage1_kernel(LogitsArgs a) {
+  typedef typename std::conditional<FP64, double, float>::type T;
+  const int64_t b = (int64_t)blockIdx.x / a.nT;
+  const int chunk = (int)((int64_t)blockIdx.x - b * a.nT);
+  const int64_t V = a.V;
+  const float t = a.temp[b];
+  const bool greedy = !(t > 0.0f);  // uniform across the workgroup
+  const T inv_t = greedy ? T(1) : T(1) / T(t);
+  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
+  const float* x = a.X + b * V;
+
+  T bm = neg_inf<T>();
+  int32_t bi = kNoIndex;
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t i0 = (int64_t)chunk * kLogitsChunk + 4 * (threadIdx.x + kThreads * it);
+    if (i0 >= V) break;
+    float y[4];
+    if (a.vec4 && i0 + 3 < V) {
+      const float4 v = *reinterpret_cast<const float4*>(x + i0);
+      y[0] = v.x; y[1] = v.y; y[2] = v.z; y[3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = (i0 + j < V) ? x[i0 + j] : neg_inf<float>();
+    }
+    T s[4];
+    if (greedy) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j] = T(y[j]);
+    } else if (!FP64) {
+      const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), rid);
+      s[0] = T(y[0] * inv_t) + T(gumbel_f32(w.w0));
+      s[1] = T(y[1] * inv_t) + T(gumbel_f32(w.w1));
+      s[2] = T(y[2] * inv_t) + T(gumbel_f32(w.w2));
+      s[3] = T(y[3] * inv_t) + T(gumbel_f32(w.w3));
+    } else {
+      const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), rid);
+      const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, rid);
+      s[0] = T(y[0]) * inv_t + T(gumbel_f64(w0.w0, w0.w1));
+      s[1] = T(y[1]) * inv_t + T(gumbel_f64(w0.w2, w0.w3));
+      s[2] = T(y[2]) * inv_t + T(gumbel_f64(w1.w0, w1.w1));
+      s[3] = T(y[3]) * inv_t + T(gumbel_f64(w1.w2, w1.w3));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t i = (int32_t)(i0 + j);
+      if (i0 + j < V && beats(s[j], i, bm, bi)) {
+        bm = s[j];
+        bi = i;
+      }
+    }
+  }
+
+  wave_argmax_xor(bm, bi, 0);
+  __shared__ Cand<T> wbest[kThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) wbest[wave] = Cand<T>{bm, bi};
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Cand<T> best = wbest[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w)
+      if (beats(wbest[w].m, wbest[w].idx, best.m, best.idx)) best = wbest[w];
+    reinterpret_cast<Cand<T>*>(a.cand)[b * a.nT + chunk] = best;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_logits_stage1(const LogitsArgs& a, bool fp64, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.B * a.nT));
+  if (fp64)
+    hipLaunchKernelGGL(logits_stage1_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(logits_stage1_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fs

@@ -1,0 +1,187 @@
+/*
+ * fsample.h -- C ABI of libfsample.so: exact categorical sampling fused into an
+ * LM-head matmul, and the standalone sampler over materialised logits, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Citations name the page and the section that defines each operation:
+ *   [FS]  "FlashSampling: fast and memory-efficient exact sampling" (paper
+ *         summary page), sections "core method" and "algorithm details"
+ *         (Stage 1 steps (1)-(6); Stage 2).
+ *   [MG]  Megatron-LM pull request "fp64 sampling noise", sections "Problem"
+ *         and "The change".
+ *   [SD]  spec-decode-ops kernel card, sections "Usage", "API" and
+ *         "Measured behavior" (determinism).
+ *   [SK]  "Write Triton Sampling Kernel" skill page, "Required reasoning
+ *         process" items 3-4 and 10, "Correctness requirements".
+ *
+ * Conventions shared by every entry point
+ *   Pointers.   Arguments documented as "device" are device (HBM) pointers the
+ *               caller allocated; arguments documented as "host" are plain host
+ *               values.  The library allocates nothing per call and keeps no
+ *               pointer after it returns.
+ *   Layouts.    All matrices are row-major and dense: a row of n elements is
+ *               followed immediately by the next row.  bf16 values are passed
+ *               as their 16-bit patterns (fs_bf16).
+ *   Streams.    Work is enqueued on `stream` (a hipStream_t; NULL means the
+ *               default stream) and the call returns without synchronising.
+ *               Outputs are valid once that stream has reached the work.
+ *   Errors.     Every call returns an fs_status.  Arguments are checked on the
+ *               host before any HIP call, so an invalid call enqueues nothing
+ *               and leaves every output untouched.  FS_ERR_HIP reports a launch
+ *               failure (the HIP error text is available from fs_last_error()).
+ *               No call inspects device data: temperatures, biases and logits
+ *               of any value are legal and have the meaning defined below.
+ *   Determinism. For fixed inputs, seed, offset, row ids and flags, outputs
+ *               are bitwise identical from call to call, independent of the
+ *               batch position of a row, of other rows in the batch and of
+ *               concurrent work on other streams [MG "Tests"; SD determinism].
+ *               The caller advances `offset` every decode step [SK item 10].
+ *
+ * Sampling rule (both entry points), per batch row b with logical row id
+ * r = row_ids ? row_ids[b] : b, temperature t = temp[b]:
+ *   if t > 0:   s_i = (y_i + bias_i) / t + g_i              [FS (2)-(4); SK 4]
+ *   otherwise (t <= 0 or NaN, greedy): s_i = y_i + bias_i   [SK 3]
+ *   out_idx[b] = the smallest i with the largest s_i among the s_i that are
+ *   neither NaN nor -inf, or -1 if there is none            [FS (5), Stage 2]
+ * where g_i = -log(-log u_i) is Gumbel noise of a midpoint-grid uniform u_i
+ * drawn by Philox4x32-10 with key (seed lo, seed hi) and counter
+ * (j, r, offset lo, offset hi) [MG "The change"]:
+ *   default noise:  j = i >> 2, word i & 3, u = (top 23 bits + 1/2) / 2^23;
+ *   FS_FP64_NOISE:  j = i >> 1, words 2(i&1) and 2(i&1)+1, u = (top 52 bits of
+ *                   their concatenation + 1/2) / 2^52, and the score is formed
+ *                   in float64 (noise in [1.1e-16, 36.7], a tail of about 40
+ *                   rather than 20 nats [MG "What does this PR do"]).
+ * This is an exact draw from softmax((y + bias) / t) [FS prerequisites].
+ */
+#ifndef FSAMPLE_H
+#define FSAMPLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fs_status {
+    FS_OK = 0,
+    FS_ERR_INVALID_ARG = 1, /* null required pointer, non-positive size, V >= 2^31 */
+    FS_ERR_UNSUPPORTED = 2, /* D not a multiple of 8, H/W not 16-byte aligned, B > 2^22 (fused) */
+    FS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fs_workspace_bytes() */
+    FS_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} fs_status;
+
+typedef uint16_t fs_bf16;   /* bfloat16 bit pattern */
+typedef void *fs_stream_t;  /* hipStream_t */
+
+/* flags for fs_sample_fused and fs_workspace_bytes */
+#define FS_FP64_NOISE 0x1u
+
+/*
+ * Bytes of device workspace the sampling calls need for a batch of B rows over
+ * a vocabulary of V entries (covers both fs_sample_fused and fs_sample_logits;
+ * pass FS_FP64_NOISE in flags if either call will use float64 noise).  The
+ * workspace holds the per-tile candidates (m, idx) of Stage 1 [FS Stage 1
+ * step (6)]; the caller allocates it, may reuse it across calls on one stream,
+ * and must not share it between calls that can run concurrently.  Host only;
+ * returns 0 for invalid sizes.
+ */
+size_t fs_workspace_bytes(int64_t B, int64_t V, uint32_t flags);
+
+/*
+ * Fused LM-head + exact sampling [FS "core method", "algorithm details"].
+ *   H        device, bf16 [B, D]   hidden states of the decode batch
+ *   W        device, bf16 [V, D]   LM-head weight (nn.Linear layout)
+ *   B, D, V  host sizes: 0 <= B <= 2^22 (0 is a no-op), D >= 8 with
+ *            D % 8 == 0, 1 <= V < 2^31
+ *   temp     device, float [B]     per-row temperature (see the sampling rule)
+ *   bias     device, float [B, V] or NULL: additive logit bias; -inf masks a
+ *            token.  Added before the division by temperature [SK item 4].
+ *   seed, offset  host: Philox key and the decode-step/position counter words
+ *   out_idx  device, int64 [B]     sampled token per row, or -1
+ *   row_ids  device, uint32 [B] or NULL (then row b has logical id b): the row
+ *            identity the noise is keyed by, so that a row's draw does not depend
+ *            on its batch position [MG "The change"]
+ *   flags    host: 0 or FS_FP64_NOISE
+ *   workspace, workspace_bytes  device scratch of at least
+ *            fs_workspace_bytes(B, V, flags) bytes
+ *   stream   hipStream_t
+ * Computes y = H W^T tile by tile on chip (bf16 inputs, float32 accumulation)
+ * and never writes the [B, V] logits: Stage 1 keeps each row's per-tile
+ * (max score, index), Stage 2 reduces those to out_idx [FS Stage 1, Stage 2].
+ * H and W must be 16-byte aligned.
+ */
+fs_status fs_sample_fused(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t D,
+                          int64_t V, const float *temp, const float *bias,
+                          uint64_t seed, uint64_t offset, int64_t *out_idx,
+                          const uint32_t *row_ids, uint32_t flags, void *workspace,
+                          size_t workspace_bytes, fs_stream_t stream);
+
+/*
+ * Standalone exact sampler over materialised float32 logits [MG "Problem",
+ * "The change"; SD "Usage" sample(logits, temperature, seed, offset)].
+ *   logits   device, float [B, V]  y_i of each row (no bias term)
+ *   B, V     host sizes: B >= 0 (0 is a no-op), 1 <= V < 2^31
+ *   temp     device, float [B]
+ *   seed, offset  host
+ *   fp64_noise    host: nonzero selects float64 race noise (52-bit uniforms
+ *            from two Philox words) [MG "The change"]
+ *   out_idx  device, int64 [B]
+ *   row_ids  device, uint32 [B] or NULL
+ *   workspace, workspace_bytes  as for fs_sample_fused (size it with
+ *            FS_FP64_NOISE when fp64_noise is set)
+ *   stream   hipStream_t
+ * Same rule and the same Philox stream as fs_sample_fused, given the same
+ * y + bias: the draw for (row id, vocabulary index) is identical in both.
+ */
+fs_status fs_sample_logits(const float *logits, int64_t B, int64_t V, const float *temp,
+                           uint64_t seed, uint64_t offset, int fp64_noise,
+                           int64_t *out_idx, const uint32_t *row_ids, void *workspace,
+                           size_t workspace_bytes, fs_stream_t stream);
+
+/*
+ * Kernel timing.  Between fs_profile_begin() and fs_profile_end(), every
+ * fs_sample_fused and fs_sample_logits call also records HIP events on its
+ * stream around its Stage 1 and its Stage 2 launch (the FlashSampling page,
+ * "reproduction", times kernels the same way: per-kernel device timestamps).
+ * fs_profile_end() waits for those events, writes the summed Stage 1 and
+ * Stage 2 durations in milliseconds and the number of timed calls (any of the
+ * three pointers may be NULL; host memory), and stops recording.  At most 4096
+ * calls are timed per begin/end pair; later calls run untimed.  Enabling adds
+ * three event records per call and nothing else.  Process-wide; host only.
+ */
+fs_status fs_profile_begin(void);
+fs_status fs_profile_end(double *stage1_ms, double *stage2_ms, int64_t *calls);
+
+/* Static description of a status code. */
+const char *fs_status_string(fs_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *fs_last_error(void);
+
+/*
+ * Test hook: the Philox4x32-10 words the samplers draw from.  For row b
+ * (logical id row_ids[b], or b if row_ids is NULL) and counter j in
+ * [0, n_ctr), out[(b * n_ctr + j) * 4 + w] is word w of counter
+ * (j, id, offset lo, offset hi) under key (seed lo, seed hi).
+ *   row_ids  device uint32 [B] or NULL;  out  device uint32 [B, n_ctr, 4]
+ *   B >= 0, n_ctr >= 0, B * n_ctr < 2^31.
+ */
+fs_status fs_debug_philox_words(uint64_t seed, uint64_t offset, const uint32_t *row_ids,
+                                int64_t B, int64_t n_ctr, uint32_t *out,
+                                fs_stream_t stream);
+
+/*
+ * Test hook: the logits y = H W^T of the fused path, written to Y (device,
+ * float [B, V]).  Runs the same matmul code as fs_sample_fused (same tiling and
+ * accumulation order) with a store in place of the sampling epilogue.
+ * Same size and alignment rules as fs_sample_fused.
+ */
+fs_status fs_debug_logits(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t D,
+                          int64_t V, float *Y, fs_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSAMPLE_H */

@@ -69,7 +69,7 @@ def _load():
         lib.oracle_sample_logits.argtypes = [P, i64, i64, P, u64, u64, P, i32, P, P, P]
         lib.oracle_sample_repeated_row.restype = None
         lib.oracle_sample_repeated_row.argtypes = [P, i64, ctypes.c_float, u64, u64, P,
-                                                   i64, i32, P]
+                                                   i64, i32, P, P]
         _lib = lib
         return lib
 
@@ -182,11 +182,14 @@ def sample_logits(logits_f32, temp, *, seed: int, offset: int, row_ids=None,
 
 
 def sample_repeated_row(row_f32, temp: float, *, seed: int, offset: int, row_ids,
-                        fp64_noise: bool = False) -> np.ndarray:
-    """Sampled indices of many logical rows that all carry the logits row_f32[V]."""
+                        fp64_noise: bool = False, with_gap: bool = False):
+    """Sampled indices of many logical rows that all carry the logits row_f32[V]
+    (and their top-2 gaps if with_gap)."""
     x = np.ascontiguousarray(np.asarray(row_f32, dtype=np.float32).reshape(-1))
     rid = np.ascontiguousarray(np.asarray(row_ids, dtype=np.uint32).reshape(-1))
     out = np.zeros(rid.shape[0], dtype=np.int64)
+    gap = np.zeros(rid.shape[0], dtype=np.float64) if with_gap else None
     _load().oracle_sample_repeated_row(_ptr(x), x.shape[0], float(temp), seed, offset,
-                                       _ptr(rid), rid.shape[0], int(fp64_noise), _ptr(out))
-    return out
+                                       _ptr(rid), rid.shape[0], int(fp64_noise), _ptr(out),
+                                       _ptr(gap))
+    return (out, gap) if with_gap else out

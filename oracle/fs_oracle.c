@@ -312,11 +312,11 @@ void oracle_sample_logits(const float *logits, int64_t B, int64_t V,
  * logical id row_ids[k] and the logits of `logits[0..V)`.  This is the same
  * computation as oracle_sample_logits with the row repeated, without
  * materialising the repeats (used by the tail-rate and chi-square tests,
- * whose rows are identical by construction). */
+ * whose rows are identical by construction).  out_gap may be NULL. */
 void oracle_sample_repeated_row(const float *logits, int64_t V, float temp,
                                 uint64_t seed, uint64_t offset,
                                 const uint32_t *row_ids, int64_t n_rows,
-                                int fp64_noise, int64_t *out_idx)
+                                int fp64_noise, int64_t *out_idx, double *out_gap)
 {
     #pragma omp parallel
     {
@@ -328,6 +328,7 @@ void oracle_sample_repeated_row(const float *logits, int64_t V, float temp,
                 s[i] = score_of((double)logits[i], 0.0, (double)temp, seed, offset,
                                 row_ids[k], i, fp64_noise);
             select_row(s, V, &out_idx[k], &gap, &best);
+            if (out_gap) out_gap[k] = gap;
         }
         free(s);
     }
