@@ -68,8 +68,8 @@ def measured_traffic():
 
 
 def fused_tiles(V: int, cus: int) -> int:
-    """Vocabulary tiles of the fused Stage 1 (two workgroups per CU, 16-row blocks)."""
-    return max(1, min((V + 15) // 16, 2 * cus))
+    """Vocabulary tiles of the fused Stage 1 (one workgroup per CU, 8-row units)."""
+    return max(1, min((V + 7) // 8, cus))
 
 
 def stage1_alg_bytes(B: int, D: int, V: int, n_tiles: int, bias: bool = False) -> int:

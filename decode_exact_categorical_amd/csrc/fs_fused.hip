@@ -6,26 +6,36 @@
 // per-row tile maximum and its vocabulary index are written out.  The [B, V]
 // logits never reach HBM.
 //
-// Design for MI355X (differs from the page's Triton kernel, written for NVIDIA):
-//  * W streams from HBM exactly once.  A workgroup owns a contiguous range of
-//    16-row vocabulary blocks (about nblk / grid blocks each, so the 256 CUs
-//    finish within one 16-row block of each other) and walks it in passes of
-//    64 rows.
-//  * The 4 waves of a workgroup split the contraction dimension D into four
-//    contiguous quarters.  Each wave streams its quarter of the pass's 64 W
-//    rows straight into VGPRs in the bf16 MFMA A-operand layout (lane l reads
-//    16 bytes of row l%16; the 4 lanes of a row cover 64 contiguous bytes per
-//    instruction) and the matching H fragments (B operand, batch as the MFMA
-//    N dimension), one or two k-slices per pipeline stage, double-buffered.
-//    v_mfma_f32_16x16x32_bf16 accumulates in fp32.
-//  * The four partial sums meet in LDS and are added in a fixed order (wave 0,
-//    1, 2, 3), so every logit has one accumulation order that depends neither
-//    on B nor on the row's batch position.
-//  * Epilogue: wave w takes row block w of the pass.  In the MFMA output
-//    layout a lane holds 4 consecutive vocabulary rows of one batch column, so
-//    one Philox4x32-10 call gives the noise of all four (two calls for float64
-//    noise).  Scores feed a per-lane running argmax; at the end, xor-shuffles
-//    and LDS reduce it to one candidate per batch row for the workgroup.
+// Design for MI355X (the page's Triton kernel was written for NVIDIA parts):
+//  * One workgroup per CU streams a contiguous slice of W exactly once.  Its
+//    8 waves (two per SIMD) each own a contiguous run of vocabulary rows,
+//    assigned in 8-row units so every wave of the chip ends within 8 rows of
+//    the others.  A wave walks its rows in passes of up to 4 or 5 MFMA row
+//    blocks (64 or 80 rows).
+//  * W goes straight from HBM into VGPRs in the bf16 MFMA A-operand layout
+//    (lane l holds 16 bytes of row l % 16; the four lanes of a row read 64
+//    contiguous bytes), two k-steps of 32 in flight per row block.
+//  * H is the MFMA B operand (batch as the N dimension, 16 to 64 columns).  It
+//    is staged through LDS in chunks of 256 k, double-buffered and padded so
+//    the fragment reads are bank-conflict free, and shared by the 8 waves: H
+//    crosses L2 once per pass of the workgroup rather than once per wave.
+//  * v_mfma_f32_16x16x32_bf16 accumulates in fp32, k ascending, so every
+//    logit has one accumulation order that depends neither on B nor on the
+//    row's batch position.
+//  * Float32 noise is not left for the end: the Gumbel noise of one output
+//    fragment (4 vocabulary rows x 1 batch column per lane, one Philox4x32-10
+//    call) is computed inside the memory-bound k-loop and folded into that
+//    fragment's accumulator as bias + t * g, at a k-step fixed by the
+//    fragment's row block and column block.  After the k-loop the score is
+//    acc / t, i.e. (y + bias) / t + g up to fp32 rounding, and the epilogue
+//    is a multiply and a compare.  Greedy columns (t <= 0 or NaN) fold in the
+//    bias only.  Columns with an infinite (or beyond 2^60) temperature fold in
+//    the bias and add g after the division, which keeps (y + bias) / t + g.
+//  * Float64 noise keeps the score in float64: y + bias and the noise are
+//    combined after the k-loop, with two Philox calls per fragment.
+//  * Scores feed a per-lane running argmax (larger score, then smaller index);
+//    xor-shuffles and LDS reduce it to one candidate per batch row per
+//    workgroup.
 #include <type_traits>
 
 #include "fs_launch.hpp"
@@ -36,10 +46,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;                // K-split across the waves of a workgroup
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRB = 4;                   // 16-row blocks per pass
-constexpr int kBatchTile = 64;           // batch columns per workgroup (<= 4 MFMA blocks)
+constexpr int kKC = 256;          // k per H chunk in LDS
+constexpr int kStepsPerChunk = kKC / 32;
+constexpr int kHPad = 8;          // bf16 padding per LDS column row (16 bytes)
+constexpr int kHRow = kKC + kHPad;
+constexpr int kBatchTile = 64;    // batch columns per workgroup (4 MFMA column blocks)
+constexpr int kNoiseSlots = 4;    // fragment (rb, cb) gets its noise at k-step 4*rb + cb
+constexpr float kInfTemp = 0x1p60f;  // at or above this, t * g is not kept in the accumulator
+
+enum ColMode { kGreedy = 0, kSample = 1, kInfT = 2 };
 
 template <int EPI>
 struct ScoreType {
@@ -50,61 +67,81 @@ struct ScoreType<kEpiSample64> {
   typedef double type;
 };
 
-__device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Fragments travel as raw 32-bit words and become bf16 only at the MFMA: a
+// select between a loaded bf16 vector and a constant makes the compiler
+// repack the vector as soon as it lands, i.e. wait for every load in flight.
+__device__ __forceinline__ u32x4 load_frag(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
-__device__ __forceinline__ bf16x8 zero_frag() {
-  bf16x8 z;
+__device__ __forceinline__ bf16x8 as_bf16(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Bias of 4 consecutive vocabulary rows i0..i0+3 of batch row b (0 past V).
+__device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_t i0, float beta[4]) {
+  beta[0] = beta[1] = beta[2] = beta[3] = 0.f;
+  if (!a.bias) return;
+  const float* bp = a.bias + b * a.V + i0;
+  if (a.bias_vec4 && i0 + 3 < a.V) {
+    const float4 v = *reinterpret_cast<const float4*>(bp);
+    beta[0] = v.x;
+    beta[1] = v.y;
+    beta[2] = v.z;
+    beta[3] = v.w;
+  } else {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
-  return z;
+    for (int j = 0; j < 4; ++j)
+      if (i0 + j < a.V) beta[j] = bp[j];
+  }
 }
 
-// 32-wide k-slices per pipeline stage: two while the register file allows it
-// (at two waves per SIMD a wave has 256 VGPRs), one for three or four column
-// blocks, whose accumulators and H fragments need the room.
+// MFMA row blocks (16 rows) per wave per pass: five, or four with four column
+// blocks, where the accumulators and the noise fold need the room (a wave has
+// 256 VGPRs at two waves per SIMD).
 template <int NB>
-struct Stage {
-  static constexpr int kS = NB <= 2 ? 2 : 1;
+struct RowBlocks {
+  static constexpr int value = NB >= 4 ? 4 : 5;
 };
 
-template <int NB, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void fused_stage1_kernel(FusedArgs a) {
+template <int NB, int EPI, bool HAS_BIAS>
+__global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
-  constexpr int kS = Stage<NB>::kS;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int grp = lane >> 4;  // k-group of the operands, row group of the output
-  const int col = lane & 15;  // A row / B column / output column within a block
+  constexpr int kRB = RowBlocks<NB>::value;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // The wave index is wave-uniform; saying so keeps every quantity derived
+  // from it (row range, row-block count) in scalar registers, so branches on
+  // them are scalar and do not force the compiler to drain loads in flight.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4;  // operand k-group; output row group
+  const int col = lane & 15;  // A row / B column / output column in a block
 
   const int64_t B = a.B, D = a.D, V = a.V;
   const int64_t bt0 = (int64_t)blockIdx.y * kBatchTile;
 
-  // This workgroup's 16-row vocabulary blocks [blk0, blk1).
-  const int64_t nblk = (V + 15) >> 4;
-  const int64_t blk0 = nblk * (int64_t)blockIdx.x / gridDim.x;
-  const int64_t blk1 = nblk * (int64_t)(blockIdx.x + 1) / gridDim.x;
+  // Rows of this workgroup and of this wave, in 8-row units.
+  const int64_t nunits = (V + 7) >> 3;
+  const int64_t g0 = nunits * (int64_t)blockIdx.x / gridDim.x;
+  const int64_t g1 = nunits * (int64_t)(blockIdx.x + 1) / gridDim.x;
+  const int64_t nu = g1 - g0;
+  const int64_t r0 = (g0 + nu * wave / kWaves) * 8;
+  int64_t r1 = (g0 + nu * (wave + 1) / kWaves) * 8;
+  if (r1 > V) r1 = V;
+  const int nrb_wave = r1 > r0 ? (int)((r1 - r0 + 15) >> 4) : 0;
+  // Passes are uniform across the workgroup (its waves meet at every H chunk).
+  const int max_rb = (int)((((nu + kWaves - 1) / kWaves) * 8 + 15) >> 4);
+  const int npass = (max_rb + kRB - 1) / kRB;
 
-  // This wave's 32-wide k-steps [ks0, ks1).
   const int KS = (int)((D + 31) >> 5);
-  const int ks0 = KS * wave / kWaves;
-  const int ks1 = KS * (wave + 1) / kWaves;
+  const int NC = (KS + kStepsPerChunk - 1) / kStepsPerChunk;
 
-  // H fragment pointers, one per 16-column batch block (rows past B are
-  // clamped to B-1; their results are discarded by the epilogue).
-  const uint16_t* hp[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    int64_t b = bt0 + 16 * cb + col;
-    if (b > B - 1) b = B - 1;
-    hp[cb] = a.H + b * D + 8 * grp;
-  }
-
-  // Per-column sampling constants.
-  bool col_ok[NB], greedy[NB];
+  // Per-column constants.
+  int mode[NB];
   T inv_t[NB];
+  float tval[NB];
   uint32_t rid[NB];
+  bool col_ok[NB];
   T bm[NB];
   int32_t bi[NB];
 #pragma unroll
@@ -114,23 +151,59 @@ __global__ __launch_bounds__(kThreads, 2) void fused_stage1_kernel(FusedArgs a) 
     const int64_t bc = col_ok[cb] ? b : 0;
     float t = 1.0f;
     if (EPI != kEpiStore) t = a.temp[bc];
-    greedy[cb] = !(t > 0.0f);
-    inv_t[cb] = greedy[cb] ? T(1) : T(1) / T(t);
+    mode[cb] = !(t > 0.0f) ? kGreedy : (t < kInfTemp ? kSample : kInfT);
+    tval[cb] = t;
+    inv_t[cb] = mode[cb] == kGreedy ? T(1) : T(1) / T(t);
     rid[cb] = a.row_ids ? a.row_ids[bc] : (uint32_t)bc;
     bm[cb] = neg_inf<T>();
     bi[cb] = kNoIndex;
   }
 
-  __shared__ f32x4 red[kWaves][kRB][NB][64];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[2][16 * NB][kHRow];
 
-  for (int64_t pb = blk0; pb < blk1; pb += kRB) {
-    const int nrb = (int)((blk1 - pb) < kRB ? (blk1 - pb) : kRB);
+  // H chunk staging.  A chunk is 16*NB columns x 256 k = 32*16*NB pieces of
+  // 16 bytes; thread t stages pieces t + 512*q, q < NB, so every thread issues
+  // the same NB loads and NB LDS stores (no branch around either).  Loads use a
+  // clamped, always valid address; pieces past D or past B are stored as zero.
+  u32x4 hstage[NB];
+  bool hvalid[NB];
+  auto h_load = [&](int c) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int piece = tid + kThreads * q;
+      const int hc = piece >> 5;                 // column within the tile
+      const int64_t k = (int64_t)c * kKC + (piece & 31) * 8;
+      const int64_t b = bt0 + hc;
+      hvalid[q] = b < B && k < D;
+      hstage[q] = load_frag(a.H + (hvalid[q] ? b * D + k : 0));
+    }
+  };
+  auto h_store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int piece = tid + kThreads * q;
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&hs[buf][piece >> 5][(piece & 31) * 8]) = hvalid[q] ? hstage[q] : z;
+    }
+  };
 
+  for (int p = 0; p < npass; ++p) {
+    const int rb_first = p * kRB;
+    int nrb = nrb_wave - rb_first;
+    nrb = nrb < 0 ? 0 : (nrb > kRB ? kRB : nrb);
+
+    // Every k-step issues the same kRB loads and kRB x NB MFMAs, whatever the
+    // wave's row count: a load or MFMA under a branch leaves the compiler unsure
+    // how many loads are in flight, and it then drains them all before using
+    // any.  Lanes past the wave's last row, and row blocks past nrb, re-read the
+    // wave's last row (same cache lines, no extra HBM traffic); their results
+    // are never scored.
     const uint16_t* wp[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      int64_t row = (pb + rb) * 16 + col;
-      if (row > V - 1) row = V - 1;
+      int64_t row = r0 + 16 * (rb_first + rb) + col;
+      if (row > r1 - 1) row = r1 - 1;
+      if (row < 0) row = 0;
       wp[rb] = a.W + row * D + 8 * grp;
     }
 
@@ -140,126 +213,264 @@ __global__ __launch_bounds__(kThreads, 2) void fused_stage1_kernel(FusedArgs a) 
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8 wb[2][kS][kRB];
-    bf16x8 hb[2][kS][NB];
-
-    // Loads of one pipeline stage (kS k-steps) into buffer BUF.  A k-step that
-    // runs past D (D % 32 != 0) zero-fills the lanes whose 8 elements lie past D.
-    auto load_stage = [&](auto BUFC, int ksb) {
-      constexpr int BUF = decltype(BUFC)::value;
+    // Float32 noise of fragment slot f = 4*rb + cb (rb < kRB): bias + t * g of
+    // the lane's 4 rows, or the bias alone for greedy and infinite-temperature
+    // columns; the caller folds it into acc[rb][cb] (FS_FOLD_SLOT).  The bias
+    // arrives from bias_slot_load, issued two k-steps earlier, so this issues no
+    // memory operation.
+    struct Fold {
+      float v[4];
+      bool any;
+    };
+    auto slot_noise = [&](int f, const f32x4& beta) -> Fold {
+      Fold out = {{0.f, 0.f, 0.f, 0.f}, false};
+      if (EPI != kEpiSample32 || f >= kRB * kNoiseSlots) return out;
+      const int rb = f / kNoiseSlots, cb = f - rb * kNoiseSlots;
+      if (rb >= nrb || cb >= NB) return out;
+      out.any = true;
+      int m = kGreedy;
+      float t = 1.f;
+      uint32_t r = 0;
+      bool ok = false;
 #pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        const int ks = ksb + s;
-        if (ks < ks1) {
-          const int64_t k = (int64_t)ks * 32;
-          if (k + 32 <= D) {
-#pragma unroll
-            for (int rb = 0; rb < kRB; ++rb)
-              if (rb < nrb) wb[BUF][s][rb] = load_frag(wp[rb] + k);
-#pragma unroll
-            for (int cb = 0; cb < NB; ++cb) hb[BUF][s][cb] = load_frag(hp[cb] + k);
-          } else {
-            const bool in = k + 8 * grp < D;
-#pragma unroll
-            for (int rb = 0; rb < kRB; ++rb)
-              if (rb < nrb) wb[BUF][s][rb] = in ? load_frag(wp[rb] + k) : zero_frag();
-#pragma unroll
-            for (int cb = 0; cb < NB; ++cb) hb[BUF][s][cb] = in ? load_frag(hp[cb] + k) : zero_frag();
-          }
+      for (int c = 0; c < NB; ++c)
+        if (c == cb) {
+          m = mode[c];
+          t = tval[c];
+          r = rid[c];
+          ok = col_ok[c];
+        }
+      const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+      if (ok && i0 < r1) {
+        if (HAS_BIAS) {
+          out.v[0] = beta[0];
+          out.v[1] = beta[1];
+          out.v[2] = beta[2];
+          out.v[3] = beta[3];
+        }
+        if (m == kSample) {
+          const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), r);
+          out.v[0] += t * gumbel_f32(w.w0);
+          out.v[1] += t * gumbel_f32(w.w1);
+          out.v[2] += t * gumbel_f32(w.w2);
+          out.v[3] += t * gumbel_f32(w.w3);
         }
       }
+      return out;
     };
-    auto compute_stage = [&](auto BUFC, int ksb) {
-      constexpr int BUF = decltype(BUFC)::value;
+    // Bias of fragment slot f: four scalar loads from clamped, valid addresses
+    // (the slot's values where they exist, something harmless elsewhere).
+    auto bias_slot_load = [&](f32x4& dst, int f) {
+      if (!HAS_BIAS || EPI != kEpiSample32) return;
+      const int ff = f < kRB * kNoiseSlots ? f : 0;
+      const int rb = ff / kNoiseSlots, cb = ff - rb * kNoiseSlots;
+      int64_t b = bt0 + 16 * cb + col;
+      if (b > B - 1) b = B - 1;
+      const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
 #pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        if (ksb + s < ks1) {
-#pragma unroll
-          for (int rb = 0; rb < kRB; ++rb)
-            if (rb < nrb)
-#pragma unroll
-              for (int cb = 0; cb < NB; ++cb)
-                acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    wb[BUF][s][rb], hb[BUF][s][cb], acc[rb][cb], 0, 0, 0);
-        }
+      for (int j = 0; j < 4; ++j) {
+        int64_t i = i0 + j;
+        if (i > V - 1) i = V - 1;
+        if (i < 0) i = 0;
+        dst[j] = a.bias[b * V + i];
       }
     };
+#define FS_FOLD_SLOT(F, BETA)                                            \
+  do {                                                                   \
+    const int f_ = (F);                                                  \
+    const Fold n_ = slot_noise(f_, (BETA));                              \
+    if (n_.any) {                                                        \
+      _Pragma("unroll") for (int rb2 = 0; rb2 < kRB; ++rb2)              \
+        _Pragma("unroll") for (int cb2 = 0; cb2 < NB; ++cb2)             \
+          if (rb2 * kNoiseSlots + cb2 == f_) {                           \
+            acc[rb2][cb2][0] += n_.v[0];                                 \
+            acc[rb2][cb2][1] += n_.v[1];                                 \
+            acc[rb2][cb2][2] += n_.v[2];                                 \
+            acc[rb2][cb2][3] += n_.v[3];                                 \
+          }                                                              \
+    }                                                                    \
+  } while (0)
 
-    typedef std::integral_constant<int, 0> Buf0;
-    typedef std::integral_constant<int, 1> Buf1;
-    load_stage(Buf0{}, ks0);
-    for (int ks = ks0; ks < ks1; ks += 2 * kS) {
-      load_stage(Buf1{}, ks + kS);
-      compute_stage(Buf0{}, ks);
-      load_stage(Buf0{}, ks + 2 * kS);
-      compute_stage(Buf1{}, ks + kS);
-    }
+    // W fragments of k-step ks (a prefetch past the last k-step re-reads it).
+    // In a final k-step that runs past D (D % 32 != 0) the lanes past D read
+    // k = 0 instead; H is zero there, so their products vanish for finite W.
+    auto load_w = [&](u32x4 (&dst)[kRB], int ks) {
+      if (ks > KS - 1) ks = KS - 1;
+      const int64_t k = (int64_t)ks * 32;
+      if (k + 32 <= D) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) dst[rb] = load_frag(wp[rb] + k);
+      } else {
+        const int64_t kl = (k + 8 * grp < D) ? k : -8 * grp;
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) dst[rb] = load_frag(wp[rb] + kl);
+      }
+    };
+    auto mma = [&](const u32x4 (&w)[kRB], int buf, int kk) {
+      bf16x8 hf[NB];
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+        hf[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 8 * grp]);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[rb]), hf[cb], acc[rb][cb], 0, 0, 0);
+    };
 
-    // Partial sums of the four K quarters meet in LDS.
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) red[wave][rb][cb][lane] = acc[rb][cb];
+    // The k-loop is straight-line: every k-step issues the same loads in the
+    // same order (kRB W fragments, then the bias of the slot folded two steps
+    // later), every chunk the same NB H loads, and every pass runs NC * 8
+    // k-steps (steps past the last real one re-read it against zero H).  The
+    // compiler can then count loads in flight exactly and waits only for the
+    // ones it needs, keeping two k-steps of W in flight across the barriers.
+    h_load(0);
+    h_store(0);
     __syncthreads();
 
-    if (wave < nrb) {
-      const int rb = wave;
-      const int64_t i0 = (pb + rb) * 16 + 4 * grp;  // first of this lane's 4 rows
+    u32x4 wa[kRB], wb[kRB];
+    f32x4 ba = f32x4{0.f, 0.f, 0.f, 0.f}, bb = f32x4{0.f, 0.f, 0.f, 0.f};
+    load_w(wa, 0);
+    bias_slot_load(ba, 0);
+    load_w(wb, 1);
+    bias_slot_load(bb, 1);
+    for (int c = 0; c < NC; ++c) {
+      const int buf = c & 1;
+      h_load(c + 1 < NC ? c + 1 : c);
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        f32x4 y = red[0][rb][cb][lane];
-        y += red[1][rb][cb][lane];
-        y += red[2][rb][cb][lane];
-        y += red[3][rb][cb][lane];
-        if (!col_ok[cb]) continue;
-        const int64_t b = bt0 + 16 * cb + col;
-        if (EPI == kEpiStore) {
+      for (int j = 0; j < kStepsPerChunk; j += 2) {
+        const int ks = c * kStepsPerChunk + j;
+        // sched_barrier keeps the compiler from moving the loads of step ks + 2
+        // next to their use: each phase stays where it is written, so two
+        // k-steps of W stay in flight.
+        mma(wa, buf, j * 32);
+        FS_FOLD_SLOT(ks, ba);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(wa, ks + 2);
+        bias_slot_load(ba, ks + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(wb, buf, (j + 1) * 32);
+        FS_FOLD_SLOT(ks + 1, bb);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(wb, ks + 3);
+        bias_slot_load(bb, ks + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        // The other buffer was last read in the previous chunk, before the
+        // barrier that ended it, so the next chunk can land there at once.
+        if (j == 0) h_store(buf ^ 1);
+      }
+      __syncthreads();
+    }
+    // Short contractions (fewer than kRB * 4 k-steps): the remaining slots.
+    for (int f = NC * kStepsPerChunk; f < kRB * kNoiseSlots; ++f) {
+      f32x4 bt = f32x4{0.f, 0.f, 0.f, 0.f};
+      bias_slot_load(bt, f);
+      FS_FOLD_SLOT(f, bt);
+    }
+#undef FS_FOLD_SLOT
+
+    // End of pass: scores of this wave's fragments.
+    if (EPI != kEpiSample64) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (i0 + j < V) a.Y[b * V + i0 + j] = y[j];
-          continue;
-        }
-        float beta[4] = {0.f, 0.f, 0.f, 0.f};
-        if (a.bias) {
-          const float* bp = a.bias + b * V + i0;
-          if (a.bias_vec4 && i0 + 3 < V) {
-            const float4 v = *reinterpret_cast<const float4*>(bp);
-            beta[0] = v.x; beta[1] = v.y; beta[2] = v.z; beta[3] = v.w;
-          } else {
+      for (int rb = 0; rb < kRB; ++rb) {
+        if (rb >= nrb) continue;
+        const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          if (!col_ok[cb]) continue;
+          const int64_t b = bt0 + 16 * cb + col;
+          const f32x4 y = acc[rb][cb];
+          if (EPI == kEpiStore) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if (i0 + j < V) beta[j] = bp[j];
+              if (i0 + j < r1) a.Y[b * V + i0 + j] = y[j];
+            continue;
+          }
+          T s[4];
+          if (mode[cb] == kSample) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] = T(y[j] * (float)inv_t[cb]);
+          } else if (mode[cb] == kGreedy) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] = T(y[j]);
+          } else {  // infinite temperature: (y + bias) / t + g
+            const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), rid[cb]);
+            s[0] = T(y[0] * (float)inv_t[cb] + gumbel_f32(w.w0));
+            s[1] = T(y[1] * (float)inv_t[cb] + gumbel_f32(w.w1));
+            s[2] = T(y[2] * (float)inv_t[cb] + gumbel_f32(w.w2));
+            s[3] = T(y[3] * (float)inv_t[cb] + gumbel_f32(w.w3));
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int32_t i = (int32_t)(i0 + j);
+            if (i0 + j < r1 && beats(s[j], i, bm[cb], bi[cb])) {
+              bm[cb] = s[j];
+              bi[cb] = i;
+            }
           }
         }
+      }
+    } else {
+      // Float64 noise, score in float64.  The per-fragment work (two Philox
+      // calls, four float64 logs) is large, so the loop stays rolled and the
+      // fragment is picked out of the accumulators by uniform branches.
+#pragma unroll 1
+      for (int f = 0; f < kRB * NB; ++f) {
+        const int rb = f / NB, cb = f - rb * NB;
+        if (rb >= nrb) break;
+        f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+        int m = kGreedy;
+        T it = T(1), lbm = neg_inf<T>();
+        uint32_t r = 0;
+        bool ok = false;
+        int32_t lbi = kNoIndex;
+#pragma unroll
+        for (int rb2 = 0; rb2 < kRB; ++rb2)
+#pragma unroll
+          for (int cb2 = 0; cb2 < NB; ++cb2)
+            if (rb2 == rb && cb2 == cb) y = acc[rb2][cb2];
+#pragma unroll
+        for (int c = 0; c < NB; ++c)
+          if (c == cb) {
+            m = mode[c];
+            it = inv_t[c];
+            r = rid[c];
+            ok = col_ok[c];
+            lbm = bm[c];
+            lbi = bi[c];
+          }
+        if (!ok) continue;
+        const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+        float beta[4];
+        load_bias4(a, bt0 + 16 * cb + col, i0, beta);
         T s[4];
-        if (greedy[cb]) {
+        if (m == kGreedy) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) s[j] = T(y[j]) + T(beta[j]);
-        } else if (EPI == kEpiSample32) {
-          const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), rid[cb]);
-          s[0] = T((y[0] + beta[0]) * inv_t[cb]) + T(gumbel_f32(w.w0));
-          s[1] = T((y[1] + beta[1]) * inv_t[cb]) + T(gumbel_f32(w.w1));
-          s[2] = T((y[2] + beta[2]) * inv_t[cb]) + T(gumbel_f32(w.w2));
-          s[3] = T((y[3] + beta[3]) * inv_t[cb]) + T(gumbel_f32(w.w3));
         } else {
-          const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), rid[cb]);
-          const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, rid[cb]);
-          s[0] = (T(y[0]) + T(beta[0])) * inv_t[cb] + T(gumbel_f64(w0.w0, w0.w1));
-          s[1] = (T(y[1]) + T(beta[1])) * inv_t[cb] + T(gumbel_f64(w0.w2, w0.w3));
-          s[2] = (T(y[2]) + T(beta[2])) * inv_t[cb] + T(gumbel_f64(w1.w0, w1.w1));
-          s[3] = (T(y[3]) + T(beta[3])) * inv_t[cb] + T(gumbel_f64(w1.w2, w1.w3));
+          const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), r);
+          const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, r);
+          s[0] = (T(y[0]) + T(beta[0])) * it + T(gumbel_f64(w0.w0, w0.w1));
+          s[1] = (T(y[1]) + T(beta[1])) * it + T(gumbel_f64(w0.w2, w0.w3));
+          s[2] = (T(y[2]) + T(beta[2])) * it + T(gumbel_f64(w1.w0, w1.w1));
+          s[3] = (T(y[3]) + T(beta[3])) * it + T(gumbel_f64(w1.w2, w1.w3));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int32_t i = (int32_t)(i0 + j);
-          if (i0 + j < V && beats(s[j], i, bm[cb], bi[cb])) {
-            bm[cb] = s[j];
-            bi[cb] = i;
+          if (i0 + j < r1 && beats(s[j], i, lbm, lbi)) {
+            lbm = s[j];
+            lbi = i;
           }
         }
+#pragma unroll
+        for (int c = 0; c < NB; ++c)
+          if (c == cb) {
+            bm[c] = lbm;
+            bi[c] = lbi;
+          }
       }
     }
-    __syncthreads();
   }
 
   if (EPI == kEpiStore) return;
@@ -268,22 +479,22 @@ __global__ __launch_bounds__(kThreads, 2) void fused_stage1_kernel(FusedArgs a) 
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) wave_argmax_xor(bm[cb], bi[cb], 4);
 
-  // Across the 4 waves, in wave order, through LDS (the reduction buffer is free).
-  Cand<T>* wbest = reinterpret_cast<Cand<T>*>(&red[0][0][0][0]);
+  // Across the waves, in wave order, through LDS (the H buffers are free: the
+  // last chunk ended with a barrier).
+  Cand<T>* wbest = reinterpret_cast<Cand<T>*>(&hs[0][0][0]);
   if (grp == 0) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) wbest[wave * (NB * 16) + cb * 16 + col] = Cand<T>{bm[cb], bi[cb]};
   }
   __syncthreads();
-  if (threadIdx.x < NB * 16) {
-    const int c = threadIdx.x;
-    Cand<T> best = wbest[c];
+  if (tid < NB * 16) {
+    Cand<T> best = wbest[tid];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      const Cand<T> o = wbest[w * (NB * 16) + c];
+      const Cand<T> o = wbest[w * (NB * 16) + tid];
       if (beats(o.m, o.idx, best.m, best.idx)) best = o;
     }
-    const int64_t b = bt0 + c;
+    const int64_t b = bt0 + tid;
     if (b < B) reinterpret_cast<Cand<T>*>(a.cand)[b * a.nT + blockIdx.x] = best;
   }
 }
@@ -292,13 +503,20 @@ template <int NB>
 hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream) {
   switch (epi) {
     case kEpiSample32:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32>), grid, dim3(kThreads), 0, stream, a);
+      if (a.bias)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, true>), grid, dim3(kThreads), 0,
+                           stream, a);
+      else
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, false>), grid, dim3(kThreads), 0,
+                           stream, a);
       break;
     case kEpiSample64:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample64>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample64, false>), grid, dim3(kThreads), 0,
+                         stream, a);
       break;
     default:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiStore>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiStore, false>), grid, dim3(kThreads), 0,
+                         stream, a);
       break;
   }
   return hipGetLastError();
@@ -307,9 +525,9 @@ hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream)
 }  // namespace
 
 int fused_num_tiles(int64_t V, int num_cus) {
-  const int64_t nblk = (V + 15) >> 4;
-  int64_t g = 2 * (int64_t)num_cus;  // two workgroups per CU
-  if (g > nblk) g = nblk;
+  const int64_t nunits = (V + 7) >> 3;
+  int64_t g = num_cus;  // one workgroup per CU
+  if (g > nunits) g = nunits;
   if (g < 1) g = 1;
   return (int)g;
 }

@@ -54,7 +54,7 @@ def test_workspace_bytes():
     assert lib.fs_workspace_bytes(4, 2**31, 0) == 0
     a = lib.fs_workspace_bytes(64, 151936, 0)
     b = lib.fs_workspace_bytes(64, 151936, fs.FS_FP64_NOISE)
-    assert 64 * 512 * 8 <= a < b
+    assert 64 * 256 * 8 <= a < b
     assert lib.fs_workspace_bytes(4096, 131072, 1) >= 4096 * 64 * 16
 
 

@@ -223,14 +223,21 @@ def test_replay_under_side_stream_contention(dev):
 
 
 def test_fused_matches_logits_sampler_stream(dev):
-    """Equal y + bias gives equal draws: sample the fused path's own logits with the
-    standalone sampler (same Philox stream, same rule)."""
+    """Same y + bias, same draws: the standalone sampler over the fused path's own
+    logits draws from the same Philox stream.  With float64 noise both form the
+    score as (y + bias) / t + g in float64, so they agree bitwise.  With float32
+    noise the fused kernel folds t * g into the accumulator, so the scores differ
+    by fp32 rounding and the draws agree on every row the oracle decides."""
     say("fused vs standalone on the same logits")
     B, D, V = 24, 512, 4096
     H, W, temp, _ = _case(B, D, V, seed_base=70)
     Hd, Wd, td = to_dev(H, W, temp, dev=dev)
     y = fs.debug_logits(Hd, Wd)
-    for fp64 in (False, True):
-        a = fs.sample_fused(Hd, Wd, td, seed=5, offset=6, fp64_noise=fp64)
-        b = fs.sample_logits(y, td, seed=5, offset=6, fp64_noise=fp64)
-        assert torch.equal(a, b)
+    a = fs.sample_fused(Hd, Wd, td, seed=5, offset=6, fp64_noise=True)
+    b = fs.sample_logits(y, td, seed=5, offset=6, fp64_noise=True)
+    assert torch.equal(a, b)
+    a = fs.sample_fused(Hd, Wd, td, seed=5, offset=6).cpu().numpy()
+    b = fs.sample_logits(y, td, seed=5, offset=6).cpu().numpy()
+    ref, gap, _ = oracle.sample_logits(y.cpu().numpy(), temp.numpy(), seed=5, offset=6)
+    check_index_parity(b, ref, gap, "standalone on fused logits")
+    check_index_parity(a, ref, gap, "fused vs oracle on fused logits")
