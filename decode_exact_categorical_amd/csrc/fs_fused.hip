@@ -10,8 +10,8 @@
 //  * One workgroup per CU streams a contiguous slice of W exactly once.  Its
 //    8 waves (two per SIMD) each own a contiguous run of vocabulary rows,
 //    assigned in 8-row units so every wave of the chip ends within 8 rows of
-//    the others.  A wave walks its rows in passes of up to 4 or 5 MFMA row
-//    blocks (64 or 80 rows).
+//    the others.  A wave walks its rows in passes of up to 5 MFMA row blocks
+//    (80 rows; 4 blocks with 64 batch columns).
 //  * W goes straight from HBM into VGPRs in the bf16 MFMA A-operand layout
 //    (lane l holds 16 bytes of row l % 16; the four lanes of a row read 64
 //    contiguous bytes), two k-steps of 32 in flight per row block.
@@ -97,8 +97,8 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
 }
 
 // MFMA row blocks (16 rows) per wave per pass: five, or four with four column
-// blocks, where the accumulators and the noise fold need the room (a wave has
-// 256 VGPRs at two waves per SIMD).
+// blocks, where the accumulators need the room (a wave has 256 VGPRs at two
+// waves per SIMD).
 template <int NB>
 struct RowBlocks {
   static constexpr int value = NB >= 4 ? 4 : 5;
@@ -136,25 +136,34 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   const int KS = (int)((D + 31) >> 5);
   const int NC = (KS + kStepsPerChunk - 1) / kStepsPerChunk;
 
-  // Per-column constants.
-  int mode[NB];
-  T inv_t[NB];
-  float tval[NB];
-  uint32_t rid[NB];
+  // Per-column sampling constants live in LDS (16 bytes a column), read when a
+  // fragment is folded or scored; registers hold only each column's running
+  // best (score, index).
+  struct ColInfo {
+    float t;
+    float inv_t;
+    uint32_t rid;
+    int mode;
+  };
+  __shared__ ColInfo cols[16 * NB];
+  if (tid < 16 * NB) {
+    const int64_t b = bt0 + tid;
+    const int64_t bc = b < B ? b : 0;
+    float t = 1.0f;
+    if (EPI != kEpiStore) t = a.temp[bc];
+    ColInfo ci;
+    ci.mode = !(t > 0.0f) ? kGreedy : (t < kInfTemp ? kSample : kInfT);
+    ci.t = t;
+    ci.inv_t = ci.mode == kGreedy ? 1.0f : 1.0f / t;
+    ci.rid = a.row_ids ? a.row_ids[bc] : (uint32_t)bc;
+    cols[tid] = ci;
+  }
   bool col_ok[NB];
   T bm[NB];
   int32_t bi[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
-    const int64_t b = bt0 + 16 * cb + col;
-    col_ok[cb] = b < B;
-    const int64_t bc = col_ok[cb] ? b : 0;
-    float t = 1.0f;
-    if (EPI != kEpiStore) t = a.temp[bc];
-    mode[cb] = !(t > 0.0f) ? kGreedy : (t < kInfTemp ? kSample : kInfT);
-    tval[cb] = t;
-    inv_t[cb] = mode[cb] == kGreedy ? T(1) : T(1) / T(t);
-    rid[cb] = a.row_ids ? a.row_ids[bc] : (uint32_t)bc;
+    col_ok[cb] = bt0 + 16 * cb + col < B;
     bm[cb] = neg_inf<T>();
     bi[cb] = kNoIndex;
   }
@@ -167,9 +176,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   // clamped, always valid address; pieces past D or past B are stored as zero.
   u32x4 hstage[NB];
   bool hvalid[NB];
-  auto h_load = [&](int c) {
+  // Half QH of the pieces (the first (NB+1)/2 or the rest), so only half the
+  // staging registers are live at a time.
+  constexpr int kQSplit = (NB + 1) / 2;
+  auto h_load = [&](int c, auto QH) {
+    constexpr int q0 = decltype(QH)::value == 0 ? 0 : kQSplit;
+    constexpr int q1 = decltype(QH)::value == 0 ? kQSplit : NB;
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
+    for (int q = q0; q < q1; ++q) {
       const int piece = tid + kThreads * q;
       const int hc = piece >> 5;                 // column within the tile
       const int64_t k = (int64_t)c * kKC + (piece & 31) * 8;
@@ -178,9 +192,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       hstage[q] = load_frag(a.H + (hvalid[q] ? b * D + k : 0));
     }
   };
-  auto h_store = [&](int buf) {
+  auto h_store = [&](int buf, auto QH) {
+    constexpr int q0 = decltype(QH)::value == 0 ? 0 : kQSplit;
+    constexpr int q1 = decltype(QH)::value == 0 ? kQSplit : NB;
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
+    for (int q = q0; q < q1; ++q) {
       const int piece = tid + kThreads * q;
       const u32x4 z = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&hs[buf][piece >> 5][(piece & 31) * 8]) = hvalid[q] ? hstage[q] : z;
@@ -198,13 +214,17 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // any.  Lanes past the wave's last row, and row blocks past nrb, re-read the
     // wave's last row (same cache lines, no extra HBM traffic); their results
     // are never scored.
-    const uint16_t* wp[kRB];
+    // Addresses: a wave-uniform base (scalar registers) plus a 32-bit element
+    // offset per row block and lane.  A wave without rows reads row 0.
+    const int64_t rbase = nrb_wave > 0 ? r0 : 0;
+    const int64_t rlast = nrb_wave > 0 ? r1 - 1 : 0;
+    const uint16_t* wwave = a.W + rbase * D;
+    uint32_t woff[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       int64_t row = r0 + 16 * (rb_first + rb) + col;
-      if (row > r1 - 1) row = r1 - 1;
-      if (row < 0) row = 0;
-      wp[rb] = a.W + row * D + 8 * grp;
+      if (row > rlast) row = rlast;
+      woff[rb] = (uint32_t)((row - rbase) * D + 8 * grp);
     }
 
     f32x4 acc[kRB][NB];
@@ -228,18 +248,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       const int rb = f / kNoiseSlots, cb = f - rb * kNoiseSlots;
       if (rb >= nrb || cb >= NB) return out;
       out.any = true;
-      int m = kGreedy;
-      float t = 1.f;
-      uint32_t r = 0;
-      bool ok = false;
-#pragma unroll
-      for (int c = 0; c < NB; ++c)
-        if (c == cb) {
-          m = mode[c];
-          t = tval[c];
-          r = rid[c];
-          ok = col_ok[c];
-        }
+      const ColInfo ci = cols[16 * cb + col];
+      const int m = ci.mode;
+      const float t = ci.t;
+      const uint32_t r = ci.rid;
+      const bool ok = bt0 + 16 * cb + col < B;
       const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
       if (ok && i0 < r1) {
         if (HAS_BIAS) {
@@ -297,13 +310,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     auto load_w = [&](u32x4 (&dst)[kRB], int ks) {
       if (ks > KS - 1) ks = KS - 1;
       const int64_t k = (int64_t)ks * 32;
+      const uint16_t* wk = wwave + k;
       if (k + 32 <= D) {
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) dst[rb] = load_frag(wp[rb] + k);
+        for (int rb = 0; rb < kRB; ++rb) dst[rb] = load_frag(wk + woff[rb]);
       } else {
-        const int64_t kl = (k + 8 * grp < D) ? k : -8 * grp;
+        const int64_t kl = (k + 8 * grp < D) ? 0 : -k - 8 * grp;
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) dst[rb] = load_frag(wp[rb] + kl);
+        for (int rb = 0; rb < kRB; ++rb) dst[rb] = load_frag(wk + kl + woff[rb]);
       }
     };
     auto mma = [&](const u32x4 (&w)[kRB], int buf, int kk) {
@@ -324,8 +338,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // k-steps (steps past the last real one re-read it against zero H).  The
     // compiler can then count loads in flight exactly and waits only for the
     // ones it needs, keeping two k-steps of W in flight across the barriers.
-    h_load(0);
-    h_store(0);
+    typedef std::integral_constant<int, 0> Half0;
+    typedef std::integral_constant<int, 1> Half1;
+    h_load(0, Half0{});
+    h_load(0, Half1{});
+    h_store(0, Half0{});
+    h_store(0, Half1{});
     __syncthreads();
 
     u32x4 wa[kRB], wb[kRB];
@@ -336,7 +354,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     bias_slot_load(bb, 1);
     for (int c = 0; c < NC; ++c) {
       const int buf = c & 1;
-      h_load(c + 1 < NC ? c + 1 : c);
+      const int cn = c + 1 < NC ? c + 1 : c;
+      h_load(cn, Half0{});
 #pragma unroll
       for (int j = 0; j < kStepsPerChunk; j += 2) {
         const int ks = c * kStepsPerChunk + j;
@@ -357,7 +376,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         __builtin_amdgcn_sched_barrier(0);
         // The other buffer was last read in the previous chunk, before the
         // barrier that ended it, so the next chunk can land there at once.
-        if (j == 0) h_store(buf ^ 1);
+        if (j == 0) {
+          h_store(buf ^ 1, Half0{});
+          h_load(cn, Half1{});
+        }
+        if (j == 2) h_store(buf ^ 1, Half1{});
       }
       __syncthreads();
     }
@@ -386,19 +409,20 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
               if (i0 + j < r1) a.Y[b * V + i0 + j] = y[j];
             continue;
           }
+          const ColInfo ci = cols[16 * cb + col];
           T s[4];
-          if (mode[cb] == kSample) {
+          if (ci.mode == kSample) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s[j] = T(y[j] * (float)inv_t[cb]);
-          } else if (mode[cb] == kGreedy) {
+            for (int j = 0; j < 4; ++j) s[j] = T(y[j] * ci.inv_t);
+          } else if (ci.mode == kGreedy) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) s[j] = T(y[j]);
           } else {  // infinite temperature: (y + bias) / t + g
-            const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), rid[cb]);
-            s[0] = T(y[0] * (float)inv_t[cb] + gumbel_f32(w.w0));
-            s[1] = T(y[1] * (float)inv_t[cb] + gumbel_f32(w.w1));
-            s[2] = T(y[2] * (float)inv_t[cb] + gumbel_f32(w.w2));
-            s[3] = T(y[3] * (float)inv_t[cb] + gumbel_f32(w.w3));
+            const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), ci.rid);
+            s[0] = T(y[0] * ci.inv_t + gumbel_f32(w.w0));
+            s[1] = T(y[1] * ci.inv_t + gumbel_f32(w.w1));
+            s[2] = T(y[2] * ci.inv_t + gumbel_f32(w.w2));
+            s[3] = T(y[3] * ci.inv_t + gumbel_f32(w.w3));
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -419,10 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         const int rb = f / NB, cb = f - rb * NB;
         if (rb >= nrb) break;
         f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
-        int m = kGreedy;
-        T it = T(1), lbm = neg_inf<T>();
-        uint32_t r = 0;
-        bool ok = false;
+        T lbm = neg_inf<T>();
         int32_t lbi = kNoIndex;
 #pragma unroll
         for (int rb2 = 0; rb2 < kRB; ++rb2)
@@ -432,14 +453,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 #pragma unroll
         for (int c = 0; c < NB; ++c)
           if (c == cb) {
-            m = mode[c];
-            it = inv_t[c];
-            r = rid[c];
-            ok = col_ok[c];
             lbm = bm[c];
             lbi = bi[c];
           }
-        if (!ok) continue;
+        const ColInfo ci = cols[16 * cb + col];
+        const int m = ci.mode;
+        const T it = m == kGreedy ? T(1) : T(1) / T(ci.t);
+        const uint32_t r = ci.rid;
+        if (bt0 + 16 * cb + col >= B) continue;
         const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
         float beta[4];
         load_bias4(a, bt0 + 16 * cb + col, i0, beta);
