@@ -122,6 +122,9 @@ def main() -> int:
     ap.add_argument("--only-fused", action="store_true",
                     help="time the fused step only (no sweep, baselines or CPU oracle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device-to-device copy of 1 GiB, --steps times (the known-size "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -129,8 +132,19 @@ def main() -> int:
               "(sharding the vocabulary across GPUs is not built).", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return 0
 
     import decode_exact_categorical_amd as fs
     import synthetic

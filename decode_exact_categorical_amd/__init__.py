@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "FS_FP64_NOISE", "FSampleError", "sample_fused", "sample_logits", "workspace_bytes",
-    "debug_philox_words", "debug_logits", "library_path", "load_library", "KernelTimer",
+    "debug_philox_words", "debug_logits", "debug_noise", "library_path", "load_library",
+    "KernelTimer",
 ]
 
 FS_FP64_NOISE = 0x1
@@ -71,6 +72,8 @@ def load_library():
         lib.fs_profile_begin.argtypes = []
         lib.fs_profile_end.restype = i32
         lib.fs_profile_end.argtypes = [P, P, P]
+        lib.fs_debug_noise.restype = i32
+        lib.fs_debug_noise.argtypes = [P, i64, i32, P, P, P]
         lib.fs_debug_logits.restype = i32
         lib.fs_debug_logits.argtypes = [P, P, i64, i64, i64, P, P]
         _lib = lib
@@ -217,6 +220,20 @@ def debug_philox_words(seed: int, offset: int, B: int, n_ctr: int, *,
     _check(lib.fs_debug_philox_words(seed, offset, _ptr(rid), B, n_ctr, _ptr(out), _stream(dev)),
            "fs_debug_philox_words")
     return out
+
+
+def debug_noise(words: torch.Tensor, fp64_noise: bool = False):
+    """(E, g) float64 tensors the kernels derive from int32 `words` (uint32 bits):
+    one word per variate, or two consecutive words with float64 noise (test hook)."""
+    lib = load_library()
+    dev = words.device
+    _need(words, "words", torch.int32, dev)
+    n = words.numel() // 2 if fp64_noise else words.numel()
+    E = torch.empty(n, dtype=torch.float64, device=dev)
+    g = torch.empty(n, dtype=torch.float64, device=dev)
+    _check(lib.fs_debug_noise(_ptr(words), n, int(bool(fp64_noise)), _ptr(E), _ptr(g), _stream(dev)),
+           "fs_debug_noise")
+    return E, g
 
 
 def debug_logits(H: torch.Tensor, W: torch.Tensor) -> torch.Tensor:

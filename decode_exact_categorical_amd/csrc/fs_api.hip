@@ -269,6 +269,18 @@ fs_status fs_debug_philox_words(uint64_t seed, uint64_t offset, const uint32_t* 
   return FS_OK;
 }
 
+fs_status fs_debug_noise(const uint32_t* words, int64_t n, int fp64, double* E, double* g,
+                         fs_stream_t stream) {
+  g_last_error[0] = 0;
+  if (n < 0 || n >= ((int64_t)1 << 31)) return fail(FS_ERR_INVALID_ARG, "n = %lld", (long long)n);
+  if (n == 0) return FS_OK;
+  if (words == nullptr || E == nullptr || g == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "words, E or g is null");
+  hipError_t e = fs::launch_noise(words, n, fp64 != 0, E, g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "noise launch");
+  return FS_OK;
+}
+
 fs_status fs_debug_logits(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D, int64_t V,
                           float* Y, fs_stream_t stream) {
   g_last_error[0] = 0;

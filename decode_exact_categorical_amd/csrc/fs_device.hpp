@@ -28,16 +28,15 @@ __device__ __forceinline__ Words philox4x32_10(uint32_t c0, uint32_t c1, uint32_
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo0 = 0xD2511F53u * c0;
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
-    const uint32_t n0 = hi1 ^ c1 ^ k0;
-    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    // one v_mad_u64_u32 per product gives both halves
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
     c0 = n0;
-    c1 = lo1;
     c2 = n2;
-    c3 = lo0;
   }
   return Words{c0, c1, c2, c3};
 }
@@ -59,24 +58,67 @@ __device__ __forceinline__ Words noise_words(const NoiseKey& k, uint32_t j, uint
 }
 
 // ---------------------------------------------------------------------------
-// Uniform -> Gumbel.  u lies on a midpoint grid, (k + 1/2) / 2^23 from the top 23
-// bits of one word (float32 noise) or (k + 1/2) / 2^52 from the top 52 bits of
-// two words (float64 noise); every grid point and u - 1 are exact in the working
-// precision, so E = -log u is taken as -log1p(u - 1), which keeps E's relative
-// accuracy where u is close to 1 (E tiny, g large: the deep tail).  g = -log E.
+// Uniform -> exponential -> Gumbel.  u lies on a midpoint grid: (k + 1/2) / 2^23
+// from the top 23 bits of one word (float32 noise) or (k + 1/2) / 2^52 from the
+// top 52 bits of two words (float64 noise).  E = -log u is standard
+// exponential, g = -log E standard Gumbel.
+//
+// E must keep its relative accuracy where it is tiny (u near 1: the deep tail,
+// where g is large).  For u >= 1/2, E = -log u = 2 atanh(x) with
+// x = (1 - u) / (1 + u) in [0, 1/3]; 1 - u is exact on both grids, and the odd
+// series 2x (1 + x^2/3 + x^4/5 + ...) is summed to its last significant term
+// (8 terms in float32, 16 in float64, each first omitted term below the
+// precision's rounding unit).  For u < 1/2, E >= ln 2 and the hardware log2
+// (v_log_f32) times ln 2 is accurate to a few float32 ulps.  g = -ln 2 *
+// log2(E) by the hardware log2: an absolute error of ~1e-7 in g.
+//
+// Float64 noise keeps the 52-bit grid exactly and E's float64 relative accuracy
+// on u >= 1/2, which is what carries the tail from ~20 to ~40 nats; E for
+// u < 1/2 (E in [ln 2, 36.7]) and g are taken to float32 accuracy, and the
+// score is then formed and compared in float64.  Both transforms are checked
+// against float64 references over the whole float32 grid and on samples of the
+// float64 grid.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float gumbel_f32(uint32_t w) {
+constexpr float kLn2f = 0x1.62e43p-1f;
+
+__device__ __forceinline__ float exp1_f32(uint32_t w) {
   const uint32_t k = w >> 9;
   const float u = (float)(2u * k + 1u) * 0x1p-24f;
-  const float E = -log1pf(u - 1.0f);
-  return -logf(E);
+  const float x = (1.0f - u) * __builtin_amdgcn_rcpf(1.0f + u);
+  const float z = x * x;
+  float p = 1.0f / 15.0f;
+  p = __builtin_fmaf(p, z, 1.0f / 13.0f);
+  p = __builtin_fmaf(p, z, 1.0f / 11.0f);
+  p = __builtin_fmaf(p, z, 1.0f / 9.0f);
+  p = __builtin_fmaf(p, z, 1.0f / 7.0f);
+  p = __builtin_fmaf(p, z, 1.0f / 5.0f);
+  p = __builtin_fmaf(p, z, 1.0f / 3.0f);
+  p = __builtin_fmaf(p, z, 1.0f);
+  const float e_tail = 2.0f * x * p;
+  const float e_body = -kLn2f * __builtin_amdgcn_logf(u);
+  return u >= 0.5f ? e_tail : e_body;
+}
+
+__device__ __forceinline__ float gumbel_f32(uint32_t w) {
+  return -kLn2f * __builtin_amdgcn_logf(exp1_f32(w));
+}
+
+__device__ __forceinline__ double exp1_f64(uint32_t hi, uint32_t lo) {
+  const uint64_t k = ((((uint64_t)hi) << 32) | (uint64_t)lo) >> 12;
+  const double u = (double)(2ull * k + 1ull) * 0x1p-53;
+  if (u >= 0.5) {
+    const double x = (1.0 - u) / (1.0 + u);
+    const double z = x * x;
+    double p = 1.0 / 31.0;
+#pragma unroll
+    for (int n = 14; n >= 0; --n) p = __builtin_fma(p, z, 1.0 / (2 * n + 1));
+    return 2.0 * x * p;
+  }
+  return (double)(-kLn2f * __builtin_amdgcn_logf((float)u));
 }
 
 __device__ __forceinline__ double gumbel_f64(uint32_t hi, uint32_t lo) {
-  const uint64_t k = ((((uint64_t)hi) << 32) | (uint64_t)lo) >> 12;
-  const double u = (double)(2ull * k + 1ull) * 0x1p-53;
-  const double E = -log1p(u - 1.0);
-  return -log(E);
+  return (double)(-kLn2f * __builtin_amdgcn_logf((float)exp1_f64(hi, lo)));
 }
 
 // ---------------------------------------------------------------------------

@@ -11,7 +11,7 @@
 //    8 waves (two per SIMD) each own a contiguous run of vocabulary rows,
 //    assigned in 8-row units so every wave of the chip ends within 8 rows of
 //    the others.  A wave walks its rows in passes of up to 5 MFMA row blocks
-//    (80 rows; 4 blocks with 64 batch columns).
+//    (80 rows).
 //  * W goes straight from HBM into VGPRs in the bf16 MFMA A-operand layout
 //    (lane l holds 16 bytes of row l % 16; the four lanes of a row read 64
 //    contiguous bytes), two k-steps of 32 in flight per row block.
@@ -31,6 +31,8 @@
 //    is a multiply and a compare.  Greedy columns (t <= 0 or NaN) fold in the
 //    bias only.  Columns with an infinite (or beyond 2^60) temperature fold in
 //    the bias and add g after the division, which keeps (y + bias) / t + g.
+//    With 64 batch columns the fold's registers do not fit beside the
+//    accumulators, and the noise is added after the k-loop instead.
 //  * Float64 noise keeps the score in float64: y + bias and the noise are
 //    combined after the k-loop, with two Philox calls per fragment.
 //  * Scores feed a per-lane running argmax (larger score, then smaller index);
@@ -96,18 +98,22 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
   }
 }
 
-// MFMA row blocks (16 rows) per wave per pass: five, or four with four column
-// blocks, where the accumulators need the room (a wave has 256 VGPRs at two
-// waves per SIMD).
-template <int NB>
-struct RowBlocks {
-  static constexpr int value = NB >= 4 ? 4 : 5;
+// MFMA row blocks (16 rows) per wave per pass.
+constexpr int kRB = 5;
+
+// Whether float32 noise is folded into the accumulators inside the k-loop.
+// With 64 batch columns the fold's registers do not fit beside the
+// accumulators (a wave has 256 VGPRs at two waves per SIMD); the noise is then
+// added after the k-loop instead, still in one pass over the wave's rows.
+template <int NB, int EPI>
+struct FoldNoise {
+  static constexpr bool value = EPI == kEpiSample32 && NB <= 3;
 };
 
 template <int NB, int EPI, bool HAS_BIAS>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
-  constexpr int kRB = RowBlocks<NB>::value;
+  constexpr bool kFold = FoldNoise<NB, EPI>::value;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // The wave index is wave-uniform; saying so keeps every quantity derived
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     };
     auto slot_noise = [&](int f, const f32x4& beta) -> Fold {
       Fold out = {{0.f, 0.f, 0.f, 0.f}, false};
-      if (EPI != kEpiSample32 || f >= kRB * kNoiseSlots) return out;
+      if (!kFold || f >= kRB * kNoiseSlots) return out;
       const int rb = f / kNoiseSlots, cb = f - rb * kNoiseSlots;
       if (rb >= nrb || cb >= NB) return out;
       out.any = true;
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // Bias of fragment slot f: four scalar loads from clamped, valid addresses
     // (the slot's values where they exist, something harmless elsewhere).
     auto bias_slot_load = [&](f32x4& dst, int f) {
-      if (!HAS_BIAS || EPI != kEpiSample32) return;
+      if (!HAS_BIAS || !kFold) return;
       const int ff = f < kRB * kNoiseSlots ? f : 0;
       const int rb = ff / kNoiseSlots, cb = ff - rb * kNoiseSlots;
       int64_t b = bt0 + 16 * cb + col;
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 #undef FS_FOLD_SLOT
 
     // End of pass: scores of this wave's fragments.
-    if (EPI != kEpiSample64) {
+    if (EPI == kEpiStore || kFold) {
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         if (rb >= nrb) continue;
@@ -435,9 +441,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         }
       }
     } else {
-      // Float64 noise, score in float64.  The per-fragment work (two Philox
-      // calls, four float64 logs) is large, so the loop stays rolled and the
-      // fragment is picked out of the accumulators by uniform branches.
+      // Noise added after the k-loop: float64 noise (score in float64), or
+      // float32 noise for 64 batch columns.  The per-fragment work (Philox,
+      // four logs) is large, so the loop stays rolled and the fragment is
+      // picked out of the accumulators by uniform branches.
 #pragma unroll 1
       for (int f = 0; f < kRB * NB; ++f) {
         const int rb = f / NB, cb = f - rb * NB;
@@ -468,13 +475,19 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         if (m == kGreedy) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) s[j] = T(y[j]) + T(beta[j]);
-        } else {
+        } else if (EPI == kEpiSample64) {
           const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), r);
           const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, r);
           s[0] = (T(y[0]) + T(beta[0])) * it + T(gumbel_f64(w0.w0, w0.w1));
           s[1] = (T(y[1]) + T(beta[1])) * it + T(gumbel_f64(w0.w2, w0.w3));
           s[2] = (T(y[2]) + T(beta[2])) * it + T(gumbel_f64(w1.w0, w1.w1));
           s[3] = (T(y[3]) + T(beta[3])) * it + T(gumbel_f64(w1.w2, w1.w3));
+        } else {
+          const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), r);
+          s[0] = T((y[0] + beta[0]) * (float)it + gumbel_f32(w.w0));
+          s[1] = T((y[1] + beta[1]) * (float)it + gumbel_f32(w.w1));
+          s[2] = T((y[2] + beta[2]) * (float)it + gumbel_f32(w.w2));
+          s[3] = T((y[3] + beta[3]) * (float)it + gumbel_f32(w.w3));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

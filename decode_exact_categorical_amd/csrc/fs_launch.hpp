@@ -49,6 +49,10 @@ hipError_t launch_logits_stage1(const LogitsArgs& a, bool fp64, hipStream_t stre
 hipError_t launch_stage2(const void* cand, int64_t B, int nT, bool fp64, int64_t* out,
                          hipStream_t stream);
 
+// Test hook: the noise transforms applied to given words.
+hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,
+                        hipStream_t stream);
+
 // Test hook: Philox words.
 hipError_t launch_philox_words(NoiseKey key, const uint32_t* row_ids, int64_t B,
                                int64_t n_ctr, uint32_t* out, hipStream_t stream);

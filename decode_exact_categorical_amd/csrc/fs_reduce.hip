@@ -1,4 +1,4 @@
-// fs_reduce.hip -- Stage 2 of both samplers, and the Philox test hook.
+// fs_reduce.hip -- Stage 2 of both samplers, and the Philox and noise test hooks.
 //
 // Stage 2 follows the FlashSampling page ("algorithm details", Stage 2): for each
 // row, the tile whose candidate score is largest gives the sampled index.  One
@@ -46,7 +46,27 @@ __global__ __launch_bounds__(256) void philox_words_kernel(NoiseKey key, const u
   reinterpret_cast<uint4*>(out)[t] = v;
 }
 
+__global__ __launch_bounds__(256) void noise_kernel(const uint32_t* words, int64_t n, bool fp64,
+                                                    double* E, double* g) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  if (fp64) {
+    E[t] = exp1_f64(words[2 * t], words[2 * t + 1]);
+    g[t] = gumbel_f64(words[2 * t], words[2 * t + 1]);
+  } else {
+    E[t] = (double)exp1_f32(words[t]);
+    g[t] = (double)gumbel_f32(words[t]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,
+                        hipStream_t stream) {
+  const dim3 grid((unsigned)((n + 255) / 256));
+  hipLaunchKernelGGL(noise_kernel, grid, dim3(256), 0, stream, words, n, fp64, E, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_stage2(const void* cand, int64_t B, int nT, bool fp64, int64_t* out,
                          hipStream_t stream) {

@@ -172,6 +172,16 @@ fs_status fs_debug_philox_words(uint64_t seed, uint64_t offset, const uint32_t *
                                 fs_stream_t stream);
 
 /*
+ * Test hook: the noise transforms the samplers apply to Philox words.
+ * Default noise (fp64 == 0): for t < n, E[t] and g[t] are the exponential and
+ * Gumbel variates the kernels derive from the single word words[t].
+ * Float64 noise (fp64 != 0): from the word pair (words[2t], words[2t+1]).
+ *   words device uint32 [n] or [2n];  E, g device float64 [n];  0 <= n < 2^31.
+ */
+fs_status fs_debug_noise(const uint32_t *words, int64_t n, int fp64, double *E, double *g,
+                         fs_stream_t stream);
+
+/*
  * Test hook: the logits y = H W^T of the fused path, written to Y (device,
  * float [B, V]).  Runs the same matmul code as fs_sample_fused (same tiling and
  * accumulation order) with a store in place of the sampling epilogue.

@@ -60,6 +60,8 @@ def _load():
         lib.oracle_noise_at.argtypes = [u64, u64, u32, i64, i32, P, P, P]
         lib.oracle_noise_of_uniform.restype = None
         lib.oracle_noise_of_uniform.argtypes = [ctypes.c_double, P, P]
+        lib.oracle_noise_grid.restype = None
+        lib.oracle_noise_grid.argtypes = [i32, u64, i64, P, P]
         lib.oracle_logits.restype = None
         lib.oracle_logits.argtypes = [P, P, i64, i64, i64, P]
         lib.oracle_sample_fused.restype = None
@@ -133,6 +135,14 @@ def noise_of_uniform(u: float):
     E, g = ctypes.c_double(), ctypes.c_double()
     _load().oracle_noise_of_uniform(float(u), ctypes.byref(E), ctypes.byref(g))
     return E.value, g.value
+
+
+def noise_grid(fp64: bool, k0: int, n: int):
+    """(E, g) float64 for the midpoint-grid points k0 .. k0+n-1 (23 or 52 bits)."""
+    E = np.zeros(n, dtype=np.float64)
+    g = np.zeros(n, dtype=np.float64)
+    _load().oracle_noise_grid(int(fp64), k0, n, _ptr(E), _ptr(g))
+    return E, g
 
 
 def logits(H, W) -> np.ndarray:

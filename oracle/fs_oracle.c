@@ -195,6 +195,20 @@ void oracle_noise_of_uniform(double u, double *E, double *g)
     *g = gumbel_of(u);
 }
 
+/* E and g for the grid points k0 .. k0+n-1 of the 23-bit (fp64 == 0) or 52-bit
+ * midpoint grid, u = (k + 1/2) / 2^bits [MG change; FS (3)]. */
+void oracle_noise_grid(int fp64, uint64_t k0, int64_t n, double *E, double *g)
+{
+    const double scale = fp64 ? 4503599627370496.0 : 8388608.0;   /* 2^52 or 2^23 */
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double u = ((double)(k0 + (uint64_t)t) + 0.5) / scale;
+        double e = exponential_of(u);
+        E[t] = e;
+        g[t] = -log(e);
+    }
+}
+
 /* Logits Y[b,i] = sum_d H[b,d] W[i,d], float64, d ascending [FS (1)].
  * H[B,D] and W[V,D] are bf16 bit patterns, row-major. */
 void oracle_logits(const uint16_t *H, const uint16_t *W, int64_t B, int64_t D,

@@ -241,3 +241,64 @@ def test_fused_matches_logits_sampler_stream(dev):
     ref, gap, _ = oracle.sample_logits(y.cpu().numpy(), temp.numpy(), seed=5, offset=6)
     check_index_parity(b, ref, gap, "standalone on fused logits")
     check_index_parity(a, ref, gap, "fused vs oracle on fused logits")
+
+
+def test_noise_transform_float32_full_grid(dev):
+    """The float32 E and g of every one of the 2^23 grid points, against the
+    oracle's float64 values: E to a few float32 ulps relative (including the
+    deep tail, u near 1), g to a few float32 ulps of max(1, |g|)."""
+    say("noise transform: all 2^23 float32 grid points")
+    k = np.arange(2**23, dtype=np.uint64)
+    low = np.random.default_rng(3).integers(0, 512, size=k.size, dtype=np.uint64)
+    words = ((k << np.uint64(9)) | low).astype(np.uint32)
+    E, g = fs.debug_noise(torch.from_numpy(words.view(np.int32)).to(dev))
+    E, g = E.cpu().numpy(), g.cpu().numpy()
+    Eo, go = oracle.noise_grid(False, 0, 2**23)
+    relE = np.abs(E - Eo) / Eo
+    errg = np.abs(g - go) / np.maximum(1.0, np.abs(go))
+    say(f"  max rel err E = {relE.max():.3e} (at u index {relE.argmax()}), "
+        f"max err g / max(1,|g|) = {errg.max():.3e}")
+    assert relE.max() <= NOISE32_E_REL and errg.max() <= NOISE32_G_REL
+
+
+def test_noise_transform_float64_samples(dev):
+    """Float64 noise on 64 runs of 16384 consecutive points of the 52-bit grid at
+    random places plus both ends: E keeps float64 relative accuracy where
+    u >= 1/2 (E < ln 2, the tail), float32 accuracy elsewhere; g is float32-accurate."""
+    say("noise transform: float64 grid samples")
+    rng = np.random.default_rng(4)
+    starts = [0, 2**52 - 16384, 2**51 - 8192] + [int(x) for x in
+                                                 rng.integers(0, 2**52 - 16384, size=61)]
+    ks, Eo, go = [], [], []
+    for k0 in starts:
+        e, gg = oracle.noise_grid(True, k0, 16384)
+        ks.append(np.arange(k0, k0 + 16384, dtype=np.uint64))
+        Eo.append(e)
+        go.append(gg)
+    k = np.concatenate(ks)
+    Eo, go = np.concatenate(Eo), np.concatenate(go)
+    low = rng.integers(0, 4096, size=k.size, dtype=np.uint64)
+    full = (k << np.uint64(12)) | low
+    words = np.empty(2 * k.size, dtype=np.uint32)
+    words[0::2] = (full >> np.uint64(32)).astype(np.uint32)
+    words[1::2] = (full & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+    E, g = fs.debug_noise(torch.from_numpy(words.view(np.int32)).to(dev), fp64_noise=True)
+    E, g = E.cpu().numpy(), g.cpu().numpy()
+    relE = np.abs(E - Eo) / Eo
+    tail = Eo < np.log(2.0)
+    errg = np.abs(g - go) / np.maximum(1.0, np.abs(go))
+    say(f"  max rel err E: tail {relE[tail].max():.3e}, body {relE[~tail].max():.3e}; "
+        f"max err g / max(1,|g|) = {errg.max():.3e}; E range [{E.min():.4e}, {E.max():.4f}]")
+    assert relE[tail].max() <= NOISE64_E_TAIL_REL
+    assert relE[~tail].max() <= NOISE32_E_REL
+    assert errg.max() <= NOISE32_G_REL
+    assert E.min() == pytest.approx(1.1102230246251565e-16, rel=1e-12)
+
+
+# Bounds for the noise transforms (float32 unit roundoff u32 = 2^-24 ~ 6e-8):
+# E is a handful of float32 operations (reciprocal, 8-term series or hardware
+# log2, scaling), g one hardware log2 and one scaling; float64 E in the tail
+# is a float64 division and a 16-term series.
+NOISE32_E_REL = 8 * 2.0**-24
+NOISE32_G_REL = 8 * 2.0**-24
+NOISE64_E_TAIL_REL = 16 * 2.0**-53
