@@ -11,7 +11,7 @@
 //    8 waves (two per SIMD) each own a contiguous run of vocabulary rows,
 //    assigned in 8-row units so every wave of the chip ends within 8 rows of
 //    the others.  A wave walks its rows in passes of up to 5 MFMA row blocks
-//    (80 rows).
+//    (80 rows; 4 with float64 noise and 64 batch columns).
 //  * W goes straight from HBM into VGPRs in the bf16 MFMA A-operand layout
 //    (lane l holds 16 bytes of row l % 16; the four lanes of a row read 64
 //    contiguous bytes), two k-steps of 32 in flight per row block.
@@ -31,8 +31,8 @@
 //    is a multiply and a compare.  Greedy columns (t <= 0 or NaN) fold in the
 //    bias only.  Columns with an infinite (or beyond 2^60) temperature fold in
 //    the bias and add g after the division, which keeps (y + bias) / t + g.
-//    With 64 batch columns the fold's registers do not fit beside the
-//    accumulators, and the noise is added after the k-loop instead.
+//    With 64 batch columns and a bias the fold's registers do not fit beside
+//    the accumulators, and the noise is added after the k-loop instead.
 //  * Float64 noise keeps the score in float64: y + bias and the noise are
 //    combined after the k-loop, with two Philox calls per fragment.
 //  * Scores feed a per-lane running argmax (larger score, then smaller index);
@@ -98,22 +98,29 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
   }
 }
 
-// MFMA row blocks (16 rows) per wave per pass.
-constexpr int kRB = 5;
+// MFMA row blocks (16 rows) per wave per pass: five, or four where float64
+// running bests beside 64 batch columns of accumulators would not fit in a
+// wave's 256 VGPRs (two waves per SIMD).
+template <int NB, int EPI>
+struct RowBlocks {
+  static constexpr int value = NB >= 4 && EPI == kEpiSample64 ? 4 : 5;
+};
 
 // Whether float32 noise is folded into the accumulators inside the k-loop.
-// With 64 batch columns the fold's registers do not fit beside the
-// accumulators (a wave has 256 VGPRs at two waves per SIMD); the noise is then
-// added after the k-loop instead, still in one pass over the wave's rows.
-template <int NB, int EPI>
+// With 64 batch columns and a bias the fold's registers (the prefetched bias
+// slots) do not fit beside the accumulators (a wave has 256 VGPRs at two waves
+// per SIMD); the noise is then added after the k-loop instead, still in one
+// pass over the wave's rows.
+template <int NB, int EPI, bool HAS_BIAS>
 struct FoldNoise {
-  static constexpr bool value = EPI == kEpiSample32 && NB <= 3;
+  static constexpr bool value = EPI == kEpiSample32 && (NB <= 3 || !HAS_BIAS);
 };
 
 template <int NB, int EPI, bool HAS_BIAS>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
-  constexpr bool kFold = FoldNoise<NB, EPI>::value;
+  constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS>::value;
+  constexpr int kRB = RowBlocks<NB, EPI>::value;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // The wave index is wave-uniform; saying so keeps every quantity derived
@@ -442,9 +449,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       }
     } else {
       // Noise added after the k-loop: float64 noise (score in float64), or
-      // float32 noise for 64 batch columns.  The per-fragment work (Philox,
-      // four logs) is large, so the loop stays rolled and the fragment is
-      // picked out of the accumulators by uniform branches.
+      // float32 noise for 64 batch columns with a bias.  The per-fragment work
+      // (Philox, four logs) is large, so the loop stays rolled and the
+      // fragment is picked out of the accumulators by uniform branches.
 #pragma unroll 1
       for (int f = 0; f < kRB * NB; ++f) {
         const int rb = f / NB, cb = f - rb * NB;
