@@ -14,7 +14,8 @@
 //    (80 rows; 4 with float64 noise and 64 batch columns).
 //  * W goes straight from HBM into VGPRs in the bf16 MFMA A-operand layout
 //    (lane l holds 16 bytes of row l % 16; the four lanes of a row read 64
-//    contiguous bytes), two k-steps of 32 in flight per row block.
+//    contiguous bytes).  Loads go in k-step pairs, the two halves of each
+//    row's 128-byte segment back to back, with two pairs in flight.
 //  * H is the MFMA B operand (batch as the N dimension, 16 to 64 columns).  It
 //    is staged through LDS in chunks of 256 k, double-buffered and padded so
 //    the fragment reads are bank-conflict free, and shared by the 8 waves: H
@@ -98,22 +99,20 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
   }
 }
 
-// MFMA row blocks (16 rows) per wave per pass: five, or four where float64
-// running bests beside 64 batch columns of accumulators would not fit in a
-// wave's 256 VGPRs (two waves per SIMD).
+// MFMA row blocks (16 rows) per wave per pass: five with up to 32 batch
+// columns, three with more, where two k-step pairs of W fragments in flight
+// beside the accumulators would not fit in a wave's 256 VGPRs (two waves per
+// SIMD).  Four row blocks stream W markedly slower than three or five.
 template <int NB, int EPI>
 struct RowBlocks {
-  static constexpr int value = NB >= 4 && EPI == kEpiSample64 ? 4 : 5;
+  static constexpr int value = NB <= 2 ? 5 : 3;
 };
 
-// Whether float32 noise is folded into the accumulators inside the k-loop.
-// With 64 batch columns and a bias the fold's registers (the prefetched bias
-// slots) do not fit beside the accumulators (a wave has 256 VGPRs at two waves
-// per SIMD); the noise is then added after the k-loop instead, still in one
-// pass over the wave's rows.
+// Whether float32 noise is folded into the accumulators inside the k-loop
+// (otherwise it is added after the k-loop, still in one pass over the rows).
 template <int NB, int EPI, bool HAS_BIAS>
 struct FoldNoise {
-  static constexpr bool value = EPI == kEpiSample32 && (NB <= 3 || !HAS_BIAS);
+  static constexpr bool value = EPI == kEpiSample32;
 };
 
 template <int NB, int EPI, bool HAS_BIAS>
@@ -249,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // Float32 noise of fragment slot f = 4*rb + cb (rb < kRB): bias + t * g of
     // the lane's 4 rows, or the bias alone for greedy and infinite-temperature
     // columns; the caller folds it into acc[rb][cb] (FS_FOLD_SLOT).  The bias
-    // arrives from bias_slot_load, issued two k-steps earlier, so this issues no
+    // arrives from bias_slot_load, issued four k-steps earlier, so this issues no
     // memory operation.
     struct Fold {
       float v[4];
@@ -317,20 +316,27 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }                                                                    \
   } while (0)
 
-    // W fragments of k-step ks (a prefetch past the last k-step re-reads it).
-    // In a final k-step that runs past D (D % 32 != 0) the lanes past D read
-    // k = 0 instead; H is zero there, so their products vanish for finite W.
-    auto load_w = [&](u32x4 (&dst)[kRB], int ks) {
+    // W fragments of the k-step pair (2q, 2q + 1), row block by row block, so
+    // the two 64-byte halves of each row's 128-byte segment are requested back
+    // to back: HBM streams markedly faster so than when a whole k-step of row
+    // blocks is requested at a time.  A step past the last one re-reads the
+    // last one.  In a final k-step that runs past D (D % 32 != 0) the lanes
+    // past D read k = 0 instead; H is zero there, so their products vanish for
+    // finite W.
+    auto step_base = [&](int ks) -> const uint16_t* {
       if (ks > KS - 1) ks = KS - 1;
       const int64_t k = (int64_t)ks * 32;
-      const uint16_t* wk = wwave + k;
-      if (k + 32 <= D) {
+      int64_t kl = 0;
+      if (k + 32 > D) kl = (k + 8 * grp < D) ? 0 : -k - 8 * grp;
+      return wwave + k + kl;
+    };
+    auto load_pair = [&](u32x4 (&dst)[2][kRB], int q) {
+      const uint16_t* w0 = step_base(2 * q);
+      const uint16_t* w1 = step_base(2 * q + 1);
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) dst[rb] = load_frag(wk + woff[rb]);
-      } else {
-        const int64_t kl = (k + 8 * grp < D) ? 0 : -k - 8 * grp;
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) dst[rb] = load_frag(wk + kl + woff[rb]);
+      for (int rb = 0; rb < kRB; ++rb) {
+        dst[0][rb] = load_frag(w0 + woff[rb]);
+        dst[1][rb] = load_frag(w1 + woff[rb]);
       }
     };
     auto mma = [&](const u32x4 (&w)[kRB], int buf, int kk) {
@@ -345,12 +351,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[rb]), hf[cb], acc[rb][cb], 0, 0, 0);
     };
 
-    // The k-loop is straight-line: every k-step issues the same loads in the
-    // same order (kRB W fragments, then the bias of the slot folded two steps
-    // later), every chunk the same NB H loads, and every pass runs NC * 8
-    // k-steps (steps past the last real one re-read it against zero H).  The
-    // compiler can then count loads in flight exactly and waits only for the
-    // ones it needs, keeping two k-steps of W in flight across the barriers.
+    // The k-loop is straight-line: every k-step pair issues the same loads in
+    // the same order (2 x kRB W fragments, then the biases of the slots folded
+    // four steps later), every chunk the same NB H loads, and every pass runs
+    // NC * 8 k-steps (steps past the last real one re-read it against zero H).
+    // The compiler can then count loads in flight exactly and waits only for
+    // the ones it needs, keeping two k-step pairs of W in flight across the
+    // barriers.
     typedef std::integral_constant<int, 0> Half0;
     typedef std::integral_constant<int, 1> Half1;
     h_load(0, Half0{});
@@ -359,41 +366,52 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     h_store(0, Half1{});
     __syncthreads();
 
-    u32x4 wa[kRB], wb[kRB];
-    f32x4 ba = f32x4{0.f, 0.f, 0.f, 0.f}, bb = f32x4{0.f, 0.f, 0.f, 0.f};
-    load_w(wa, 0);
-    bias_slot_load(ba, 0);
-    load_w(wb, 1);
-    bias_slot_load(bb, 1);
+    u32x4 pa[2][kRB], pb[2][kRB];
+    const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 ba0 = z4, ba1 = z4, bb0 = z4, bb1 = z4;
+    load_pair(pa, 0);
+    bias_slot_load(ba0, 0);
+    bias_slot_load(ba1, 1);
+    load_pair(pb, 1);
+    bias_slot_load(bb0, 2);
+    bias_slot_load(bb1, 3);
+    static_assert(kStepsPerChunk % 4 == 0, "a chunk holds whole pairs of pairs");
     for (int c = 0; c < NC; ++c) {
       const int buf = c & 1;
       const int cn = c + 1 < NC ? c + 1 : c;
       h_load(cn, Half0{});
 #pragma unroll
-      for (int j = 0; j < kStepsPerChunk; j += 2) {
+      for (int j = 0; j < kStepsPerChunk; j += 4) {
         const int ks = c * kStepsPerChunk + j;
-        // sched_barrier keeps the compiler from moving the loads of step ks + 2
-        // next to their use: each phase stays where it is written, so two
-        // k-steps of W stay in flight.
-        mma(wa, buf, j * 32);
-        FS_FOLD_SLOT(ks, ba);
+        const int q = ks >> 1;
+        // sched_barrier keeps each phase where it is written, so the compiler
+        // does not move the loads of a pair next to their use.
+        mma(pa[0], buf, j * 32);
+        FS_FOLD_SLOT(ks, ba0);
+        mma(pa[1], buf, (j + 1) * 32);
+        FS_FOLD_SLOT(ks + 1, ba1);
         __builtin_amdgcn_sched_barrier(0);
-        load_w(wa, ks + 2);
-        bias_slot_load(ba, ks + 2);
+        load_pair(pa, q + 2);
+        bias_slot_load(ba0, ks + 4);
+        bias_slot_load(ba1, ks + 5);
         __builtin_amdgcn_sched_barrier(0);
-        mma(wb, buf, (j + 1) * 32);
-        FS_FOLD_SLOT(ks + 1, bb);
+        mma(pb[0], buf, (j + 2) * 32);
+        FS_FOLD_SLOT(ks + 2, bb0);
+        mma(pb[1], buf, (j + 3) * 32);
+        FS_FOLD_SLOT(ks + 3, bb1);
         __builtin_amdgcn_sched_barrier(0);
-        load_w(wb, ks + 3);
-        bias_slot_load(bb, ks + 3);
+        load_pair(pb, q + 3);
+        bias_slot_load(bb0, ks + 6);
+        bias_slot_load(bb1, ks + 7);
         __builtin_amdgcn_sched_barrier(0);
         // The other buffer was last read in the previous chunk, before the
         // barrier that ended it, so the next chunk can land there at once.
         if (j == 0) {
           h_store(buf ^ 1, Half0{});
           h_load(cn, Half1{});
+        } else {
+          h_store(buf ^ 1, Half1{});
         }
-        if (j == 2) h_store(buf ^ 1, Half1{});
       }
       __syncthreads();
     }
