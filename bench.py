@@ -7,12 +7,15 @@ N(0, 0.02), per-row temperature ~ U[0.5, 1.2], seeded per row, exact
 sampling with float32 noise (no filtering); B = 64 is the headline, B = 1, 8, 32 are reported
 beside it.  Inputs are synthetic and already resident in HBM when timing starts.
 
-One step = one fs_sample_fused call (Stage 1 + Stage 2), offset advancing each
-step.  Prints one JSON line: `value` is microseconds per decode step at B = 64;
-`roofline` prices the Stage 1 kernel's algorithmic HBM bytes against its own
-average duration, read from HIP events the library records around it on the
-stream it runs on, over the same timed region; `cpu_baseline` is the float64 CPU
-oracle computing the same step on this host's cores.
+One step = one fs_sample_fused call: a single kernel launch, Stage 1 with
+Stage 2 in the last workgroup of each batch tile, offset advancing each step.
+Prints one JSON line: `value` is microseconds per decode step at B = 64 (mean
+over the timed steps; p10/p50/p90 of the per-step times beside it);
+`roofline` prices that kernel's algorithmic HBM bytes against its own average
+duration, read from HIP events the library records around it on the stream it
+runs on, over the same timed region; `standalone_sampler` does the same for
+fs_sample_logits; `cpu_baseline` is the float64 CPU oracle computing the same
+step on this host's cores.
 """
 from __future__ import annotations
 
@@ -29,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("µs/decode-step & achieved HBM GB/s (fused LM-head+sample), "
           "D=4096 V=151936 B=1–64")
 D_MODEL, VOCAB = 4096, 151936
+LOGITS_CHUNK = 2048             # logits per workgroup of the standalone sampler
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_stage1_qwen3_8b_b64_traffic.txt")
 KERNEL_SOURCES = ["decode_exact_categorical_amd/csrc/fs_fused.hip",
@@ -72,31 +76,47 @@ def fused_tiles(V: int, cus: int) -> int:
     return max(1, min((V + 7) // 8, cus))
 
 
-def stage1_alg_bytes(B: int, D: int, V: int, n_tiles: int, bias: bool = False) -> int:
-    """What Stage 1 must move: W once, H once, temperatures, [bias], candidates out."""
-    return V * D * 2 + B * D * 2 + 4 * B + (4 * B * V if bias else 0) + 8 * B * n_tiles
+def kernel_alg_bytes(B: int, D: int, V: int, n_tiles: int, bias: bool = False, cand: int = 8) -> int:
+    """What one fused sampling launch must move (Stage 1 and Stage 2 in one kernel):
+    W once, H once, temperatures, [bias], candidates written and read back once,
+    the sampled indices written."""
+    return (V * D * 2 + B * D * 2 + 4 * B + (4 * B * V if bias else 0)
+            + 2 * cand * B * n_tiles + 8 * B)
 
 
-def step_alg_bytes(B: int, D: int, V: int, n_tiles: int) -> int:
-    """One decode step (Stage 1 + Stage 2): candidates written and read once, out written."""
-    return V * D * 2 + B * D * 2 + 4 * B + 2 * 8 * B * n_tiles + 8 * B
+def logits_alg_bytes(B: int, V: int, cand: int = 8) -> int:
+    """What one standalone sampling launch must move: the float32 logits once,
+    temperatures, candidates written and read back once, the indices written."""
+    n_tiles = (V + LOGITS_CHUNK - 1) // LOGITS_CHUNK
+    return 4 * B * V + 4 * B + 2 * cand * B * n_tiles + 8 * B
 
 
-def time_fused(fs, torch, H, W, temp, steps, warmup, offset0=0):
-    """(ms per step over `steps` timed calls, mean Stage 1 ms, mean Stage 2 ms)."""
+def percentiles(xs, qs=(10, 50, 90)):
+    ys = sorted(xs)
+    out = {}
+    for q in qs:
+        k = min(len(ys) - 1, max(0, int(round(q / 100 * (len(ys) - 1)))))
+        out[f"p{q}"] = ys[k]
+    return out
+
+
+def time_calls(torch, fs, call, steps, warmup):
+    """Time `steps` calls of call(s) after `warmup` untimed ones: (mean ms per step
+    over the timed region, mean kernel ms from the library's own events on the
+    stream the kernel runs on, per-step ms percentiles from events between steps)."""
     for s in range(warmup):
-        fs.sample_fused(H, W, temp, seed=1234, offset=offset0 + s)
+        call(s)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     with fs.KernelTimer() as kt:
-        e0.record()
+        ev[0].record()
         for s in range(steps):
-            fs.sample_fused(H, W, temp, seed=1234, offset=offset0 + warmup + s)
-        e1.record()
+            call(warmup + s)
+            ev[s + 1].record()
         torch.cuda.synchronize()
-    total = e0.elapsed_time(e1)
-    n = max(1, kt.calls)
-    return total / steps, kt.stage1_ms / n, kt.stage2_ms / n
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total = ev[0].elapsed_time(ev[steps])
+    return total / steps, kt.kernel_ms / max(1, kt.calls), percentiles(per_step)
 
 
 def time_region(torch, fn, steps, warmup):
@@ -166,15 +186,15 @@ def main() -> int:
     torch.cuda.synchronize()
 
     nT = fused_tiles(VOCAB, cus)
+    Hb, Tb = H[:B].contiguous(), temp[:B].contiguous()
     log(f"timing fused step B={B}: {args.warmup} warmup + {args.steps} timed steps")
     t0 = time.perf_counter()
-    ms_step, s1_ms, s2_ms = time_fused(fs, torch, H[:B].contiguous(), W, temp[:B].contiguous(),
-                                       args.steps, args.warmup)
+    ms_step, k_ms, pct = time_calls(
+        torch, fs, lambda s: fs.sample_fused(Hb, W, Tb, seed=1234, offset=s), args.steps, args.warmup)
     wall = time.perf_counter() - t0
     us_step = ms_step * 1e3
-    step_bytes = step_alg_bytes(B, D_MODEL, VOCAB, nT)
-    s1_bytes = stage1_alg_bytes(B, D_MODEL, VOCAB, nT)
-    s1_gbs = s1_bytes / (s1_ms * 1e-3) / 1e9
+    k_bytes = kernel_alg_bytes(B, D_MODEL, VOCAB, nT)
+    k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
     traffic = measured_traffic()
     result = {
         "metric": METRIC,
@@ -196,37 +216,62 @@ def main() -> int:
             "offset": "advances every step",
         },
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
-        "hbm_gbs_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_gbs_step": round(k_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_us_percentiles": {k: round(v * 1e3, 2) for k, v in pct.items()},
         "roofline": {
-            "kernel": "fused_stage1_kernel (matmul + transform + noise + tile argmax)",
+            "kernel": "fused_stage1_kernel (matmul + transform + noise + tile argmax; "
+                      "Stage 2 in the last workgroup of each batch tile)",
             "bound": "hbm",
-            "achieved": round(s1_gbs, 1),
+            "achieved": round(k_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(s1_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(k_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "alg_bytes_per_launch": s1_bytes,
-            "avg_launch_us": round(s1_ms * 1e3, 2),
+            "alg_bytes_per_launch": k_bytes,
+            "avg_launch_us": round(k_ms * 1e3, 2),
         },
-        "stage2_avg_us": round(s2_ms * 1e3, 2),
         "timed_wall_s": round(wall, 3),
     }
 
     if not args.only_fused:
         per = {}
         for b in sweep:
-            ms, a1, a2 = time_fused(fs, torch, H[:b].contiguous(), W, temp[:b].contiguous(),
-                                    max(20, args.steps // 2), args.warmup, offset0=10**6)
+            Hs, Ts = H[:b].contiguous(), temp[:b].contiguous()
+            ms, kms, pc = time_calls(
+                torch, fs, lambda s: fs.sample_fused(Hs, W, Ts, seed=1234, offset=10**6 + s),
+                max(20, args.steps // 2), args.warmup)
+            kb = kernel_alg_bytes(b, D_MODEL, VOCAB, nT)
             per[str(b)] = {"us_per_step": round(ms * 1e3, 2),
-                           "stage1_us": round(a1 * 1e3, 2),
-                           "stage1_gbs": round(stage1_alg_bytes(b, D_MODEL, VOCAB, nT) / (a1 * 1e-3) / 1e9, 1),
+                           "p50_us": round(pc["p50"] * 1e3, 2),
+                           "kernel_us": round(kms * 1e3, 2),
+                           "kernel_gbs": round(kb / (kms * 1e-3) / 1e9, 1),
+                           "kernel_frac": round(kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "tokens_per_s": round(b / (ms * 1e-3), 1)}
             log(f"  B={b}: {per[str(b)]}")
         result["batch_sweep"] = per
 
+        # The standalone sampler over float32 logits: the tail-rate workload's
+        # chunk shape (4096 rows x 131072) and a decode-sized batch.
+        log("timing the standalone sampler")
+        sa = {}
+        for (bl, vl, f64) in ((64, 131072, False), (4096, 131072, False), (4096, 131072, True)):
+            g = torch.Generator(device=dev).manual_seed(5)
+            X = torch.randn(bl, vl, generator=g, dtype=torch.float32, device=dev)
+            Tl = torch.full((bl,), 0.8, dtype=torch.float32, device=dev)
+            ms, kms, pc = time_calls(
+                torch, fs, lambda s: fs.sample_logits(X, Tl, seed=99, offset=s, fp64_noise=f64),
+                max(20, args.steps // 4), 5)
+            lb = logits_alg_bytes(bl, vl, 16 if f64 else 8)
+            key = f"B{bl}_V{vl}_{'fp64' if f64 else 'fp32'}_noise"
+            sa[key] = {"us_per_call": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
+                       "alg_bytes": lb, "kernel_gbs": round(lb / (kms * 1e-3) / 1e9, 1),
+                       "kernel_frac": round(lb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"  {key}: {sa[key]}")
+            del X
+        result["standalone_sampler"] = sa
+
         # Baselines on the same data: (1) unfused: rocBLAS/hipBLASLt GEMM writes bf16
         # logits to HBM, then the standalone sampler; (2) softmax + multinomial.
-        Hb, Tb = H[:B].contiguous(), temp[:B].contiguous()
         log("timing unfused baselines")
 
         def unfused(s):

@@ -71,7 +71,7 @@ def load_library():
         lib.fs_profile_begin.restype = i32
         lib.fs_profile_begin.argtypes = []
         lib.fs_profile_end.restype = i32
-        lib.fs_profile_end.argtypes = [P, P, P]
+        lib.fs_profile_end.argtypes = [P, P]
         lib.fs_debug_noise.restype = i32
         lib.fs_debug_noise.argtypes = [P, i64, i32, P, P, P]
         lib.fs_debug_logits.restype = i32
@@ -128,11 +128,12 @@ def workspace_bytes(B: int, V: int, fp64_noise: bool = False) -> int:
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A cached uint8 workspace for the current stream of `device` (stream-ordered reuse)."""
+    """A cached uint8 workspace for the current stream of `device` (stream-ordered reuse).
+    Zero-filled when allocated, as the library requires; each call leaves it zeroed."""
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -193,20 +194,20 @@ def sample_logits(logits: torch.Tensor, temp, *, seed: int, offset: int,
 
 
 class KernelTimer:
-    """Context manager: summed Stage 1 / Stage 2 kernel milliseconds of the sampling
-    calls made inside it, from HIP events the library records on each call's stream."""
+    """Context manager: summed kernel milliseconds of the sampling calls made inside
+    it (one launch per call), from HIP events the library records on each call's
+    stream."""
 
     def __enter__(self):
         _check(load_library().fs_profile_begin(), "fs_profile_begin")
-        self.stage1_ms = self.stage2_ms = 0.0
+        self.kernel_ms = 0.0
         self.calls = 0
         return self
 
     def __exit__(self, *exc):
-        a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
-        _check(load_library().fs_profile_end(ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)),
-               "fs_profile_end")
-        self.stage1_ms, self.stage2_ms, self.calls = a.value, b.value, n.value
+        a, n = ctypes.c_double(), ctypes.c_int64()
+        _check(load_library().fs_profile_end(ctypes.byref(a), ctypes.byref(n)), "fs_profile_end")
+        self.kernel_ms, self.calls = a.value, n.value
         return False
 
 

@@ -1,6 +1,7 @@
 // fs_api.hip -- the C ABI of libfsample.so (declared and documented in
 // include/fsample.h): argument checks on the host, workspace sizing, and the
-// Stage 1 + Stage 2 launches on the caller's stream.
+// sampling launches (Stage 1 with Stage 2 in its last workgroups) on the
+// caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -37,23 +38,23 @@ constexpr int64_t kMaxFusedB = (int64_t)1 << 22;  // 65536 batch tiles of 64 alo
 struct Profiler {
   std::mutex mu;
   bool on = false;
-  std::vector<hipEvent_t> pool;  // 3 events per timed call
+  std::vector<hipEvent_t> pool;  // 2 events per timed call
   size_t used = 0;               // calls recorded since begin
   static constexpr size_t kMaxCalls = 4096;
 };
 Profiler g_prof;
 
-// Events (start, after stage 1, after stage 2) for one call, or null if not timing.
+// Events (before, after the sampling kernel) for one call, or null if not timing.
 hipEvent_t* prof_slot() {
   std::lock_guard<std::mutex> lock(g_prof.mu);
   if (!g_prof.on || g_prof.used >= Profiler::kMaxCalls) return nullptr;
-  const size_t need = 3 * (g_prof.used + 1);
+  const size_t need = 2 * (g_prof.used + 1);
   while (g_prof.pool.size() < need) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     g_prof.pool.push_back(e);
   }
-  hipEvent_t* slot = &g_prof.pool[3 * g_prof.used];
+  hipEvent_t* slot = &g_prof.pool[2 * g_prof.used];
   ++g_prof.used;
   return slot;
 }
@@ -91,6 +92,27 @@ fs_status check_sizes(int64_t B, int64_t V) {
   return FS_OK;
 }
 
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout: a fixed region of kCounterWords completion counters at the
+// start (one per batch tile of the fused kernel, one per row of a standalone
+// launch), then the [B, tiles] candidates (tiles = the larger tile count of the
+// two samplers, at the most CUs the library uses).  Candidates of any call
+// never overlap the counters, so the counters stay zero between calls whatever
+// shapes share the workspace.
+constexpr int64_t kCounterWords = 65536;
+constexpr size_t kCounterBytes = (size_t)kCounterWords * sizeof(uint32_t);
+
+size_t cand_region_bytes(int64_t B, int64_t V, uint32_t flags) {
+  int64_t tiles = fs::fused_num_tiles(V, kAssumedCUs);
+  const int64_t lt = logits_tiles(V);
+  if (lt > tiles) tiles = lt;
+  return align_up((size_t)B * (size_t)tiles * cand_bytes(flags));
+}
+
+uint32_t* counters_of(void* ws) { return static_cast<uint32_t*>(ws); }
+void* candidates_of(void* ws) { return static_cast<char*>(ws) + kCounterBytes; }
+
 fs_status check_workspace(void* ws, size_t have, int64_t B, int64_t V, uint32_t flags) {
   const size_t need = fs_workspace_bytes(B, V, flags);
   if (ws == nullptr || have < need)
@@ -118,11 +140,7 @@ extern "C" {
 
 size_t fs_workspace_bytes(int64_t B, int64_t V, uint32_t flags) {
   if (B < 0 || V < 1 || V >= kMaxV) return 0;
-  int64_t tiles = fs::fused_num_tiles(V, kAssumedCUs);
-  const int64_t lt = logits_tiles(V);
-  if (lt > tiles) tiles = lt;
-  const size_t bytes = (size_t)B * (size_t)tiles * cand_bytes(flags);
-  return (bytes + kAlign - 1) / kAlign * kAlign + kAlign;
+  return kCounterBytes + cand_region_bytes(B, V, flags);
 }
 
 const char* fs_status_string(fs_status status) {
@@ -165,19 +183,18 @@ fs_status fs_sample_fused(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t
   a.bias = bias;
   a.row_ids = row_ids;
   a.key = fs::make_key(seed, offset);
-  a.cand = workspace;
+  a.cand = candidates_of(workspace);
   a.nT = fs::fused_num_tiles(V, cus);
+  a.counters = counters_of(workspace);  // ceil(B / 64) <= 65536 words (B <= 2^22)
+  a.out = out_idx;
   a.Y = nullptr;
   a.bias_vec4 = bias != nullptr && aligned16(bias) && (V % 4 == 0);
   hipStream_t st = (hipStream_t)stream;
   hipEvent_t* ev = prof_slot();
   if (ev) (void)hipEventRecord(ev[0], st);
   hipError_t e = fs::launch_fused_stage1(a, fp64 ? fs::kEpiSample64 : fs::kEpiSample32, st);
-  if (e != hipSuccess) return hip_fail(e, "fused stage 1 launch");
+  if (e != hipSuccess) return hip_fail(e, "fused sampling launch");
   if (ev) (void)hipEventRecord(ev[1], st);
-  e = fs::launch_stage2(workspace, B, a.nT, fp64, out_idx, st);
-  if (e != hipSuccess) return hip_fail(e, "stage 2 launch");
-  if (ev) (void)hipEventRecord(ev[2], st);
   return FS_OK;
 }
 
@@ -199,25 +216,30 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
   s = check_workspace(workspace, workspace_bytes, B, V, flags);
   if (s != FS_OK) return s;
 
-  fs::LogitsArgs a;
-  a.X = logits;
-  a.B = B;
-  a.V = V;
-  a.temp = temp;
-  a.row_ids = row_ids;
-  a.key = fs::make_key(seed, offset);
-  a.cand = workspace;
-  a.nT = nT;
-  a.vec4 = aligned16(logits) && (V % 4 == 0);
+  // One launch per run of at most kCounterWords rows (one counter per row);
+  // the launches follow each other on the stream and reuse the workspace.
   hipStream_t st = (hipStream_t)stream;
   hipEvent_t* ev = prof_slot();
   if (ev) (void)hipEventRecord(ev[0], st);
-  hipError_t e = fs::launch_logits_stage1(a, fp64_noise != 0, st);
-  if (e != hipSuccess) return hip_fail(e, "logits stage 1 launch");
+  for (int64_t b0 = 0; b0 < B; b0 += kCounterWords) {
+    const int64_t nb = B - b0 < kCounterWords ? B - b0 : kCounterWords;
+    fs::LogitsArgs a;
+    a.X = logits + b0 * V;
+    a.B = nb;
+    a.V = V;
+    a.temp = temp + b0;
+    a.row_ids = row_ids ? row_ids + b0 : nullptr;
+    a.rid_base = (uint32_t)b0;
+    a.key = fs::make_key(seed, offset);
+    a.cand = candidates_of(workspace);
+    a.nT = nT;
+    a.counters = counters_of(workspace);
+    a.out = out_idx + b0;
+    a.vec4 = aligned16(logits) && (V % 4 == 0);
+    hipError_t e = fs::launch_logits_stage1(a, fp64_noise != 0, st);
+    if (e != hipSuccess) return hip_fail(e, "logits sampling launch");
+  }
   if (ev) (void)hipEventRecord(ev[1], st);
-  e = fs::launch_stage2(workspace, B, nT, fp64_noise != 0, out_idx, st);
-  if (e != hipSuccess) return hip_fail(e, "stage 2 launch");
-  if (ev) (void)hipEventRecord(ev[2], st);
   return FS_OK;
 }
 
@@ -229,26 +251,23 @@ fs_status fs_profile_begin(void) {
   return FS_OK;
 }
 
-fs_status fs_profile_end(double* stage1_ms, double* stage2_ms, int64_t* calls) {
+fs_status fs_profile_end(double* kernel_ms, int64_t* calls) {
   g_last_error[0] = 0;
   std::lock_guard<std::mutex> lock(g_prof.mu);
-  double t1 = 0.0, t2 = 0.0;
+  double total = 0.0;
   fs_status status = FS_OK;
   for (size_t c = 0; c < g_prof.used; ++c) {
-    hipEvent_t* ev = &g_prof.pool[3 * c];
-    float a = 0.f, b = 0.f;
-    hipError_t e = hipEventSynchronize(ev[2]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&a, ev[0], ev[1]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&b, ev[1], ev[2]);
+    hipEvent_t* ev = &g_prof.pool[2 * c];
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(ev[1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
     if (e != hipSuccess) {
       status = hip_fail(e, "profile events");
       break;
     }
-    t1 += a;
-    t2 += b;
+    total += ms;
   }
-  if (stage1_ms) *stage1_ms = t1;
-  if (stage2_ms) *stage2_ms = t2;
+  if (kernel_ms) *kernel_ms = total;
   if (calls) *calls = (int64_t)g_prof.used;
   g_prof.on = false;
   g_prof.used = 0;

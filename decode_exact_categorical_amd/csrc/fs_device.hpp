@@ -166,4 +166,94 @@ __device__ __forceinline__ void wave_argmax_xor(T& m, int32_t& i, int lo_bit) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Stage 2 inside the sampling kernel [FlashSampling, "algorithm details",
+// Stage 2].  The workgroups of one group (a batch tile of the fused kernel, a
+// row of the standalone sampler) each publish their candidates and count
+// themselves done on the group's counter; the workgroup that counts last
+// reduces the group's candidates to out_idx and clears the counter for the
+// next call.  No workgroup ever waits for another, so a group cannot stall.
+//
+// Publishing needs no L2 write-back (an agent-scope release fence writes back
+// the whole L2 of the XCD, which serialises at hundreds of nanoseconds per
+// workgroup): candidates are written and read with agent-scope relaxed
+// atomics, which gfx950 performs at the device coherence point (stores
+// written through, loads not served from a possibly stale L1 or L2), and each
+// writer waits for its stores to complete before its workgroup counts itself
+// done.  A count therefore implies that the counted workgroup's candidates
+// are readable by the workgroup that counts last, whatever XCD it runs on.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void cand_store_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t cand_load_u64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Candidate (m, idx) as one (float) or two (double) 64-bit words, in the
+// struct's own byte layout.
+__device__ __forceinline__ void store_cand(Cand<float>* p, const Cand<float>& c) {
+  cand_store_u64(reinterpret_cast<uint64_t*>(p),
+                 (uint64_t)__float_as_uint(c.m) | ((uint64_t)(uint32_t)c.idx << 32));
+}
+__device__ __forceinline__ void store_cand(Cand<double>* p, const Cand<double>& c) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  cand_store_u64(q, (uint64_t)__double_as_longlong(c.m));
+  cand_store_u64(q + 1, (uint64_t)(uint32_t)c.idx);
+}
+__device__ __forceinline__ Cand<float> load_cand(const Cand<float>* p) {
+  const uint64_t v = cand_load_u64(reinterpret_cast<const uint64_t*>(p));
+  return Cand<float>{__uint_as_float((uint32_t)v), (int32_t)(uint32_t)(v >> 32)};
+}
+__device__ __forceinline__ Cand<double> load_cand(const Cand<double>* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t m = cand_load_u64(q);
+  const uint64_t i = cand_load_u64(q + 1);
+  return Cand<double>{__longlong_as_double((long long)m), (int32_t)(uint32_t)i};
+}
+
+// Wait until this thread's stores have completed (vmcnt(0); the other
+// counters of the gfx9 s_waitcnt encoding at their maximum, i.e. not waited).
+__device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// True, in every thread, for the workgroup that completes its group of
+// `group_size` workgroups on `counter`.  Writer threads call store_cand and
+// wait_stores_complete before this.
+__device__ __forceinline__ bool finish_last(uint32_t* counter, uint32_t group_size) {
+  __shared__ uint32_t last;
+  __syncthreads();  // every writer's stores have completed
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   group_size - 1u
+               ? 1u
+               : 0u;
+  __syncthreads();
+  return last != 0u;
+}
+
+// Leave a group's counter at zero for the next call (one thread, after the
+// group's Stage 2).
+__device__ __forceinline__ void clear_counter(uint32_t* counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The winner of one row's nT candidates, reduced by one wave (lane-strided
+// scan, then xor-shuffles; the order is total, so this is the serial scan's
+// result): its index, or -1 if the best score is -inf (no finite score).
+template <typename T>
+__device__ __forceinline__ int64_t row_winner(const Cand<T>* c, int nT, int lane) {
+  T bm = neg_inf<T>();
+  int32_t bi = kNoIndex;
+  for (int t = lane; t < nT; t += 64) {
+    const Cand<T> o = load_cand(c + t);
+    if (beats(o.m, o.idx, bm, bi)) {
+      bm = o.m;
+      bi = o.idx;
+    }
+  }
+  wave_argmax_xor(bm, bi, 0);
+  return bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
+}
+
 }  // namespace fs

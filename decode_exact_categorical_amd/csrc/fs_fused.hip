@@ -1,17 +1,18 @@
-// fs_fused.hip -- fused LM-head matmul + exact sampling, Stage 1, for gfx950.
+// fs_fused.hip -- fused LM-head matmul + exact sampling for gfx950.
 //
-// Follows the FlashSampling page ("algorithm details", Stage 1 steps (1)-(6)):
-// for a (batch tile x vocabulary tile) the logits Y = H W^T are formed on chip,
-// transformed (bias, temperature), perturbed with Gumbel noise, and only the
-// per-row tile maximum and its vocabulary index are written out.  The [B, V]
-// logits never reach HBM.
+// Follows the FlashSampling page ("algorithm details", Stage 1 steps (1)-(6)
+// and Stage 2): for a (batch tile x vocabulary tile) the logits Y = H W^T are
+// formed on chip, transformed (bias, temperature), perturbed with Gumbel
+// noise, and only the per-row tile maximum and its vocabulary index are
+// written out.  The [B, V] logits never reach HBM.  Stage 2 runs in the same
+// launch: the last workgroup to finish a batch tile reduces its candidates.
 //
 // Design for MI355X (the page's Triton kernel was written for NVIDIA parts):
 //  * One workgroup per CU streams a contiguous slice of W exactly once.  Its
 //    8 waves (two per SIMD) each own a contiguous run of vocabulary rows,
 //    assigned in 8-row units so every wave of the chip ends within 8 rows of
 //    the others.  A wave walks its rows in passes of up to 5 MFMA row blocks
-//    (80 rows; 4 with float64 noise and 64 batch columns).
+//    (80 rows; 3 blocks, 48 rows, with more than 32 batch columns).
 //  * W goes straight from HBM into VGPRs in the bf16 MFMA A-operand layout
 //    (lane l holds 16 bytes of row l % 16; the four lanes of a row read 64
 //    contiguous bytes).  Loads go in k-step pairs, the two halves of each
@@ -32,13 +33,16 @@
 //    is a multiply and a compare.  Greedy columns (t <= 0 or NaN) fold in the
 //    bias only.  Columns with an infinite (or beyond 2^60) temperature fold in
 //    the bias and add g after the division, which keeps (y + bias) / t + g.
-//    With 64 batch columns and a bias the fold's registers do not fit beside
-//    the accumulators, and the noise is added after the k-loop instead.
 //  * Float64 noise keeps the score in float64: y + bias and the noise are
 //    combined after the k-loop, with two Philox calls per fragment.
 //  * Scores feed a per-lane running argmax (larger score, then smaller index);
 //    xor-shuffles and LDS reduce it to one candidate per batch row per
 //    workgroup.
+//  * Stage 2 needs no second launch: the workgroup that counts last on its
+//    batch tile's counter reduces the tile's candidates (finish_last and
+//    row_winner, fs_device.hpp), saving the launch and the gap between two
+//    kernels, several microseconds against a ~220 us step.  Candidates are
+//    published with device-coherent atomic stores, not an L2 write-back.
 #include <type_traits>
 
 #include "fs_launch.hpp"
@@ -108,8 +112,8 @@ struct RowBlocks {
   static constexpr int value = NB <= 2 ? 5 : 3;
 };
 
-// Whether float32 noise is folded into the accumulators inside the k-loop
-// (otherwise it is added after the k-loop, still in one pass over the rows).
+// Whether the noise is folded into the accumulators inside the k-loop: float32
+// noise is; float64 noise is added after the k-loop, still in the same pass.
 template <int NB, int EPI, bool HAS_BIAS>
 struct FoldNoise {
   static constexpr bool value = EPI == kEpiSample32;
@@ -466,10 +470,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         }
       }
     } else {
-      // Noise added after the k-loop: float64 noise (score in float64), or
-      // float32 noise for 64 batch columns with a bias.  The per-fragment work
-      // (Philox, four logs) is large, so the loop stays rolled and the
-      // fragment is picked out of the accumulators by uniform branches.
+      // Float64 noise, added after the k-loop (the score is formed in
+      // float64).  The per-fragment work (two Philox calls, four transforms)
+      // is large, so the loop stays rolled and the fragment is picked out of
+      // the accumulators by uniform branches.
 #pragma unroll 1
       for (int f = 0; f < kRB * NB; ++f) {
         const int rb = f / NB, cb = f - rb * NB;
@@ -500,19 +504,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         if (m == kGreedy) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) s[j] = T(y[j]) + T(beta[j]);
-        } else if (EPI == kEpiSample64) {
+        } else {
           const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), r);
           const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, r);
           s[0] = (T(y[0]) + T(beta[0])) * it + T(gumbel_f64(w0.w0, w0.w1));
           s[1] = (T(y[1]) + T(beta[1])) * it + T(gumbel_f64(w0.w2, w0.w3));
           s[2] = (T(y[2]) + T(beta[2])) * it + T(gumbel_f64(w1.w0, w1.w1));
           s[3] = (T(y[3]) + T(beta[3])) * it + T(gumbel_f64(w1.w2, w1.w3));
-        } else {
-          const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), r);
-          s[0] = T((y[0] + beta[0]) * (float)it + gumbel_f32(w.w0));
-          s[1] = T((y[1] + beta[1]) * (float)it + gumbel_f32(w.w1));
-          s[2] = T((y[2] + beta[2]) * (float)it + gumbel_f32(w.w2));
-          s[3] = T((y[3] + beta[3]) * (float)it + gumbel_f32(w.w3));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -554,8 +552,22 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       if (beats(o.m, o.idx, best.m, best.idx)) best = o;
     }
     const int64_t b = bt0 + tid;
-    if (b < B) reinterpret_cast<Cand<T>*>(a.cand)[b * a.nT + blockIdx.x] = best;
+    if (b < B) {
+      store_cand(reinterpret_cast<Cand<T>*>(a.cand) + b * a.nT + blockIdx.x, best);
+      wait_stores_complete();
+    }
   }
+
+  // Stage 2 of this batch tile, in the workgroup that finishes it last.
+  if (!finish_last(a.counters + blockIdx.y, gridDim.x)) return;
+  const Cand<T>* cand = reinterpret_cast<const Cand<T>*>(a.cand);
+  for (int r = wave; r < kBatchTile; r += kWaves) {
+    const int64_t b = bt0 + r;
+    if (b >= B) break;
+    const int64_t o = row_winner(cand + b * a.nT, a.nT, lane);
+    if (lane == 0) a.out[b] = o;
+  }
+  if (tid == 0) clear_counter(a.counters + blockIdx.y);
 }
 
 template <int NB>

@@ -9,8 +9,8 @@
 
 namespace fs {
 
-// Fused Stage 1 (matmul + transform + noise + per-tile argmax) and its
-// logits-store twin.
+// Fused sampling kernel (Stage 1: matmul + transform + noise + per-tile argmax;
+// Stage 2 in the last workgroup of each batch tile) and its logits-store twin.
 struct FusedArgs {
   const uint16_t* H;  // [B, D] bf16
   const uint16_t* W;  // [V, D] bf16
@@ -21,6 +21,8 @@ struct FusedArgs {
   NoiseKey key;
   void* cand;  // [B, nT] candidates
   int nT;      // vocabulary tiles = workgroups along x
+  uint32_t* counters;  // [ceil(B / 64)] completion counters, zero between calls
+  int64_t* out;        // [B] sampled indices
   float* Y;    // [B, V] (store epilogue only)
   int bias_vec4;  // bias rows are 16-byte aligned
 };
@@ -31,23 +33,23 @@ enum FusedEpilogue { kEpiSample32 = 0, kEpiSample64 = 1, kEpiStore = 2 };
 int fused_num_tiles(int64_t V, int num_cus);
 hipError_t launch_fused_stage1(const FusedArgs& a, int epilogue, hipStream_t stream);
 
-// Standalone Stage 1 over float32 logits.
+// Standalone sampler over float32 logits (Stage 1, Stage 2 in the last
+// workgroup of each row).
 constexpr int kLogitsChunk = 2048;  // logits per workgroup
 struct LogitsArgs {
   const float* X;  // [B, V]
   int64_t B, V;
   const float* temp;
-  const uint32_t* row_ids;
+  const uint32_t* row_ids;  // [B] or null: then row b has id rid_base + b
+  uint32_t rid_base;
   NoiseKey key;
   void* cand;  // [B, nT]
   int nT;      // ceil(V / kLogitsChunk)
+  uint32_t* counters;  // [B] completion counters (B <= 65536), zero between calls
+  int64_t* out;        // [B] sampled indices
   int vec4;    // rows 16-byte aligned
 };
 hipError_t launch_logits_stage1(const LogitsArgs& a, bool fp64, hipStream_t stream);
-
-// Stage 2: per row, the best of its nT candidates -> out_idx.
-hipError_t launch_stage2(const void* cand, int64_t B, int nT, bool fp64, int64_t* out,
-                         hipStream_t stream);
 
 // Test hook: the noise transforms applied to given words.
 hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,

@@ -5,9 +5,10 @@
 // materialises the noise and the ratio p/E in HBM, and that one program per
 // row is latency-bound at small batch.  Here the noise is generated in
 // registers and each row is split over ceil(V / 2048) workgroups, each
-// reducing 2048 logits to one (score, index) candidate; Stage 2
-// (fs_reduce.hip) picks each row's winner.  Same transform, noise stream
-// and tie rule as the fused path, so equal y + bias gives equal draws.
+// reducing 2048 logits to one (score, index) candidate; the last of them to
+// finish runs Stage 2, picking the row's winner (finish_last, row_winner in
+// fs_device.hpp).  Same transform, noise stream and tie rule as the fused
+// path, so equal y + bias gives equal draws.
 #include <type_traits>
 
 #include "fs_launch.hpp"
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(kThreads) void logits_stage1_kernel(LogitsArgs a) {
   const float t = a.temp[b];
   const bool greedy = !(t > 0.0f);  // uniform across the workgroup
   const T inv_t = greedy ? T(1) : T(1) / T(t);
-  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
+  const uint32_t rid = a.row_ids ? a.row_ids[b] : a.rid_base + (uint32_t)b;
   const float* x = a.X + b * V;
 
   T bm = neg_inf<T>();
@@ -82,8 +83,17 @@ __global__ __launch_bounds__(kThreads) void logits_stage1_kernel(LogitsArgs a) {
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w)
       if (beats(wbest[w].m, wbest[w].idx, best.m, best.idx)) best = wbest[w];
-    reinterpret_cast<Cand<T>*>(a.cand)[b * a.nT + chunk] = best;
+    store_cand(reinterpret_cast<Cand<T>*>(a.cand) + b * a.nT + chunk, best);
+    wait_stores_complete();
   }
+
+  // Stage 2 of this row, in the workgroup that finishes it last.
+  if (!finish_last(a.counters + b, (uint32_t)a.nT)) return;
+  if (wave == 0) {
+    const int64_t o = row_winner(reinterpret_cast<const Cand<T>*>(a.cand) + b * a.nT, a.nT, lane);
+    if (lane == 0) a.out[b] = o;
+  }
+  if (threadIdx.x == 0) clear_counter(a.counters + b);
 }
 
 }  // namespace

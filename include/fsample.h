@@ -81,10 +81,16 @@ typedef void *fs_stream_t;  /* hipStream_t */
  * Bytes of device workspace the sampling calls need for a batch of B rows over
  * a vocabulary of V entries (covers both fs_sample_fused and fs_sample_logits;
  * pass FS_FP64_NOISE in flags if either call will use float64 noise).  The
- * workspace holds the per-tile candidates (m, idx) of Stage 1 [FS Stage 1
- * step (6)]; the caller allocates it, may reuse it across calls on one stream,
- * and must not share it between calls that can run concurrently.  Host only;
- * returns 0 for invalid sizes.
+ * workspace starts with a fixed 256 KiB region of completion counters, which
+ * pick, for each batch tile (fused) or row (standalone), the workgroup that
+ * runs Stage 2; the per-tile candidates (m, idx) of Stage 1 [FS Stage 1 step
+ * (6)] follow it.  The caller allocates the workspace and must zero-fill it
+ * once before its first use (hipMemset, torch.zeros); every call returns the
+ * counters to zero by the time its work completes, so the workspace can then
+ * be reused call after call, for any sizes, on one stream without clearing.
+ * It must not be shared between calls that can run concurrently.  Counters
+ * that are not zero give wrong or missing out_idx values (never a fault or a
+ * hang).  Host only; returns 0 for invalid sizes.
  */
 size_t fs_workspace_bytes(int64_t B, int64_t V, uint32_t flags);
 
@@ -104,12 +110,13 @@ size_t fs_workspace_bytes(int64_t B, int64_t V, uint32_t flags);
  *            on its batch position [MG "The change"]
  *   flags    host: 0 or FS_FP64_NOISE
  *   workspace, workspace_bytes  device scratch of at least
- *            fs_workspace_bytes(B, V, flags) bytes
+ *            fs_workspace_bytes(B, V, flags) bytes, zero-filled before its
+ *            first use (see fs_workspace_bytes)
  *   stream   hipStream_t
  * Computes y = H W^T tile by tile on chip (bf16 inputs, float32 accumulation)
  * and never writes the [B, V] logits: Stage 1 keeps each row's per-tile
  * (max score, index), Stage 2 reduces those to out_idx [FS Stage 1, Stage 2].
- * H and W must be 16-byte aligned.
+ * Both stages run in one kernel launch.  H and W must be 16-byte aligned.
  */
 fs_status fs_sample_fused(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t D,
                           int64_t V, const float *temp, const float *bias,
@@ -142,16 +149,16 @@ fs_status fs_sample_logits(const float *logits, int64_t B, int64_t V, const floa
 /*
  * Kernel timing.  Between fs_profile_begin() and fs_profile_end(), every
  * fs_sample_fused and fs_sample_logits call also records HIP events on its
- * stream around its Stage 1 and its Stage 2 launch (the FlashSampling page,
- * "reproduction", times kernels the same way: per-kernel device timestamps).
- * fs_profile_end() waits for those events, writes the summed Stage 1 and
- * Stage 2 durations in milliseconds and the number of timed calls (any of the
- * three pointers may be NULL; host memory), and stops recording.  At most 4096
- * calls are timed per begin/end pair; later calls run untimed.  Enabling adds
- * three event records per call and nothing else.  Process-wide; host only.
+ * stream around its one launch (Stage 1 with Stage 2 in its last workgroups;
+ * the FlashSampling page, "reproduction", times kernels the same way: device
+ * timestamps per kernel).  fs_profile_end() waits for those events, writes the
+ * summed kernel duration in milliseconds and the number of timed calls
+ * (either pointer may be NULL; host memory), and stops recording.  At most
+ * 4096 calls are timed per begin/end pair; later calls run untimed.  Enabling
+ * adds two event records per call and nothing else.  Process-wide; host only.
  */
 fs_status fs_profile_begin(void);
-fs_status fs_profile_end(double *stage1_ms, double *stage2_ms, int64_t *calls);
+fs_status fs_profile_end(double *kernel_ms, int64_t *calls);
 
 /* Static description of a status code. */
 const char *fs_status_string(fs_status status);

@@ -1,0 +1,118 @@
+"""The workspace contract of the C ABI, on the GPU.
+
+Stage 2 runs in the last workgroup of each batch tile (fused) or row
+(standalone), chosen by completion counters in a fixed region at the start of
+the workspace.  The caller zero-fills the workspace once; every call must leave
+the counters zero again, so one workspace serves calls of any shape in turn.
+The standalone sampler splits batches beyond the counter region over several
+launches, which must not change any row's draw.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_exact_categorical_amd as fs
+import oracle
+import synthetic
+from gpu_common import check_index_parity, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+COUNTER_BYTES = 65536 * 4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def _fused(lib, H, W, temp, ws, seed, offset, fp64):
+    B, D = H.shape
+    V = W.shape[0]
+    out = torch.full((B,), -7, dtype=torch.int64, device=H.device)
+    st = lib.fs_sample_fused(fs._ptr(H), fs._ptr(W), B, D, V, fs._ptr(temp), None, seed, offset,
+                             fs._ptr(out), None, fs.FS_FP64_NOISE if fp64 else 0, fs._ptr(ws),
+                             ws.numel(), fs._stream(H.device))
+    assert st == 0, lib.fs_last_error()
+    return out
+
+
+def _logits(lib, X, temp, ws, seed, offset, fp64, row_ids=None):
+    B, V = X.shape
+    out = torch.full((B,), -7, dtype=torch.int64, device=X.device)
+    st = lib.fs_sample_logits(fs._ptr(X), B, V, fs._ptr(temp), seed, offset, int(fp64),
+                              fs._ptr(out), fs._ptr(row_ids), fs._ptr(ws), ws.numel(),
+                              fs._stream(X.device))
+    assert st == 0, lib.fs_last_error()
+    return out
+
+
+def test_one_workspace_serves_every_shape(dev):
+    """Calls of different kinds and shapes, in turn, on one workspace give the
+    draws each gives on a fresh workspace, and leave the counters zero."""
+    lib = fs.load_library()
+    g = torch.Generator(device="cpu").manual_seed(7)
+    cases = []
+    for (kind, B, D, V, fp64) in [("fused", 64, 512, 32768, False),
+                                  ("logits", 300, 0, 5000, True),
+                                  ("fused", 1, 256, 70000, True),
+                                  ("fused", 130, 128, 1000, False),
+                                  ("logits", 3, 0, 10, False),
+                                  ("logits", 4096, 0, 2048, False)]:
+        temp = (0.5 + torch.rand(B, generator=g)).to(dev)
+        if kind == "fused":
+            args = (synthetic.hidden(B, D, seed=B).to(dev),
+                    synthetic.weight(V, D, std=0.05, seed=V).to(dev), temp)
+        else:
+            args = (torch.randn(B, V, generator=g).to(dev), temp)
+        need = lib.fs_workspace_bytes(B, V, fs.FS_FP64_NOISE if fp64 else 0)
+        cases.append((kind, B, V, fp64, args, need))
+    size = max(c[5] for c in cases)
+    assert size > COUNTER_BYTES
+
+    def run(c, ws, offset):
+        kind, B, V, fp64, args, _ = c
+        if kind == "fused":
+            return _fused(lib, *args, ws, 31, offset, fp64)
+        return _logits(lib, *args, ws, 31, offset, fp64)
+
+    refs = []
+    for i, c in enumerate(cases):
+        say(f"fresh workspace: {c[0]} B={c[1]} V={c[2]} fp64={c[3]}")
+        refs.append(run(c, torch.zeros(c[5], dtype=torch.uint8, device=dev), 100 + i).cpu())
+    torch.cuda.synchronize()
+    shared = torch.zeros(size, dtype=torch.uint8, device=dev)
+    for rep in range(3):
+        for i, c in enumerate(cases):
+            say(f"shared workspace, round {rep}: {c[0]} B={c[1]} V={c[2]} fp64={c[3]}")
+            got = run(c, shared, 100 + i).cpu()
+            assert torch.equal(got, refs[i]), f"case {i} differs on the shared workspace"
+            assert (got >= 0).all()
+    torch.cuda.synchronize()
+    assert int(shared[:COUNTER_BYTES].count_nonzero()) == 0, "counters not left at zero"
+
+
+def test_logits_batch_beyond_one_launch(dev):
+    """More rows than the counter region: split over launches, default row ids
+    continue across them, and sampled rows match the oracle."""
+    lib = fs.load_library()
+    B, V = 65536 + 1500, 24
+    g = torch.Generator(device="cpu").manual_seed(8)
+    X = torch.randn(B, V, generator=g) * 2.0
+    temp = torch.full((B,), 0.9)
+    Xd, Td = X.to(dev), temp.to(dev)
+    ws = torch.zeros(lib.fs_workspace_bytes(B, V, 0), dtype=torch.uint8, device=dev)
+    say(f"standalone B={B} V={V}, default row ids")
+    a = _logits(lib, Xd, Td, ws, 5, 77, False)
+    ids = torch.arange(B, dtype=torch.int32, device=dev)
+    say(f"standalone B={B} V={V}, explicit row ids 0..B-1")
+    b = _logits(lib, Xd, Td, ws, 5, 77, False, row_ids=ids)
+    torch.cuda.synchronize()
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    np.testing.assert_array_equal(a, b)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 65535, 65536, B - 1], rng.integers(0, B, 60)]))
+    ref, gap, _ = oracle.sample_logits(X.numpy()[rows], temp.numpy()[rows], seed=5, offset=77,
+                                       row_ids=rows.astype(np.uint32))
+    check_index_parity(a[rows], ref, gap, f"standalone B={B} sampled rows")
+    assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
