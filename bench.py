@@ -101,22 +101,31 @@ def percentiles(xs, qs=(10, 50, 90)):
 
 
 def time_calls(torch, fs, call, steps, warmup):
-    """Time `steps` calls of call(s) after `warmup` untimed ones: (mean ms per step
-    over the timed region, mean kernel ms from the library's own events on the
-    stream the kernel runs on, per-step ms percentiles from events between steps)."""
+    """Time `steps` calls of call(s) after `warmup` untimed ones.  Returns (mean ms
+    per step, mean kernel ms, per-step ms percentiles).  The mean step comes from
+    a pass with only the two events that bracket it; a second pass, with HIP
+    events around every kernel (the library's, on the stream the kernel runs on)
+    and between steps, gives the kernel time and the spread, since those extra
+    events add work to the queue."""
     for s in range(warmup):
         call(s)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        call(warmup + s)
+    e1.record()
+    torch.cuda.synchronize()
+    mean_step = e0.elapsed_time(e1) / steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     with fs.KernelTimer() as kt:
         ev[0].record()
         for s in range(steps):
-            call(warmup + s)
+            call(warmup + steps + s)
             ev[s + 1].record()
         torch.cuda.synchronize()
     per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    total = ev[0].elapsed_time(ev[steps])
-    return total / steps, kt.kernel_ms / max(1, kt.calls), percentiles(per_step)
+    return mean_step, kt.kernel_ms / max(1, kt.calls), percentiles(per_step)
 
 
 def time_region(torch, fn, steps, warmup):

@@ -232,7 +232,8 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
     a.rid_base = (uint32_t)b0;
     a.key = fs::make_key(seed, offset);
     a.cand = candidates_of(workspace);
-    a.nT = nT;
+    a.chunk = fs::logits_chunk(nb, V);
+    a.nT = (int)((V + a.chunk - 1) / a.chunk);  // <= nT at the smallest chunk
     a.counters = counters_of(workspace);
     a.out = out_idx + b0;
     a.vec4 = aligned16(logits) && (V % 4 == 0);

@@ -35,7 +35,9 @@ hipError_t launch_fused_stage1(const FusedArgs& a, int epilogue, hipStream_t str
 
 // Standalone sampler over float32 logits (Stage 1, Stage 2 in the last
 // workgroup of each row).
-constexpr int kLogitsChunk = 2048;  // logits per workgroup
+constexpr int kLogitsChunk = 2048;      // fewest logits per workgroup (sizes the workspace)
+constexpr int kLogitsChunkMax = 32768;  // most logits per workgroup
+int logits_chunk(int64_t B, int64_t V);  // logits per workgroup for a launch
 struct LogitsArgs {
   const float* X;  // [B, V]
   int64_t B, V;
@@ -44,7 +46,8 @@ struct LogitsArgs {
   uint32_t rid_base;
   NoiseKey key;
   void* cand;  // [B, nT]
-  int nT;      // ceil(V / kLogitsChunk)
+  int chunk;   // logits per workgroup: kLogitsChunk * 2^k <= kLogitsChunkMax
+  int nT;      // ceil(V / chunk)
   uint32_t* counters;  // [B] completion counters (B <= 65536), zero between calls
   int64_t* out;        // [B] sampled indices
   int vec4;    // rows 16-byte aligned
