@@ -373,13 +373,24 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     u32x4 pa[2][kRB], pb[2][kRB];
     const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 ba0 = z4, ba1 = z4, bb0 = z4, bb1 = z4;
+    // The prologue issues pair 0 before pair 1, as the loop does: were the
+    // scheduler to swap them, the first pass through the loop head would see
+    // pair 0 as the newest loads, and the compiler would wait for nearly all
+    // loads there on every pass.
+    __builtin_amdgcn_sched_barrier(0);
     load_pair(pa, 0);
     bias_slot_load(ba0, 0);
     bias_slot_load(ba1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     load_pair(pb, 1);
     bias_slot_load(bb0, 2);
     bias_slot_load(bb1, 3);
+    __builtin_amdgcn_sched_barrier(0);
     static_assert(kStepsPerChunk % 4 == 0, "a chunk holds whole pairs of pairs");
+    // One H chunk per iteration, not unrolled: an unrolled or peeled copy
+    // enters the loop with its loads in another order, and the compiler then
+    // waits for nearly all loads in flight at the loop head.
+#pragma unroll 1
     for (int c = 0; c < NC; ++c) {
       const int buf = c & 1;
       const int cn = c + 1 < NC ? c + 1 : c;
