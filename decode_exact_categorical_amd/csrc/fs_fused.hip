@@ -124,6 +124,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   typedef typename ScoreType<EPI>::type T;
   constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS>::value;
   constexpr int kRB = RowBlocks<NB, EPI>::value;
+  // Per-row-block reloads (mma_reload) need both k-steps' H fragments at
+  // once; with 64 columns and a bias or float64 running bests those do not
+  // fit, and the pair is reloaded after all its MFMAs instead.
+  constexpr bool kInterleave = !(NB == 4 && (HAS_BIAS || EPI == kEpiSample64));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // The wave index is wave-uniform; saying so keeps every quantity derived
@@ -343,6 +347,32 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         dst[1][rb] = load_frag(w1 + woff[rb]);
       }
     };
+    // The MFMAs of one k-step pair, row block by row block, each row block's
+    // W registers reloaded (pair q) as soon as its MFMAs have issued, so the
+    // first loads of the next pair leave one row block after the data
+    // arrived rather than a whole phase later.
+    auto mma_reload = [&](u32x4 (&w)[2][kRB], int buf, int kk, int q) {
+      bf16x8 h0[NB], h1[NB];
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        h0[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 8 * grp]);
+        h1[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 32 + 8 * grp]);
+      }
+      const uint16_t* w0 = step_base(2 * q);
+      const uint16_t* w1 = step_base(2 * q + 1);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[0][rb]), h0[cb], acc[rb][cb], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[1][rb]), h1[cb], acc[rb][cb], 0, 0, 0);
+        w[0][rb] = load_frag(w0 + woff[rb]);
+        w[1][rb] = load_frag(w1 + woff[rb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
     auto mma = [&](const u32x4 (&w)[kRB], int buf, int kk) {
       bf16x8 hf[NB];
 #pragma unroll
@@ -401,21 +431,35 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         const int q = ks >> 1;
         // sched_barrier keeps each phase where it is written, so the compiler
         // does not move the loads of a pair next to their use.
-        mma(pa[0], buf, j * 32);
-        FS_FOLD_SLOT(ks, ba0);
-        mma(pa[1], buf, (j + 1) * 32);
-        FS_FOLD_SLOT(ks + 1, ba1);
+        if constexpr (kInterleave) {
+          mma_reload(pa, buf, j * 32, q + 2);
+          FS_FOLD_SLOT(ks, ba0);
+          FS_FOLD_SLOT(ks + 1, ba1);
+        } else {
+          mma(pa[0], buf, j * 32);
+          FS_FOLD_SLOT(ks, ba0);
+          mma(pa[1], buf, (j + 1) * 32);
+          FS_FOLD_SLOT(ks + 1, ba1);
+          __builtin_amdgcn_sched_barrier(0);
+          load_pair(pa, q + 2);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        load_pair(pa, q + 2);
         bias_slot_load(ba0, ks + 4);
         bias_slot_load(ba1, ks + 5);
         __builtin_amdgcn_sched_barrier(0);
-        mma(pb[0], buf, (j + 2) * 32);
-        FS_FOLD_SLOT(ks + 2, bb0);
-        mma(pb[1], buf, (j + 3) * 32);
-        FS_FOLD_SLOT(ks + 3, bb1);
+        if constexpr (kInterleave) {
+          mma_reload(pb, buf, (j + 2) * 32, q + 3);
+          FS_FOLD_SLOT(ks + 2, bb0);
+          FS_FOLD_SLOT(ks + 3, bb1);
+        } else {
+          mma(pb[0], buf, (j + 2) * 32);
+          FS_FOLD_SLOT(ks + 2, bb0);
+          mma(pb[1], buf, (j + 3) * 32);
+          FS_FOLD_SLOT(ks + 3, bb1);
+          __builtin_amdgcn_sched_barrier(0);
+          load_pair(pb, q + 3);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        load_pair(pb, q + 3);
         bias_slot_load(bb0, ks + 6);
         bias_slot_load(bb1, ks + 7);
         __builtin_amdgcn_sched_barrier(0);
