@@ -613,14 +613,39 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
   }
 
-  // Stage 2 of this batch tile, in the workgroup that finishes it last.
+  // Stage 2 of this batch tile, in the workgroup that finishes it last.  Wave
+  // w takes rows w, w + 8, ... of the tile and issues every candidate load of
+  // all its rows (clamped, always valid addresses) before reducing any, so the
+  // tail costs one round trip to the coherence point, not one per row.
   if (!finish_last(a.counters + blockIdx.y, gridDim.x)) return;
+  constexpr int kRowsPerWave = kBatchTile / kWaves;
+  constexpr int kLoadsPerRow = kMaxFusedTiles / 64;
   const Cand<T>* cand = reinterpret_cast<const Cand<T>*>(a.cand);
-  for (int r = wave; r < kBatchTile; r += kWaves) {
-    const int64_t b = bt0 + r;
+  Cand<T> c[kRowsPerWave][kLoadsPerRow];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    int64_t b = bt0 + wave + kWaves * i;
+    if (b > B - 1) b = B - 1;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerRow; ++j) {
+      const int t = lane + 64 * j < a.nT ? lane + 64 * j : a.nT - 1;
+      c[i][j] = load_cand(cand + b * a.nT + t);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t b = bt0 + wave + kWaves * i;
     if (b >= B) break;
-    const int64_t o = row_winner(cand + b * a.nT, a.nT, lane);
-    if (lane == 0) a.out[b] = o;
+    T bm = neg_inf<T>();
+    int32_t bi = kNoIndex;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerRow; ++j)
+      if (lane + 64 * j < a.nT && beats(c[i][j].m, c[i][j].idx, bm, bi)) {
+        bm = c[i][j].m;
+        bi = c[i][j].idx;
+      }
+    wave_argmax_xor(bm, bi, 0);
+    if (lane == 0) a.out[b] = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
   }
   if (tid == 0) clear_counter(a.counters + blockIdx.y);
 }
@@ -652,7 +677,7 @@ hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream)
 
 int fused_num_tiles(int64_t V, int num_cus) {
   const int64_t nunits = (V + 7) >> 3;
-  int64_t g = num_cus;  // one workgroup per CU
+  int64_t g = num_cus < kMaxFusedTiles ? num_cus : kMaxFusedTiles;  // one workgroup per CU
   if (g > nunits) g = nunits;
   if (g < 1) g = 1;
   return (int)g;

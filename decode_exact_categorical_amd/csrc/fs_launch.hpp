@@ -29,7 +29,11 @@ struct FusedArgs {
 
 enum FusedEpilogue { kEpiSample32 = 0, kEpiSample64 = 1, kEpiStore = 2 };
 
-// Number of vocabulary tiles (workgroups along x) the fused kernel uses.
+// Number of vocabulary tiles (workgroups along x) the fused kernel uses: one
+// per CU, at most kMaxFusedTiles (Stage 2 reads a row's candidates in
+// kMaxFusedTiles / 64 loads per lane).
+constexpr int kMaxFusedTiles = 256;
+static_assert(kMaxFusedTiles % 64 == 0, "whole waves of candidates");
 int fused_num_tiles(int64_t V, int num_cus);
 hipError_t launch_fused_stage1(const FusedArgs& a, int epilogue, hipStream_t stream);
 
