@@ -103,13 +103,26 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
   }
 }
 
-// MFMA row blocks (16 rows) per wave per pass: five with up to 32 batch
-// columns, three with more, where two k-step pairs of W fragments in flight
-// beside the accumulators would not fit in a wave's 256 VGPRs (two waves per
-// SIMD).  Four row blocks stream W markedly slower than three or five.
-template <int NB, int EPI>
-struct RowBlocks {
-  static constexpr int value = NB <= 2 ? 5 : 3;
+// How W flows through a wave, per batch width and epilogue (a wave has 256
+// VGPRs at two waves per SIMD):
+//  * up to 32 columns: 5 MFMA row blocks (80 rows) per pass, two k-step pairs
+//    of W in flight, each row block reloaded as soon as its MFMAs issue;
+//  * 48 and 64 columns: 5 row blocks with one pair in flight, each row block
+//    reloaded as soon as its MFMAs issue ("ring of one"): a wave covers its
+//    ~74 rows in one pass, where two pairs in flight would need passes of 3
+//    row blocks, i.e. two passes, each restaging H and refilling the pipe.
+//    Where the two k-steps' H fragments do not fit at once, they are read one
+//    after the other (half_h);
+//  * 64 columns with a bias or float64 noise: 3 row blocks, two pairs in
+//    flight, each pair reloaded after all its MFMAs (no room for more).
+// Passes of 4 row blocks (64 rows) stream W markedly slower than 3 or 5.
+template <int NB, int EPI, bool HAS_BIAS>
+struct Pipeline {
+  static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || EPI == kEpiSample64);
+  static constexpr bool ring1 = NB >= 3 && !wide_extra;
+  static constexpr int row_blocks = (NB <= 2 || ring1) ? 5 : 3;
+  static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || EPI == kEpiSample64);
+  static constexpr bool interleave = !wide_extra;
 };
 
 // Whether the noise is folded into the accumulators inside the k-loop: float32
@@ -123,11 +136,10 @@ template <int NB, int EPI, bool HAS_BIAS>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
   constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS>::value;
-  constexpr int kRB = RowBlocks<NB, EPI>::value;
-  // Per-row-block reloads (mma_reload) need both k-steps' H fragments at
-  // once; with 64 columns and a bias or float64 running bests those do not
-  // fit, and the pair is reloaded after all its MFMAs instead.
-  constexpr bool kInterleave = !(NB == 4 && (HAS_BIAS || EPI == kEpiSample64));
+  typedef Pipeline<NB, EPI, HAS_BIAS> Pipe;
+  constexpr int kRB = Pipe::row_blocks;
+  constexpr bool kRing1 = Pipe::ring1;
+  constexpr bool kInterleave = Pipe::interleave;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // The wave index is wave-uniform; saying so keeps every quantity derived
@@ -179,13 +191,16 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     cols[tid] = ci;
   }
   bool col_ok[NB];
-  T bm[NB];
-  int32_t bi[NB];
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    col_ok[cb] = bt0 + 16 * cb + col < B;
-    bm[cb] = neg_inf<T>();
-    bi[cb] = kNoIndex;
+  for (int cb = 0; cb < NB; ++cb) col_ok[cb] = bt0 + 16 * cb + col < B;
+
+  // Running best (score, index) of each batch column of this wave across its
+  // passes, in a wave-private LDS slot: registers hold one pass's bests, and
+  // only after that pass's k-loop.
+  __shared__ Cand<T> wrun[kWaves][16 * NB];
+  if (EPI != kEpiStore && grp == 0) {
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) wrun[wave][16 * cb + col] = Cand<T>{neg_inf<T>(), kNoIndex};
   }
 
   __shared__ __attribute__((aligned(16))) uint16_t hs[2][16 * NB][kHRow];
@@ -352,25 +367,55 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // first loads of the next pair leave one row block after the data
     // arrived rather than a whole phase later.
     auto mma_reload = [&](u32x4 (&w)[2][kRB], int buf, int kk, int q) {
-      bf16x8 h0[NB], h1[NB];
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        h0[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 8 * grp]);
-        h1[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 32 + 8 * grp]);
-      }
       const uint16_t* w0 = step_base(2 * q);
       const uint16_t* w1 = step_base(2 * q + 1);
+      if constexpr (Pipe::half_h) {
+        // The first k-step's MFMAs over every row block, then the second
+        // k-step's with the reloads: one k-step of H fragments live at a time.
+        {
+          bf16x8 h0[NB];
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
+          for (int cb = 0; cb < NB; ++cb)
+            h0[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 8 * grp]);
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[0][rb]), h0[cb], acc[rb][cb], 0, 0, 0);
+          for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[1][rb]), h1[cb], acc[rb][cb], 0, 0, 0);
-        w[0][rb] = load_frag(w0 + woff[rb]);
-        w[1][rb] = load_frag(w1 + woff[rb]);
+            for (int cb = 0; cb < NB; ++cb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[0][rb]), h0[cb], acc[rb][cb], 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        bf16x8 h1[NB];
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+          h1[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 32 + 8 * grp]);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[1][rb]), h1[cb], acc[rb][cb], 0, 0, 0);
+          w[0][rb] = load_frag(w0 + woff[rb]);
+          w[1][rb] = load_frag(w1 + woff[rb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        bf16x8 h0[NB], h1[NB];
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          h0[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 8 * grp]);
+          h1[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 32 + 8 * grp]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[0][rb]), h0[cb], acc[rb][cb], 0, 0, 0);
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[1][rb]), h1[cb], acc[rb][cb], 0, 0, 0);
+          w[0][rb] = load_frag(w0 + woff[rb]);
+          w[1][rb] = load_frag(w1 + woff[rb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     };
     auto mma = [&](const u32x4 (&w)[kRB], int buf, int kk) {
@@ -412,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     bias_slot_load(ba0, 0);
     bias_slot_load(ba1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    load_pair(pb, 1);
+    if constexpr (!kRing1) load_pair(pb, 1);
     bias_slot_load(bb0, 2);
     bias_slot_load(bb1, 3);
     __builtin_amdgcn_sched_barrier(0);
@@ -431,7 +476,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         const int q = ks >> 1;
         // sched_barrier keeps each phase where it is written, so the compiler
         // does not move the loads of a pair next to their use.
-        if constexpr (kInterleave) {
+        if constexpr (kRing1) {
+          mma_reload(pa, buf, j * 32, q + 1);
+          FS_FOLD_SLOT(ks, ba0);
+          FS_FOLD_SLOT(ks + 1, ba1);
+        } else if constexpr (kInterleave) {
           mma_reload(pa, buf, j * 32, q + 2);
           FS_FOLD_SLOT(ks, ba0);
           FS_FOLD_SLOT(ks + 1, ba1);
@@ -447,7 +496,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         bias_slot_load(ba0, ks + 4);
         bias_slot_load(ba1, ks + 5);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kInterleave) {
+        if constexpr (kRing1) {
+          mma_reload(pa, buf, (j + 2) * 32, q + 2);
+          FS_FOLD_SLOT(ks + 2, bb0);
+          FS_FOLD_SLOT(ks + 3, bb1);
+        } else if constexpr (kInterleave) {
           mma_reload(pb, buf, (j + 2) * 32, q + 3);
           FS_FOLD_SLOT(ks + 2, bb0);
           FS_FOLD_SLOT(ks + 3, bb1);
@@ -483,6 +536,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 #undef FS_FOLD_SLOT
 
     // End of pass: scores of this wave's fragments.
+    T bm[NB];
+    int32_t bi[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      bm[cb] = neg_inf<T>();
+      bi[cb] = kNoIndex;
+    }
     if (EPI == kEpiStore || kFold) {
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
@@ -583,27 +643,29 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           }
       }
     }
+    if (EPI != kEpiStore) {
+      // Lanes that share a column (the 4 row groups) -> one value per column,
+      // merged into the wave's running best.
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        wave_argmax_xor(bm[cb], bi[cb], 4);
+        if (grp == 0) {
+          const Cand<T> o = wrun[wave][16 * cb + col];
+          if (beats(bm[cb], bi[cb], o.m, o.idx)) wrun[wave][16 * cb + col] = Cand<T>{bm[cb], bi[cb]};
+        }
+      }
+    }
   }
 
   if (EPI == kEpiStore) return;
 
-  // Lanes that share a column (the 4 row groups) -> one value per column.
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) wave_argmax_xor(bm[cb], bi[cb], 4);
-
-  // Across the waves, in wave order, through LDS (the H buffers are free: the
-  // last chunk ended with a barrier).
-  Cand<T>* wbest = reinterpret_cast<Cand<T>*>(&hs[0][0][0]);
-  if (grp == 0) {
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) wbest[wave * (NB * 16) + cb * 16 + col] = Cand<T>{bm[cb], bi[cb]};
-  }
+  // Across the waves, in wave order, through LDS.
   __syncthreads();
   if (tid < NB * 16) {
-    Cand<T> best = wbest[tid];
+    Cand<T> best = wrun[0][tid];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      const Cand<T> o = wbest[w * (NB * 16) + tid];
+      const Cand<T> o = wrun[w][tid];
       if (beats(o.m, o.idx, best.m, best.idx)) best = o;
     }
     const int64_t b = bt0 + tid;
