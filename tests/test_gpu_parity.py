@@ -85,6 +85,15 @@ FUSED_CASES = [
     dict(B=70, D=520, V=777, bias=True),
     dict(B=16, D=4096, V=5000, greedy_rows=(3,)),
     dict(B=3, D=64, V=13, w_std=1.0),
+    # every batch width of a tile (16 / 32 / 48 / 64 columns), with and without
+    # a bias, D % 32 != 0 and ragged V
+    dict(B=24, D=96, V=1500, bias=True),
+    dict(B=48, D=128, V=2500, greedy_rows=(1,)),
+    dict(B=64, D=264, V=3001),
+    # more than 80 rows per wave: several passes over each wave's rows at
+    # every width, the running bests merged across passes
+    dict(B=64, D=64, V=170001, greedy_rows=(2, 40)),
+    dict(B=20, D=64, V=170001, bias=True),
 ]
 
 
