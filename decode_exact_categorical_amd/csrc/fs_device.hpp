@@ -64,13 +64,14 @@ __device__ __forceinline__ Words noise_words(const NoiseKey& k, uint32_t j, uint
 // exponential, g = -log E standard Gumbel.
 //
 // E must keep its relative accuracy where it is tiny (u near 1: the deep tail,
-// where g is large).  For u >= 1/2, E = -log u = 2 atanh(x) with
-// x = (1 - u) / (1 + u) in [0, 1/3]; 1 - u is exact on both grids, and the odd
-// series 2x (1 + x^2/3 + x^4/5 + ...) is summed to its last significant term
-// (8 terms in float32, 16 in float64, each first omitted term below the
-// precision's rounding unit).  For u < 1/2, E >= ln 2 and the hardware log2
-// (v_log_f32) times ln 2 is accurate to a few float32 ulps.  g = -ln 2 *
-// log2(E) by the hardware log2: an absolute error of ~1e-7 in g.
+// where g is large).  There E = -log u = 2 atanh(x) with x = (1 - u) / (1 + u);
+// 1 - u is exact on both grids, and the odd series 2x (1 + x^2/3 + x^4/5 + ...)
+// is summed to its last significant term, the first omitted term below the
+// precision's rounding unit: in float32 for u >= 3/4 (x <= 1/7, 5 terms), in
+// float64 for u >= 1/2 (x <= 1/3, 16 terms).  Below those points log2 u is
+// at least 0.41 in magnitude and the hardware log2 (v_log_f32) times ln 2 is
+// accurate to a few float32 ulps.  g = -ln 2 * log2(E) by the hardware log2:
+// an absolute error of ~1e-7 in g.
 //
 // Float64 noise keeps the 52-bit grid exactly and E's float64 relative accuracy
 // on u >= 1/2, which is what carries the tail from ~20 to ~40 nats; E for
@@ -86,17 +87,14 @@ __device__ __forceinline__ float exp1_f32(uint32_t w) {
   const float u = (float)(2u * k + 1u) * 0x1p-24f;
   const float x = (1.0f - u) * __builtin_amdgcn_rcpf(1.0f + u);
   const float z = x * x;
-  float p = 1.0f / 15.0f;
-  p = __builtin_fmaf(p, z, 1.0f / 13.0f);
-  p = __builtin_fmaf(p, z, 1.0f / 11.0f);
-  p = __builtin_fmaf(p, z, 1.0f / 9.0f);
+  float p = 1.0f / 9.0f;
   p = __builtin_fmaf(p, z, 1.0f / 7.0f);
   p = __builtin_fmaf(p, z, 1.0f / 5.0f);
   p = __builtin_fmaf(p, z, 1.0f / 3.0f);
   p = __builtin_fmaf(p, z, 1.0f);
   const float e_tail = 2.0f * x * p;
   const float e_body = -kLn2f * __builtin_amdgcn_logf(u);
-  return u >= 0.5f ? e_tail : e_body;
+  return u >= 0.75f ? e_tail : e_body;
 }
 
 __device__ __forceinline__ float gumbel_f32(uint32_t w) {

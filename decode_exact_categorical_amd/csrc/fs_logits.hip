@@ -47,12 +47,14 @@ __device__ __forceinline__ void score4(const LogitsArgs& a, bool greedy, T inv_t
     s[2] = T(y2) * inv_t + T(gumbel_f64(w1.w0, w1.w1));
     s[3] = T(y3) * inv_t + T(gumbel_f64(w1.w2, w1.w3));
   }
+  // A thread meets its logits in increasing index order, so a strictly larger
+  // score is the only way to beat the running best: on equal scores the
+  // earlier (smaller) index stays, as the candidate order requires.
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int32_t i = (int32_t)(i0 + j);
-    if (i0 + j < hi && beats(s[j], i, bm, bi)) {
+    if (i0 + j < hi && s[j] > bm) {
       bm = s[j];
-      bi = i;
+      bi = (int32_t)(i0 + j);
     }
   }
 }
