@@ -34,6 +34,7 @@ METRIC = ("µs/decode-step & achieved HBM GB/s (fused LM-head+sample), "
 D_MODEL, VOCAB = 4096, 151936
 LOGITS_CHUNK = 2048             # logits per workgroup of the standalone sampler
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_stage1_qwen3_8b_b64_traffic.txt")
 KERNEL_SOURCES = ["decode_exact_categorical_amd/csrc/fs_fused.hip",
                   "decode_exact_categorical_amd/csrc/fs_device.hpp",
@@ -151,6 +152,9 @@ def main() -> int:
     ap.add_argument("--only-fused", action="store_true",
                     help="time the fused step only (no sweep, baselines or CPU oracle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--standalone-sweep", action="store_true",
+                    help="only time fs_sample_logits at the row counts and vocabulary sizes of "
+                         "the Megatron fp64-noise page's cost table, float32 and float64 noise")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB, --steps times (the known-size "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -177,6 +181,26 @@ def main() -> int:
 
     import decode_exact_categorical_amd as fs
     import synthetic
+
+    if args.standalone_sweep:
+        dev = torch.device("cuda:0")
+        rows = {}
+        for (vl, bl) in ((131072, 1), (131072, 8), (131072, 64), (131072, 256), (131072, 1024),
+                         (262144, 64), (262144, 256)):
+            g = torch.Generator(device=dev).manual_seed(5)
+            X = torch.randn(bl, vl, generator=g, dtype=torch.float32, device=dev)
+            Tl = torch.full((bl,), 0.8, dtype=torch.float32, device=dev)
+            for f64 in (False, True):
+                ms, kms, pc = time_calls(
+                    torch, fs, lambda s: fs.sample_logits(X, Tl, seed=99, offset=s, fp64_noise=f64),
+                    args.steps, args.warmup)
+                rows[f"V{vl}_B{bl}_{'fp64' if f64 else 'fp32'}"] = {
+                    "us_per_call": round(ms * 1e3, 2), "p50_us": round(pc["p50"] * 1e3, 2),
+                    "kernel_us": round(kms * 1e3, 2)}
+                log(f"  V={vl} B={bl} fp64={f64}: {rows[list(rows)[-1]]}")
+            del X
+        print(json.dumps({"standalone_sweep": rows, "unit": "us"}), flush=True)
+        return 0
 
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
@@ -278,6 +302,33 @@ def main() -> int:
             log(f"  {key}: {sa[key]}")
             del X
         result["standalone_sampler"] = sa
+
+        # The large-batch end: the Llama-3-shaped head at the compute crossover
+        # (H [256, 4096], W [128256, 4096], per-row temperature, fp32 bias with
+        # 10% of each row masked), reported against both the MFMA and the HBM peak.
+        log("timing the large-batch head (B=256, V=128256, bias + mask)")
+        gl = torch.Generator(device=dev).manual_seed(7)
+        VL, BL = 128256, 256
+        WL = (torch.randn(VL, D_MODEL, generator=gl, device=dev) * 0.02).to(torch.bfloat16)
+        HL = torch.randn(BL, D_MODEL, generator=gl, device=dev).to(torch.bfloat16)
+        TL = 0.5 + 0.7 * torch.rand(BL, generator=gl, device=dev)
+        biasL = torch.randn(BL, VL, generator=gl, device=dev)
+        biasL.masked_fill_(torch.rand(BL, VL, generator=gl, device=dev) < 0.1, float("-inf"))
+        ms, kms, pc = time_calls(
+            torch, fs, lambda s: fs.sample_fused(HL, WL, TL, biasL, seed=77, offset=s),
+            max(20, args.steps // 4), 5)
+        flops = 2 * BL * VL * D_MODEL
+        lb = kernel_alg_bytes(BL, D_MODEL, VL, fused_tiles(VL, cus), bias=True)
+        result["large_batch"] = {
+            "workload": "B=256, D=4096, V=128256, fp32 bias with 10% -inf, fp32 noise",
+            "us_per_call": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
+            "tflops": round(flops / (kms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (kms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+            "alg_bytes": lb, "hbm_gbs": round(lb / (kms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(lb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        log(f"  {result['large_batch']}")
+        del WL, HL, biasL
 
         # Baselines on the same data: (1) unfused: rocBLAS/hipBLASLt GEMM writes bf16
         # logits to HBM, then the standalone sampler; (2) softmax + multinomial.

@@ -150,12 +150,24 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   const int col = lane & 15;  // A row / B column / output column in a block
 
   const int64_t B = a.B, D = a.D, V = a.V;
-  const int64_t bt0 = (int64_t)blockIdx.y * kBatchTile;
+  // Which (vocabulary tile, batch tile) this workgroup takes.  Workgroups go
+  // to the 8 XCDs round-robin in launch order, so with several batch tiles the
+  // linear id is remapped to put every batch tile of a vocabulary tile on one
+  // XCD, launched together: they stream the same W rows at the same time and
+  // all but one read them from that XCD's L2.
+  const int nT = (int)gridDim.x, nbt = (int)gridDim.y;
+  int tile = (int)blockIdx.x, btile = (int)blockIdx.y;
+  if (nbt > 1 && nT % 8 == 0) {
+    const int lin = (int)blockIdx.y * nT + (int)blockIdx.x;
+    tile = (lin / (8 * nbt)) * 8 + lin % 8;
+    btile = (lin / 8) % nbt;
+  }
+  const int64_t bt0 = (int64_t)btile * kBatchTile;
 
   // Rows of this workgroup and of this wave, in 8-row units.
   const int64_t nunits = (V + 7) >> 3;
-  const int64_t g0 = nunits * (int64_t)blockIdx.x / gridDim.x;
-  const int64_t g1 = nunits * (int64_t)(blockIdx.x + 1) / gridDim.x;
+  const int64_t g0 = nunits * (int64_t)tile / nT;
+  const int64_t g1 = nunits * (int64_t)(tile + 1) / nT;
   const int64_t nu = g1 - g0;
   const int64_t r0 = (g0 + nu * wave / kWaves) * 8;
   int64_t r1 = (g0 + nu * (wave + 1) / kWaves) * 8;
@@ -670,7 +682,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
     const int64_t b = bt0 + tid;
     if (b < B) {
-      store_cand(reinterpret_cast<Cand<T>*>(a.cand) + b * a.nT + blockIdx.x, best);
+      store_cand(reinterpret_cast<Cand<T>*>(a.cand) + b * a.nT + tile, best);
       wait_stores_complete();
     }
   }
@@ -679,7 +691,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   // w takes rows w, w + 8, ... of the tile and issues every candidate load of
   // all its rows (clamped, always valid addresses) before reducing any, so the
   // tail costs one round trip to the coherence point, not one per row.
-  if (!finish_last(a.counters + blockIdx.y, gridDim.x)) return;
+  if (!finish_last(a.counters + btile, (uint32_t)nT)) return;
   constexpr int kRowsPerWave = kBatchTile / kWaves;
   constexpr int kLoadsPerRow = kMaxFusedTiles / 64;
   const Cand<T>* cand = reinterpret_cast<const Cand<T>*>(a.cand);
@@ -709,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     wave_argmax_xor(bm, bi, 0);
     if (lane == 0) a.out[b] = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
   }
-  if (tid == 0) clear_counter(a.counters + blockIdx.y);
+  if (tid == 0) clear_counter(a.counters + btile);
 }
 
 template <int NB>
