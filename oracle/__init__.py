@@ -67,6 +67,13 @@ def _load():
         lib.oracle_sample_fused.restype = None
         lib.oracle_sample_fused.argtypes = [P, P, i64, i64, i64, P, P, u64, u64, P,
                                             i32, P, P, P]
+        lib.oracle_e4m3_to_double.restype = ctypes.c_double
+        lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_logits_w8.restype = None
+        lib.oracle_logits_w8.argtypes = [P, P, P, i64, i64, i64, P]
+        lib.oracle_sample_fused_w8.restype = None
+        lib.oracle_sample_fused_w8.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P,
+                                               i32, P, P, P]
         lib.oracle_sample_logits.restype = None
         lib.oracle_sample_logits.argtypes = [P, i64, i64, P, u64, u64, P, i32, P, P, P]
         lib.oracle_sample_repeated_row.restype = None
@@ -173,6 +180,51 @@ def sample_fused(H, W, temp, bias=None, *, seed: int, offset: int, row_ids=None,
     best = np.zeros(B, dtype=np.float64)
     _load().oracle_sample_fused(_ptr(h), _ptr(w), B, D, V, _ptr(t), _ptr(bb), seed, offset,
                                 _ptr(rid), int(fp64_noise), _ptr(idx), _ptr(gap), _ptr(best))
+    return idx, gap, best
+
+
+def e4m3_to_double(codes) -> np.ndarray:
+    """float64 values of OCP FP8 E4M3 bit patterns (uint8 array)."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8)).reshape(-1)
+    f = _load().oracle_e4m3_to_double
+    return np.array([f(int(v)) for v in c], dtype=np.float64).reshape(np.shape(codes))
+
+
+def logits_w8(H, W8, scale) -> np.ndarray:
+    """float64[B, V] = scale[i] * (H @ e4m3(W8).T), H bf16 [B,D], W8 uint8 [V,D]."""
+    h = _bf16_bits(H)
+    w = np.ascontiguousarray(np.asarray(W8, dtype=np.uint8))
+    sc = np.ascontiguousarray(np.asarray(scale, dtype=np.float32).reshape(-1))
+    B, D = h.shape
+    V, D2 = w.shape
+    assert D == D2 and sc.shape[0] == V
+    Y = np.zeros((B, V), dtype=np.float64)
+    _load().oracle_logits_w8(_ptr(h), _ptr(w), _ptr(sc), B, D, V, _ptr(Y))
+    return Y
+
+
+def sample_fused_w8(H, W8, scale, temp, bias=None, *, seed: int, offset: int, row_ids=None,
+                    fp64_noise: bool = False):
+    """(idx, gap, best) for the fused definition over FP8 E4M3 weights with one
+    float32 scale per vocabulary row."""
+    h = _bf16_bits(H)
+    w = np.ascontiguousarray(np.asarray(W8, dtype=np.uint8))
+    sc = np.ascontiguousarray(np.asarray(scale, dtype=np.float32).reshape(-1))
+    B, D = h.shape
+    V = w.shape[0]
+    assert w.shape[1] == D and sc.shape[0] == V
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    bb = None
+    if bias is not None:
+        bb = np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+        assert bb.shape == (B, V)
+    rid = _u32_or_none(row_ids, B)
+    idx = np.zeros(B, dtype=np.int64)
+    gap = np.zeros(B, dtype=np.float64)
+    best = np.zeros(B, dtype=np.float64)
+    _load().oracle_sample_fused_w8(_ptr(h), _ptr(w), _ptr(sc), B, D, V, _ptr(t), _ptr(bb), seed,
+                                   offset, _ptr(rid), int(fp64_noise), _ptr(idx), _ptr(gap),
+                                   _ptr(best))
     return idx, gap, best
 
 

@@ -23,6 +23,9 @@
  *         and "Correctness requirements" (smallest-index tie-break).
  *   [PH]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *         1, 2, 3", SC'11, section 4 (the Philox-4x32 bijection, 10 rounds).
+ *   [OFP8] OCP 8-bit Floating Point Specification (OFP8), revision 1.0: the
+ *         E4M3 encoding of 8-bit weights (FP8 weights are the future work the
+ *         FlashSampling page's limitations section names).
  *
  * Definition computed (per batch row b, logical row id r = row_ids[b] or b):
  *   y_i   = sum_d H[b,d] * W[i,d]           float64, d ascending   [FS (1)]
@@ -137,9 +140,25 @@ static double bf16_to_double(uint16_t h)
     return (double)f;
 }
 
+/* OCP 8-bit floating point E4M3 bit pattern -> double (exact) [OFP8]: sign
+ * bit, 4 exponent bits with bias 7, 3 mantissa bits.  Exponent 0 encodes
+ * subnormals m/8 * 2^-6; exponent 15 with mantissa 7 is the only NaN (the
+ * format has no infinities, so 0x7E = 448 is the largest value). */
+static double e4m3_to_double(uint8_t v)
+{
+    int sign = v >> 7, e = (v >> 3) & 15, m = v & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp((double)m / 8.0, -6);
+    else mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
 /* ------------------------------------------------------------------ */
 /* Exported helpers.                                                    */
 /* ------------------------------------------------------------------ */
+
+double oracle_e4m3_to_double(uint8_t v) { return e4m3_to_double(v); }
 
 int oracle_num_threads(void)
 {
@@ -228,6 +247,26 @@ void oracle_logits(const uint16_t *H, const uint16_t *W, int64_t B, int64_t D,
     free(hrow);
 }
 
+/* Logits of an LM head whose weight is stored as 8-bit floats with one scale
+ * per vocabulary row (the FP8 weights [FS limitations] names as future work):
+ * Y[b,i] = scale[i] * sum_d H[b,d] * e4m3(W8[i,d]), float64, d ascending. */
+void oracle_logits_w8(const uint16_t *H, const uint8_t *W8, const float *scale,
+                      int64_t B, int64_t D, int64_t V, double *Y)
+{
+    double *hrow = (double *)malloc((size_t)D * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t d = 0; d < D; ++d) hrow[d] = bf16_to_double(H[b * D + d]);
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i) {
+            const uint8_t *w = W8 + i * D;
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc += hrow[d] * e4m3_to_double(w[d]);
+            Y[b * V + i] = (double)scale[i] * acc;
+        }
+    }
+    free(hrow);
+}
+
 /* Perturbed score of one element [FS (2)-(4); SK 3-4].  y is the logit, beta
  * the additive bias (NULL bias means 0), t the row temperature. */
 static double score_of(double y, double beta, double t, uint64_t seed,
@@ -292,6 +331,35 @@ void oracle_sample_fused(const uint16_t *H, const uint16_t *W, int64_t B,
             const uint16_t *w = W + i * D;
             double y = 0.0;
             for (int64_t d = 0; d < D; ++d) y += hrow[d] * bf16_to_double(w[d]);
+            double beta = bias ? (double)bias[b * V + i] : 0.0;
+            s[i] = score_of(y, beta, t, seed, offset, r, i, fp64_noise);
+        }
+        select_row(s, V, &out_idx[b], &out_gap[b], &out_best[b]);
+    }
+    free(hrow);
+    free(s);
+}
+
+/* Fused path over FP8 weights: the logits of oracle_logits_w8, then the same
+ * transform, noise and selection as oracle_sample_fused. */
+void oracle_sample_fused_w8(const uint16_t *H, const uint8_t *W8, const float *scale,
+                            int64_t B, int64_t D, int64_t V, const float *temp,
+                            const float *bias, uint64_t seed, uint64_t offset,
+                            const uint32_t *row_ids, int fp64_noise,
+                            int64_t *out_idx, double *out_gap, double *out_best)
+{
+    double *s = (double *)malloc((size_t)V * sizeof(double));
+    double *hrow = (double *)malloc((size_t)D * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        double t = (double)temp[b];
+        for (int64_t d = 0; d < D; ++d) hrow[d] = bf16_to_double(H[b * D + d]);
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i) {
+            const uint8_t *w = W8 + i * D;
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc += hrow[d] * e4m3_to_double(w[d]);
+            double y = (double)scale[i] * acc;
             double beta = bias ? (double)bias[b * V + i] : 0.0;
             s[i] = score_of(y, beta, t, seed, offset, r, i, fp64_noise);
         }

@@ -33,6 +33,25 @@ def weight(V: int, D: int, std: float, seed: int = SEED_W, chunk_rows: int = 819
     return W
 
 
+def weight_fp8(V: int, D: int, std: float, seed: int = SEED_W, chunk_rows: int = 8192):
+    """An FP8 LM-head weight: (W8 uint8 [V, D] OCP E4M3 bit patterns, scale fp32 [V]).
+
+    Each row of a N(0, std^2) draw is stored as e4m3 values times one float32
+    scale, the row's largest magnitude over 448 (the largest E4M3 value), the
+    usual per-channel weight quantisation; torch's float8_e4m3fn conversion
+    rounds each value to nearest."""
+    W8 = torch.empty((V, D), dtype=torch.uint8)
+    scale = torch.empty((V,), dtype=torch.float32)
+    g = _gen(seed)
+    for r0 in range(0, V, chunk_rows):
+        r1 = min(V, r0 + chunk_rows)
+        w = torch.randn((r1 - r0, D), generator=g) * std
+        s = (w.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
+        W8[r0:r1] = (w / s[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        scale[r0:r1] = s
+    return W8, scale
+
+
 def hidden(B: int, D: int, std: float = 1.0, seed: int = SEED_H) -> torch.Tensor:
     """H[B, D] bf16 ~ N(0, std^2)."""
     return (torch.randn((B, D), generator=_gen(seed)) * std).to(torch.bfloat16)
