@@ -77,11 +77,14 @@ def fused_tiles(V: int, cus: int) -> int:
     return max(1, min((V + 7) // 8, cus))
 
 
-def kernel_alg_bytes(B: int, D: int, V: int, n_tiles: int, bias: bool = False, cand: int = 8) -> int:
+def kernel_alg_bytes(B: int, D: int, V: int, n_tiles: int, bias: bool = False, cand: int = 8,
+                     fp8: bool = False) -> int:
     """What one fused sampling launch must move (Stage 1 and Stage 2 in one kernel):
-    W once, H once, temperatures, [bias], candidates written and read back once,
-    the sampled indices written."""
-    return (V * D * 2 + B * D * 2 + 4 * B + (4 * B * V if bias else 0)
+    W once (bf16, or FP8 codes plus one float32 scale per row), H once,
+    temperatures, [bias], candidates written and read back once, the sampled
+    indices written."""
+    w_bytes = V * D + 4 * V if fp8 else V * D * 2
+    return (w_bytes + B * D * 2 + 4 * B + (4 * B * V if bias else 0)
             + 2 * cand * B * n_tiles + 8 * B)
 
 
@@ -282,6 +285,34 @@ def main() -> int:
                            "tokens_per_s": round(b / (ms * 1e-3), 1)}
             log(f"  B={b}: {per[str(b)]}")
         result["batch_sweep"] = per
+
+        # FP8 weights: the same head quantised per row to OCP E4M3 codes with one
+        # float32 scale per row (the row's largest magnitude over 448), on the GPU.
+        log("timing the FP8-weight fused step")
+        amax = W.float().abs().amax(dim=1)
+        W_scale = (amax / 448.0).clamp_min(1e-30).contiguous()
+        W8 = torch.empty((VOCAB, D_MODEL), dtype=torch.uint8, device=dev)
+        for r0 in range(0, VOCAB, 16384):
+            r1 = min(VOCAB, r0 + 16384)
+            W8[r0:r1] = (W[r0:r1].float() / W_scale[r0:r1, None]).to(torch.float8_e4m3fn).view(
+                torch.uint8)
+        f8 = {"workload": "W [151936, 4096] OCP E4M3 + float32 row scales, fp32 noise"}
+        for b in sorted(set(sweep + [B])):
+            Hs, Ts = H[:b].contiguous(), temp[:b].contiguous()
+            ms, kms, pc = time_calls(
+                torch, fs,
+                lambda s: fs.sample_fused_w8(Hs, W8, W_scale, Ts, seed=1234, offset=2 * 10**6 + s),
+                max(20, args.steps // 2), args.warmup)
+            kb = kernel_alg_bytes(b, D_MODEL, VOCAB, nT, fp8=True)
+            f8[str(b)] = {"us_per_step": round(ms * 1e3, 2),
+                          "p50_us": round(pc["p50"] * 1e3, 2),
+                          "kernel_us": round(kms * 1e3, 2),
+                          "kernel_gbs": round(kb / (kms * 1e-3) / 1e9, 1),
+                          "kernel_frac": round(kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "tokens_per_s": round(b / (ms * 1e-3), 1)}
+            log(f"  fp8 B={b}: {f8[str(b)]}")
+        result["fp8_weights"] = f8
+        del W8, amax
 
         # The standalone sampler over float32 logits: the tail-rate workload's
         # chunk shape (4096 rows x 131072) and a decode-sized batch.

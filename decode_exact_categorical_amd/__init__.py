@@ -7,6 +7,7 @@ per (device, stream), and passes raw pointers.  PyTorch provides device memory
 and streams.  If the library has not been built, every call raises.
 
     tok = sample_fused(H, W, temp, bias=None, seed=1234, offset=step)   # [B] int64
+    tok = sample_fused_w8(H, W8, w_scale, temp, seed=1234, offset=step)  # FP8 E4M3 W
     tok = sample_logits(logits, temp, seed=1234, offset=step, fp64_noise=True)
 """
 from __future__ import annotations
@@ -18,8 +19,8 @@ import threading
 import torch
 
 __all__ = [
-    "FS_FP64_NOISE", "FSampleError", "sample_fused", "sample_logits", "workspace_bytes",
-    "debug_philox_words", "debug_logits", "debug_noise", "library_path", "load_library",
+    "FS_FP64_NOISE", "FSampleError", "sample_fused", "sample_fused_w8", "sample_logits",
+    "workspace_bytes", "debug_philox_words", "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
     "KernelTimer",
 ]
 
@@ -76,6 +77,11 @@ def load_library():
         lib.fs_debug_noise.argtypes = [P, i64, i32, P, P, P]
         lib.fs_debug_logits.restype = i32
         lib.fs_debug_logits.argtypes = [P, P, i64, i64, i64, P, P]
+        lib.fs_sample_fused_w8.restype = i32
+        lib.fs_sample_fused_w8.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P, P, u32, P,
+                                           sz, P]
+        lib.fs_debug_logits_w8.restype = i32
+        lib.fs_debug_logits_w8.argtypes = [P, P, P, i64, i64, i64, P, P]
         _lib = lib
         return lib
 
@@ -168,6 +174,48 @@ def sample_fused(H: torch.Tensor, W: torch.Tensor, temp, bias: torch.Tensor | No
     return out
 
 
+def _w8_bytes(W8: torch.Tensor, dev, V: int, D: int) -> torch.Tensor:
+    """FP8 E4M3 weights as their uint8 codes (a float8_e4m3fn tensor is viewed)."""
+    if W8.dtype == torch.float8_e4m3fn:
+        W8 = W8.view(torch.uint8)
+    _need(W8, "W8", torch.uint8, dev, (V, D))
+    return W8
+
+
+def sample_fused_w8(H: torch.Tensor, W8: torch.Tensor, w_scale: torch.Tensor, temp,
+                    bias: torch.Tensor | None = None, *, seed: int, offset: int,
+                    row_ids: torch.Tensor | None = None, fp64_noise: bool = False,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """sample_fused with FP8 E4M3 weights: row i of W is w_scale[i] * e4m3(W8[i]).
+    W8 is [V, D] uint8 codes or float8_e4m3fn; w_scale [V] float32."""
+    lib = load_library()
+    dev = H.device
+    if dev.type != "cuda":
+        raise ValueError("H must be a GPU tensor")
+    if H.dim() != 2 or W8.dim() != 2:
+        raise ValueError("H must be [B, D] and W8 [V, D]")
+    B, D = H.shape
+    V = W8.shape[0]
+    _need(H, "H", torch.bfloat16, dev, (B, D))
+    W8 = _w8_bytes(W8, dev, V, D)
+    _need(w_scale, "w_scale", torch.float32, dev, (V,))
+    t = _temp_tensor(temp, B, dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (B, V))
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B,))
+    flags = FS_FP64_NOISE if fp64_noise else 0
+    need = int(lib.fs_workspace_bytes(B, V, flags)) if V > 0 else 0
+    ws = _workspace(dev, need)
+    st = lib.fs_sample_fused_w8(_ptr(H), _ptr(W8), _ptr(w_scale), B, D, V, _ptr(t), _ptr(bias),
+                                seed, offset, _ptr(out), _ptr(rid), flags, _ptr(ws), ws.numel(),
+                                _stream(dev))
+    _check(st, "fs_sample_fused_w8")
+    return out
+
+
 def sample_logits(logits: torch.Tensor, temp, *, seed: int, offset: int,
                   row_ids: torch.Tensor | None = None, fp64_noise: bool = False,
                   out: torch.Tensor | None = None) -> torch.Tensor:
@@ -248,4 +296,19 @@ def debug_logits(H: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
     Y = torch.empty((B, V), dtype=torch.float32, device=dev)
     _check(lib.fs_debug_logits(_ptr(H), _ptr(W), B, D, V, _ptr(Y), _stream(dev)),
            "fs_debug_logits")
+    return Y
+
+
+def debug_logits_w8(H: torch.Tensor, W8: torch.Tensor, w_scale: torch.Tensor) -> torch.Tensor:
+    """float32 [B, V] logits from the FP8 path's matmul code and row scales (test hook)."""
+    lib = load_library()
+    dev = H.device
+    B, D = H.shape
+    V = W8.shape[0]
+    _need(H, "H", torch.bfloat16, dev, (B, D))
+    W8 = _w8_bytes(W8, dev, V, D)
+    _need(w_scale, "w_scale", torch.float32, dev, (V,))
+    Y = torch.empty((B, V), dtype=torch.float32, device=dev)
+    _check(lib.fs_debug_logits_w8(_ptr(H), _ptr(W8), _ptr(w_scale), B, D, V, _ptr(Y),
+                                  _stream(dev)), "fs_debug_logits_w8")
     return Y

@@ -121,16 +121,106 @@ fs_status check_workspace(void* ws, size_t have, int64_t B, int64_t V, uint32_t 
   return FS_OK;
 }
 
-fs_status check_fused(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D, int64_t V) {
+// Size and pointer checks shared by the bf16 (W) and FP8 (W8 + w_scale)
+// weight formats.  An FP8 row is D bytes, so D % 16 == 0 keeps every row's
+// 16-byte lane loads inside the row and aligned.
+fs_status check_fused(const fs_bf16* H, const void* W, bool w8, const float* w_scale, int64_t B,
+                      int64_t D, int64_t V) {
   fs_status s = check_sizes(B, V);
   if (s != FS_OK) return s;
   if (B > kMaxFusedB) return fail(FS_ERR_UNSUPPORTED, "B = %lld > 2^22", (long long)B);
   if (D < 1) return fail(FS_ERR_INVALID_ARG, "D = %lld must be positive", (long long)D);
-  if (D % 8 != 0) return fail(FS_ERR_UNSUPPORTED, "D = %lld is not a multiple of 8", (long long)D);
+  const int dmul = w8 ? 16 : 8;
+  if (D % dmul != 0)
+    return fail(FS_ERR_UNSUPPORTED, "D = %lld is not a multiple of %d", (long long)D, dmul);
   if (D > ((int64_t)1 << 24)) return fail(FS_ERR_UNSUPPORTED, "D = %lld too large", (long long)D);
   if (B > 0 && (H == nullptr || W == nullptr)) return fail(FS_ERR_INVALID_ARG, "H or W is null");
+  if (B > 0 && w8 && w_scale == nullptr) return fail(FS_ERR_INVALID_ARG, "w_scale is null");
   if (B > 0 && (!aligned16(H) || !aligned16(W)))
     return fail(FS_ERR_UNSUPPORTED, "H and W must be 16-byte aligned");
+  return FS_OK;
+}
+
+// The kernel addresses one wave's W rows through 32-bit offsets.
+fs_status check_span(int64_t V, int64_t D, int nT, bool w8) {
+  if (fs::fused_wave_span_bytes(V, D, nT, w8 ? 1 : 2) >= ((int64_t)1 << 31))
+    return fail(FS_ERR_UNSUPPORTED, "V * D too large (V = %lld, D = %lld)", (long long)V,
+                (long long)D);
+  return FS_OK;
+}
+
+fs_status sample_fused(const fs_bf16* H, const void* W, bool w8, const float* w_scale, int64_t B,
+                       int64_t D, int64_t V, const float* temp, const float* bias, uint64_t seed,
+                       uint64_t offset, int64_t* out_idx, const uint32_t* row_ids, uint32_t flags,
+                       void* workspace, size_t workspace_bytes, fs_stream_t stream) {
+  fs_status s = check_fused(H, W, w8, w_scale, B, D, V);
+  if (s != FS_OK) return s;
+  if (flags & ~FS_FP64_NOISE) return fail(FS_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (B == 0) return FS_OK;
+  if (temp == nullptr || out_idx == nullptr) return fail(FS_ERR_INVALID_ARG, "temp or out_idx is null");
+  s = check_workspace(workspace, workspace_bytes, B, V, flags);
+  if (s != FS_OK) return s;
+
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != FS_OK) return s;
+  const int nT = fs::fused_num_tiles(V, cus);
+  s = check_span(V, D, nT, w8);
+  if (s != FS_OK) return s;
+  const bool fp64 = (flags & FS_FP64_NOISE) != 0;
+  fs::FusedArgs a;
+  memset(&a, 0, sizeof a);
+  a.H = H;
+  a.W = w8 ? nullptr : static_cast<const uint16_t*>(W);
+  a.W8 = w8 ? static_cast<const uint8_t*>(W) : nullptr;
+  a.w_scale = w8 ? w_scale : nullptr;
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.temp = temp;
+  a.bias = bias;
+  a.row_ids = row_ids;
+  a.key = fs::make_key(seed, offset);
+  a.cand = candidates_of(workspace);
+  a.nT = nT;
+  a.counters = counters_of(workspace);  // ceil(B / 64) <= 65536 words (B <= 2^22)
+  a.out = out_idx;
+  a.Y = nullptr;
+  a.bias_vec4 = bias != nullptr && aligned16(bias) && (V % 4 == 0);
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  if (ev) (void)hipEventRecord(ev[0], st);
+  hipError_t e = fs::launch_fused_stage1(a, fp64 ? fs::kEpiSample64 : fs::kEpiSample32, st);
+  if (e != hipSuccess) return hip_fail(e, "fused sampling launch");
+  if (ev) (void)hipEventRecord(ev[1], st);
+  return FS_OK;
+}
+
+fs_status debug_logits(const fs_bf16* H, const void* W, bool w8, const float* w_scale, int64_t B,
+                       int64_t D, int64_t V, float* Y, fs_stream_t stream) {
+  fs_status s = check_fused(H, W, w8, w_scale, B, D, V);
+  if (s != FS_OK) return s;
+  if (B == 0) return FS_OK;
+  if (Y == nullptr) return fail(FS_ERR_INVALID_ARG, "Y is null");
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != FS_OK) return s;
+  const int nT = fs::fused_num_tiles(V, cus);
+  s = check_span(V, D, nT, w8);
+  if (s != FS_OK) return s;
+  fs::FusedArgs a;
+  memset(&a, 0, sizeof a);
+  a.H = H;
+  a.W = w8 ? nullptr : static_cast<const uint16_t*>(W);
+  a.W8 = w8 ? static_cast<const uint8_t*>(W) : nullptr;
+  a.w_scale = w8 ? w_scale : nullptr;
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.nT = nT;
+  a.Y = Y;
+  hipError_t e = fs::launch_fused_stage1(a, fs::kEpiStore, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fused logits launch");
   return FS_OK;
 }
 
@@ -161,41 +251,18 @@ fs_status fs_sample_fused(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t
                           int64_t* out_idx, const uint32_t* row_ids, uint32_t flags,
                           void* workspace, size_t workspace_bytes, fs_stream_t stream) {
   g_last_error[0] = 0;
-  fs_status s = check_fused(H, W, B, D, V);
-  if (s != FS_OK) return s;
-  if (flags & ~FS_FP64_NOISE) return fail(FS_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-  if (B == 0) return FS_OK;
-  if (temp == nullptr || out_idx == nullptr) return fail(FS_ERR_INVALID_ARG, "temp or out_idx is null");
-  s = check_workspace(workspace, workspace_bytes, B, V, flags);
-  if (s != FS_OK) return s;
+  return sample_fused(H, W, false, nullptr, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
+                      flags, workspace, workspace_bytes, stream);
+}
 
-  int cus = 0;
-  s = device_cus(&cus);
-  if (s != FS_OK) return s;
-  const bool fp64 = (flags & FS_FP64_NOISE) != 0;
-  fs::FusedArgs a;
-  a.H = H;
-  a.W = W;
-  a.B = B;
-  a.D = D;
-  a.V = V;
-  a.temp = temp;
-  a.bias = bias;
-  a.row_ids = row_ids;
-  a.key = fs::make_key(seed, offset);
-  a.cand = candidates_of(workspace);
-  a.nT = fs::fused_num_tiles(V, cus);
-  a.counters = counters_of(workspace);  // ceil(B / 64) <= 65536 words (B <= 2^22)
-  a.out = out_idx;
-  a.Y = nullptr;
-  a.bias_vec4 = bias != nullptr && aligned16(bias) && (V % 4 == 0);
-  hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = prof_slot();
-  if (ev) (void)hipEventRecord(ev[0], st);
-  hipError_t e = fs::launch_fused_stage1(a, fp64 ? fs::kEpiSample64 : fs::kEpiSample32, st);
-  if (e != hipSuccess) return hip_fail(e, "fused sampling launch");
-  if (ev) (void)hipEventRecord(ev[1], st);
-  return FS_OK;
+fs_status fs_sample_fused_w8(const fs_bf16* H, const uint8_t* W8, const float* w_scale, int64_t B,
+                             int64_t D, int64_t V, const float* temp, const float* bias,
+                             uint64_t seed, uint64_t offset, int64_t* out_idx,
+                             const uint32_t* row_ids, uint32_t flags, void* workspace,
+                             size_t workspace_bytes, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  return sample_fused(H, W8, true, w_scale, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
+                      flags, workspace, workspace_bytes, stream);
 }
 
 fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const float* temp,
@@ -304,25 +371,13 @@ fs_status fs_debug_noise(const uint32_t* words, int64_t n, int fp64, double* E, 
 fs_status fs_debug_logits(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D, int64_t V,
                           float* Y, fs_stream_t stream) {
   g_last_error[0] = 0;
-  fs_status s = check_fused(H, W, B, D, V);
-  if (s != FS_OK) return s;
-  if (B == 0) return FS_OK;
-  if (Y == nullptr) return fail(FS_ERR_INVALID_ARG, "Y is null");
-  int cus = 0;
-  s = device_cus(&cus);
-  if (s != FS_OK) return s;
-  fs::FusedArgs a;
-  memset(&a, 0, sizeof a);
-  a.H = H;
-  a.W = W;
-  a.B = B;
-  a.D = D;
-  a.V = V;
-  a.nT = fs::fused_num_tiles(V, cus);
-  a.Y = Y;
-  hipError_t e = fs::launch_fused_stage1(a, fs::kEpiStore, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "fused logits launch");
-  return FS_OK;
+  return debug_logits(H, W, false, nullptr, B, D, V, Y, stream);
+}
+
+fs_status fs_debug_logits_w8(const fs_bf16* H, const uint8_t* W8, const float* w_scale, int64_t B,
+                             int64_t D, int64_t V, float* Y, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  return debug_logits(H, W8, true, w_scale, B, D, V, Y, stream);
 }
 
 }  // extern "C"

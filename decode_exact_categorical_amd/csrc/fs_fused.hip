@@ -35,6 +35,11 @@
 //    the bias and add g after the division, which keeps (y + bias) / t + g.
 //  * Float64 noise keeps the score in float64: y + bias and the noise are
 //    combined after the k-loop, with two Philox calls per fragment.
+//  * FP8 weights (OCP E4M3 codes, a float32 scale per vocabulary row) stream
+//    at one byte per element: a lane's 16-byte load holds two MFMA k-steps of
+//    its row, widened on chip to bf16 (exact for every E4M3 value) before the
+//    same bf16 MFMAs; the row scale multiplies the finished sum in float32,
+//    and the noise is added after the k-loop.
 //  * Scores feed a per-lane running argmax (larger score, then smaller index);
 //    xor-shuffles and LDS reduce it to one candidate per batch row per
 //    workgroup.
@@ -82,6 +87,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 load_frag(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+__device__ __forceinline__ u32x4 load_frag(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Sixteen OCP FP8 E4M3 values (16 bytes, k ascending) as two bf16x8 MFMA
+// operands: bytes 0..7 and bytes 8..15.  Every E4M3 value is a bf16 value, so
+// the conversion (v_cvt_scalef32_pk_bf16_fp8, scale 1) is exact.
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4 v, u32x4& lo, u32x4& hi) {
+#define FS_CVT(W, HIGH) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((W), 1.0f, HIGH))
+  lo = u32x4{FS_CVT(v[0], false), FS_CVT(v[0], true), FS_CVT(v[1], false), FS_CVT(v[1], true)};
+  hi = u32x4{FS_CVT(v[2], false), FS_CVT(v[2], true), FS_CVT(v[3], false), FS_CVT(v[3], true)};
+#undef FS_CVT
+}
 
 __device__ __forceinline__ bf16x8 as_bf16(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -116,27 +134,38 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
 //  * 64 columns with a bias or float64 noise: 3 row blocks, two pairs in
 //    flight, each pair reloaded after all its MFMAs (no room for more).
 // Passes of 4 row blocks (64 rows) stream W markedly slower than 3 or 5.
-template <int NB, int EPI, bool HAS_BIAS>
+// FP8 weights (W8) take the simplest of these: two pairs in flight, 5 row
+// blocks up to 32 columns and 3 beyond, each pair reloaded after its MFMAs.
+template <int NB, int EPI, bool HAS_BIAS, bool W8>
 struct Pipeline {
   static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || EPI == kEpiSample64);
-  static constexpr bool ring1 = NB >= 3 && !wide_extra;
+  static constexpr bool ring1 = !W8 && NB >= 3 && !wide_extra;
   static constexpr int row_blocks = (NB <= 2 || ring1) ? 5 : 3;
   static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || EPI == kEpiSample64);
-  static constexpr bool interleave = !wide_extra;
+  static constexpr bool interleave = !W8 && !wide_extra;
 };
 
 // Whether the noise is folded into the accumulators inside the k-loop: float32
-// noise is; float64 noise is added after the k-loop, still in the same pass.
-template <int NB, int EPI, bool HAS_BIAS>
+// noise over bf16 weights is.  Float64 noise, and any noise over FP8 weights
+// (whose per-row scale multiplies the sum only), is added after the k-loop,
+// still in the same pass.
+template <int NB, int EPI, bool HAS_BIAS, bool W8>
 struct FoldNoise {
-  static constexpr bool value = EPI == kEpiSample32;
+  static constexpr bool value = EPI == kEpiSample32 && !W8;
 };
 
-template <int NB, int EPI, bool HAS_BIAS>
+template <int NB, int EPI, bool HAS_BIAS, bool W8>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
-  constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS>::value;
-  typedef Pipeline<NB, EPI, HAS_BIAS> Pipe;
+  constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS, W8>::value;
+  typedef Pipeline<NB, EPI, HAS_BIAS, W8> Pipe;
+  // W element bytes, and k per 16-byte lane load (one MFMA k-step of bf16,
+  // two of FP8).
+  constexpr int kEB = W8 ? 1 : 2;
+  constexpr int kKPerLoad = W8 ? 64 : 32;
+  constexpr int kLoadsPerChunk = kKC / kKPerLoad;
+  typedef typename std::conditional<W8, uint8_t, uint16_t>::type WElem;
+  const WElem* const wbase = W8 ? reinterpret_cast<const WElem*>(a.W8) : reinterpret_cast<const WElem*>(a.W);
   constexpr int kRB = Pipe::row_blocks;
   constexpr bool kRing1 = Pipe::ring1;
   constexpr bool kInterleave = Pipe::interleave;
@@ -177,8 +206,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   const int max_rb = (int)((((nu + kWaves - 1) / kWaves) * 8 + 15) >> 4);
   const int npass = (max_rb + kRB - 1) / kRB;
 
-  const int KS = (int)((D + 31) >> 5);
-  const int NC = (KS + kStepsPerChunk - 1) / kStepsPerChunk;
+  const int KLS = (int)((D + kKPerLoad - 1) / kKPerLoad);  // load steps
+  const int NC = (KLS + kLoadsPerChunk - 1) / kLoadsPerChunk;
 
   // Per-column sampling constants live in LDS (16 bytes a column), read when a
   // fragment is folded or scored; registers hold only each column's running
@@ -262,16 +291,18 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // wave's last row (same cache lines, no extra HBM traffic); their results
     // are never scored.
     // Addresses: a wave-uniform base (scalar registers) plus a 32-bit element
-    // offset per row block and lane.  A wave without rows reads row 0.
+    // offset per row block and lane (the host checks that a wave's rows span
+    // less than 2^31 bytes).  A wave without rows reads row 0.  A lane's 16
+    // bytes start 16 * grp bytes into each load step, in both formats.
     const int64_t rbase = nrb_wave > 0 ? r0 : 0;
     const int64_t rlast = nrb_wave > 0 ? r1 - 1 : 0;
-    const uint16_t* wwave = a.W + rbase * D;
+    const WElem* wwave = wbase + rbase * D;
     uint32_t woff[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       int64_t row = r0 + 16 * (rb_first + rb) + col;
       if (row > rlast) row = rlast;
-      woff[rb] = (uint32_t)((row - rbase) * D + 8 * grp);
+      woff[rb] = (uint32_t)((row - rbase) * D + (16 / kEB) * grp);
     }
 
     f32x4 acc[kRB][NB];
@@ -351,23 +382,24 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }                                                                    \
   } while (0)
 
-    // W fragments of the k-step pair (2q, 2q + 1), row block by row block, so
-    // the two 64-byte halves of each row's 128-byte segment are requested back
-    // to back: HBM streams markedly faster so than when a whole k-step of row
-    // blocks is requested at a time.  A step past the last one re-reads the
-    // last one.  In a final k-step that runs past D (D % 32 != 0) the lanes
-    // past D read k = 0 instead; H is zero there, so their products vanish for
-    // finite W.
-    auto step_base = [&](int ks) -> const uint16_t* {
-      if (ks > KS - 1) ks = KS - 1;
-      const int64_t k = (int64_t)ks * 32;
+    // W of the load-step pair (2q, 2q + 1), row block by row block, so the
+    // two 64-byte halves of each row's 128-byte segment are requested back to
+    // back: HBM streams markedly faster so than when a whole step of row blocks
+    // is requested at a time.  A load step is one k-step of 32 bf16 or two of
+    // 64 FP8 values; a step past the last one re-reads the last one.  In a
+    // final step that runs past D the lanes past D read k = 0 instead; H is
+    // zero there, so their products vanish for finite W.
+    auto step_base = [&](int ls) -> const WElem* {
+      if (ls > KLS - 1) ls = KLS - 1;
+      const int64_t k = (int64_t)ls * kKPerLoad;
+      const int kg = (kKPerLoad / 4) * grp;  // the lane's first k
       int64_t kl = 0;
-      if (k + 32 > D) kl = (k + 8 * grp < D) ? 0 : -k - 8 * grp;
+      if (k + kKPerLoad > D) kl = (k + kg < D) ? 0 : -k - kg;
       return wwave + k + kl;
     };
     auto load_pair = [&](u32x4 (&dst)[2][kRB], int q) {
-      const uint16_t* w0 = step_base(2 * q);
-      const uint16_t* w1 = step_base(2 * q + 1);
+      const WElem* w0 = step_base(2 * q);
+      const WElem* w1 = step_base(2 * q + 1);
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         dst[0][rb] = load_frag(w0 + woff[rb]);
@@ -379,8 +411,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // first loads of the next pair leave one row block after the data
     // arrived rather than a whole phase later.
     auto mma_reload = [&](u32x4 (&w)[2][kRB], int buf, int kk, int q) {
-      const uint16_t* w0 = step_base(2 * q);
-      const uint16_t* w1 = step_base(2 * q + 1);
+      const WElem* w0 = step_base(2 * q);
+      const WElem* w1 = step_base(2 * q + 1);
       if constexpr (Pipe::half_h) {
         // The first k-step's MFMAs over every row block, then the second
         // k-step's with the reloads: one k-step of H fragments live at a time.
@@ -441,6 +473,32 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         for (int cb = 0; cb < NB; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[rb]), hf[cb], acc[rb][cb], 0, 0, 0);
     };
+    // FP8: the four MFMA k-steps of one load-step pair starting at chunk
+    // offset kk.  Load step ls of lane group g holds k in [64 ls + 16 g, +16):
+    // its first 8 values meet H at k = kk + 64 ls + 16 g, the next 8 at +8.
+    // The order of k inside an MFMA's sum is the hardware's either way; which
+    // k a lane carries is a choice the A and B operands make together.
+    auto mma8 = [&](const u32x4 (&w)[2][kRB], int buf, int kk) {
+#pragma unroll
+      for (int ls = 0; ls < 2; ++ls) {
+        bf16x8 h0[NB], h1[NB];
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          h0[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 64 * ls + 16 * grp]);
+          h1[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 64 * ls + 16 * grp + 8]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          u32x4 lo, hi;
+          e4m3x16_to_bf16(w[ls][rb], lo, hi);
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb) {
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(lo), h0[cb], acc[rb][cb], 0, 0, 0);
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(hi), h1[cb], acc[rb][cb], 0, 0, 0);
+          }
+        }
+      }
+    };
 
     // The k-loop is straight-line: every k-step pair issues the same loads in
     // the same order (2 x kRB W fragments, then the biases of the slots folded
@@ -482,6 +540,26 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       const int buf = c & 1;
       const int cn = c + 1 < NC ? c + 1 : c;
       h_load(cn, Half0{});
+      if constexpr (W8) {
+        // FP8: a chunk of 256 k is two load-step pairs, 2c (pa) and 2c + 1 (pb).
+        // The next chunk's H is loaded first and stored last: waiting for it
+        // earlier would also wait for every W load issued before it (loads
+        // complete in order), draining the pipe to one pair.
+        h_load(cn, Half1{});
+        __builtin_amdgcn_sched_barrier(0);
+        mma8(pa, buf, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair(pa, 2 * c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma8(pb, buf, 128);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair(pb, 2 * c + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        h_store(buf ^ 1, Half0{});
+        h_store(buf ^ 1, Half1{});
+        __syncthreads();
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < kStepsPerChunk; j += 4) {
         const int ks = c * kStepsPerChunk + j;
@@ -547,6 +625,18 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
 #undef FS_FOLD_SLOT
 
+    // FP8 weights: the scales of the lane's 4 output rows in each row block,
+    // applied to the finished dot products (clamped, always valid addresses).
+    float wsc[kRB][4];
+    if constexpr (W8) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wsc[rb][j] = a.w_scale[i0 + j < V ? i0 + j : V - 1];
+      }
+    }
+
     // End of pass: scores of this wave's fragments.
     T bm[NB];
     int32_t bi[NB];
@@ -568,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           if (EPI == kEpiStore) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if (i0 + j < r1) a.Y[b * V + i0 + j] = y[j];
+              if (i0 + j < r1) a.Y[b * V + i0 + j] = W8 ? y[j] * wsc[rb][j] : y[j];
             continue;
           }
           const ColInfo ci = cols[16 * cb + col];
@@ -597,10 +687,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         }
       }
     } else {
-      // Float64 noise, added after the k-loop (the score is formed in
-      // float64).  The per-fragment work (two Philox calls, four transforms)
-      // is large, so the loop stays rolled and the fragment is picked out of
-      // the accumulators by uniform branches.
+      // Noise added after the k-loop: float64 noise (the score is formed in
+      // float64), and float32 noise over FP8 weights (after the row scale).
+      // The per-fragment work (one or two Philox calls, four transforms) is
+      // large, so the loop stays rolled and the fragment is picked out of the
+      // accumulators by uniform branches.
 #pragma unroll 1
       for (int f = 0; f < kRB * NB; ++f) {
         const int rb = f / NB, cb = f - rb * NB;
@@ -627,17 +718,38 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
         float beta[4];
         load_bias4(a, bt0 + 16 * cb + col, i0, beta);
+        // FP8 weights: the row scale applies in float32, as in the logits the
+        // store epilogue writes.
+        if constexpr (W8) {
+#pragma unroll
+          for (int rb2 = 0; rb2 < kRB; ++rb2)
+            if (rb2 == rb) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) y[j] *= wsc[rb2][j];
+            }
+        }
+        T yv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yv[j] = T(y[j]);
         T s[4];
         if (m == kGreedy) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[j] = T(y[j]) + T(beta[j]);
+          for (int j = 0; j < 4; ++j) s[j] = yv[j] + T(beta[j]);
+        } else if constexpr (EPI == kEpiSample32) {
+          // Float32 noise that is not folded into the k-loop (FP8 weights,
+          // whose row scale only applies after it).
+          const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), r);
+          s[0] = (yv[0] + beta[0]) * it + gumbel_f32(w.w0);
+          s[1] = (yv[1] + beta[1]) * it + gumbel_f32(w.w1);
+          s[2] = (yv[2] + beta[2]) * it + gumbel_f32(w.w2);
+          s[3] = (yv[3] + beta[3]) * it + gumbel_f32(w.w3);
         } else {
           const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), r);
           const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, r);
-          s[0] = (T(y[0]) + T(beta[0])) * it + T(gumbel_f64(w0.w0, w0.w1));
-          s[1] = (T(y[1]) + T(beta[1])) * it + T(gumbel_f64(w0.w2, w0.w3));
-          s[2] = (T(y[2]) + T(beta[2])) * it + T(gumbel_f64(w1.w0, w1.w1));
-          s[3] = (T(y[3]) + T(beta[3])) * it + T(gumbel_f64(w1.w2, w1.w3));
+          s[0] = (yv[0] + T(beta[0])) * it + T(gumbel_f64(w0.w0, w0.w1));
+          s[1] = (yv[1] + T(beta[1])) * it + T(gumbel_f64(w0.w2, w0.w3));
+          s[2] = (yv[2] + T(beta[2])) * it + T(gumbel_f64(w1.w0, w1.w1));
+          s[3] = (yv[3] + T(beta[3])) * it + T(gumbel_f64(w1.w2, w1.w3));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -724,27 +836,39 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   if (tid == 0) clear_counter(a.counters + btile);
 }
 
-template <int NB>
+// FP8 weights take no bias template: their noise is never folded, and the
+// bias is read after the k-loop whichever way.
+template <int NB, bool W8>
 hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream) {
   switch (epi) {
     case kEpiSample32:
-      if (a.bias)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, true>), grid, dim3(kThreads), 0,
+      if (a.bias && !W8)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, !W8, W8>), grid, dim3(kThreads), 0,
                            stream, a);
       else
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, false>), grid, dim3(kThreads), 0,
-                           stream, a);
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, false, W8>), grid, dim3(kThreads),
+                           0, stream, a);
       break;
     case kEpiSample64:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample64, false>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample64, false, W8>), grid, dim3(kThreads), 0,
                          stream, a);
       break;
     default:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiStore, false>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiStore, false, W8>), grid, dim3(kThreads), 0,
                          stream, a);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool W8>
+hipError_t launch_w(const FusedArgs& a, int epi, dim3 grid, int nb, hipStream_t stream) {
+  switch (nb) {
+    case 1: return launch_nb<1, W8>(a, epi, grid, stream);
+    case 2: return launch_nb<2, W8>(a, epi, grid, stream);
+    case 3: return launch_nb<3, W8>(a, epi, grid, stream);
+    default: return launch_nb<4, W8>(a, epi, grid, stream);
+  }
 }
 
 }  // namespace
@@ -765,12 +889,15 @@ hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) 
   // any row's arithmetic.
   const int64_t cols = a.B >= kBatchTile ? kBatchTile : a.B;
   const int nb = (int)((cols + 15) / 16);
-  switch (nb) {
-    case 1: return launch_nb<1>(a, epi, grid, stream);
-    case 2: return launch_nb<2>(a, epi, grid, stream);
-    case 3: return launch_nb<3>(a, epi, grid, stream);
-    default: return launch_nb<4>(a, epi, grid, stream);
-  }
+  return a.W8 ? launch_w<true>(a, epi, grid, nb, stream) : launch_w<false>(a, epi, grid, nb, stream);
+}
+
+int64_t fused_wave_span_bytes(int64_t V, int64_t D, int nT, int elem_bytes) {
+  // Most 8-row units of one workgroup, then of one of its waves.
+  const int64_t nunits = (V + 7) >> 3;
+  const int64_t nu = (nunits + nT - 1) / nT;
+  const int64_t rows = ((nu + kWaves - 1) / kWaves) * 8;
+  return rows * D * elem_bytes;
 }
 
 }  // namespace fs

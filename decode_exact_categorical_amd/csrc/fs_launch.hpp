@@ -13,7 +13,9 @@ namespace fs {
 // Stage 2 in the last workgroup of each batch tile) and its logits-store twin.
 struct FusedArgs {
   const uint16_t* H;  // [B, D] bf16
-  const uint16_t* W;  // [V, D] bf16
+  const uint16_t* W;  // [V, D] bf16, or null when W8 is given
+  const uint8_t* W8;       // [V, D] OCP FP8 E4M3, or null
+  const float* w_scale;    // [V] scale per vocabulary row (with W8)
   int64_t B, D, V;
   const float* temp;       // [B]
   const float* bias;       // [B, V] or null
@@ -35,6 +37,8 @@ enum FusedEpilogue { kEpiSample32 = 0, kEpiSample64 = 1, kEpiStore = 2 };
 constexpr int kMaxFusedTiles = 256;
 static_assert(kMaxFusedTiles % 64 == 0, "whole waves of candidates");
 int fused_num_tiles(int64_t V, int num_cus);
+// Largest byte span of W rows one wave addresses through 32-bit offsets.
+int64_t fused_wave_span_bytes(int64_t V, int64_t D, int nT, int elem_bytes);
 hipError_t launch_fused_stage1(const FusedArgs& a, int epilogue, hipStream_t stream);
 
 // Standalone sampler over float32 logits (Stage 1, Stage 2 in the last

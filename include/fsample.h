@@ -13,6 +13,9 @@
  *         "Measured behavior" (determinism).
  *   [SK]  "Write Triton Sampling Kernel" skill page, "Required reasoning
  *         process" items 3-4 and 10, "Correctness requirements".
+ *   [OFP8] OCP 8-bit Floating Point Specification (OFP8), revision 1.0, the
+ *         E4M3 format (FP8 weights: the FlashSampling page's "limitations"
+ *         section names low-precision weights as future work).
  *
  * Conventions shared by every entry point
  *   Pointers.   Arguments documented as "device" are device (HBM) pointers the
@@ -66,7 +69,8 @@ extern "C" {
 typedef enum fs_status {
     FS_OK = 0,
     FS_ERR_INVALID_ARG = 1, /* null required pointer, non-positive size, V >= 2^31 */
-    FS_ERR_UNSUPPORTED = 2, /* D not a multiple of 8, H/W not 16-byte aligned, B > 2^22 (fused) */
+    FS_ERR_UNSUPPORTED = 2, /* D not a multiple of 8 (16 for FP8 W), H/W not 16-byte aligned,
+                               B > 2^22 or V * D beyond the addressable span (fused) */
     FS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fs_workspace_bytes() */
     FS_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 } fs_status;
@@ -74,14 +78,14 @@ typedef enum fs_status {
 typedef uint16_t fs_bf16;   /* bfloat16 bit pattern */
 typedef void *fs_stream_t;  /* hipStream_t */
 
-/* flags for fs_sample_fused and fs_workspace_bytes */
+/* flags for fs_sample_fused, fs_sample_fused_w8 and fs_workspace_bytes */
 #define FS_FP64_NOISE 0x1u
 
 /*
  * Bytes of device workspace the sampling calls need for a batch of B rows over
- * a vocabulary of V entries (covers both fs_sample_fused and fs_sample_logits;
- * pass FS_FP64_NOISE in flags if either call will use float64 noise).  The
- * workspace starts with a fixed 256 KiB region of completion counters, which
+ * a vocabulary of V entries (covers fs_sample_fused, fs_sample_fused_w8 and
+ * fs_sample_logits; pass FS_FP64_NOISE in flags if any of them will use
+ * float64 noise).  The workspace starts with a fixed 256 KiB region of completion counters, which
  * pick, for each batch tile (fused) or row (standalone), the workgroup that
  * runs Stage 2; the per-tile candidates (m, idx) of Stage 1 [FS Stage 1 step
  * (6)] follow it.  The caller allocates the workspace and must zero-fill it
@@ -125,6 +129,31 @@ fs_status fs_sample_fused(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t
                           size_t workspace_bytes, fs_stream_t stream);
 
 /*
+ * Fused LM-head + exact sampling with FP8 weights: W8 holds OCP FP8 E4M3 codes
+ * [OFP8] (sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities;
+ * 0x7F and 0xFF are NaN) and row i of the weight is w_scale[i] * W8[i, :].
+ *   H        device, bf16 [B, D]
+ *   W8       device, uint8 [V, D]  E4M3 codes, row-major
+ *   w_scale  device, float [V]     one scale per vocabulary row; the caller
+ *            keeps it finite and positive (a zero, negative or non-finite
+ *            scale gives that row's logits the IEEE meaning of the product)
+ *   B, D, V  host sizes: 0 <= B <= 2^22, D >= 16 with D % 16 == 0,
+ *            1 <= V < 2^31
+ *   the other arguments, the workspace and the sampling rule are those of
+ *   fs_sample_fused, with y_i = w_scale[i] * sum_d H[b,d] * e4m3(W8[i,d]).
+ * Every E4M3 value is exactly a bf16 value: the kernel widens W8 on chip and
+ * runs the same bf16 MFMA contraction (float32 accumulation) as
+ * fs_sample_fused, then multiplies each row's sum by its scale.  W crosses
+ * HBM at one byte per element, half the bytes of fs_sample_fused.  H and W8
+ * must be 16-byte aligned.
+ */
+fs_status fs_sample_fused_w8(const fs_bf16 *H, const uint8_t *W8, const float *w_scale,
+                             int64_t B, int64_t D, int64_t V, const float *temp,
+                             const float *bias, uint64_t seed, uint64_t offset,
+                             int64_t *out_idx, const uint32_t *row_ids, uint32_t flags,
+                             void *workspace, size_t workspace_bytes, fs_stream_t stream);
+
+/*
  * Standalone exact sampler over materialised float32 logits [MG "Problem",
  * "The change"; SD "Usage" sample(logits, temperature, seed, offset)].
  *   logits   device, float [B, V]  y_i of each row (no bias term)
@@ -148,14 +177,15 @@ fs_status fs_sample_logits(const float *logits, int64_t B, int64_t V, const floa
 
 /*
  * Kernel timing.  Between fs_profile_begin() and fs_profile_end(), every
- * fs_sample_fused and fs_sample_logits call also records HIP events on its
- * stream around its one launch (Stage 1 with Stage 2 in its last workgroups;
- * the FlashSampling page, "reproduction", times kernels the same way: device
- * timestamps per kernel).  fs_profile_end() waits for those events, writes the
- * summed kernel duration in milliseconds and the number of timed calls
- * (either pointer may be NULL; host memory), and stops recording.  At most
- * 4096 calls are timed per begin/end pair; later calls run untimed.  Enabling
- * adds two event records per call and nothing else.  Process-wide; host only.
+ * fs_sample_fused, fs_sample_fused_w8 and fs_sample_logits call also records
+ * HIP events on its stream around its one launch (Stage 1 with Stage 2 in its
+ * last workgroups; the FlashSampling page, "reproduction", times kernels the
+ * same way: device timestamps per kernel).  fs_profile_end() waits for those
+ * events, writes the summed kernel duration in milliseconds and the number of
+ * timed calls (either pointer may be NULL; host memory), and stops recording.
+ * At most 4096 calls are timed per begin/end pair; later calls run untimed.
+ * Enabling adds two event records per call and nothing else.  Process-wide;
+ * host only.
  */
 fs_status fs_profile_begin(void);
 fs_status fs_profile_end(double *kernel_ms, int64_t *calls);
@@ -196,6 +226,14 @@ fs_status fs_debug_noise(const uint32_t *words, int64_t n, int fp64, double *E, 
  */
 fs_status fs_debug_logits(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t D,
                           int64_t V, float *Y, fs_stream_t stream);
+
+/*
+ * Test hook: the logits y = w_scale[i] * H e4m3(W8)^T of the FP8 path, written
+ * to Y (device, float [B, V]); the twin of fs_debug_logits for
+ * fs_sample_fused_w8, with its size and alignment rules.
+ */
+fs_status fs_debug_logits_w8(const fs_bf16 *H, const uint8_t *W8, const float *w_scale,
+                             int64_t B, int64_t D, int64_t V, float *Y, fs_stream_t stream);
 
 #ifdef __cplusplus
 }
