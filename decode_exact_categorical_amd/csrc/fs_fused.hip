@@ -21,9 +21,13 @@
 //    is staged through LDS in chunks of 256 k, double-buffered and padded so
 //    the fragment reads are bank-conflict free, and shared by the 8 waves: H
 //    crosses L2 once per pass of the workgroup rather than once per wave.
-//  * v_mfma_f32_16x16x32_bf16 accumulates in fp32, k ascending, so every
-//    logit has one accumulation order that depends neither on B nor on the
-//    row's batch position.
+//  * v_mfma_f32_16x16x32_bf16 accumulates in fp32, in one fixed k order per
+//    vocabulary tile (its 256-k chunks from a per-tile starting chunk on,
+//    wrapping around; ascending inside a chunk), so every logit's
+//    accumulation order depends neither on B nor on the row's batch position.
+//    The per-tile rotation keeps the chip's concurrent W requests spread over
+//    the HBM channels; without it the stream rate depends markedly on where W
+//    sits in physical memory.
 //  * Float32 noise is not left for the end: the Gumbel noise of one output
 //    fragment (4 vocabulary rows x 1 batch column per lane, one Philox4x32-10
 //    call) is computed inside the memory-bound k-loop and folded into that
@@ -208,6 +212,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 
   const int KLS = (int)((D + kKPerLoad - 1) / kKPerLoad);  // load steps
   const int NC = (KLS + kLoadsPerChunk - 1) / kLoadsPerChunk;
+  // The k-loop of a workgroup visits the H chunks from chunk `rot` on,
+  // wrapping around (a rotation fixed per vocabulary tile).  Workgroups then
+  // read different k ranges of their rows at the same moment, which spreads
+  // the chip's concurrent W requests over more of the HBM channels than rows
+  // read in lockstep at one k offset do.
+  const int rot = tile % NC;
+  // Logical chunk -> the chunk of k it holds.
+  auto phys_chunk = [&](int c) -> int { return c + rot < NC ? c + rot : c + rot - NC; };
 
   // Per-column sampling constants live in LDS (16 bytes a column), read when a
   // fragment is folded or scored; registers hold only each column's running
@@ -262,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     for (int q = q0; q < q1; ++q) {
       const int piece = tid + kThreads * q;
       const int hc = piece >> 5;                 // column within the tile
-      const int64_t k = (int64_t)c * kKC + (piece & 31) * 8;
+      const int64_t k = (int64_t)phys_chunk(c) * kKC + (piece & 31) * 8;
       const int64_t b = bt0 + hc;
       hvalid[q] = b < B && k < D;
       hstage[q] = load_frag(a.H + (hvalid[q] ? b * D + k : 0));
@@ -390,6 +402,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // final step that runs past D the lanes past D read k = 0 instead; H is
     // zero there, so their products vanish for finite W.
     auto step_base = [&](int ls) -> const WElem* {
+      // Logical step (loop order; past the end: the last one) -> k step.
+      if (ls > NC * kLoadsPerChunk - 1) ls = NC * kLoadsPerChunk - 1;
+      ls = phys_chunk(ls / kLoadsPerChunk) * kLoadsPerChunk + ls % kLoadsPerChunk;
       if (ls > KLS - 1) ls = KLS - 1;
       const int64_t k = (int64_t)ls * kKPerLoad;
       const int kg = (kKPerLoad / 4) * grp;  // the lane's first k
@@ -509,11 +524,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // barriers.
     typedef std::integral_constant<int, 0> Half0;
     typedef std::integral_constant<int, 1> Half1;
+    // The first H chunk's loads go out first and its LDS stores come after the
+    // first W loads, so the W stream starts one H round trip earlier (loads
+    // complete in order: waiting for H then waits for nothing issued later).
     h_load(0, Half0{});
     h_load(0, Half1{});
-    h_store(0, Half0{});
-    h_store(0, Half1{});
-    __syncthreads();
 
     u32x4 pa[2][kRB], pb[2][kRB];
     const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -530,6 +545,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     if constexpr (!kRing1) load_pair(pb, 1);
     bias_slot_load(bb0, 2);
     bias_slot_load(bb1, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    h_store(0, Half0{});
+    h_store(0, Half1{});
+    __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     static_assert(kStepsPerChunk % 4 == 0, "a chunk holds whole pairs of pairs");
     // One H chunk per iteration, not unrolled: an unrolled or peeled copy
@@ -646,43 +665,58 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       bi[cb] = kNoIndex;
     }
     if (EPI == kEpiStore || kFold) {
+      const int32_t r1s = (int32_t)r1;  // V < 2^31
+      // Per column: 1 / t (1 for greedy) and whether any column of the wave
+      // has an infinite temperature (a wave-uniform test, so the rare noise
+      // path stays a branch rather than being computed for every fragment).
+      float inv_t[NB];
+      bool inf_any[NB];
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const ColInfo ci = cols[16 * cb + col];
+        inv_t[cb] = ci.inv_t;
+        inf_any[cb] = EPI != kEpiStore && __builtin_amdgcn_ballot_w64(ci.mode == kInfT) != 0;
+      }
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         if (rb >= nrb) continue;
         const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+        const int32_t i0s = (int32_t)i0;
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
-          if (!col_ok[cb]) continue;
-          const int64_t b = bt0 + 16 * cb + col;
           const f32x4 y = acc[rb][cb];
           if (EPI == kEpiStore) {
+            if (!col_ok[cb]) continue;
+            const int64_t b = bt0 + 16 * cb + col;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               if (i0 + j < r1) a.Y[b * V + i0 + j] = W8 ? y[j] * wsc[rb][j] : y[j];
             continue;
           }
-          const ColInfo ci = cols[16 * cb + col];
-          T s[4];
-          if (ci.mode == kSample) {
+          // Greedy columns carry inv_t = 1, so one multiply scores both folded
+          // modes; infinite temperatures add their noise after it.  Columns
+          // past B are scored too and never published.
+          float s[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s[j] = T(y[j] * ci.inv_t);
-          } else if (ci.mode == kGreedy) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s[j] = T(y[j]);
-          } else {  // infinite temperature: (y + bias) / t + g
-            const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), ci.rid);
-            s[0] = T(y[0] * ci.inv_t + gumbel_f32(w.w0));
-            s[1] = T(y[1] * ci.inv_t + gumbel_f32(w.w1));
-            s[2] = T(y[2] * ci.inv_t + gumbel_f32(w.w2));
-            s[3] = T(y[3] * ci.inv_t + gumbel_f32(w.w3));
+          for (int j = 0; j < 4; ++j) s[j] = y[j] * inv_t[cb];
+          if (inf_any[cb]) {
+            const ColInfo ci = cols[16 * cb + col];
+            if (ci.mode == kInfT) {
+              const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), ci.rid);
+              s[0] += gumbel_f32(w.w0);
+              s[1] += gumbel_f32(w.w1);
+              s[2] += gumbel_f32(w.w2);
+              s[3] += gumbel_f32(w.w3);
+            }
           }
+          // A lane meets the rows of one column in increasing index order,
+          // so only a strictly larger score takes over (a tie keeps the
+          // smaller index; NaN never takes over).
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int32_t i = (int32_t)(i0 + j);
-            if (i0 + j < r1 && beats(s[j], i, bm[cb], bi[cb])) {
-              bm[cb] = s[j];
-              bi[cb] = i;
-            }
+            const bool take = (i0s + j < r1s) & (T(s[j]) > bm[cb]);
+            bm[cb] = take ? T(s[j]) : bm[cb];
+            bi[cb] = take ? i0s + j : bi[cb];
           }
         }
       }
