@@ -64,12 +64,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKC = 256;          // k per H chunk in LDS
-constexpr int kStepsPerChunk = kKC / 32;
 constexpr int kHPad = 8;          // bf16 padding per LDS column row (16 bytes)
-constexpr int kHRow = kKC + kHPad;
-constexpr int kBatchTile = 64;    // batch columns per workgroup (4 MFMA column blocks)
-constexpr int kNoiseSlots = 4;    // fragment (rb, cb) gets its noise at k-step 4*rb + cb
 constexpr float kInfTemp = 0x1p60f;  // at or above this, t * g is not kept in the accumulator
 
 enum ColMode { kGreedy = 0, kSample = 1, kInfT = 2 };
@@ -140,13 +135,23 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
 // Passes of 4 row blocks (64 rows) stream W markedly slower than 3 or 5.
 // FP8 weights (W8) take the simplest of these: two pairs in flight, 5 row
 // blocks up to 32 columns and 3 beyond, each pair reloaded after its MFMAs.
+// Batch tiles wider than 64 columns (8 column blocks: the large-batch end,
+// where the contraction approaches the MFMA roofline) use every W fragment
+// for 8 MFMAs: 2 row blocks a pass (64 accumulators a lane), two pairs in
+// flight, and H chunks of 128 k.  There the fragment slots that receive the
+// noise are one per (row block, column block).
 template <int NB, int EPI, bool HAS_BIAS, bool W8>
 struct Pipeline {
+  static constexpr bool wide = NB > 4;
   static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || EPI == kEpiSample64);
-  static constexpr bool ring1 = !W8 && NB >= 3 && !wide_extra;
-  static constexpr int row_blocks = (NB <= 2 || ring1) ? 5 : 3;
+  static constexpr bool ring1 = !W8 && !wide && NB >= 3 && !wide_extra;
+  static constexpr int row_blocks = wide ? 2 : ((NB <= 2 || ring1) ? 5 : 3);
   static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || EPI == kEpiSample64);
-  static constexpr bool interleave = !W8 && !wide_extra;
+  static constexpr bool interleave = !W8 && !wide && !wide_extra;
+  static constexpr int chunk_k = wide ? 128 : 256;   // k per H chunk in LDS
+  // Fragment (rb, cb) gets its noise at k-step noise_slots * rb + cb.
+  static constexpr int noise_slots = wide ? NB : 4;
+  static_assert(!(wide && W8), "FP8 weights use batch tiles of at most 64 columns");
 };
 
 // Whether the noise is folded into the accumulators inside the k-loop: float32
@@ -167,6 +172,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   // two of FP8).
   constexpr int kEB = W8 ? 1 : 2;
   constexpr int kKPerLoad = W8 ? 64 : 32;
+  constexpr int kKC = Pipe::chunk_k;
+  constexpr int kStepsPerChunk = kKC / 32;
+  constexpr int kHRow = kKC + kHPad;
+  constexpr int kTile = 16 * NB;  // batch columns of the workgroup
+  constexpr int kNoiseSlots = Pipe::noise_slots;
   constexpr int kLoadsPerChunk = kKC / kKPerLoad;
   typedef typename std::conditional<W8, uint8_t, uint16_t>::type WElem;
   const WElem* const wbase = W8 ? reinterpret_cast<const WElem*>(a.W8) : reinterpret_cast<const WElem*>(a.W);
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     tile = (lin / (8 * nbt)) * 8 + lin % 8;
     btile = (lin / 8) % nbt;
   }
-  const int64_t bt0 = (int64_t)btile * kBatchTile;
+  const int64_t bt0 = (int64_t)btile * kTile;
 
   // Rows of this workgroup and of this wave, in 8-row units.
   const int64_t nunits = (V + 7) >> 3;
@@ -258,23 +268,27 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 
   __shared__ __attribute__((aligned(16))) uint16_t hs[2][16 * NB][kHRow];
 
-  // H chunk staging.  A chunk is 16*NB columns x 256 k = 32*16*NB pieces of
-  // 16 bytes; thread t stages pieces t + 512*q, q < NB, so every thread issues
-  // the same NB loads and NB LDS stores (no branch around either).  Loads use a
-  // clamped, always valid address; pieces past D or past B are stored as zero.
-  u32x4 hstage[NB];
-  bool hvalid[NB];
+  // H chunk staging.  A chunk is 16*NB columns x kKC k = 16*NB*kKC/8 pieces of
+  // 16 bytes; thread t stages pieces t + 512*q, q < kHQ, so every thread
+  // issues the same kHQ loads and LDS stores (no branch around either).  Loads
+  // use a clamped, always valid address; pieces past D or past B are stored as
+  // zero.
+  constexpr int kPPC = kKC / 8;                        // pieces per column
+  constexpr int kHQ = 16 * NB * kPPC / kThreads;        // pieces per thread
+  static_assert(16 * NB * kPPC % kThreads == 0, "whole pieces per thread");
+  u32x4 hstage[kHQ];
+  bool hvalid[kHQ];
   // Half QH of the pieces (the first (NB+1)/2 or the rest), so only half the
   // staging registers are live at a time.
-  constexpr int kQSplit = (NB + 1) / 2;
+  constexpr int kQSplit = (kHQ + 1) / 2;
   auto h_load = [&](int c, auto QH) {
     constexpr int q0 = decltype(QH)::value == 0 ? 0 : kQSplit;
-    constexpr int q1 = decltype(QH)::value == 0 ? kQSplit : NB;
+    constexpr int q1 = decltype(QH)::value == 0 ? kQSplit : kHQ;
 #pragma unroll
     for (int q = q0; q < q1; ++q) {
       const int piece = tid + kThreads * q;
-      const int hc = piece >> 5;                 // column within the tile
-      const int64_t k = (int64_t)phys_chunk(c) * kKC + (piece & 31) * 8;
+      const int hc = piece / kPPC;               // column within the tile
+      const int64_t k = (int64_t)phys_chunk(c) * kKC + (piece % kPPC) * 8;
       const int64_t b = bt0 + hc;
       hvalid[q] = b < B && k < D;
       hstage[q] = load_frag(a.H + (hvalid[q] ? b * D + k : 0));
@@ -282,12 +296,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   };
   auto h_store = [&](int buf, auto QH) {
     constexpr int q0 = decltype(QH)::value == 0 ? 0 : kQSplit;
-    constexpr int q1 = decltype(QH)::value == 0 ? kQSplit : NB;
+    constexpr int q1 = decltype(QH)::value == 0 ? kQSplit : kHQ;
 #pragma unroll
     for (int q = q0; q < q1; ++q) {
       const int piece = tid + kThreads * q;
       const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&hs[buf][piece >> 5][(piece & 31) * 8]) = hvalid[q] ? hstage[q] : z;
+      *reinterpret_cast<u32x4*>(&hs[buf][piece / kPPC][(piece % kPPC) * 8]) = hvalid[q] ? hstage[q] : z;
     }
   };
 
@@ -478,6 +492,17 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       }
     };
     auto mma = [&](const u32x4 (&w)[kRB], int buf, int kk) {
+      if constexpr (Pipe::wide) {
+        // One H fragment at a time, used by every row block.
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          const bf16x8 hf = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 8 * grp]);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[rb]), hf, acc[rb][cb], 0, 0, 0);
+        }
+        return;
+      }
       bf16x8 hf[NB];
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb)
@@ -559,6 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       const int buf = c & 1;
       const int cn = c + 1 < NC ? c + 1 : c;
       h_load(cn, Half0{});
+      if constexpr (Pipe::wide) h_load(cn, Half1{});
       if constexpr (W8) {
         // FP8: a chunk of 256 k is two load-step pairs, 2c (pa) and 2c + 1 (pb).
         // The next chunk's H is loaded first and stored last: waiting for it
@@ -627,7 +653,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         __builtin_amdgcn_sched_barrier(0);
         // The other buffer was last read in the previous chunk, before the
         // barrier that ended it, so the next chunk can land there at once.
-        if (j == 0) {
+        // Wide tiles (one j step a chunk) store the whole next chunk here,
+        // loaded at the chunk's start: only W loads issued after it are in
+        // flight behind it.
+        if constexpr (Pipe::wide) {
+          h_store(buf ^ 1, Half0{});
+          h_store(buf ^ 1, Half1{});
+        } else if (j == 0) {
           h_store(buf ^ 1, Half0{});
           h_load(cn, Half1{});
         } else {
@@ -835,37 +867,43 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 
   // Stage 2 of this batch tile, in the workgroup that finishes it last.  Wave
   // w takes rows w, w + 8, ... of the tile and issues every candidate load of
-  // all its rows (clamped, always valid addresses) before reducing any, so the
-  // tail costs one round trip to the coherence point, not one per row.
+  // 8 of its rows at a time (clamped, always valid addresses) before reducing
+  // any, so the tail costs one round trip to the coherence point per 8 rows
+  // of a wave, not one per row.
   if (!finish_last(a.counters + btile, (uint32_t)nT)) return;
-  constexpr int kRowsPerWave = kBatchTile / kWaves;
+  constexpr int kRowsPerWave = kTile / kWaves;
+  constexpr int kRowGroup = kRowsPerWave < 8 ? kRowsPerWave : 8;
   constexpr int kLoadsPerRow = kMaxFusedTiles / 64;
   const Cand<T>* cand = reinterpret_cast<const Cand<T>*>(a.cand);
-  Cand<T> c[kRowsPerWave][kLoadsPerRow];
+#pragma unroll 1
+  for (int i0 = 0; i0 < kRowsPerWave; i0 += kRowGroup) {
+    if (bt0 + wave + kWaves * i0 >= B) break;
+    Cand<T> c[kRowGroup][kLoadsPerRow];
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    int64_t b = bt0 + wave + kWaves * i;
-    if (b > B - 1) b = B - 1;
+    for (int i = 0; i < kRowGroup; ++i) {
+      int64_t b = bt0 + wave + kWaves * (i0 + i);
+      if (b > B - 1) b = B - 1;
 #pragma unroll
-    for (int j = 0; j < kLoadsPerRow; ++j) {
-      const int t = lane + 64 * j < a.nT ? lane + 64 * j : a.nT - 1;
-      c[i][j] = load_cand(cand + b * a.nT + t);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int64_t b = bt0 + wave + kWaves * i;
-    if (b >= B) break;
-    T bm = neg_inf<T>();
-    int32_t bi = kNoIndex;
-#pragma unroll
-    for (int j = 0; j < kLoadsPerRow; ++j)
-      if (lane + 64 * j < a.nT && beats(c[i][j].m, c[i][j].idx, bm, bi)) {
-        bm = c[i][j].m;
-        bi = c[i][j].idx;
+      for (int j = 0; j < kLoadsPerRow; ++j) {
+        const int t = lane + 64 * j < a.nT ? lane + 64 * j : a.nT - 1;
+        c[i][j] = load_cand(cand + b * a.nT + t);
       }
-    wave_argmax_xor(bm, bi, 0);
-    if (lane == 0) a.out[b] = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
+    }
+#pragma unroll
+    for (int i = 0; i < kRowGroup; ++i) {
+      const int64_t b = bt0 + wave + kWaves * (i0 + i);
+      if (b >= B) break;
+      T bm = neg_inf<T>();
+      int32_t bi = kNoIndex;
+#pragma unroll
+      for (int j = 0; j < kLoadsPerRow; ++j)
+        if (lane + 64 * j < a.nT && beats(c[i][j].m, c[i][j].idx, bm, bi)) {
+          bm = c[i][j].m;
+          bi = c[i][j].idx;
+        }
+      wave_argmax_xor(bm, bi, 0);
+      if (lane == 0) a.out[b] = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
+    }
   }
   if (tid == 0) clear_counter(a.counters + btile);
 }
@@ -905,6 +943,11 @@ hipError_t launch_w(const FusedArgs& a, int epi, dim3 grid, int nb, hipStream_t 
   }
 }
 
+// Wide batch tiles (128 columns): bf16 weights only.
+hipError_t launch_wide(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream) {
+  return launch_nb<8, false>(a, epi, grid, stream);
+}
+
 }  // namespace
 
 int fused_num_tiles(int64_t V, int num_cus) {
@@ -915,15 +958,27 @@ int fused_num_tiles(int64_t V, int num_cus) {
   return (int)g;
 }
 
+int fused_column_blocks(int64_t B, bool fp8_weights, bool fp64_noise) {
+  if (B <= 64 || fp8_weights) {
+    const int64_t cols = B >= 64 ? 64 : B;
+    return cols < 1 ? 1 : (int)((cols + 15) / 16);
+  }
+  // Beyond 64 columns: tiles of 128 columns.  Wider tiles would need more
+  // than the 256 registers a lane has at two waves per SIMD.
+  (void)fp64_noise;
+  return 8;
+}
+
 hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) {
-  const int64_t nbt = (a.B + kBatchTile - 1) / kBatchTile;
+  const int nb = fused_column_blocks(a.B, a.W8 != nullptr, epi == kEpiSample64);
+  const int64_t tile = 16 * nb;
+  const int64_t nbt = (a.B + tile - 1) / tile;
   const dim3 grid((unsigned)a.nT, (unsigned)nbt);
-  // 16-wide column blocks per batch tile: enough for the widest tile.  Each
-  // column's logits come from its own MFMA column, so this does not change
-  // any row's arithmetic.
-  const int64_t cols = a.B >= kBatchTile ? kBatchTile : a.B;
-  const int nb = (int)((cols + 15) / 16);
-  return a.W8 ? launch_w<true>(a, epi, grid, nb, stream) : launch_w<false>(a, epi, grid, nb, stream);
+  // Each column's logits come from its own MFMA column, so the tile width
+  // does not change any row's arithmetic.
+  if (a.W8) return launch_w<true>(a, epi, grid, nb, stream);
+  if (nb > 4) return launch_wide(a, epi, grid, stream);
+  return launch_w<false>(a, epi, grid, nb, stream);
 }
 
 int64_t fused_wave_span_bytes(int64_t V, int64_t D, int nT, int elem_bytes) {

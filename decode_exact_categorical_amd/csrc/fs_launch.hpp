@@ -37,6 +37,9 @@ enum FusedEpilogue { kEpiSample32 = 0, kEpiSample64 = 1, kEpiStore = 2 };
 constexpr int kMaxFusedTiles = 256;
 static_assert(kMaxFusedTiles % 64 == 0, "whole waves of candidates");
 int fused_num_tiles(int64_t V, int num_cus);
+// MFMA column blocks of 16 per batch tile: up to 4 (64 columns) for B <= 64
+// or FP8 weights, else 8 (tiles of 128 columns).
+int fused_column_blocks(int64_t B, bool fp8_weights, bool fp64_noise);
 // Largest byte span of W rows one wave addresses through 32-bit offsets.
 int64_t fused_wave_span_bytes(int64_t V, int64_t D, int nT, int elem_bytes);
 hipError_t launch_fused_stage1(const FusedArgs& a, int epilogue, hipStream_t stream);

@@ -94,6 +94,11 @@ FUSED_CASES = [
     # every width, the running bests merged across passes
     dict(B=64, D=64, V=170001, greedy_rows=(2, 40)),
     dict(B=20, D=64, V=170001, bias=True),
+    # batch tiles of 128 columns (B > 64): one partial tile, two tiles with a
+    # bias and a contraction shorter than the noise slots, a full-width D
+    dict(B=100, D=256, V=5001, greedy_rows=(7,)),
+    dict(B=200, D=160, V=3001, bias=True, greedy_rows=(130,)),
+    dict(B=129, D=4096, V=2000),
 ]
 
 
