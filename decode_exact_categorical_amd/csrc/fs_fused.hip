@@ -163,7 +163,9 @@ struct FoldNoise {
   static constexpr bool value = EPI == kEpiSample32 && !W8;
 };
 
-template <int NB, int EPI, bool HAS_BIAS, bool W8>
+// BV4: the bias rows are 16-byte aligned (V % 4 == 0), so a fragment's four
+// biases come in one load.
+template <int NB, int EPI, bool HAS_BIAS, bool W8, bool BV4 = false>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
   constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS, W8>::value;
@@ -384,6 +386,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       int64_t b = bt0 + 16 * cb + col;
       if (b > B - 1) b = B - 1;
       const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+      if constexpr (BV4) {
+        // With V % 4 == 0 a fragment's rows are wholly inside or past V.
+        int64_t i = i0 > V - 4 ? V - 4 : i0;
+        if (i < 0) i = 0;
+        dst = *reinterpret_cast<const f32x4*>(a.bias + b * V + i);
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         int64_t i = i0 + j;
@@ -914,7 +923,10 @@ template <int NB, bool W8>
 hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream) {
   switch (epi) {
     case kEpiSample32:
-      if (a.bias && !W8)
+      if (a.bias && !W8 && a.bias_vec4)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, !W8, W8, !W8>), grid, dim3(kThreads),
+                           0, stream, a);
+      else if (a.bias && !W8)
         hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, !W8, W8>), grid, dim3(kThreads), 0,
                            stream, a);
       else

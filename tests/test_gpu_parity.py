@@ -99,6 +99,7 @@ FUSED_CASES = [
     dict(B=100, D=256, V=5001, greedy_rows=(7,)),
     dict(B=200, D=160, V=3001, bias=True, greedy_rows=(130,)),
     dict(B=129, D=4096, V=2000),
+    dict(B=72, D=128, V=4000, bias=True),       # 16-byte bias rows, wide tile
 ]
 
 
