@@ -74,6 +74,14 @@ def _load():
         lib.oracle_sample_fused_w8.restype = None
         lib.oracle_sample_fused_w8.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P,
                                                i32, P, P, P]
+        lib.oracle_sample_fused_topk.restype = None
+        lib.oracle_sample_fused_topk.argtypes = [P, P, i64, i64, i64, P, P, u64, u64, P, i32,
+                                                 i32, P, P]
+        lib.oracle_sample_logits_topk.restype = None
+        lib.oracle_sample_logits_topk.argtypes = [P, i64, i64, P, u64, u64, P, i32, i32, P, P]
+        lib.oracle_topk_repeated_row.restype = None
+        lib.oracle_topk_repeated_row.argtypes = [P, i64, ctypes.c_float, u64, u64, P, i64,
+                                                 i32, i32, P]
         lib.oracle_sample_logits.restype = None
         lib.oracle_sample_logits.argtypes = [P, i64, i64, P, u64, u64, P, i32, P, P, P]
         lib.oracle_sample_repeated_row.restype = None
@@ -241,6 +249,55 @@ def sample_logits(logits_f32, temp, *, seed: int, offset: int, row_ids=None,
     _load().oracle_sample_logits(_ptr(x), B, V, _ptr(t), seed, offset, _ptr(rid),
                                  int(fp64_noise), _ptr(idx), _ptr(gap), _ptr(best))
     return idx, gap, best
+
+
+def sample_fused_topk(H, W, temp, bias=None, *, k: int, seed: int, offset: int, row_ids=None,
+                      fp64_noise: bool = False):
+    """(idx [B, k], top [B, k + 1]) for Gumbel-top-k over the fused definition:
+    the k largest perturbed scores' indices, largest first (-1 past the valid
+    ones), and the k + 1 largest scores (-inf past the valid ones)."""
+    h = _bf16_bits(H)
+    w = _bf16_bits(W)
+    B, D = h.shape
+    V = w.shape[0]
+    assert w.shape[1] == D and k >= 1
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    bb = None
+    if bias is not None:
+        bb = np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+        assert bb.shape == (B, V)
+    rid = _u32_or_none(row_ids, B)
+    idx = np.zeros((B, k), dtype=np.int64)
+    top = np.zeros((B, k + 1), dtype=np.float64)
+    _load().oracle_sample_fused_topk(_ptr(h), _ptr(w), B, D, V, _ptr(t), _ptr(bb), seed, offset,
+                                     _ptr(rid), int(fp64_noise), k, _ptr(idx), _ptr(top))
+    return idx, top
+
+
+def sample_logits_topk(logits_f32, temp, *, k: int, seed: int, offset: int, row_ids=None,
+                       fp64_noise: bool = False):
+    """(idx [B, k], top [B, k + 1]) for Gumbel-top-k over float32 logits[B,V]."""
+    x = np.ascontiguousarray(np.asarray(logits_f32, dtype=np.float32))
+    B, V = x.shape
+    assert k >= 1
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    rid = _u32_or_none(row_ids, B)
+    idx = np.zeros((B, k), dtype=np.int64)
+    top = np.zeros((B, k + 1), dtype=np.float64)
+    _load().oracle_sample_logits_topk(_ptr(x), B, V, _ptr(t), seed, offset, _ptr(rid),
+                                      int(fp64_noise), k, _ptr(idx), _ptr(top))
+    return idx, top
+
+
+def topk_repeated_row(row_f32, temp: float, *, k: int, seed: int, offset: int, row_ids,
+                      fp64_noise: bool = False):
+    """idx [n, k]: Gumbel-top-k of one logits row under n logical row ids."""
+    x = np.ascontiguousarray(np.asarray(row_f32, dtype=np.float32).reshape(-1))
+    rid = np.ascontiguousarray(np.asarray(row_ids, dtype=np.uint32).reshape(-1))
+    idx = np.zeros((rid.shape[0], k), dtype=np.int64)
+    _load().oracle_topk_repeated_row(_ptr(x), x.shape[0], float(temp), seed, offset, _ptr(rid),
+                                     rid.shape[0], int(fp64_noise), k, _ptr(idx))
+    return idx
 
 
 def sample_repeated_row(row_f32, temp: float, *, seed: int, offset: int, row_ids,

@@ -26,6 +26,11 @@
  *   [OFP8] OCP 8-bit Floating Point Specification (OFP8), revision 1.0: the
  *         E4M3 encoding of 8-bit weights (FP8 weights are the future work the
  *         FlashSampling page's limitations section names).
+ *   [GTK] Gumbel-top-k: the FlashSampling page's limitations and future-work
+ *         sections name the top-k extension (k draws without replacement from
+ *         the k largest perturbed scores, proved in its appendix D); the
+ *         result is the standard one of Kool, van Hoof and Welling, "Stochastic
+ *         Beams and Where to Find Them", ICML 2019, section 3.
  *
  * Definition computed (per batch row b, logical row id r = row_ids[b] or b):
  *   y_i   = sum_d H[b,d] * W[i,d]           float64, d ascending   [FS (1)]
@@ -42,6 +47,9 @@
  *   out = smallest i attaining max s_i over the i whose s_i is neither NaN nor
  *         -inf; -1 if there is none.                  [FS (5), Stage 2; SK]
  *   gap = s_(1) - s_(2), the top-2 gap of those scores (+inf if only one).
+ *   top-k (k draws without replacement) [GTK]: the indices of the k largest
+ *         valid s_i, largest first, equal scores in increasing index order;
+ *         -1 in the places past the number of valid scores.
  *
  * Parity pins (tests marked "not gpu"): the Philox words against an
  * independent engine (the one PyTorch ships as a header); the uniform, E and
@@ -311,6 +319,38 @@ static void select_row(const double *s, int64_t V, int64_t *idx, double *gap,
     }
 }
 
+/* The k largest valid scores [GTK], largest first, equal scores in
+ * increasing index order: idx[0..k) (-1 past the number of valid scores) and
+ * their scores top[0..k] with one more place (-inf past the end), so a caller
+ * can see the margin between consecutive places.  A plain repeated scan: the
+ * j-th place is the best valid score not taken by an earlier place. */
+static void select_topk(const double *s, int64_t V, int k, int64_t *idx, double *top)
+{
+    for (int j = 0; j <= k; ++j) {
+        int64_t bi = -1;
+        double bv = -INFINITY;
+        for (int64_t i = 0; i < V; ++i) {
+            double v = s[i];
+            if (isnan(v) || v == -INFINITY) continue;
+            int taken = 0;
+            for (int q = 0; q < j; ++q)
+                if (idx[q] == i) taken = 1;
+            if (taken) continue;
+            if (bi < 0 || v > bv) {    /* equal scores keep the smaller index */
+                bi = i;
+                bv = v;
+            }
+        }
+        if (j < k) idx[j] = bi;
+        top[j] = bv;
+        if (bi < 0) {                  /* no valid score left */
+            for (int q = j + 1; q < k; ++q) idx[q] = -1;
+            for (int q = j + 1; q <= k; ++q) top[q] = -INFINITY;
+            break;
+        }
+    }
+}
+
 /* Fused path: logits from H and W, then transform, noise and selection.
  * temp[B]; bias[B,V] or NULL; row_ids[B] or NULL.  Outputs per row: the
  * sampled index, the top-2 perturbed-score gap and the winning score. */
@@ -367,6 +407,75 @@ void oracle_sample_fused_w8(const uint16_t *H, const uint8_t *W8, const float *s
     }
     free(hrow);
     free(s);
+}
+
+/* Gumbel-top-k over the fused path's scores [GTK]: per row, k places of
+ * out_idx[B, k] and k + 1 places of out_top[B, k + 1] (see select_topk). */
+void oracle_sample_fused_topk(const uint16_t *H, const uint16_t *W, int64_t B,
+                              int64_t D, int64_t V, const float *temp,
+                              const float *bias, uint64_t seed, uint64_t offset,
+                              const uint32_t *row_ids, int fp64_noise, int k,
+                              int64_t *out_idx, double *out_top)
+{
+    double *s = (double *)malloc((size_t)V * sizeof(double));
+    double *hrow = (double *)malloc((size_t)D * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        double t = (double)temp[b];
+        for (int64_t d = 0; d < D; ++d) hrow[d] = bf16_to_double(H[b * D + d]);
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i) {
+            const uint16_t *w = W + i * D;
+            double y = 0.0;
+            for (int64_t d = 0; d < D; ++d) y += hrow[d] * bf16_to_double(w[d]);
+            double beta = bias ? (double)bias[b * V + i] : 0.0;
+            s[i] = score_of(y, beta, t, seed, offset, r, i, fp64_noise);
+        }
+        select_topk(s, V, k, out_idx + b * k, out_top + b * (k + 1));
+    }
+    free(hrow);
+    free(s);
+}
+
+/* Gumbel-top-k over materialised float32 logits[B,V] [GTK; MG problem]. */
+void oracle_sample_logits_topk(const float *logits, int64_t B, int64_t V,
+                               const float *temp, uint64_t seed, uint64_t offset,
+                               const uint32_t *row_ids, int fp64_noise, int k,
+                               int64_t *out_idx, double *out_top)
+{
+    double *s = (double *)malloc((size_t)V * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        double t = (double)temp[b];
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i)
+            s[i] = score_of((double)logits[b * V + i], 0.0, t, seed, offset, r, i,
+                            fp64_noise);
+        select_topk(s, V, k, out_idx + b * k, out_top + b * (k + 1));
+    }
+    free(s);
+}
+
+/* Gumbel-top-k for many logical rows sharing one logits row (law tests);
+ * out_idx[n_rows, k]. */
+void oracle_topk_repeated_row(const float *logits, int64_t V, float temp,
+                              uint64_t seed, uint64_t offset, const uint32_t *row_ids,
+                              int64_t n_rows, int fp64_noise, int k, int64_t *out_idx)
+{
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)V * sizeof(double));
+        double *top = (double *)malloc((size_t)(k + 1) * sizeof(double));
+        #pragma omp for schedule(static)
+        for (int64_t q = 0; q < n_rows; ++q) {
+            for (int64_t i = 0; i < V; ++i)
+                s[i] = score_of((double)logits[i], 0.0, (double)temp, seed, offset,
+                                row_ids[q], i, fp64_noise);
+            select_topk(s, V, k, out_idx + q * k, top);
+        }
+        free(top);
+        free(s);
+    }
 }
 
 /* Standalone sampler over materialised float32 logits[B,V]: the same
