@@ -19,12 +19,13 @@ import threading
 import torch
 
 __all__ = [
-    "FS_FP64_NOISE", "FSampleError", "sample_fused", "sample_fused_w8", "sample_logits",
-    "workspace_bytes", "debug_philox_words", "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
+    "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused", "sample_fused_w8",
+    "sample_logits", "sample_logits_topk", "workspace_bytes", "debug_philox_words", "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
     "KernelTimer",
 ]
 
 FS_FP64_NOISE = 0x1
+FS_TOPK_MAX = 8
 _STATUS = {0: "FS_OK", 1: "FS_ERR_INVALID_ARG", 2: "FS_ERR_UNSUPPORTED", 3: "FS_ERR_WORKSPACE",
            4: "FS_ERR_HIP"}
 
@@ -77,6 +78,10 @@ def load_library():
         lib.fs_debug_noise.argtypes = [P, i64, i32, P, P, P]
         lib.fs_debug_logits.restype = i32
         lib.fs_debug_logits.argtypes = [P, P, i64, i64, i64, P, P]
+        lib.fs_workspace_bytes_topk.restype = sz
+        lib.fs_workspace_bytes_topk.argtypes = [i64, i64, u32]
+        lib.fs_sample_logits_topk.restype = i32
+        lib.fs_sample_logits_topk.argtypes = [P, i64, i64, P, u64, u64, i32, i32, P, P, P, sz, P]
         lib.fs_sample_fused_w8.restype = i32
         lib.fs_sample_fused_w8.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P, P, u32, P,
                                            sz, P]
@@ -238,6 +243,34 @@ def sample_logits(logits: torch.Tensor, temp, *, seed: int, offset: int,
     st = lib.fs_sample_logits(_ptr(logits), B, V, _ptr(t), seed, offset, int(bool(fp64_noise)),
                               _ptr(out), _ptr(rid), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "fs_sample_logits")
+    return out
+
+
+def sample_logits_topk(logits: torch.Tensor, temp, *, k: int, seed: int, offset: int,
+                       row_ids: torch.Tensor | None = None, fp64_noise: bool = False,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """Gumbel-top-k: k draws without replacement per row from softmax(logits / temp),
+    the indices of the k largest perturbed scores, largest first; [B, k] int64
+    (-1 past a row's valid scores)."""
+    lib = load_library()
+    dev = logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    B, V = logits.shape
+    _need(logits, "logits", torch.float32, dev, (B, V))
+    t = _temp_tensor(temp, B, dev)
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B, k))
+    flags = FS_FP64_NOISE if fp64_noise else 0
+    need = int(lib.fs_workspace_bytes_topk(B, V, flags)) if V > 0 else 0
+    ws = _workspace(dev, need)
+    st = lib.fs_sample_logits_topk(_ptr(logits), B, V, _ptr(t), seed, offset, int(bool(fp64_noise)),
+                                   k, _ptr(out), _ptr(rid), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "fs_sample_logits_topk")
     return out
 
 

@@ -113,8 +113,9 @@ size_t cand_region_bytes(int64_t B, int64_t V, uint32_t flags) {
 uint32_t* counters_of(void* ws) { return static_cast<uint32_t*>(ws); }
 void* candidates_of(void* ws) { return static_cast<char*>(ws) + kCounterBytes; }
 
-fs_status check_workspace(void* ws, size_t have, int64_t B, int64_t V, uint32_t flags) {
-  const size_t need = fs_workspace_bytes(B, V, flags);
+fs_status check_workspace(void* ws, size_t have, int64_t B, int64_t V, uint32_t flags,
+                          bool topk = false) {
+  const size_t need = topk ? fs_workspace_bytes_topk(B, V, flags) : fs_workspace_bytes(B, V, flags);
   if (ws == nullptr || have < need)
     return fail(FS_ERR_WORKSPACE, "workspace %p of %zu bytes, need %zu", ws, have, need);
   if (((uintptr_t)ws & 15u) != 0) return fail(FS_ERR_WORKSPACE, "workspace not 16-byte aligned");
@@ -233,6 +234,11 @@ size_t fs_workspace_bytes(int64_t B, int64_t V, uint32_t flags) {
   return kCounterBytes + cand_region_bytes(B, V, flags);
 }
 
+size_t fs_workspace_bytes_topk(int64_t B, int64_t V, uint32_t flags) {
+  if (B < 0 || V < 1 || V >= kMaxV) return 0;
+  return kCounterBytes + cand_region_bytes(B, V, flags) * fs::kTopKMax;
+}
+
 const char* fs_status_string(fs_status status) {
   switch (status) {
     case FS_OK: return "FS_OK";
@@ -304,8 +310,57 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
     a.counters = counters_of(workspace);
     a.out = out_idx + b0;
     a.vec4 = aligned16(logits) && (V % 4 == 0);
+    a.k = 1;
     hipError_t e = fs::launch_logits_stage1(a, fp64_noise != 0, st);
     if (e != hipSuccess) return hip_fail(e, "logits sampling launch");
+  }
+  if (ev) (void)hipEventRecord(ev[1], st);
+  return FS_OK;
+}
+
+fs_status fs_sample_logits_topk(const float* logits, int64_t B, int64_t V, const float* temp,
+                                uint64_t seed, uint64_t offset, int fp64_noise, int k,
+                                int64_t* out_idx, const uint32_t* row_ids, void* workspace,
+                                size_t workspace_bytes, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_sizes(B, V);
+  if (s != FS_OK) return s;
+  if (k < 1 || k > fs::kTopKMax)
+    return fail(FS_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, fs::kTopKMax);
+  if (B == 0) return FS_OK;
+  if (logits == nullptr || temp == nullptr || out_idx == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "logits, temp or out_idx is null");
+  if (((uintptr_t)logits & 3u) != 0) return fail(FS_ERR_UNSUPPORTED, "logits not 4-byte aligned");
+  const int nT = logits_tiles(V);
+  if ((int64_t)B * nT * fs::kTopKMax >= ((int64_t)1 << 31))
+    return fail(FS_ERR_INVALID_ARG, "B * ceil(V / %d) * %d exceeds 2^31", fs::kLogitsChunk,
+                fs::kTopKMax);
+  const uint32_t flags = fp64_noise ? FS_FP64_NOISE : 0u;
+  s = check_workspace(workspace, workspace_bytes, B, V, flags, true);
+  if (s != FS_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  if (ev) (void)hipEventRecord(ev[0], st);
+  for (int64_t b0 = 0; b0 < B; b0 += kCounterWords) {
+    const int64_t nb = B - b0 < kCounterWords ? B - b0 : kCounterWords;
+    fs::LogitsArgs a;
+    a.X = logits + b0 * V;
+    a.B = nb;
+    a.V = V;
+    a.temp = temp + b0;
+    a.row_ids = row_ids ? row_ids + b0 : nullptr;
+    a.rid_base = (uint32_t)b0;
+    a.key = fs::make_key(seed, offset);
+    a.cand = candidates_of(workspace);
+    a.chunk = fs::logits_chunk(nb, V);
+    a.nT = (int)((V + a.chunk - 1) / a.chunk);
+    a.counters = counters_of(workspace);
+    a.out = out_idx + b0 * k;
+    a.vec4 = aligned16(logits) && (V % 4 == 0);
+    a.k = k;
+    hipError_t e = fs::launch_logits_topk(a, fp64_noise != 0, st);
+    if (e != hipSuccess) return hip_fail(e, "logits top-k launch");
   }
   if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;

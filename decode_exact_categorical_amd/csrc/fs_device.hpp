@@ -254,4 +254,54 @@ __device__ __forceinline__ int64_t row_winner(const Cand<T>* c, int nT, int lane
   return bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
 }
 
+// ---------------------------------------------------------------------------
+// Gumbel-top-k [FlashSampling, "limitations" and future work: the k largest
+// perturbed scores are k draws without replacement].  Places are ordered by
+// larger score, then smaller index; NaN and -inf never take a place.
+// ---------------------------------------------------------------------------
+constexpr int kTopKMax = 8;  // places kept per (row, tile)
+
+// x comes strictly after w in place order.
+template <typename T>
+__device__ __forceinline__ bool after(T m, int32_t i, T wm, int32_t wi) {
+  return m < wm || (m == wm && i > wi);
+}
+
+// Insert (s, i) into a lane's sorted list (m, id) of K places.  Scores reach
+// a lane in increasing index order, so an equal score goes below the places
+// already held (strict compares); NaN never enters.
+template <typename T, int K>
+__device__ __forceinline__ void topk_insert(T (&m)[K], int32_t (&id)[K], T s, int32_t i) {
+#pragma unroll
+  for (int j = K - 1; j > 0; --j) {
+    const bool up = s > m[j - 1];  // s goes above place j - 1: place j takes it
+    const bool here = s > m[j];
+    m[j] = up ? m[j - 1] : (here ? s : m[j]);
+    id[j] = up ? id[j - 1] : (here ? i : id[j]);
+  }
+  const bool top = s > m[0];
+  m[0] = top ? s : m[0];
+  id[0] = top ? i : id[0];
+}
+
+// The next place after (pm, pi) among a wave's candidates: every lane offers
+// its best candidate that comes after the previous place (first: any), and
+// the wave picks the best offer.  Returns it in every lane ((-inf, kNoIndex)
+// when none is left).
+template <typename T, int N>
+__device__ __forceinline__ Cand<T> next_place(const Cand<T> (&c)[N], bool first, T pm, int32_t pi) {
+  T bm = neg_inf<T>();
+  int32_t bi = kNoIndex;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const bool ok = first || after(c[q].m, c[q].idx, pm, pi);
+    if (ok && beats(c[q].m, c[q].idx, bm, bi)) {
+      bm = c[q].m;
+      bi = c[q].idx;
+    }
+  }
+  wave_argmax_xor(bm, bi, 0);
+  return Cand<T>{bm, bi};
+}
+
 }  // namespace fs

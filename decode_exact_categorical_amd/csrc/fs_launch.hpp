@@ -62,8 +62,10 @@ struct LogitsArgs {
   uint32_t* counters;  // [B] completion counters (B <= 65536), zero between calls
   int64_t* out;        // [B] sampled indices
   int vec4;    // rows 16-byte aligned
+  int k;       // Gumbel-top-k only: places per row (out is [B, k]); cand is [B, nT, kTopKMax]
 };
 hipError_t launch_logits_stage1(const LogitsArgs& a, bool fp64, hipStream_t stream);
+hipError_t launch_logits_topk(const LogitsArgs& a, bool fp64, hipStream_t stream);
 
 // Test hook: the noise transforms applied to given words.
 hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,

@@ -16,6 +16,10 @@
  *   [OFP8] OCP 8-bit Floating Point Specification (OFP8), revision 1.0, the
  *         E4M3 format (FP8 weights: the FlashSampling page's "limitations"
  *         section names low-precision weights as future work).
+ *   [GTK] Gumbel-top-k: the FlashSampling page's "limitations" and future
+ *         work name the top-k extension (k draws without replacement, the k
+ *         largest perturbed scores; its appendix D proves it); the standard
+ *         statement is Kool, van Hoof and Welling, ICML 2019, section 3.
  *
  * Conventions shared by every entry point
  *   Pointers.   Arguments documented as "device" are device (HBM) pointers the
@@ -98,6 +102,18 @@ typedef void *fs_stream_t;  /* hipStream_t */
  */
 size_t fs_workspace_bytes(int64_t B, int64_t V, uint32_t flags);
 
+/* Most places a Gumbel-top-k call returns per row. */
+#define FS_TOPK_MAX 8
+
+/*
+ * Workspace bytes for the Gumbel-top-k calls (fs_sample_logits_topk,
+ * fs_sample_fused_topk): the same counter region, then FS_TOPK_MAX candidates
+ * per (row, tile).  Same zero-fill and reuse contract as fs_workspace_bytes;
+ * a workspace of this size also serves every other call.  Host only; 0 for
+ * invalid sizes.
+ */
+size_t fs_workspace_bytes_topk(int64_t B, int64_t V, uint32_t flags);
+
 /*
  * Fused LM-head + exact sampling [FS "core method", "algorithm details"].
  *   H        device, bf16 [B, D]   hidden states of the decode batch
@@ -174,6 +190,28 @@ fs_status fs_sample_logits(const float *logits, int64_t B, int64_t V, const floa
                            uint64_t seed, uint64_t offset, int fp64_noise,
                            int64_t *out_idx, const uint32_t *row_ids, void *workspace,
                            size_t workspace_bytes, fs_stream_t stream);
+
+/*
+ * Gumbel-top-k over materialised float32 logits [GTK]: k draws without
+ * replacement per row, the places of the k largest perturbed scores s_i of
+ * the sampling rule above (same transform, noise stream and keys as
+ * fs_sample_logits), largest first; equal scores in increasing index order;
+ * scores that are NaN or -inf never take a place.
+ *   k        host, 1 <= k <= FS_TOPK_MAX
+ *   out_idx  device, int64 [B, k] row-major: place j of row b at b * k + j,
+ *            -1 for places past the row's number of valid scores
+ *   workspace, workspace_bytes  at least fs_workspace_bytes_topk(B, V, flags)
+ *            bytes (flags = FS_FP64_NOISE when fp64_noise is set)
+ *   the other arguments as for fs_sample_logits.
+ * Place 0 is the draw fs_sample_logits makes for the same arguments; the
+ * places in order are a draw of k distinct tokens without replacement from
+ * softmax(y / t) (Plackett-Luce); greedy rows (t <= 0 or NaN) get the k
+ * largest y_i.
+ */
+fs_status fs_sample_logits_topk(const float *logits, int64_t B, int64_t V, const float *temp,
+                                uint64_t seed, uint64_t offset, int fp64_noise, int k,
+                                int64_t *out_idx, const uint32_t *row_ids, void *workspace,
+                                size_t workspace_bytes, fs_stream_t stream);
 
 /*
  * Kernel timing.  Between fs_profile_begin() and fs_profile_end(), every
