@@ -314,6 +314,23 @@ def main() -> int:
         result["fp8_weights"] = f8
         del W8, amax
 
+        # Gumbel-top-k (k = 8 draws without replacement per row), fused into the
+        # same head, float32 noise.
+        log("timing the fused Gumbel-top-k step (k = 8)")
+        tk = {"workload": "W [151936, 4096] bf16, k = 8 places per row, fp32 noise"}
+        for b in sorted(set(sweep + [B])):
+            Hs, Ts = H[:b].contiguous(), temp[:b].contiguous()
+            ms, kms, pc = time_calls(
+                torch, fs,
+                lambda s: fs.sample_fused_topk(Hs, W, Ts, k=8, seed=1234, offset=3 * 10**6 + s),
+                max(20, args.steps // 4), args.warmup)
+            kb = kernel_alg_bytes(b, D_MODEL, VOCAB, nT, cand=64)
+            tk[str(b)] = {"us_per_step": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
+                          "kernel_gbs": round(kb / (kms * 1e-3) / 1e9, 1),
+                          "kernel_frac": round(kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"  top-k B={b}: {tk[str(b)]}")
+        result["fused_topk"] = tk
+
         # The standalone sampler over float32 logits: the tail-rate workload's
         # chunk shape (4096 rows x 131072) and a decode-sized batch.
         log("timing the standalone sampler")

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused", "sample_fused_w8",
-    "sample_logits", "sample_logits_topk", "workspace_bytes", "debug_philox_words", "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
+    "sample_fused_topk", "sample_logits", "sample_logits_topk", "workspace_bytes", "debug_philox_words", "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
     "KernelTimer",
 ]
 
@@ -80,6 +80,9 @@ def load_library():
         lib.fs_debug_logits.argtypes = [P, P, i64, i64, i64, P, P]
         lib.fs_workspace_bytes_topk.restype = sz
         lib.fs_workspace_bytes_topk.argtypes = [i64, i64, u32]
+        lib.fs_sample_fused_topk.restype = i32
+        lib.fs_sample_fused_topk.argtypes = [P, P, i64, i64, i64, P, P, u64, u64, i32, P, P, u32,
+                                             P, sz, P]
         lib.fs_sample_logits_topk.restype = i32
         lib.fs_sample_logits_topk.argtypes = [P, i64, i64, P, u64, u64, i32, i32, P, P, P, sz, P]
         lib.fs_sample_fused_w8.restype = i32
@@ -243,6 +246,37 @@ def sample_logits(logits: torch.Tensor, temp, *, seed: int, offset: int,
     st = lib.fs_sample_logits(_ptr(logits), B, V, _ptr(t), seed, offset, int(bool(fp64_noise)),
                               _ptr(out), _ptr(rid), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "fs_sample_logits")
+    return out
+
+
+def sample_fused_topk(H: torch.Tensor, W: torch.Tensor, temp, bias: torch.Tensor | None = None, *,
+                      k: int, seed: int, offset: int, row_ids: torch.Tensor | None = None,
+                      fp64_noise: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Gumbel-top-k fused into the LM head: k draws without replacement per row from
+    softmax((H W^T + bias) / temp); [B, k] int64, largest perturbed score first."""
+    lib = load_library()
+    dev = H.device
+    if dev.type != "cuda":
+        raise ValueError("H must be a GPU tensor")
+    if H.dim() != 2 or W.dim() != 2:
+        raise ValueError("H must be [B, D] and W [V, D]")
+    B, D = H.shape
+    V = W.shape[0]
+    _need(H, "H", torch.bfloat16, dev, (B, D))
+    _need(W, "W", torch.bfloat16, dev, (V, D))
+    t = _temp_tensor(temp, B, dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (B, V))
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B, k))
+    flags = FS_FP64_NOISE if fp64_noise else 0
+    need = int(lib.fs_workspace_bytes_topk(B, V, flags)) if V > 0 else 0
+    ws = _workspace(dev, need)
+    st = lib.fs_sample_fused_topk(_ptr(H), _ptr(W), B, D, V, _ptr(t), _ptr(bias), seed, offset, k,
+                                  _ptr(out), _ptr(rid), flags, _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "fs_sample_fused_topk")
     return out
 
 

@@ -150,16 +150,22 @@ fs_status check_span(int64_t V, int64_t D, int nT, bool w8) {
   return FS_OK;
 }
 
+// k = 0: one draw per row; 1 <= k <= kTopKMax: Gumbel-top-k (bf16 weights).
 fs_status sample_fused(const fs_bf16* H, const void* W, bool w8, const float* w_scale, int64_t B,
                        int64_t D, int64_t V, const float* temp, const float* bias, uint64_t seed,
                        uint64_t offset, int64_t* out_idx, const uint32_t* row_ids, uint32_t flags,
-                       void* workspace, size_t workspace_bytes, fs_stream_t stream) {
+                       void* workspace, size_t workspace_bytes, fs_stream_t stream, int k = 0) {
   fs_status s = check_fused(H, W, w8, w_scale, B, D, V);
   if (s != FS_OK) return s;
   if (flags & ~FS_FP64_NOISE) return fail(FS_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (k < 0 || k > fs::kTopKMax)
+    return fail(FS_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, fs::kTopKMax);
+  // Gumbel-top-k tiles hold 16 or 32 rows, one completion counter each.
+  if (k > 0 && B > 16 * kCounterWords)
+    return fail(FS_ERR_UNSUPPORTED, "B = %lld > 2^20 for Gumbel-top-k", (long long)B);
   if (B == 0) return FS_OK;
   if (temp == nullptr || out_idx == nullptr) return fail(FS_ERR_INVALID_ARG, "temp or out_idx is null");
-  s = check_workspace(workspace, workspace_bytes, B, V, flags);
+  s = check_workspace(workspace, workspace_bytes, B, V, flags, k > 0);
   if (s != FS_OK) return s;
 
   int cus = 0;
@@ -188,10 +194,13 @@ fs_status sample_fused(const fs_bf16* H, const void* W, bool w8, const float* w_
   a.out = out_idx;
   a.Y = nullptr;
   a.bias_vec4 = bias != nullptr && aligned16(bias) && (V % 4 == 0);
+  a.k = k;
+  const int epi = k > 0 ? (fp64 ? fs::kEpiTopK64 : fs::kEpiTopK32)
+                        : (fp64 ? fs::kEpiSample64 : fs::kEpiSample32);
   hipStream_t st = (hipStream_t)stream;
   hipEvent_t* ev = prof_slot();
   if (ev) (void)hipEventRecord(ev[0], st);
-  hipError_t e = fs::launch_fused_stage1(a, fp64 ? fs::kEpiSample64 : fs::kEpiSample32, st);
+  hipError_t e = fs::launch_fused_stage1(a, epi, st);
   if (e != hipSuccess) return hip_fail(e, "fused sampling launch");
   if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
@@ -259,6 +268,17 @@ fs_status fs_sample_fused(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t
   g_last_error[0] = 0;
   return sample_fused(H, W, false, nullptr, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
                       flags, workspace, workspace_bytes, stream);
+}
+
+fs_status fs_sample_fused_topk(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D,
+                               int64_t V, const float* temp, const float* bias, uint64_t seed,
+                               uint64_t offset, int k, int64_t* out_idx, const uint32_t* row_ids,
+                               uint32_t flags, void* workspace, size_t workspace_bytes,
+                               fs_stream_t stream) {
+  g_last_error[0] = 0;
+  if (k < 1) return fail(FS_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, fs::kTopKMax);
+  return sample_fused(H, W, false, nullptr, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
+                      flags, workspace, workspace_bytes, stream, k);
 }
 
 fs_status fs_sample_fused_w8(const fs_bf16* H, const uint8_t* W8, const float* w_scale, int64_t B,

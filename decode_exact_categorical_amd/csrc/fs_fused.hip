@@ -77,6 +77,10 @@ template <>
 struct ScoreType<kEpiSample64> {
   typedef double type;
 };
+template <>
+struct ScoreType<kEpiTopK64> {
+  typedef double type;
+};
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -169,6 +173,7 @@ template <int NB, int EPI, bool HAS_BIAS, bool W8, bool BV4 = false>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
   constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS, W8>::value;
+  constexpr bool kTopK = EPI == kEpiTopK32 || EPI == kEpiTopK64;
   typedef Pipeline<NB, EPI, HAS_BIAS, W8> Pipe;
   // W element bytes, and k per 16-byte lane load (one MFMA k-step of bf16,
   // two of FP8).
@@ -266,6 +271,17 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   if (EPI != kEpiStore && grp == 0) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) wrun[wave][16 * cb + col] = Cand<T>{neg_inf<T>(), kNoIndex};
+  }
+  // Gumbel-top-k: each lane's sorted list of kTopKMax places per column
+  // block, across passes (lane-private LDS slots; place j of a lane's list
+  // for column block cb at tkl[wave][cb][j][lane]).
+  constexpr int kTKW = kTopK ? kWaves : 1, kTKB = kTopK ? NB : 1, kTKK = kTopK ? kTopKMax : 1;
+  __shared__ Cand<T> tkl[kTKW][kTKB][kTKK][64];
+  if constexpr (kTopK) {
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int j = 0; j < kTopKMax; ++j) tkl[wave][cb][j][lane] = Cand<T>{neg_inf<T>(), kNoIndex};
   }
 
   __shared__ __attribute__((aligned(16))) uint16_t hs[2][16 * NB][kHRow];
@@ -705,7 +721,59 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       bm[cb] = neg_inf<T>();
       bi[cb] = kNoIndex;
     }
-    if (EPI == kEpiStore || kFold) {
+    if constexpr (kTopK) {
+      // Column block by column block: the lane's list into registers, the
+      // scores of its rows in increasing index order inserted, the list back.
+#pragma unroll 1
+      for (int cb = 0; cb < NB; ++cb) {
+        T lm[kTopKMax];
+        int32_t li[kTopKMax];
+#pragma unroll
+        for (int j = 0; j < kTopKMax; ++j) {
+          const Cand<T> o = tkl[wave][cb][j][lane];
+          lm[j] = o.m;
+          li[j] = o.idx;
+        }
+        const ColInfo ci = cols[16 * cb + col];
+        const bool greedy = ci.mode == kGreedy;
+        const T it = greedy ? T(1) : T(1) / T(ci.t);
+        const int64_t bcol = bt0 + 16 * cb + col < B ? bt0 + 16 * cb + col : B - 1;
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          if (rb >= nrb) break;
+          f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c2 = 0; c2 < NB; ++c2)
+            if (c2 == cb) y = acc[rb][c2];
+          const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+          float beta[4];
+          load_bias4(a, bcol, i0, beta);
+          T s[4];
+          if (greedy) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] = T(y[j]) + T(beta[j]);
+          } else if constexpr (EPI == kEpiTopK32) {
+            const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), ci.rid);
+            s[0] = (y[0] + beta[0]) * it + gumbel_f32(w.w0);
+            s[1] = (y[1] + beta[1]) * it + gumbel_f32(w.w1);
+            s[2] = (y[2] + beta[2]) * it + gumbel_f32(w.w2);
+            s[3] = (y[3] + beta[3]) * it + gumbel_f32(w.w3);
+          } else {
+            const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), ci.rid);
+            const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, ci.rid);
+            s[0] = (T(y[0]) + T(beta[0])) * it + T(gumbel_f64(w0.w0, w0.w1));
+            s[1] = (T(y[1]) + T(beta[1])) * it + T(gumbel_f64(w0.w2, w0.w3));
+            s[2] = (T(y[2]) + T(beta[2])) * it + T(gumbel_f64(w1.w0, w1.w1));
+            s[3] = (T(y[3]) + T(beta[3])) * it + T(gumbel_f64(w1.w2, w1.w3));
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (i0 + j < r1) topk_insert(lm, li, s[j], (int32_t)(i0 + j));
+        }
+#pragma unroll
+        for (int j = 0; j < kTopKMax; ++j) tkl[wave][cb][j][lane] = Cand<T>{lm[j], li[j]};
+      }
+    } else if (EPI == kEpiStore || kFold) {
       const int32_t r1s = (int32_t)r1;  // V < 2^31
       // Per column: 1 / t (1 for greedy) and whether any column of the wave
       // has an infinite temperature (a wave-uniform test, so the rare noise
@@ -842,7 +910,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           }
       }
     }
-    if (EPI != kEpiStore) {
+    if (EPI != kEpiStore && !kTopK) {
       // Lanes that share a column (the 4 row groups) -> one value per column,
       // merged into the wave's running best.
 #pragma unroll
@@ -857,6 +925,61 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   }
 
   if (EPI == kEpiStore) return;
+
+  if constexpr (kTopK) {
+    // Per column, its kTopKMax places among the 8 waves x 4 row groups x
+    // kTopKMax places of the lists: wave w takes columns w, w + 8, ...
+    __syncthreads();
+    constexpr int kItems = kWaves * 4 * kTopKMax / 64;
+#pragma unroll 1
+    for (int c = wave; c < 16 * NB; c += kWaves) {
+      const int cb = c >> 4, cl = c & 15;
+      Cand<T> it[kItems];
+#pragma unroll
+      for (int q = 0; q < kItems; ++q) {
+        const int e = lane + 64 * q;
+        const int w = e / (4 * kTopKMax), g = (e / kTopKMax) % 4, j = e % kTopKMax;
+        it[q] = tkl[w][cb][j][16 * g + cl];
+      }
+      const int64_t b = bt0 + c;
+      Cand<T>* dst = reinterpret_cast<Cand<T>*>(a.cand) + (b * a.nT + tile) * kTopKMax;
+      Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
+#pragma unroll 1
+      for (int r = 0; r < kTopKMax; ++r) {
+        pl = next_place(it, r == 0, pl.m, pl.idx);
+        if (lane == 0 && b < B) store_cand(dst + r, pl);
+      }
+    }
+    wait_stores_complete();
+
+    // Stage 2: wave w takes rows w, w + 8, ... of the tile; a row's
+    // nT * kTopKMax candidates are read once (clamped addresses), then its
+    // places are picked one after the other.
+    if (!finish_last(a.counters + btile, (uint32_t)nT)) return;
+    constexpr int kPer = kMaxFusedTiles * kTopKMax / 64;
+    const int n = a.nT * kTopKMax;
+#pragma unroll 1
+    for (int i = wave; i < kTile; i += kWaves) {
+      const int64_t b = bt0 + i;
+      if (b >= B) break;
+      const Cand<T>* rc = reinterpret_cast<const Cand<T>*>(a.cand) + b * a.nT * kTopKMax;
+      Cand<T> c[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int e = lane + 64 * q;
+        c[q] = load_cand(rc + (e < n ? e : n - 1));
+        if (e >= n) c[q] = Cand<T>{neg_inf<T>(), kNoIndex};
+      }
+      Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
+#pragma unroll 1
+      for (int r = 0; r < a.k; ++r) {
+        pl = next_place(c, r == 0, pl.m, pl.idx);
+        if (lane == 0) a.out[b * a.k + r] = pl.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)pl.idx;
+      }
+    }
+    if (tid == 0) clear_counter(a.counters + btile);
+    return;
+  }
 
   // Across the waves, in wave order, through LDS.
   __syncthreads();
@@ -937,6 +1060,22 @@ hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream)
       hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample64, false, W8>), grid, dim3(kThreads), 0,
                          stream, a);
       break;
+    case kEpiTopK32:
+      // Gumbel-top-k keeps per-lane lists in LDS: tiles of at most 32 columns
+      // (16 with float64 noise), bf16 weights.
+      if constexpr (NB <= 2 && !W8)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK32, false, false>), grid, dim3(kThreads),
+                           0, stream, a);
+      else
+        return hipErrorInvalidValue;
+      break;
+    case kEpiTopK64:
+      if constexpr (NB == 1 && !W8)
+        hipLaunchKernelGGL((fused_stage1_kernel<1, kEpiTopK64, false, false>), grid, dim3(kThreads),
+                           0, stream, a);
+      else
+        return hipErrorInvalidValue;
+      break;
     default:
       hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiStore, false, W8>), grid, dim3(kThreads), 0,
                          stream, a);
@@ -982,6 +1121,11 @@ int fused_column_blocks(int64_t B, bool fp8_weights, bool fp64_noise) {
 }
 
 hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) {
+  if (epi == kEpiTopK32 || epi == kEpiTopK64) {
+    const int nb = (epi == kEpiTopK64 || a.B <= 16) ? 1 : 2;
+    const dim3 grid((unsigned)a.nT, (unsigned)((a.B + 16 * nb - 1) / (16 * nb)));
+    return nb == 1 ? launch_nb<1, false>(a, epi, grid, stream) : launch_nb<2, false>(a, epi, grid, stream);
+  }
   const int nb = fused_column_blocks(a.B, a.W8 != nullptr, epi == kEpiSample64);
   const int64_t tile = 16 * nb;
   const int64_t nbt = (a.B + tile - 1) / tile;

@@ -27,9 +27,16 @@ struct FusedArgs {
   int64_t* out;        // [B] sampled indices
   float* Y;    // [B, V] (store epilogue only)
   int bias_vec4;  // bias rows are 16-byte aligned
+  int k;          // Gumbel-top-k: places per row (out is [B, k]; cand is [B, nT, kTopKMax])
 };
 
-enum FusedEpilogue { kEpiSample32 = 0, kEpiSample64 = 1, kEpiStore = 2 };
+enum FusedEpilogue {
+  kEpiSample32 = 0,  // one draw per row, float32 noise
+  kEpiSample64 = 1,  // one draw per row, float64 noise
+  kEpiStore = 2,     // logits to Y (test hook)
+  kEpiTopK32 = 3,    // Gumbel-top-k, float32 noise
+  kEpiTopK64 = 4     // Gumbel-top-k, float64 noise
+};
 
 // Number of vocabulary tiles (workgroups along x) the fused kernel uses: one
 // per CU, at most kMaxFusedTiles (Stage 2 reads a row's candidates in

@@ -214,6 +214,27 @@ fs_status fs_sample_logits_topk(const float *logits, int64_t B, int64_t V, const
                                 size_t workspace_bytes, fs_stream_t stream);
 
 /*
+ * Gumbel-top-k fused into the LM head [GTK; FS "algorithm details"]: the
+ * places of the k largest perturbed scores of fs_sample_fused's rule (same
+ * logits, transform, noise stream and keys), largest first; equal scores in
+ * increasing index order; NaN and -inf never take a place.
+ *   k        host, 1 <= k <= FS_TOPK_MAX
+ *   out_idx  device, int64 [B, k] row-major, -1 past a row's valid scores
+ *   workspace, workspace_bytes  at least fs_workspace_bytes_topk(B, V, flags)
+ *   the other arguments as for fs_sample_fused (bf16 W), with B <= 2^20.
+ * Stage 1 keeps each row's FS_TOPK_MAX best places per vocabulary tile,
+ * Stage 2 picks the row's k places from them; the [B, V] logits are never
+ * written.  The noise is added after each pass's contraction (as with
+ * FS_FP64_NOISE), so place 0 equals fs_sample_fused's draw wherever that
+ * draw is not a near-tie in float32.
+ */
+fs_status fs_sample_fused_topk(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t D,
+                               int64_t V, const float *temp, const float *bias,
+                               uint64_t seed, uint64_t offset, int k, int64_t *out_idx,
+                               const uint32_t *row_ids, uint32_t flags, void *workspace,
+                               size_t workspace_bytes, fs_stream_t stream);
+
+/*
  * Kernel timing.  Between fs_profile_begin() and fs_profile_end(), every
  * fs_sample_fused, fs_sample_fused_w8 and fs_sample_logits call also records
  * HIP events on its stream around its one launch (Stage 1 with Stage 2 in its

@@ -152,3 +152,99 @@ def test_topk_argument_errors(dev):
         assert lib.fs_sample_logits_topk(fs._ptr(x), 2, 10, fs._ptr(t), 1, 1, 0, 2, fs._ptr(out),
                                          None, fs._ptr(small), small.numel(),
                                          fs._stream(dev)) == 3
+
+
+def _fused_case(B, D, V, *, bias=False, greedy_rows=(), seed_base=0, w_std=0.02):
+    H = synthetic.hidden(B, D, seed=220 + seed_base)
+    W = synthetic.weight(V, D, std=w_std, seed=221 + seed_base)
+    temp = synthetic.temperatures(B, seed=222 + seed_base)
+    for r in greedy_rows:
+        temp[r] = [0.0, -1.0, float("nan")][r % 3]
+    bb = synthetic.bias_with_mask(B, V, 0.1, seed=223 + seed_base) if bias else None
+    return H, W, temp, bb
+
+
+FUSED_TOPK_CASES = [
+    dict(B=4, D=512, V=32768, k=8),
+    dict(B=37, D=200, V=1001, k=4, bias=True, greedy_rows=(0, 5, 9)),
+    dict(B=20, D=64, V=170001, k=8),            # two passes per wave
+    dict(B=3, D=64, V=13, k=8, w_std=1.0),
+    dict(B=33, D=256, V=4000, k=2, bias=True),   # 16-byte bias rows, three tiles of 16 / two of 32
+]
+
+
+@pytest.mark.parametrize("fp64", [False, True])
+@pytest.mark.parametrize("case", FUSED_TOPK_CASES)
+def test_fused_topk_parity(dev, case, fp64):
+    case = dict(case)
+    B, D, V, k = case.pop("B"), case.pop("D"), case.pop("V"), case.pop("k")
+    say(f"fused top-k B={B} D={D} V={V} k={k} fp64={fp64} {case}")
+    H, W, temp, bias = _fused_case(B, D, V, **case)
+    Hd, Wd, td, bd = to_dev(H, W, temp, bias, dev=dev)
+    rid = synthetic.row_ids(B, start=40)
+    got = fs.sample_fused_topk(Hd, Wd, td, bd, k=k, seed=1234, offset=5, row_ids=rid.to(dev),
+                               fp64_noise=fp64)
+    torch.cuda.synchronize()
+    ref, top = oracle.sample_fused_topk(H, W, temp.numpy(), None if bias is None else bias.numpy(),
+                                        k=k, seed=1234, offset=5,
+                                        row_ids=rid.numpy().view(np.uint32), fp64_noise=fp64)
+    check_places(got.cpu().numpy(), ref, top, f"fused B={B} V={V} k={k} fp64={fp64}")
+
+
+def test_fused_topk_place0_is_the_fused_draw(dev):
+    """Float64 noise: the same logits and score expression, so place 0 equals
+    fs_sample_fused's draw bit for bit."""
+    H, W, temp, bias = _fused_case(40, 256, 5000, bias=True, seed_base=7)
+    Hd, Wd, td, bd = to_dev(H, W, temp, bias, dev=dev)
+    a = fs.sample_fused_topk(Hd, Wd, td, bd, k=3, seed=11, offset=12, fp64_noise=True)
+    b = fs.sample_fused(Hd, Wd, td, bd, seed=11, offset=12, fp64_noise=True)
+    assert torch.equal(a[:, 0], b)
+
+
+def test_fused_topk_masks(dev):
+    B, D, V, k = 6, 64, 300, 8
+    H, W, temp, _ = _fused_case(B, D, V, seed_base=8)
+    bias = torch.zeros((B, V))
+    bias[1] = float("-inf")
+    bias[2] = float("-inf")
+    bias[2, [7, 123, 299]] = 0.0
+    bias[3, ::2] = float("-inf")
+    temp[4] = 0.0
+    Hd, Wd, td, bd = to_dev(H, W, temp, bias, dev=dev)
+    got = fs.sample_fused_topk(Hd, Wd, td, bd, k=k, seed=3, offset=4).cpu().numpy()
+    assert (got[1] == -1).all()
+    assert sorted(got[2, :3].tolist()) == [7, 123, 299] and (got[2, 3:] == -1).all()
+    assert (got[3] % 2 == 1).all()
+    ref, top = oracle.sample_fused_topk(H, W, temp.numpy(), bias.numpy(), k=k, seed=3, offset=4)
+    np.testing.assert_array_equal(got[4], ref[4])                   # greedy row
+    check_places(got, ref, top, "fused masks")
+
+
+def test_fused_topk_law_on_gpu(dev):
+    """One-hot hidden rows pick logits [1, 0.5, 0, -0.75] out of W; the ordered
+    places over 131072 logical rows follow sampling without replacement."""
+    n, D, k, t = 131072, 16, 3, 0.8
+    y = torch.tensor([1.0, 0.5, 0.0, -0.75])
+    W = torch.zeros((4, D), dtype=torch.bfloat16)
+    W[:, 0] = y.to(torch.bfloat16)
+    H = torch.zeros((n, D), dtype=torch.bfloat16)
+    H[:, 0] = 1.0
+    got = fs.sample_fused_topk(H.to(dev), W.to(dev), torch.full((n,), t, device=dev), k=k, seed=99,
+                               offset=6).cpu().numpy()
+    assert (got >= 0).all() and (got < 4).all()
+    p = np.exp(y.double().numpy() / t)
+    p /= p.sum()
+    seqs = list(itertools.permutations(range(4), k))
+    expected = []
+    for s in seqs:
+        pr, left = 1.0, 1.0
+        for i in s:
+            pr *= p[i] / left
+            left -= p[i]
+        expected.append(pr)
+    expected = np.array(expected)
+    code = got[:, 0] * 16 + got[:, 1] * 4 + got[:, 2]
+    counts = np.array([(code == s[0] * 16 + s[1] * 4 + s[2]).sum() for s in seqs], dtype=np.float64)
+    chi2 = ((counts - n * expected) ** 2 / (n * expected)).sum()
+    say(f"  fused chi2 = {chi2:.1f} over {len(seqs) - 1} dof")
+    assert chi2 < stats.chi2.ppf(1 - 1e-6, len(seqs) - 1)
