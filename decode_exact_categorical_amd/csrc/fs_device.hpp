@@ -130,6 +130,12 @@ template <typename T>
 __device__ __forceinline__ bool beats(T s, int32_t i, T bs, int32_t bi) {
   return s > bs || (s == bs && i < bi);
 }
+// The same order with bitwise operators: no branches where it runs in a
+// chain (cross-lane reductions, place selection).
+template <typename T>
+__device__ __forceinline__ bool beats_nb(T s, int32_t i, T bs, int32_t bi) {
+  return (s > bs) | ((s == bs) & (i < bi));
+}
 
 template <typename T>
 struct Cand {
@@ -157,10 +163,9 @@ __device__ __forceinline__ void wave_argmax_xor(T& m, int32_t& i, int lo_bit) {
   for (int b = lo_bit; b < 6; ++b) {
     const T om = __shfl_xor(m, 1 << b, 64);
     const int32_t oi = __shfl_xor(i, 1 << b, 64);
-    if (beats(om, oi, m, i)) {
-      m = om;
-      i = oi;
-    }
+    const bool take = beats_nb(om, oi, m, i);
+    m = take ? om : m;
+    i = take ? oi : i;
   }
 }
 
@@ -261,11 +266,12 @@ __device__ __forceinline__ int64_t row_winner(const Cand<T>* c, int nT, int lane
 // ---------------------------------------------------------------------------
 constexpr int kTopKMax = 8;  // places kept per (row, tile)
 
-// x comes strictly after w in place order.
+// x comes strictly after w in place order (bitwise operators, as beats_nb).
 template <typename T>
 __device__ __forceinline__ bool after(T m, int32_t i, T wm, int32_t wi) {
-  return m < wm || (m == wm && i > wi);
+  return (m < wm) | ((m == wm) & (i > wi));
 }
+
 
 // Insert (s, i) into a lane's sorted list (m, id) of K places.  Scores reach
 // a lane in increasing index order, so an equal score goes below the places
@@ -286,21 +292,21 @@ __device__ __forceinline__ void topk_insert(T (&m)[K], int32_t (&id)[K], T s, in
 
 // The next place after (pm, pi) among a wave's candidates: every lane offers
 // its best candidate that comes after the previous place (first: any), and
-// the wave picks the best offer.  Returns it in every lane ((-inf, kNoIndex)
-// when none is left).
+// the lanes that differ only in bits lo_bit..5 of the lane id pick the best
+// offer (lo_bit = 0: the whole wave).  Returns it in each of those lanes
+// ((-inf, kNoIndex) when none is left).
 template <typename T, int N>
-__device__ __forceinline__ Cand<T> next_place(const Cand<T> (&c)[N], bool first, T pm, int32_t pi) {
+__device__ __forceinline__ Cand<T> next_place(const Cand<T> (&c)[N], bool first, T pm, int32_t pi,
+                                              int lo_bit = 0) {
   T bm = neg_inf<T>();
   int32_t bi = kNoIndex;
 #pragma unroll
   for (int q = 0; q < N; ++q) {
-    const bool ok = first || after(c[q].m, c[q].idx, pm, pi);
-    if (ok && beats(c[q].m, c[q].idx, bm, bi)) {
-      bm = c[q].m;
-      bi = c[q].idx;
-    }
+    const bool take = (first | after(c[q].m, c[q].idx, pm, pi)) & beats_nb(c[q].m, c[q].idx, bm, bi);
+    bm = take ? c[q].m : bm;
+    bi = take ? c[q].idx : bi;
   }
-  wave_argmax_xor(bm, bi, 0);
+  wave_argmax_xor(bm, bi, lo_bit);
   return Cand<T>{bm, bi};
 }
 

@@ -146,11 +146,14 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
 // noise are one per (row block, column block).
 template <int NB, int EPI, bool HAS_BIAS, bool W8>
 struct Pipeline {
+  // Noise added after the k-loop (float64 noise, Gumbel-top-k): the same
+  // register budget as float64 noise.
+  static constexpr bool late_noise = EPI == kEpiSample64 || EPI == kEpiTopK32 || EPI == kEpiTopK64;
   static constexpr bool wide = NB > 4;
-  static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || EPI == kEpiSample64);
+  static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || late_noise);
   static constexpr bool ring1 = !W8 && !wide && NB >= 3 && !wide_extra;
   static constexpr int row_blocks = wide ? 2 : ((NB <= 2 || ring1) ? 5 : 3);
-  static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || EPI == kEpiSample64);
+  static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || late_noise);
   static constexpr bool interleave = !W8 && !wide && !wide_extra;
   static constexpr int chunk_k = wide ? 128 : 256;   // k per H chunk in LDS
   // Fragment (rb, cb) gets its noise at k-step noise_slots * rb + cb.
@@ -272,16 +275,17 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) wrun[wave][16 * cb + col] = Cand<T>{neg_inf<T>(), kNoIndex};
   }
-  // Gumbel-top-k: each lane's sorted list of kTopKMax places per column
-  // block, across passes (lane-private LDS slots; place j of a lane's list
-  // for column block cb at tkl[wave][cb][j][lane]).
-  constexpr int kTKW = kTopK ? kWaves : 1, kTKB = kTopK ? NB : 1, kTKK = kTopK ? kTopKMax : 1;
-  __shared__ Cand<T> tkl[kTKW][kTKB][kTKK][64];
+  // Gumbel-top-k: the running kTopKMax places of each batch column of this
+  // wave across its passes (a wave-private LDS slot per column).
+  constexpr int kTKW = kTopK ? kWaves : 1, kTKC = kTopK ? 16 * NB : 1, kTKK = kTopK ? kTopKMax : 1;
+  __shared__ Cand<T> tkc[kTKW][kTKC][kTKK];
   if constexpr (kTopK) {
+    if (grp == 0) {
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
+      for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-      for (int j = 0; j < kTopKMax; ++j) tkl[wave][cb][j][lane] = Cand<T>{neg_inf<T>(), kNoIndex};
+        for (int j = 0; j < kTopKMax; ++j) tkc[wave][16 * cb + col][j] = Cand<T>{neg_inf<T>(), kNoIndex};
+    }
   }
 
   __shared__ __attribute__((aligned(16))) uint16_t hs[2][16 * NB][kHRow];
@@ -722,17 +726,18 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       bi[cb] = kNoIndex;
     }
     if constexpr (kTopK) {
-      // Column block by column block: the lane's list into registers, the
-      // scores of its rows in increasing index order inserted, the list back.
+      // Column block by column block: the lane's scores of the pass, in
+      // increasing index order, into a sorted list in registers; then that
+      // list, the column's other three row groups' lists and the column's
+      // running places (LDS) merge into the new running places.
 #pragma unroll 1
       for (int cb = 0; cb < NB; ++cb) {
         T lm[kTopKMax];
         int32_t li[kTopKMax];
 #pragma unroll
         for (int j = 0; j < kTopKMax; ++j) {
-          const Cand<T> o = tkl[wave][cb][j][lane];
-          lm[j] = o.m;
-          li[j] = o.idx;
+          lm[j] = neg_inf<T>();
+          li[j] = kNoIndex;
         }
         const ColInfo ci = cols[16 * cb + col];
         const bool greedy = ci.mode == kGreedy;
@@ -766,12 +771,24 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
             s[2] = (T(y[2]) + T(beta[2])) * it + T(gumbel_f64(w1.w0, w1.w1));
             s[3] = (T(y[3]) + T(beta[3])) * it + T(gumbel_f64(w1.w2, w1.w3));
           }
+          // Rows past the wave's last one enter as -inf, which never takes a
+          // place (no branch around the insert).
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (i0 + j < r1) topk_insert(lm, li, s[j], (int32_t)(i0 + j));
+            topk_insert(lm, li, i0 + j < r1 ? s[j] : neg_inf<T>(), (int32_t)(i0 + j));
         }
+        Cand<T> c[2 * kTopKMax];
 #pragma unroll
-        for (int j = 0; j < kTopKMax; ++j) tkl[wave][cb][j][lane] = Cand<T>{lm[j], li[j]};
+        for (int j = 0; j < kTopKMax; ++j) {
+          c[j] = Cand<T>{lm[j], li[j]};
+          c[kTopKMax + j] = grp == 0 ? tkc[wave][16 * cb + col][j] : Cand<T>{neg_inf<T>(), kNoIndex};
+        }
+        Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
+#pragma unroll 1
+        for (int r = 0; r < kTopKMax; ++r) {
+          pl = next_place(c, r == 0, pl.m, pl.idx, 4);
+          if (grp == 0) tkc[wave][16 * cb + col][r] = pl;
+        }
       }
     } else if (EPI == kEpiStore || kFold) {
       const int32_t r1s = (int32_t)r1;  // V < 2^31
@@ -927,20 +944,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   if (EPI == kEpiStore) return;
 
   if constexpr (kTopK) {
-    // Per column, its kTopKMax places among the 8 waves x 4 row groups x
-    // kTopKMax places of the lists: wave w takes columns w, w + 8, ...
+    // Per column, its kTopKMax places among the 8 waves' running places
+    // (one candidate a lane): wave w takes columns w, w + 8, ...
     __syncthreads();
-    constexpr int kItems = kWaves * 4 * kTopKMax / 64;
+    static_assert(kWaves * kTopKMax == 64, "one candidate per lane");
 #pragma unroll 1
     for (int c = wave; c < 16 * NB; c += kWaves) {
-      const int cb = c >> 4, cl = c & 15;
-      Cand<T> it[kItems];
-#pragma unroll
-      for (int q = 0; q < kItems; ++q) {
-        const int e = lane + 64 * q;
-        const int w = e / (4 * kTopKMax), g = (e / kTopKMax) % 4, j = e % kTopKMax;
-        it[q] = tkl[w][cb][j][16 * g + cl];
-      }
+      Cand<T> it[1];
+      it[0] = tkc[lane / kTopKMax][c][lane % kTopKMax];
       const int64_t b = bt0 + c;
       Cand<T>* dst = reinterpret_cast<Cand<T>*>(a.cand) + (b * a.nT + tile) * kTopKMax;
       Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
@@ -1061,17 +1072,18 @@ hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream)
                          stream, a);
       break;
     case kEpiTopK32:
-      // Gumbel-top-k keeps per-lane lists in LDS: tiles of at most 32 columns
-      // (16 with float64 noise), bf16 weights.
-      if constexpr (NB <= 2 && !W8)
+      // Gumbel-top-k: tiles of at most 64 columns, bf16 weights.
+      if constexpr (NB <= 4 && !W8)
         hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK32, false, false>), grid, dim3(kThreads),
                            0, stream, a);
       else
         return hipErrorInvalidValue;
       break;
     case kEpiTopK64:
-      if constexpr (NB == 1 && !W8)
-        hipLaunchKernelGGL((fused_stage1_kernel<1, kEpiTopK64, false, false>), grid, dim3(kThreads),
+      // Float64 scores: tiles of 16 or 64 columns (the 32- and 48-column
+      // layouts run out of registers).
+      if constexpr ((NB == 1 || NB == 4) && !W8)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK64, false, false>), grid, dim3(kThreads),
                            0, stream, a);
       else
         return hipErrorInvalidValue;
@@ -1122,9 +1134,10 @@ int fused_column_blocks(int64_t B, bool fp8_weights, bool fp64_noise) {
 
 hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) {
   if (epi == kEpiTopK32 || epi == kEpiTopK64) {
-    const int nb = (epi == kEpiTopK64 || a.B <= 16) ? 1 : 2;
+    int nb = fused_column_blocks(a.B, true, false);  // tiles of at most 64 columns
+    if (epi == kEpiTopK64 && nb > 1) nb = 4;
     const dim3 grid((unsigned)a.nT, (unsigned)((a.B + 16 * nb - 1) / (16 * nb)));
-    return nb == 1 ? launch_nb<1, false>(a, epi, grid, stream) : launch_nb<2, false>(a, epi, grid, stream);
+    return launch_w<false>(a, epi, grid, nb, stream);
   }
   const int nb = fused_column_blocks(a.B, a.W8 != nullptr, epi == kEpiSample64);
   const int64_t tile = 16 * nb;

@@ -77,9 +77,10 @@ __global__ __launch_bounds__(kThreads) void logits_topk_kernel(LogitsArgs a) {
       s[2] = T(y[2]) * inv_t + T(gumbel_f64(w1.w0, w1.w1));
       s[3] = T(y[3]) * inv_t + T(gumbel_f64(w1.w2, w1.w3));
     }
+    // Entries past the chunk enter as -inf, which never takes a place.
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (i0 + j < hi) topk_insert(lm, li, s[j], (int32_t)(i0 + j));
+      topk_insert(lm, li, i0 + j < hi ? s[j] : neg_inf<T>(), (int32_t)(i0 + j));
   }
 
   // The chunk's places: every thread's list through LDS to wave 0.
@@ -127,11 +128,10 @@ __global__ __launch_bounds__(kThreads) void logits_topk_kernel(LogitsArgs a) {
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const bool ok = base + lane + 64 * q < n && (r == 0 || after(c[q].m, c[q].idx, pm, pi));
-          if (ok && beats(c[q].m, c[q].idx, bm, bi)) {
-            bm = c[q].m;
-            bi = c[q].idx;
-          }
+          const bool take = (base + lane + 64 * q < n) & ((r == 0) | after(c[q].m, c[q].idx, pm, pi)) &
+                            beats_nb(c[q].m, c[q].idx, bm, bi);
+          bm = take ? c[q].m : bm;
+          bi = take ? c[q].idx : bi;
         }
       }
       wave_argmax_xor(bm, bi, 0);

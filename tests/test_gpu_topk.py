@@ -169,7 +169,9 @@ FUSED_TOPK_CASES = [
     dict(B=37, D=200, V=1001, k=4, bias=True, greedy_rows=(0, 5, 9)),
     dict(B=20, D=64, V=170001, k=8),            # two passes per wave
     dict(B=3, D=64, V=13, k=8, w_std=1.0),
-    dict(B=33, D=256, V=4000, k=2, bias=True),   # 16-byte bias rows, three tiles of 16 / two of 32
+    dict(B=33, D=256, V=4000, k=2, bias=True),   # 16-byte bias rows, a 48- or 64-column tile
+    dict(B=64, D=256, V=3001, k=8, greedy_rows=(17,)),
+    dict(B=100, D=128, V=2000, k=3, bias=True),  # two 64-column tiles
 ]
 
 
