@@ -74,6 +74,15 @@ def _load():
         lib.oracle_sample_fused_w8.restype = None
         lib.oracle_sample_fused_w8.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P,
                                                i32, P, P, P]
+        lib.oracle_e2m1_to_double.restype = ctypes.c_double
+        lib.oracle_e2m1_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0_to_double.restype = ctypes.c_double
+        lib.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_logits_w4.restype = None
+        lib.oracle_logits_w4.argtypes = [P, P, P, i64, i64, i64, P]
+        lib.oracle_sample_fused_w4.restype = None
+        lib.oracle_sample_fused_w4.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P, i32, P,
+                                               P, P]
         lib.oracle_sample_fused_topk.restype = None
         lib.oracle_sample_fused_topk.argtypes = [P, P, i64, i64, i64, P, P, u64, u64, P, i32,
                                                  i32, P, P]
@@ -248,6 +257,58 @@ def sample_logits(logits_f32, temp, *, seed: int, offset: int, row_ids=None,
     best = np.zeros(B, dtype=np.float64)
     _load().oracle_sample_logits(_ptr(x), B, V, _ptr(t), seed, offset, _ptr(rid),
                                  int(fp64_noise), _ptr(idx), _ptr(gap), _ptr(best))
+    return idx, gap, best
+
+
+def e2m1_to_double(codes) -> np.ndarray:
+    """float64 values of FP4 E2M1 codes (low 4 bits of each uint8)."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    lib = _load()
+    return np.array([lib.oracle_e2m1_to_double(int(v)) for v in c], dtype=np.float64)
+
+
+def e8m0_to_double(codes) -> np.ndarray:
+    """float64 values of E8M0 scale codes."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    lib = _load()
+    return np.array([lib.oracle_e8m0_to_double(int(v)) for v in c], dtype=np.float64)
+
+
+def logits_w4(H, W4, S) -> np.ndarray:
+    """float64[B, V] over MXFP4 weights: W4 uint8 [V, D/2] (element 2j in the low
+    nibble of byte j), S uint8 [V, D/32] E8M0 block scales."""
+    h = _bf16_bits(H)
+    w = np.ascontiguousarray(np.asarray(W4, dtype=np.uint8))
+    sc = np.ascontiguousarray(np.asarray(S, dtype=np.uint8))
+    B, D = h.shape
+    V = w.shape[0]
+    assert D % 32 == 0 and w.shape == (V, D // 2) and sc.shape == (V, D // 32)
+    Y = np.zeros((B, V), dtype=np.float64)
+    _load().oracle_logits_w4(_ptr(h), _ptr(w), _ptr(sc), B, D, V, _ptr(Y))
+    return Y
+
+
+def sample_fused_w4(H, W4, S, temp, bias=None, *, seed: int, offset: int, row_ids=None,
+                    fp64_noise: bool = False):
+    """(idx, gap, best) for the fused definition over MXFP4 weights."""
+    h = _bf16_bits(H)
+    w = np.ascontiguousarray(np.asarray(W4, dtype=np.uint8))
+    sc = np.ascontiguousarray(np.asarray(S, dtype=np.uint8))
+    B, D = h.shape
+    V = w.shape[0]
+    assert D % 32 == 0 and w.shape == (V, D // 2) and sc.shape == (V, D // 32)
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    bb = None
+    if bias is not None:
+        bb = np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+        assert bb.shape == (B, V)
+    rid = _u32_or_none(row_ids, B)
+    idx = np.zeros(B, dtype=np.int64)
+    gap = np.zeros(B, dtype=np.float64)
+    best = np.zeros(B, dtype=np.float64)
+    _load().oracle_sample_fused_w4(_ptr(h), _ptr(w), _ptr(sc), B, D, V, _ptr(t), _ptr(bb), seed,
+                                   offset, _ptr(rid), int(fp64_noise), _ptr(idx), _ptr(gap),
+                                   _ptr(best))
     return idx, gap, best
 
 

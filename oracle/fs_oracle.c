@@ -26,6 +26,10 @@
  *   [OFP8] OCP 8-bit Floating Point Specification (OFP8), revision 1.0: the
  *         E4M3 encoding of 8-bit weights (FP8 weights are the future work the
  *         FlashSampling page's limitations section names).
+ *   [MX]  OCP Microscaling Formats (MX) specification, version 1.0: MXFP4,
+ *         blocks of 32 FP4 E2M1 elements sharing one E8M0 scale (MXFP4
+ *         weights are the other low-precision input the FlashSampling page's
+ *         limitations section names).
  *   [GTK] Gumbel-top-k: the FlashSampling page's limitations and future-work
  *         sections name the top-k extension (k draws without replacement from
  *         the k largest perturbed scores, proved in its appendix D); the
@@ -162,11 +166,31 @@ static double e4m3_to_double(uint8_t v)
     return sign ? -mag : mag;
 }
 
+/* FP4 E2M1 code (low 4 bits) -> double (exact) [MX]: sign bit 3, 2 exponent
+ * bits with bias 1, 1 mantissa bit; exponent 0 encodes m/2 (0 or 0.5); no
+ * infinities or NaN, so the values are 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ * negatives. */
+static double e2m1_to_double(uint8_t v)
+{
+    int sign = (v >> 3) & 1, e = (v >> 1) & 3, m = v & 1;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, e - 1);
+    return sign ? -mag : mag;
+}
+
+/* E8M0 scale -> double [MX]: 2^(e - 127); e = 255 is NaN. */
+static double e8m0_to_double(uint8_t e)
+{
+    if (e == 255) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
 /* ------------------------------------------------------------------ */
 /* Exported helpers.                                                    */
 /* ------------------------------------------------------------------ */
 
 double oracle_e4m3_to_double(uint8_t v) { return e4m3_to_double(v); }
+double oracle_e2m1_to_double(uint8_t v) { return e2m1_to_double(v); }
+double oracle_e8m0_to_double(uint8_t e) { return e8m0_to_double(e); }
 
 int oracle_num_threads(void)
 {
@@ -270,6 +294,32 @@ void oracle_logits_w8(const uint16_t *H, const uint8_t *W8, const float *scale,
             double acc = 0.0;
             for (int64_t d = 0; d < D; ++d) acc += hrow[d] * e4m3_to_double(w[d]);
             Y[b * V + i] = (double)scale[i] * acc;
+        }
+    }
+    free(hrow);
+}
+
+/* Logits over MXFP4 weights [MX]: row i of W is stored as D/2 bytes, element
+ * d in the low nibble of byte d/2 when d is even and in the high nibble when
+ * d is odd, and block j (elements 32j .. 32j+31) shares the E8M0 scale
+ * S[i, j] (D/32 bytes per row).  y_i = sum_d H[b,d] * e2m1(W[i,d]) *
+ * e8m0(S[i, d/32]), float64, d ascending. */
+void oracle_logits_w4(const uint16_t *H, const uint8_t *W4, const uint8_t *S,
+                      int64_t B, int64_t D, int64_t V, double *Y)
+{
+    double *hrow = (double *)malloc((size_t)D * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t d = 0; d < D; ++d) hrow[d] = bf16_to_double(H[b * D + d]);
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i) {
+            const uint8_t *w = W4 + i * (D / 2);
+            const uint8_t *sc = S + i * (D / 32);
+            double y = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                uint8_t code = (d & 1) ? (uint8_t)(w[d / 2] >> 4) : (uint8_t)(w[d / 2] & 15);
+                y += hrow[d] * (e2m1_to_double(code) * e8m0_to_double(sc[d / 32]));
+            }
+            Y[b * V + i] = y;
         }
     }
     free(hrow);
@@ -407,6 +457,31 @@ void oracle_sample_fused_w8(const uint16_t *H, const uint8_t *W8, const float *s
     }
     free(hrow);
     free(s);
+}
+
+/* Fused path over MXFP4 weights: the logits of oracle_logits_w4, then the
+ * same transform, noise and selection as oracle_sample_fused. */
+void oracle_sample_fused_w4(const uint16_t *H, const uint8_t *W4, const uint8_t *S,
+                            int64_t B, int64_t D, int64_t V, const float *temp,
+                            const float *bias, uint64_t seed, uint64_t offset,
+                            const uint32_t *row_ids, int fp64_noise,
+                            int64_t *out_idx, double *out_gap, double *out_best)
+{
+    double *y = (double *)malloc((size_t)V * sizeof(double));
+    double *s = (double *)malloc((size_t)V * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        double t = (double)temp[b];
+        oracle_logits_w4(H + b * D, W4, S, 1, D, V, y);
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i) {
+            double beta = bias ? (double)bias[b * V + i] : 0.0;
+            s[i] = score_of(y[i], beta, t, seed, offset, r, i, fp64_noise);
+        }
+        select_row(s, V, &out_idx[b], &out_gap[b], &out_best[b]);
+    }
+    free(s);
+    free(y);
 }
 
 /* Gumbel-top-k over the fused path's scores [GTK]: per row, k places of

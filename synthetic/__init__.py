@@ -52,6 +52,41 @@ def weight_fp8(V: int, D: int, std: float, seed: int = SEED_W, chunk_rows: int =
     return W8, scale
 
 
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def weight_mxfp4(V: int, D: int, std: float, seed: int = SEED_W, chunk_rows: int = 4096):
+    """An MXFP4 LM-head weight: (W4 uint8 [V, D/2], S uint8 [V, D/32]).
+
+    Each block of 32 values of a N(0, std^2) draw (the same draws as weight())
+    shares the E8M0 scale 2^X with X = floor(log2(max |w|)) - 2 (2 is the
+    largest E2M1 exponent), and each value is rounded to the nearest E2M1 value
+    of w / 2^X (ties to the even code, magnitudes above 6 saturate).  Element
+    2j sits in the low nibble of byte j, element 2j + 1 in the high nibble."""
+    assert D % 32 == 0
+    W4 = np.empty((V, D // 2), dtype=np.uint8)
+    S = np.empty((V, D // 32), dtype=np.uint8)
+    g = _gen(seed)
+    odd = np.arange(8) % 2
+    for r0 in range(0, V, chunk_rows):
+        r1 = min(V, r0 + chunk_rows)
+        w = (torch.randn((r1 - r0, D), generator=g) * std).numpy().astype(np.float64)
+        blk = w.reshape(r1 - r0, D // 32, 32)
+        amax = np.abs(blk).max(axis=2)
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+        X = np.clip(X, -127, 127).astype(np.int64)
+        x = blk / np.ldexp(1.0, X)[..., None]
+        mag = np.abs(x).reshape(-1)
+        d = np.abs(mag[:, None] - _E2M1[None, :])
+        tie = d == d.min(axis=1, keepdims=True)
+        code = np.argmin(np.where(tie, odd[None, :], 9), axis=1).astype(np.uint8)
+        code |= (np.signbit(x.reshape(-1)) & (code > 0)).astype(np.uint8) << 3
+        code = code.reshape(r1 - r0, D)
+        W4[r0:r1] = code[:, 0::2] | (code[:, 1::2] << 4)
+        S[r0:r1] = (X + 127).astype(np.uint8)
+    return torch.from_numpy(W4), torch.from_numpy(S)
+
+
 def hidden(B: int, D: int, std: float = 1.0, seed: int = SEED_H) -> torch.Tensor:
     """H[B, D] bf16 ~ N(0, std^2)."""
     return (torch.randn((B, D), generator=_gen(seed)) * std).to(torch.bfloat16)
