@@ -88,6 +88,40 @@ def kernel_alg_bytes(B: int, D: int, V: int, n_tiles: int, bias: bool = False, c
             + 2 * cand * B * n_tiles + 8 * B)
 
 
+def mxfp4_alg_bytes(B: int, D: int, V: int, n_tiles: int, cand: int = 8) -> int:
+    """kernel_alg_bytes for MXFP4 weights: D/2 bytes of codes and D/32 of scales a row."""
+    return V * D // 2 + V * D // 32 + B * D * 2 + 4 * B + 2 * cand * B * n_tiles + 8 * B
+
+
+def mxfp4_from_bf16(torch, W, chunk_rows: int = 16384):
+    """MXFP4 copy of a bf16 [V, D] weight on its device: per block of 32, scale
+    2^X with X = floor(log2 max|w|) - 2, elements rounded to the nearest E2M1
+    value (ties to the even code, saturating at 6); element 2j in the low
+    nibble of byte j.  Returns (W4 uint8 [V, D/2], S uint8 [V, D/32])."""
+    V, D = W.shape
+    dev = W.device
+    mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], device=dev)
+    W4 = torch.empty((V, D // 2), dtype=torch.uint8, device=dev)
+    S = torch.empty((V, D // 32), dtype=torch.uint8, device=dev)
+    for r0 in range(0, V, chunk_rows):
+        r1 = min(V, r0 + chunk_rows)
+        blk = W[r0:r1].float().view(r1 - r0, D // 32, 32)
+        amax = blk.abs().amax(dim=2)
+        X = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-38))) - 2,
+                        torch.full_like(amax, -127.0)).clamp(-127, 127)
+        x = blk * torch.exp2(-X)[..., None]
+        mag = x.abs()
+        code = torch.bucketize(mag, mids, right=True)
+        prev = mids[(code - 1).clamp_min(0)]
+        tie = (code > 0) & (mag == prev)
+        code = torch.where(tie & (code % 2 == 1), code - 1, code)
+        code = code | ((x < 0) & (code > 0)).long() << 3
+        code = code.view(r1 - r0, D).to(torch.uint8)
+        W4[r0:r1] = code[:, 0::2] | (code[:, 1::2] << 4)
+        S[r0:r1] = (X + 127).to(torch.uint8)
+    return W4, S
+
+
 def logits_alg_bytes(B: int, V: int, cand: int = 8) -> int:
     """What one standalone sampling launch must move: the float32 logits once,
     temperatures, candidates written and read back once, the indices written."""
@@ -313,6 +347,26 @@ def main() -> int:
             log(f"  fp8 B={b}: {f8[str(b)]}")
         result["fp8_weights"] = f8
         del W8, amax
+
+        # MXFP4 weights: the same head in E2M1 with an E8M0 scale per block of 32.
+        log("timing the MXFP4-weight fused step")
+        W4, S4 = mxfp4_from_bf16(torch, W)
+        f4 = {"workload": "W [151936, 4096] MXFP4 (E2M1 + E8M0 per 32), fp32 noise"}
+        for b in sorted(set(sweep + [B])):
+            Hs, Ts = H[:b].contiguous(), temp[:b].contiguous()
+            ms, kms, pc = time_calls(
+                torch, fs,
+                lambda s: fs.sample_fused_mxfp4(Hs, W4, S4, Ts, seed=1234, offset=4 * 10**6 + s),
+                max(20, args.steps // 2), args.warmup)
+            kb = mxfp4_alg_bytes(b, D_MODEL, VOCAB, nT)
+            f4[str(b)] = {"us_per_step": round(ms * 1e3, 2), "p50_us": round(pc["p50"] * 1e3, 2),
+                          "kernel_us": round(kms * 1e3, 2),
+                          "kernel_gbs": round(kb / (kms * 1e-3) / 1e9, 1),
+                          "kernel_frac": round(kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "tokens_per_s": round(b / (ms * 1e-3), 1)}
+            log(f"  mxfp4 B={b}: {f4[str(b)]}")
+        result["mxfp4_weights"] = f4
+        del W4, S4
 
         # Gumbel-top-k (k = 8 draws without replacement per row), fused into the
         # same head, float32 noise.

@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused", "sample_fused_w8",
-    "sample_fused_topk", "sample_logits", "sample_logits_topk", "workspace_bytes", "debug_philox_words", "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
+    "sample_fused_topk", "sample_fused_mxfp4", "sample_logits", "sample_logits_topk",
+    "workspace_bytes", "debug_logits_mxfp4", "debug_philox_words", "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
     "KernelTimer",
 ]
 
@@ -85,6 +86,11 @@ def load_library():
                                              P, sz, P]
         lib.fs_sample_logits_topk.restype = i32
         lib.fs_sample_logits_topk.argtypes = [P, i64, i64, P, u64, u64, i32, i32, P, P, P, sz, P]
+        lib.fs_sample_fused_mxfp4.restype = i32
+        lib.fs_sample_fused_mxfp4.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P, P, u32, P,
+                                              sz, P]
+        lib.fs_debug_logits_mxfp4.restype = i32
+        lib.fs_debug_logits_mxfp4.argtypes = [P, P, P, i64, i64, i64, P, P]
         lib.fs_sample_fused_w8.restype = i32
         lib.fs_sample_fused_w8.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P, P, u32, P,
                                            sz, P]
@@ -221,6 +227,43 @@ def sample_fused_w8(H: torch.Tensor, W8: torch.Tensor, w_scale: torch.Tensor, te
                                 seed, offset, _ptr(out), _ptr(rid), flags, _ptr(ws), ws.numel(),
                                 _stream(dev))
     _check(st, "fs_sample_fused_w8")
+    return out
+
+
+def _mxfp4_args(H, W4, w4_scale, dev):
+    B, D = H.shape
+    V = W4.shape[0]
+    _need(H, "H", torch.bfloat16, dev, (B, D))
+    _need(W4, "W4", torch.uint8, dev, (V, D // 2))
+    _need(w4_scale, "w4_scale", torch.uint8, dev, (V, D // 32))
+    return B, D, V
+
+
+def sample_fused_mxfp4(H: torch.Tensor, W4: torch.Tensor, w4_scale: torch.Tensor, temp,
+                       bias: torch.Tensor | None = None, *, seed: int, offset: int,
+                       row_ids: torch.Tensor | None = None, fp64_noise: bool = False,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """sample_fused with MXFP4 weights: W4 uint8 [V, D/2] E2M1 codes (element 2j in
+    the low nibble of byte j), w4_scale uint8 [V, D/32] E8M0 block scales."""
+    lib = load_library()
+    dev = H.device
+    if dev.type != "cuda":
+        raise ValueError("H must be a GPU tensor")
+    B, D, V = _mxfp4_args(H, W4, w4_scale, dev)
+    t = _temp_tensor(temp, B, dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (B, V))
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B,))
+    flags = FS_FP64_NOISE if fp64_noise else 0
+    need = int(lib.fs_workspace_bytes(B, V, flags)) if V > 0 else 0
+    ws = _workspace(dev, need)
+    st = lib.fs_sample_fused_mxfp4(_ptr(H), _ptr(W4), _ptr(w4_scale), B, D, V, _ptr(t), _ptr(bias),
+                                   seed, offset, _ptr(out), _ptr(rid), flags, _ptr(ws), ws.numel(),
+                                   _stream(dev))
+    _check(st, "fs_sample_fused_mxfp4")
     return out
 
 
@@ -378,4 +421,15 @@ def debug_logits_w8(H: torch.Tensor, W8: torch.Tensor, w_scale: torch.Tensor) ->
     Y = torch.empty((B, V), dtype=torch.float32, device=dev)
     _check(lib.fs_debug_logits_w8(_ptr(H), _ptr(W8), _ptr(w_scale), B, D, V, _ptr(Y),
                                   _stream(dev)), "fs_debug_logits_w8")
+    return Y
+
+
+def debug_logits_mxfp4(H: torch.Tensor, W4: torch.Tensor, w4_scale: torch.Tensor) -> torch.Tensor:
+    """float32 [B, V] logits from the MXFP4 path's matmul code (test hook)."""
+    lib = load_library()
+    dev = H.device
+    B, D, V = _mxfp4_args(H, W4, w4_scale, dev)
+    Y = torch.empty((B, V), dtype=torch.float32, device=dev)
+    _check(lib.fs_debug_logits_mxfp4(_ptr(H), _ptr(W4), _ptr(w4_scale), B, D, V, _ptr(Y),
+                                     _stream(dev)), "fs_debug_logits_mxfp4")
     return Y

@@ -122,40 +122,59 @@ fs_status check_workspace(void* ws, size_t have, int64_t B, int64_t V, uint32_t 
   return FS_OK;
 }
 
-// Size and pointer checks shared by the bf16 (W) and FP8 (W8 + w_scale)
-// weight formats.  An FP8 row is D bytes, so D % 16 == 0 keeps every row's
-// 16-byte lane loads inside the row and aligned.
-fs_status check_fused(const fs_bf16* H, const void* W, bool w8, const float* w_scale, int64_t B,
+// Weight formats of the fused calls.
+enum WFormat { kFmtBf16 = 0, kFmtFp8 = 1, kFmtMxfp4 = 2 };
+
+// Bytes of one W row.
+int64_t row_bytes(int64_t D, int fmt) { return fmt == kFmtBf16 ? 2 * D : (fmt == kFmtFp8 ? D : D / 2); }
+
+// Size and pointer checks shared by the weight formats: bf16 (W), FP8 (W8 +
+// float32 row scales) and MXFP4 (W4 + E8M0 block scales).  D % 16 == 0 (FP8)
+// and D % 256 == 0 (MXFP4) keep every row's 16-byte lane loads inside the row
+// and aligned, and MXFP4's 8-byte scale words (a 256-k chunk's 8 blocks)
+// aligned and inside the row.
+fs_status check_fused(const fs_bf16* H, const void* W, int fmt, const void* scale, int64_t B,
                       int64_t D, int64_t V) {
   fs_status s = check_sizes(B, V);
   if (s != FS_OK) return s;
   if (B > kMaxFusedB) return fail(FS_ERR_UNSUPPORTED, "B = %lld > 2^22", (long long)B);
   if (D < 1) return fail(FS_ERR_INVALID_ARG, "D = %lld must be positive", (long long)D);
-  const int dmul = w8 ? 16 : 8;
+  const int dmul = fmt == kFmtBf16 ? 8 : (fmt == kFmtFp8 ? 16 : 256);
   if (D % dmul != 0)
     return fail(FS_ERR_UNSUPPORTED, "D = %lld is not a multiple of %d", (long long)D, dmul);
   if (D > ((int64_t)1 << 24)) return fail(FS_ERR_UNSUPPORTED, "D = %lld too large", (long long)D);
   if (B > 0 && (H == nullptr || W == nullptr)) return fail(FS_ERR_INVALID_ARG, "H or W is null");
-  if (B > 0 && w8 && w_scale == nullptr) return fail(FS_ERR_INVALID_ARG, "w_scale is null");
+  if (B > 0 && fmt != kFmtBf16 && scale == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "weight scales are null");
   if (B > 0 && (!aligned16(H) || !aligned16(W)))
     return fail(FS_ERR_UNSUPPORTED, "H and W must be 16-byte aligned");
+  if (B > 0 && fmt == kFmtMxfp4 && ((uintptr_t)scale & 7u) != 0)
+    return fail(FS_ERR_UNSUPPORTED, "MXFP4 scales must be 8-byte aligned");
   return FS_OK;
 }
 
 // The kernel addresses one wave's W rows through 32-bit offsets.
-fs_status check_span(int64_t V, int64_t D, int nT, bool w8) {
-  if (fs::fused_wave_span_bytes(V, D, nT, w8 ? 1 : 2) >= ((int64_t)1 << 31))
+fs_status check_span(int64_t V, int64_t D, int nT, int fmt) {
+  if (fs::fused_wave_span_bytes(V, row_bytes(D, fmt), nT, 1) >= ((int64_t)1 << 31))
     return fail(FS_ERR_UNSUPPORTED, "V * D too large (V = %lld, D = %lld)", (long long)V,
                 (long long)D);
   return FS_OK;
 }
 
+void set_weights(fs::FusedArgs& a, const void* W, int fmt, const void* scale) {
+  a.W = fmt == kFmtBf16 ? static_cast<const uint16_t*>(W) : nullptr;
+  a.W8 = fmt == kFmtFp8 ? static_cast<const uint8_t*>(W) : nullptr;
+  a.w_scale = fmt == kFmtFp8 ? static_cast<const float*>(scale) : nullptr;
+  a.W4 = fmt == kFmtMxfp4 ? static_cast<const uint8_t*>(W) : nullptr;
+  a.w4_scale = fmt == kFmtMxfp4 ? static_cast<const uint8_t*>(scale) : nullptr;
+}
+
 // k = 0: one draw per row; 1 <= k <= kTopKMax: Gumbel-top-k (bf16 weights).
-fs_status sample_fused(const fs_bf16* H, const void* W, bool w8, const float* w_scale, int64_t B,
+fs_status sample_fused(const fs_bf16* H, const void* W, int fmt, const void* scale, int64_t B,
                        int64_t D, int64_t V, const float* temp, const float* bias, uint64_t seed,
                        uint64_t offset, int64_t* out_idx, const uint32_t* row_ids, uint32_t flags,
                        void* workspace, size_t workspace_bytes, fs_stream_t stream, int k = 0) {
-  fs_status s = check_fused(H, W, w8, w_scale, B, D, V);
+  fs_status s = check_fused(H, W, fmt, scale, B, D, V);
   if (s != FS_OK) return s;
   if (flags & ~FS_FP64_NOISE) return fail(FS_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (k < 0 || k > fs::kTopKMax)
@@ -172,15 +191,13 @@ fs_status sample_fused(const fs_bf16* H, const void* W, bool w8, const float* w_
   s = device_cus(&cus);
   if (s != FS_OK) return s;
   const int nT = fs::fused_num_tiles(V, cus);
-  s = check_span(V, D, nT, w8);
+  s = check_span(V, D, nT, fmt);
   if (s != FS_OK) return s;
   const bool fp64 = (flags & FS_FP64_NOISE) != 0;
   fs::FusedArgs a;
   memset(&a, 0, sizeof a);
   a.H = H;
-  a.W = w8 ? nullptr : static_cast<const uint16_t*>(W);
-  a.W8 = w8 ? static_cast<const uint8_t*>(W) : nullptr;
-  a.w_scale = w8 ? w_scale : nullptr;
+  set_weights(a, W, fmt, scale);
   a.B = B;
   a.D = D;
   a.V = V;
@@ -206,9 +223,9 @@ fs_status sample_fused(const fs_bf16* H, const void* W, bool w8, const float* w_
   return FS_OK;
 }
 
-fs_status debug_logits(const fs_bf16* H, const void* W, bool w8, const float* w_scale, int64_t B,
+fs_status debug_logits(const fs_bf16* H, const void* W, int fmt, const void* scale, int64_t B,
                        int64_t D, int64_t V, float* Y, fs_stream_t stream) {
-  fs_status s = check_fused(H, W, w8, w_scale, B, D, V);
+  fs_status s = check_fused(H, W, fmt, scale, B, D, V);
   if (s != FS_OK) return s;
   if (B == 0) return FS_OK;
   if (Y == nullptr) return fail(FS_ERR_INVALID_ARG, "Y is null");
@@ -216,14 +233,12 @@ fs_status debug_logits(const fs_bf16* H, const void* W, bool w8, const float* w_
   s = device_cus(&cus);
   if (s != FS_OK) return s;
   const int nT = fs::fused_num_tiles(V, cus);
-  s = check_span(V, D, nT, w8);
+  s = check_span(V, D, nT, fmt);
   if (s != FS_OK) return s;
   fs::FusedArgs a;
   memset(&a, 0, sizeof a);
   a.H = H;
-  a.W = w8 ? nullptr : static_cast<const uint16_t*>(W);
-  a.W8 = w8 ? static_cast<const uint8_t*>(W) : nullptr;
-  a.w_scale = w8 ? w_scale : nullptr;
+  set_weights(a, W, fmt, scale);
   a.B = B;
   a.D = D;
   a.V = V;
@@ -266,7 +281,7 @@ fs_status fs_sample_fused(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t
                           int64_t* out_idx, const uint32_t* row_ids, uint32_t flags,
                           void* workspace, size_t workspace_bytes, fs_stream_t stream) {
   g_last_error[0] = 0;
-  return sample_fused(H, W, false, nullptr, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
+  return sample_fused(H, W, kFmtBf16, nullptr, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
                       flags, workspace, workspace_bytes, stream);
 }
 
@@ -277,8 +292,18 @@ fs_status fs_sample_fused_topk(const fs_bf16* H, const fs_bf16* W, int64_t B, in
                                fs_stream_t stream) {
   g_last_error[0] = 0;
   if (k < 1) return fail(FS_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, fs::kTopKMax);
-  return sample_fused(H, W, false, nullptr, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
+  return sample_fused(H, W, kFmtBf16, nullptr, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
                       flags, workspace, workspace_bytes, stream, k);
+}
+
+fs_status fs_sample_fused_mxfp4(const fs_bf16* H, const uint8_t* W4, const uint8_t* w4_scale,
+                                int64_t B, int64_t D, int64_t V, const float* temp,
+                                const float* bias, uint64_t seed, uint64_t offset,
+                                int64_t* out_idx, const uint32_t* row_ids, uint32_t flags,
+                                void* workspace, size_t workspace_bytes, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  return sample_fused(H, W4, kFmtMxfp4, w4_scale, B, D, V, temp, bias, seed, offset, out_idx,
+                      row_ids, flags, workspace, workspace_bytes, stream);
 }
 
 fs_status fs_sample_fused_w8(const fs_bf16* H, const uint8_t* W8, const float* w_scale, int64_t B,
@@ -287,7 +312,7 @@ fs_status fs_sample_fused_w8(const fs_bf16* H, const uint8_t* W8, const float* w
                              const uint32_t* row_ids, uint32_t flags, void* workspace,
                              size_t workspace_bytes, fs_stream_t stream) {
   g_last_error[0] = 0;
-  return sample_fused(H, W8, true, w_scale, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
+  return sample_fused(H, W8, kFmtFp8, w_scale, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
                       flags, workspace, workspace_bytes, stream);
 }
 
@@ -446,13 +471,19 @@ fs_status fs_debug_noise(const uint32_t* words, int64_t n, int fp64, double* E, 
 fs_status fs_debug_logits(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D, int64_t V,
                           float* Y, fs_stream_t stream) {
   g_last_error[0] = 0;
-  return debug_logits(H, W, false, nullptr, B, D, V, Y, stream);
+  return debug_logits(H, W, kFmtBf16, nullptr, B, D, V, Y, stream);
 }
 
 fs_status fs_debug_logits_w8(const fs_bf16* H, const uint8_t* W8, const float* w_scale, int64_t B,
                              int64_t D, int64_t V, float* Y, fs_stream_t stream) {
   g_last_error[0] = 0;
-  return debug_logits(H, W8, true, w_scale, B, D, V, Y, stream);
+  return debug_logits(H, W8, kFmtFp8, w_scale, B, D, V, Y, stream);
+}
+
+fs_status fs_debug_logits_mxfp4(const fs_bf16* H, const uint8_t* W4, const uint8_t* w4_scale,
+                                int64_t B, int64_t D, int64_t V, float* Y, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  return debug_logits(H, W4, kFmtMxfp4, w4_scale, B, D, V, Y, stream);
 }
 
 }  // extern "C"

@@ -69,6 +69,10 @@ constexpr float kInfTemp = 0x1p60f;  // at or above this, t * g is not kept in t
 
 enum ColMode { kGreedy = 0, kSample = 1, kInfT = 2 };
 
+// Weight formats: bf16, OCP FP8 E4M3 with a float32 scale per row, MXFP4
+// (E2M1 elements, an E8M0 scale per block of 32 along k).
+enum WeightFormat { kWBf16 = 0, kWFp8 = 1, kWFp4 = 2 };
+
 template <int EPI>
 struct ScoreType {
   typedef float type;
@@ -144,52 +148,60 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
 // for 8 MFMAs: 2 row blocks a pass (64 accumulators a lane), two pairs in
 // flight, and H chunks of 128 k.  There the fragment slots that receive the
 // noise are one per (row block, column block).
-template <int NB, int EPI, bool HAS_BIAS, bool W8>
+template <int NB, int EPI, bool HAS_BIAS, int WF>
 struct Pipeline {
+  static constexpr bool narrow = WF != kWBf16;  // FP8 or MXFP4 weights
   // Noise added after the k-loop (float64 noise, Gumbel-top-k): the same
   // register budget as float64 noise.
   static constexpr bool late_noise = EPI == kEpiSample64 || EPI == kEpiTopK32 || EPI == kEpiTopK64;
   static constexpr bool wide = NB > 4;
   static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || late_noise);
-  static constexpr bool ring1 = !W8 && !wide && NB >= 3 && !wide_extra;
+  static constexpr bool ring1 = !narrow && !wide && NB >= 3 && !wide_extra;
   static constexpr int row_blocks = wide ? 2 : ((NB <= 2 || ring1) ? 5 : 3);
   static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || late_noise);
-  static constexpr bool interleave = !W8 && !wide && !wide_extra;
+  static constexpr bool interleave = !narrow && !wide && !wide_extra;
   static constexpr int chunk_k = wide ? 128 : 256;   // k per H chunk in LDS
   // Fragment (rb, cb) gets its noise at k-step noise_slots * rb + cb.
   static constexpr int noise_slots = wide ? NB : 4;
-  static_assert(!(wide && W8), "FP8 weights use batch tiles of at most 64 columns");
+  static_assert(!(wide && narrow), "FP8 and MXFP4 weights use batch tiles of at most 64 columns");
 };
 
 // Whether the noise is folded into the accumulators inside the k-loop: float32
 // noise over bf16 weights is.  Float64 noise, and any noise over FP8 weights
 // (whose per-row scale multiplies the sum only), is added after the k-loop,
 // still in the same pass.
-template <int NB, int EPI, bool HAS_BIAS, bool W8>
+template <int NB, int EPI, bool HAS_BIAS, int WF>
 struct FoldNoise {
-  static constexpr bool value = EPI == kEpiSample32 && !W8;
+  static constexpr bool value = EPI == kEpiSample32 && WF == kWBf16;
 };
 
 // BV4: the bias rows are 16-byte aligned (V % 4 == 0), so a fragment's four
 // biases come in one load.
-template <int NB, int EPI, bool HAS_BIAS, bool W8, bool BV4 = false>
+template <int NB, int EPI, bool HAS_BIAS, int WF, bool BV4 = false>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
-  constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS, W8>::value;
+  constexpr bool W8 = WF == kWFp8, W4 = WF == kWFp4;
+  constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS, WF>::value;
   constexpr bool kTopK = EPI == kEpiTopK32 || EPI == kEpiTopK64;
-  typedef Pipeline<NB, EPI, HAS_BIAS, W8> Pipe;
+  typedef Pipeline<NB, EPI, HAS_BIAS, WF> Pipe;
   // W element bytes, and k per 16-byte lane load (one MFMA k-step of bf16,
   // two of FP8).
-  constexpr int kEB = W8 ? 1 : 2;
-  constexpr int kKPerLoad = W8 ? 64 : 32;
+  // A lane's 16-byte load holds 8 bf16, 16 FP8 or 32 FP4 values of its row;
+  // the four lanes of a row cover kKPerLoad k (one load step).  W is
+  // addressed in units of one element (bf16, FP8) or one byte (MXFP4).
+  constexpr int kKPerLoad = W4 ? 128 : (W8 ? 64 : 32);
+  constexpr int kKPerUnit = W4 ? 2 : 1;
+  constexpr int kLaneUnits = WF == kWBf16 ? 8 : 16;
   constexpr int kKC = Pipe::chunk_k;
   constexpr int kStepsPerChunk = kKC / 32;
   constexpr int kHRow = kKC + kHPad;
   constexpr int kTile = 16 * NB;  // batch columns of the workgroup
   constexpr int kNoiseSlots = Pipe::noise_slots;
   constexpr int kLoadsPerChunk = kKC / kKPerLoad;
-  typedef typename std::conditional<W8, uint8_t, uint16_t>::type WElem;
-  const WElem* const wbase = W8 ? reinterpret_cast<const WElem*>(a.W8) : reinterpret_cast<const WElem*>(a.W);
+  typedef typename std::conditional<WF != kWBf16, uint8_t, uint16_t>::type WElem;
+  const WElem* const wbase = W4   ? reinterpret_cast<const WElem*>(a.W4)
+                             : W8 ? reinterpret_cast<const WElem*>(a.W8)
+                                  : reinterpret_cast<const WElem*>(a.W);
   constexpr int kRB = Pipe::row_blocks;
   constexpr bool kRing1 = Pipe::ring1;
   constexpr bool kInterleave = Pipe::interleave;
@@ -239,7 +251,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   // read in lockstep at one k offset do.
   const int rot = tile % NC;
   // Logical chunk -> the chunk of k it holds.
-  auto phys_chunk = [&](int c) -> int { return c + rot < NC ? c + rot : c + rot - NC; };
+  // (Chunks past the last one, which only MXFP4's two-chunk loop reaches,
+  // stay past it: their H is zero.)
+  auto phys_chunk = [&](int c) -> int { return c >= NC ? c : (c + rot < NC ? c + rot : c + rot - NC); };
 
   // Per-column sampling constants live in LDS (16 bytes a column), read when a
   // fragment is folded or scored; registers hold only each column's running
@@ -344,13 +358,24 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // bytes start 16 * grp bytes into each load step, in both formats.
     const int64_t rbase = nrb_wave > 0 ? r0 : 0;
     const int64_t rlast = nrb_wave > 0 ? r1 - 1 : 0;
-    const WElem* wwave = wbase + rbase * D;
+    const int64_t row_units = D / kKPerUnit;
+    const WElem* wwave = wbase + rbase * row_units;
     uint32_t woff[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       int64_t row = r0 + 16 * (rb_first + rb) + col;
       if (row > rlast) row = rlast;
-      woff[rb] = (uint32_t)((row - rbase) * D + (16 / kEB) * grp);
+      woff[rb] = (uint32_t)((row - rbase) * row_units + kLaneUnits * grp);
+    }
+    // MXFP4: each lane's row's E8M0 scales, D/32 bytes a row; a lane reads the
+    // 4 bytes of a load step's 4 blocks (one per lane of the row).
+    const uint8_t* swave = W4 ? a.w4_scale + rbase * (D / 32) : nullptr;
+    uint32_t soff[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      int64_t row = r0 + 16 * (rb_first + rb) + col;
+      if (row > rlast) row = rlast;
+      soff[rb] = W4 ? (uint32_t)((row - rbase) * (D / 32)) : 0u;
     }
 
     f32x4 acc[kRB][NB];
@@ -444,16 +469,37 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // 64 FP8 values; a step past the last one re-reads the last one.  In a
     // final step that runs past D the lanes past D read k = 0 instead; H is
     // zero there, so their products vanish for finite W.
-    auto step_base = [&](int ls) -> const WElem* {
-      // Logical step (loop order; past the end: the last one) -> k step.
+    // Logical step (loop order; past the end: the last one) -> load step.
+    auto phys_step = [&](int ls) -> int {
       if (ls > NC * kLoadsPerChunk - 1) ls = NC * kLoadsPerChunk - 1;
       ls = phys_chunk(ls / kLoadsPerChunk) * kLoadsPerChunk + ls % kLoadsPerChunk;
-      if (ls > KLS - 1) ls = KLS - 1;
+      return ls > KLS - 1 ? KLS - 1 : ls;
+    };
+    auto step_base = [&](int ls) -> const WElem* {
+      ls = phys_step(ls);
       const int64_t k = (int64_t)ls * kKPerLoad;
       const int kg = (kKPerLoad / 4) * grp;  // the lane's first k
       int64_t kl = 0;
       if (k + kKPerLoad > D) kl = (k + kg < D) ? 0 : -k - kg;
-      return wwave + k + kl;
+      return wwave + (k + kl) / kKPerUnit;
+    };
+    // MXFP4: the W fragments of load steps (2q, 2q + 1) and their scale words,
+    // one 8-byte load for the pair (a 256-k chunk is 8 blocks of a row; D is
+    // a multiple of 256, so a real chunk's two steps are adjacent and a pair
+    // past the end re-reads the last chunk's scales, against zero H).
+    auto load_pair4 = [&](u32x4 (&dst)[2][kRB], uint32_t (&sw)[2][kRB], int q) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const WElem* w0 = step_base(2 * q);
+      const WElem* w1 = step_base(2 * q + 1);
+      const uint8_t* sp = swave + 4 * (phys_step(2 * q) & ~1);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        dst[0][rb] = load_frag(w0 + woff[rb]);
+        dst[1][rb] = load_frag(w1 + woff[rb]);
+        const u32x2 v = *reinterpret_cast<const u32x2*>(sp + soff[rb]);
+        sw[0][rb] = v[0];
+        sw[1][rb] = v[1];
+      }
     };
     auto load_pair = [&](u32x4 (&dst)[2][kRB], int q) {
       const WElem* w0 = step_base(2 * q);
@@ -542,6 +588,38 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         for (int cb = 0; cb < NB; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[rb]), hf[cb], acc[rb][cb], 0, 0, 0);
     };
+    // MXFP4: the eight MFMA k-steps of one load-step pair (a whole 256-k chunk
+    // in buffer buf).  Load step ls of lane group g holds block 4 ls + g, k in
+    // [128 ls + 32 g, +32); its dword i meets H at k = 128 ls + 32 g + 8 i.
+    // v_cvt_scalef32_pk_bf16_fp4 widens two E2M1 values times the block's
+    // scale (a power of two) to bf16: exact while the products stay in bf16's
+    // normal range.
+    auto mma4 = [&](const u32x4 (&w)[2][kRB], const uint32_t (&sw)[2][kRB], int buf) {
+#pragma unroll
+      for (int ls = 0; ls < 2; ++ls)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x8 hf[NB];
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb)
+            hf[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][128 * ls + 32 * grp + 8 * i]);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) {
+            const uint32_t e = (sw[ls][rb] >> (8 * grp)) & 255u;
+            const float sc = __builtin_bit_cast(
+                float, e == 0u ? 0x00400000u : (e == 255u ? 0x7fc00000u : e << 23));
+            const uint32_t d = w[ls][rb][i];
+            const u32x4 v = u32x4{
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3))};
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(v), hf[cb], acc[rb][cb], 0, 0, 0);
+          }
+        }
+    };
     // FP8: the four MFMA k-steps of one load-step pair starting at chunk
     // offset kk.  Load step ls of lane group g holds k in [64 ls + 16 g, +16):
     // its first 8 values meet H at k = kk + 64 ls + 16 g, the next 8 at +8.
@@ -585,6 +663,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     h_load(0, Half1{});
 
     u32x4 pa[2][kRB], pb[2][kRB];
+    uint32_t sa[2][kRB], sb[2][kRB];  // MXFP4 scale words of pa, pb
     const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 ba0 = z4, ba1 = z4, bb0 = z4, bb1 = z4;
     // The prologue issues pair 0 before pair 1, as the loop does: were the
@@ -592,11 +671,17 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // pair 0 as the newest loads, and the compiler would wait for nearly all
     // loads there on every pass.
     __builtin_amdgcn_sched_barrier(0);
-    load_pair(pa, 0);
+    if constexpr (W4)
+      load_pair4(pa, sa, 0);
+    else
+      load_pair(pa, 0);
     bias_slot_load(ba0, 0);
     bias_slot_load(ba1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!kRing1) load_pair(pb, 1);
+    if constexpr (W4)
+      load_pair4(pb, sb, 1);
+    else if constexpr (!kRing1)
+      load_pair(pb, 1);
     bias_slot_load(bb0, 2);
     bias_slot_load(bb1, 3);
     __builtin_amdgcn_sched_barrier(0);
@@ -608,8 +693,37 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // One H chunk per iteration, not unrolled: an unrolled or peeled copy
     // enters the loop with its loads in another order, and the compiler then
     // waits for nearly all loads in flight at the loop head.
+    if constexpr (W4) {
+      // MXFP4: a chunk is one load-step pair; two chunks per iteration (pa in
+      // buffer 0, pb in buffer 1) keep two pairs in flight.  An odd chunk
+      // count gets one empty chunk (zero H) at the end.
+      const int NCe = NC + (NC & 1);
 #pragma unroll 1
-    for (int c = 0; c < NC; ++c) {
+      for (int c = 0; c < NCe; c += 2) {
+        h_load(c + 1, Half0{});
+        h_load(c + 1, Half1{});
+        __builtin_amdgcn_sched_barrier(0);
+        mma4(pa, sa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair4(pa, sa, c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        h_store(1, Half0{});
+        h_store(1, Half1{});
+        __syncthreads();
+        h_load(c + 2, Half0{});
+        h_load(c + 2, Half1{});
+        __builtin_amdgcn_sched_barrier(0);
+        mma4(pb, sb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair4(pb, sb, c + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        h_store(0, Half0{});
+        h_store(0, Half1{});
+        __syncthreads();
+      }
+    }
+#pragma unroll 1
+    for (int c = 0; c < (W4 ? 0 : NC); ++c) {
       const int buf = c & 1;
       const int cn = c + 1 < NC ? c + 1 : c;
       h_load(cn, Half0{});
@@ -1053,62 +1167,63 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 
 // FP8 weights take no bias template: their noise is never folded, and the
 // bias is read after the k-loop whichever way.
-template <int NB, bool W8>
+template <int NB, int WF>
 hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream) {
+  constexpr bool BF = WF == kWBf16;
   switch (epi) {
     case kEpiSample32:
-      if (a.bias && !W8 && a.bias_vec4)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, !W8, W8, !W8>), grid, dim3(kThreads),
+      if (a.bias && BF && a.bias_vec4)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, BF, WF, BF>), grid, dim3(kThreads),
                            0, stream, a);
-      else if (a.bias && !W8)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, !W8, W8>), grid, dim3(kThreads), 0,
+      else if (a.bias && BF)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, BF, WF>), grid, dim3(kThreads), 0,
                            stream, a);
       else
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, false, W8>), grid, dim3(kThreads),
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, false, WF>), grid, dim3(kThreads),
                            0, stream, a);
       break;
     case kEpiSample64:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample64, false, W8>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample64, false, WF>), grid, dim3(kThreads), 0,
                          stream, a);
       break;
     case kEpiTopK32:
       // Gumbel-top-k: tiles of at most 64 columns, bf16 weights.
-      if constexpr (NB <= 4 && !W8)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK32, false, false>), grid, dim3(kThreads),
-                           0, stream, a);
+      if constexpr (NB <= 4 && BF)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK32, false, kWBf16>), grid,
+                           dim3(kThreads), 0, stream, a);
       else
         return hipErrorInvalidValue;
       break;
     case kEpiTopK64:
       // Float64 scores: tiles of 16 or 64 columns (the 32- and 48-column
       // layouts run out of registers).
-      if constexpr ((NB == 1 || NB == 4) && !W8)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK64, false, false>), grid, dim3(kThreads),
-                           0, stream, a);
+      if constexpr ((NB == 1 || NB == 4) && BF)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK64, false, kWBf16>), grid,
+                           dim3(kThreads), 0, stream, a);
       else
         return hipErrorInvalidValue;
       break;
     default:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiStore, false, W8>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiStore, false, WF>), grid, dim3(kThreads), 0,
                          stream, a);
       break;
   }
   return hipGetLastError();
 }
 
-template <bool W8>
+template <int WF>
 hipError_t launch_w(const FusedArgs& a, int epi, dim3 grid, int nb, hipStream_t stream) {
   switch (nb) {
-    case 1: return launch_nb<1, W8>(a, epi, grid, stream);
-    case 2: return launch_nb<2, W8>(a, epi, grid, stream);
-    case 3: return launch_nb<3, W8>(a, epi, grid, stream);
-    default: return launch_nb<4, W8>(a, epi, grid, stream);
+    case 1: return launch_nb<1, WF>(a, epi, grid, stream);
+    case 2: return launch_nb<2, WF>(a, epi, grid, stream);
+    case 3: return launch_nb<3, WF>(a, epi, grid, stream);
+    default: return launch_nb<4, WF>(a, epi, grid, stream);
   }
 }
 
 // Wide batch tiles (128 columns): bf16 weights only.
 hipError_t launch_wide(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream) {
-  return launch_nb<8, false>(a, epi, grid, stream);
+  return launch_nb<8, kWBf16>(a, epi, grid, stream);
 }
 
 }  // namespace
@@ -1137,17 +1252,19 @@ hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) 
     int nb = fused_column_blocks(a.B, true, false);  // tiles of at most 64 columns
     if (epi == kEpiTopK64 && nb > 1) nb = 4;
     const dim3 grid((unsigned)a.nT, (unsigned)((a.B + 16 * nb - 1) / (16 * nb)));
-    return launch_w<false>(a, epi, grid, nb, stream);
+    return launch_w<kWBf16>(a, epi, grid, nb, stream);
   }
-  const int nb = fused_column_blocks(a.B, a.W8 != nullptr, epi == kEpiSample64);
+  const bool narrow = a.W8 != nullptr || a.W4 != nullptr;
+  const int nb = fused_column_blocks(a.B, narrow, epi == kEpiSample64);
   const int64_t tile = 16 * nb;
   const int64_t nbt = (a.B + tile - 1) / tile;
   const dim3 grid((unsigned)a.nT, (unsigned)nbt);
   // Each column's logits come from its own MFMA column, so the tile width
   // does not change any row's arithmetic.
-  if (a.W8) return launch_w<true>(a, epi, grid, nb, stream);
+  if (a.W4) return launch_w<kWFp4>(a, epi, grid, nb, stream);
+  if (a.W8) return launch_w<kWFp8>(a, epi, grid, nb, stream);
   if (nb > 4) return launch_wide(a, epi, grid, stream);
-  return launch_w<false>(a, epi, grid, nb, stream);
+  return launch_w<kWBf16>(a, epi, grid, nb, stream);
 }
 
 int64_t fused_wave_span_bytes(int64_t V, int64_t D, int nT, int elem_bytes) {

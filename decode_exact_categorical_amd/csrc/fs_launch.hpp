@@ -16,6 +16,8 @@ struct FusedArgs {
   const uint16_t* W;  // [V, D] bf16, or null when W8 is given
   const uint8_t* W8;       // [V, D] OCP FP8 E4M3, or null
   const float* w_scale;    // [V] scale per vocabulary row (with W8)
+  const uint8_t* W4;       // [V, D/2] MXFP4 E2M1 codes (element 2j low nibble), or null
+  const uint8_t* w4_scale; // [V, D/32] E8M0 block scales (with W4)
   int64_t B, D, V;
   const float* temp;       // [B]
   const float* bias;       // [B, V] or null
@@ -45,7 +47,7 @@ constexpr int kMaxFusedTiles = 256;
 static_assert(kMaxFusedTiles % 64 == 0, "whole waves of candidates");
 int fused_num_tiles(int64_t V, int num_cus);
 // MFMA column blocks of 16 per batch tile: up to 4 (64 columns) for B <= 64
-// or FP8 weights, else 8 (tiles of 128 columns).
+// or FP8 / MXFP4 weights, else 8 (tiles of 128 columns).
 int fused_column_blocks(int64_t B, bool fp8_weights, bool fp64_noise);
 // Largest byte span of W rows one wave addresses through 32-bit offsets.
 int64_t fused_wave_span_bytes(int64_t V, int64_t D, int nT, int elem_bytes);

@@ -16,6 +16,9 @@
  *   [OFP8] OCP 8-bit Floating Point Specification (OFP8), revision 1.0, the
  *         E4M3 format (FP8 weights: the FlashSampling page's "limitations"
  *         section names low-precision weights as future work).
+ *   [MX]  OCP Microscaling Formats (MX) specification 1.0: MXFP4, blocks of 32
+ *         FP4 E2M1 elements sharing an E8M0 scale (the other low-precision
+ *         weight format the FlashSampling page's "limitations" names).
  *   [GTK] Gumbel-top-k: the FlashSampling page's "limitations" and future
  *         work name the top-k extension (k draws without replacement, the k
  *         largest perturbed scores; its appendix D proves it); the standard
@@ -73,7 +76,7 @@ extern "C" {
 typedef enum fs_status {
     FS_OK = 0,
     FS_ERR_INVALID_ARG = 1, /* null required pointer, non-positive size, V >= 2^31 */
-    FS_ERR_UNSUPPORTED = 2, /* D not a multiple of 8 (16 for FP8 W), H/W not 16-byte aligned,
+    FS_ERR_UNSUPPORTED = 2, /* D not a multiple of 8 (16 FP8, 256 MXFP4), H/W not 16-byte aligned,
                                B > 2^22 or V * D beyond the addressable span (fused) */
     FS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fs_workspace_bytes() */
     FS_ERR_HIP = 4          /* a HIP launch or runtime call failed */
@@ -214,6 +217,31 @@ fs_status fs_sample_logits_topk(const float *logits, int64_t B, int64_t V, const
                                 size_t workspace_bytes, fs_stream_t stream);
 
 /*
+ * Fused LM-head + exact sampling with MXFP4 weights [MX]: row i of the weight
+ * is D FP4 E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa bit:
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives) in blocks of 32 along D, block j
+ * scaled by the E8M0 value 2^(e - 127) of w4_scale[i, j] (e = 255 is NaN).
+ *   W4        device, uint8 [V, D/2]  element d of row i in byte i*D/2 + d/2,
+ *             the low nibble for even d, the high nibble for odd d; 16-byte
+ *             aligned
+ *   w4_scale  device, uint8 [V, D/32] E8M0 block scales, 8-byte aligned
+ *   B, D, V   host sizes: 0 <= B <= 2^22, D >= 256 with D % 256 == 0,
+ *             1 <= V < 2^31
+ *   the other arguments, the workspace and the sampling rule are those of
+ *   fs_sample_fused, with y_i = sum_d H[b,d] * e2m1(W4[i,d]) * 2^(e(i,d/32)-127).
+ * The kernel widens each element times its block scale to bf16 on chip
+ * (exact while the scaled values stay in bf16's normal range: the caller
+ * keeps 2^(e - 127) * 6 below 2^128 and 2^(e - 127) * 0.5 at least 2^-126)
+ * and runs the bf16 MFMA contraction with float32 accumulation.  W crosses
+ * HBM at half a byte per element plus one byte of scale per 32 elements.
+ */
+fs_status fs_sample_fused_mxfp4(const fs_bf16 *H, const uint8_t *W4, const uint8_t *w4_scale,
+                                int64_t B, int64_t D, int64_t V, const float *temp,
+                                const float *bias, uint64_t seed, uint64_t offset,
+                                int64_t *out_idx, const uint32_t *row_ids, uint32_t flags,
+                                void *workspace, size_t workspace_bytes, fs_stream_t stream);
+
+/*
  * Gumbel-top-k fused into the LM head [GTK; FS "algorithm details"]: the
  * places of the k largest perturbed scores of fs_sample_fused's rule (same
  * logits, transform, noise stream and keys), largest first; equal scores in
@@ -236,7 +264,8 @@ fs_status fs_sample_fused_topk(const fs_bf16 *H, const fs_bf16 *W, int64_t B, in
 
 /*
  * Kernel timing.  Between fs_profile_begin() and fs_profile_end(), every
- * fs_sample_fused, fs_sample_fused_w8 and fs_sample_logits call also records
+ * fs_sample_fused, fs_sample_fused_w8, fs_sample_fused_mxfp4 and
+ * fs_sample_logits call (and their top-k forms) also records
  * HIP events on its stream around its one launch (Stage 1 with Stage 2 in its
  * last workgroups; the FlashSampling page, "reproduction", times kernels the
  * same way: device timestamps per kernel).  fs_profile_end() waits for those
@@ -293,6 +322,14 @@ fs_status fs_debug_logits(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t
  */
 fs_status fs_debug_logits_w8(const fs_bf16 *H, const uint8_t *W8, const float *w_scale,
                              int64_t B, int64_t D, int64_t V, float *Y, fs_stream_t stream);
+
+/*
+ * Test hook: the logits of the MXFP4 path, written to Y (device, float
+ * [B, V]); the twin of fs_debug_logits for fs_sample_fused_mxfp4, with its
+ * size and alignment rules.
+ */
+fs_status fs_debug_logits_mxfp4(const fs_bf16 *H, const uint8_t *W4, const uint8_t *w4_scale,
+                                int64_t B, int64_t D, int64_t V, float *Y, fs_stream_t stream);
 
 #ifdef __cplusplus
 }

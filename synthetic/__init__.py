@@ -53,6 +53,7 @@ def weight_fp8(V: int, D: int, std: float, seed: int = SEED_W, chunk_rows: int =
 
 
 _E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MID = ((_E2M1[1:] + _E2M1[:-1]) / 2).astype(np.float32)
 
 
 def weight_mxfp4(V: int, D: int, std: float, seed: int = SEED_W, chunk_rows: int = 4096):
@@ -67,19 +68,20 @@ def weight_mxfp4(V: int, D: int, std: float, seed: int = SEED_W, chunk_rows: int
     W4 = np.empty((V, D // 2), dtype=np.uint8)
     S = np.empty((V, D // 32), dtype=np.uint8)
     g = _gen(seed)
-    odd = np.arange(8) % 2
     for r0 in range(0, V, chunk_rows):
         r1 = min(V, r0 + chunk_rows)
-        w = (torch.randn((r1 - r0, D), generator=g) * std).numpy().astype(np.float64)
+        w = (torch.randn((r1 - r0, D), generator=g) * std).numpy()      # float32
         blk = w.reshape(r1 - r0, D // 32, 32)
-        amax = np.abs(blk).max(axis=2)
+        amax = np.abs(blk).max(axis=2).astype(np.float64)
         X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
         X = np.clip(X, -127, 127).astype(np.int64)
-        x = blk / np.ldexp(1.0, X)[..., None]
+        x = blk * np.ldexp(np.float32(1.0), -X).astype(np.float32)[..., None]   # exact
         mag = np.abs(x).reshape(-1)
-        d = np.abs(mag[:, None] - _E2M1[None, :])
-        tie = d == d.min(axis=1, keepdims=True)
-        code = np.argmin(np.where(tie, odd[None, :], 9), axis=1).astype(np.uint8)
+        # nearest E2M1 magnitude: count the midpoints at or below; on a tie
+        # (exactly a midpoint) take the even code
+        code = np.searchsorted(_E2M1_MID, mag, side="right")
+        tie = (code > 0) & (mag == _E2M1_MID[np.maximum(code - 1, 0)])
+        code = np.where(tie & (code % 2 == 1), code - 1, code).astype(np.uint8)
         code |= (np.signbit(x.reshape(-1)) & (code > 0)).astype(np.uint8) << 3
         code = code.reshape(r1 - r0, D)
         W4[r0:r1] = code[:, 0::2] | (code[:, 1::2] << 4)
