@@ -167,12 +167,13 @@ struct Pipeline {
 };
 
 // Whether the noise is folded into the accumulators inside the k-loop: float32
-// noise over bf16 weights is.  Float64 noise, and any noise over FP8 weights
-// (whose per-row scale multiplies the sum only), is added after the k-loop,
-// still in the same pass.
+// noise over bf16 and MXFP4 weights is (MXFP4's block scales are applied as
+// the elements are widened, so the accumulator holds the logit itself).
+// Float64 noise, and any noise over FP8 weights (whose per-row scale
+// multiplies the sum only), is added after the k-loop, still in the same pass.
 template <int NB, int EPI, bool HAS_BIAS, int WF>
 struct FoldNoise {
-  static constexpr bool value = EPI == kEpiSample32 && WF == kWBf16;
+  static constexpr bool value = EPI == kEpiSample32 && WF != kWFp8;
 };
 
 // BV4: the bias rows are 16-byte aligned (V % 4 == 0), so a fragment's four
@@ -696,7 +697,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     if constexpr (W4) {
       // MXFP4: a chunk is one load-step pair; two chunks per iteration (pa in
       // buffer 0, pb in buffer 1) keep two pairs in flight.  An odd chunk
-      // count gets one empty chunk (zero H) at the end.
+      // count gets one empty chunk (zero H) at the end.  Noise slots 2c and
+      // 2c + 1 are folded after chunk c, their biases loaded a chunk ahead.
       const int NCe = NC + (NC & 1);
 #pragma unroll 1
       for (int c = 0; c < NCe; c += 2) {
@@ -704,8 +706,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         h_load(c + 1, Half1{});
         __builtin_amdgcn_sched_barrier(0);
         mma4(pa, sa, 0);
+        FS_FOLD_SLOT(2 * c, ba0);
+        FS_FOLD_SLOT(2 * c + 1, ba1);
         __builtin_amdgcn_sched_barrier(0);
         load_pair4(pa, sa, c + 2);
+        bias_slot_load(ba0, 2 * c + 4);
+        bias_slot_load(ba1, 2 * c + 5);
         __builtin_amdgcn_sched_barrier(0);
         h_store(1, Half0{});
         h_store(1, Half1{});
@@ -714,8 +720,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         h_load(c + 2, Half1{});
         __builtin_amdgcn_sched_barrier(0);
         mma4(pb, sb, 1);
+        FS_FOLD_SLOT(2 * c + 2, bb0);
+        FS_FOLD_SLOT(2 * c + 3, bb1);
         __builtin_amdgcn_sched_barrier(0);
         load_pair4(pb, sb, c + 3);
+        bias_slot_load(bb0, 2 * c + 6);
+        bias_slot_load(bb1, 2 * c + 7);
         __builtin_amdgcn_sched_barrier(0);
         h_store(0, Half0{});
         h_store(0, Half1{});
@@ -811,8 +821,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       }
       __syncthreads();
     }
-    // Short contractions (fewer than kRB * 4 k-steps): the remaining slots.
-    for (int f = NC * kStepsPerChunk; f < kRB * kNoiseSlots; ++f) {
+    // Short contractions (fewer k-steps, or MXFP4 chunks, than slots): the
+    // remaining slots.
+    for (int f = W4 ? 2 * (NC + (NC & 1)) : NC * kStepsPerChunk; f < kRB * kNoiseSlots; ++f) {
       f32x4 bt = f32x4{0.f, 0.f, 0.f, 0.f};
       bias_slot_load(bt, f);
       FS_FOLD_SLOT(f, bt);
@@ -1166,17 +1177,19 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 }
 
 // FP8 weights take no bias template: their noise is never folded, and the
-// bias is read after the k-loop whichever way.
+// bias is read after the k-loop whichever way.  bf16 and MXFP4 weights fold
+// the bias with the float32 noise.
 template <int NB, int WF>
 hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream) {
   constexpr bool BF = WF == kWBf16;
+  constexpr bool FB = WF != kWFp8;
   switch (epi) {
     case kEpiSample32:
-      if (a.bias && BF && a.bias_vec4)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, BF, WF, BF>), grid, dim3(kThreads),
+      if (a.bias && FB && a.bias_vec4)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, FB, WF, FB>), grid, dim3(kThreads),
                            0, stream, a);
-      else if (a.bias && BF)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, BF, WF>), grid, dim3(kThreads), 0,
+      else if (a.bias && FB)
+        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, FB, WF>), grid, dim3(kThreads), 0,
                            stream, a);
       else
         hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, false, WF>), grid, dim3(kThreads),

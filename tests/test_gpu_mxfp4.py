@@ -37,10 +37,13 @@ def _codes(W4):
 
 def test_mxfp4_decode_every_code_exact(dev):
     V, D = 16, 256
-    say("mxfp4 decode of every code in both nibbles, power-of-two block scales")
+    say("mxfp4 decode of every code in both nibbles, block scales 2^-125 to 2^125")
     codes = (np.arange(D)[None, :] + np.arange(V)[:, None]) % 16
     W4 = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    S = (127 + (np.arange(V)[:, None] + np.arange(D // 32)[None, :]) % 7 - 3).astype(np.uint8)
+    # block scales from both ends of the range the widening keeps exact (every
+    # scaled value a normal bf16 number: codes 2 to 252) and around 1
+    codes_e = np.array([2, 3, 60, 124, 125, 126, 127, 128, 129, 130, 200, 250, 252])
+    S = codes_e[(np.arange(V)[:, None] + np.arange(D // 32)[None, :]) % len(codes_e)].astype(np.uint8)
     H = torch.eye(D, dtype=torch.float32).to(torch.bfloat16)        # B = D one-hot rows
     Y = fs.debug_logits_mxfp4(H.to(dev), torch.from_numpy(W4).to(dev), torch.from_numpy(S).to(dev))
     torch.cuda.synchronize()
