@@ -160,7 +160,13 @@ struct Pipeline {
   static constexpr int row_blocks = wide ? 2 : ((NB <= 2 || ring1) ? 5 : 3);
   static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || late_noise);
   static constexpr bool interleave = !narrow && !wide && !wide_extra;
-  static constexpr int chunk_k = wide ? 128 : 256;   // k per H chunk in LDS
+  // k per H chunk in LDS.  MXFP4 at 16 and 32 columns takes chunks of two
+  // load-step pairs (512 k), as FP8's 256-k chunks are: one barrier per four
+  // 16-byte loads of a row (measured 5 us faster there; with 3-row-block
+  // passes, and at 32 columns with a bias or float64 noise, whose registers
+  // it overflows, 256-k chunks of one pair each are faster).
+  static constexpr bool w4_long = WF == kWFp4 && (NB == 1 || (NB == 2 && !HAS_BIAS && !late_noise));
+  static constexpr int chunk_k = wide ? 128 : (w4_long ? 512 : 256);
   // Fragment (rb, cb) gets its noise at k-step noise_slots * rb + cb.
   static constexpr int noise_slots = wide ? NB : 4;
   static_assert(!(wide && narrow), "FP8 and MXFP4 weights use batch tiles of at most 64 columns");
@@ -251,9 +257,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   // the chip's concurrent W requests over more of the HBM channels than rows
   // read in lockstep at one k offset do.
   const int rot = tile % NC;
-  // Logical chunk -> the chunk of k it holds.
-  // (Chunks past the last one, which only MXFP4's two-chunk loop reaches,
-  // stay past it: their H is zero.)
+  // Logical chunk -> the chunk of k it holds.  (Chunks past the last one,
+  // which only MXFP4's two-chunk loop reaches, stay past it: their H is zero.)
   auto phys_chunk = [&](int c) -> int { return c >= NC ? c : (c + rot < NC ? c + rot : c + rot - NC); };
 
   // Per-column sampling constants live in LDS (16 bytes a column), read when a
@@ -485,9 +490,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       return wwave + (k + kl) / kKPerUnit;
     };
     // MXFP4: the W fragments of load steps (2q, 2q + 1) and their scale words,
-    // one 8-byte load for the pair (a 256-k chunk is 8 blocks of a row; D is
-    // a multiple of 256, so a real chunk's two steps are adjacent and a pair
-    // past the end re-reads the last chunk's scales, against zero H).
+    // one 8-byte load for the pair (a pair's 256 k are 8 blocks of a row; D is
+    // a multiple of 256, so a pair inside D starts at an even step, and a pair
+    // past D re-reads the last pair's scales, against zero H).
     auto load_pair4 = [&](u32x4 (&dst)[2][kRB], uint32_t (&sw)[2][kRB], int q) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       const WElem* w0 = step_base(2 * q);
@@ -589,13 +594,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         for (int cb = 0; cb < NB; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(w[rb]), hf[cb], acc[rb][cb], 0, 0, 0);
     };
-    // MXFP4: the eight MFMA k-steps of one load-step pair (a whole 256-k chunk
-    // in buffer buf).  Load step ls of lane group g holds block 4 ls + g, k in
-    // [128 ls + 32 g, +32); its dword i meets H at k = 128 ls + 32 g + 8 i.
+    // MXFP4: the eight MFMA k-steps of one load-step pair (256 k from chunk
+    // offset kk in buffer buf).  Load step ls of lane group g holds block
+    // 4 ls + g, k in [kk + 128 ls + 32 g, +32); its dword i meets H at
+    // k = kk + 128 ls + 32 g + 8 i.
     // v_cvt_scalef32_pk_bf16_fp4 widens two E2M1 values times the block's
     // scale (a power of two) to bf16: exact while the products stay in bf16's
     // normal range.
-    auto mma4 = [&](const u32x4 (&w)[2][kRB], const uint32_t (&sw)[2][kRB], int buf) {
+    auto mma4 = [&](const u32x4 (&w)[2][kRB], const uint32_t (&sw)[2][kRB], int buf, int kk) {
 #pragma unroll
       for (int ls = 0; ls < 2; ++ls)
 #pragma unroll
@@ -603,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           bf16x8 hf[NB];
 #pragma unroll
           for (int cb = 0; cb < NB; ++cb)
-            hf[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][128 * ls + 32 * grp + 8 * i]);
+            hf[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 128 * ls + 32 * grp + 8 * i]);
 #pragma unroll
           for (int rb = 0; rb < kRB; ++rb) {
             const uint32_t e = (sw[ls][rb] >> (8 * grp)) & 255u;
@@ -694,18 +700,19 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // One H chunk per iteration, not unrolled: an unrolled or peeled copy
     // enters the loop with its loads in another order, and the compiler then
     // waits for nearly all loads in flight at the loop head.
-    if constexpr (W4) {
-      // MXFP4: a chunk is one load-step pair; two chunks per iteration (pa in
-      // buffer 0, pb in buffer 1) keep two pairs in flight.  An odd chunk
-      // count gets one empty chunk (zero H) at the end.  Noise slots 2c and
-      // 2c + 1 are folded after chunk c, their biases loaded a chunk ahead.
+    if constexpr (W4 && !Pipe::w4_long) {
+      // MXFP4 in 256-k chunks: a chunk is one load-step pair; two chunks per
+      // iteration (pa in buffer 0, pb in buffer 1) keep two pairs in flight.
+      // An odd chunk count gets one empty chunk (zero H) at the end.  Noise
+      // slots 2c and 2c + 1 are folded after chunk c, their biases loaded a
+      // chunk ahead.
       const int NCe = NC + (NC & 1);
 #pragma unroll 1
       for (int c = 0; c < NCe; c += 2) {
         h_load(c + 1, Half0{});
         h_load(c + 1, Half1{});
         __builtin_amdgcn_sched_barrier(0);
-        mma4(pa, sa, 0);
+        mma4(pa, sa, 0, 0);
         FS_FOLD_SLOT(2 * c, ba0);
         FS_FOLD_SLOT(2 * c + 1, ba1);
         __builtin_amdgcn_sched_barrier(0);
@@ -719,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         h_load(c + 2, Half0{});
         h_load(c + 2, Half1{});
         __builtin_amdgcn_sched_barrier(0);
-        mma4(pb, sb, 1);
+        mma4(pb, sb, 1, 0);
         FS_FOLD_SLOT(2 * c + 2, bb0);
         FS_FOLD_SLOT(2 * c + 3, bb1);
         __builtin_amdgcn_sched_barrier(0);
@@ -733,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       }
     }
 #pragma unroll 1
-    for (int c = 0; c < (W4 ? 0 : NC); ++c) {
+    for (int c = 0; c < ((W4 && !Pipe::w4_long) ? 0 : NC); ++c) {
       const int buf = c & 1;
       const int cn = c + 1 < NC ? c + 1 : c;
       h_load(cn, Half0{});
@@ -752,6 +759,35 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         mma8(pb, buf, 128);
         __builtin_amdgcn_sched_barrier(0);
         load_pair(pb, 2 * c + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        h_store(buf ^ 1, Half0{});
+        h_store(buf ^ 1, Half1{});
+        __syncthreads();
+        continue;
+      }
+      if constexpr (W4) {
+        // MXFP4 in 512-k chunks: a chunk is two load-step pairs, 2c (pa) and 2c + 1
+        // (pb), with H loaded and stored as for FP8.  Noise slots 4c + j are
+        // folded two per pair, their biases loaded a chunk ahead.  When D is
+        // an odd multiple of 256 the last chunk's second pair lies past D: it
+        // re-reads the last load step against zero H.
+        h_load(cn, Half1{});
+        __builtin_amdgcn_sched_barrier(0);
+        mma4(pa, sa, buf, 0);
+        FS_FOLD_SLOT(4 * c, ba0);
+        FS_FOLD_SLOT(4 * c + 1, ba1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair4(pa, sa, 2 * c + 2);
+        bias_slot_load(ba0, 4 * c + 4);
+        bias_slot_load(ba1, 4 * c + 5);
+        __builtin_amdgcn_sched_barrier(0);
+        mma4(pb, sb, buf, 256);
+        FS_FOLD_SLOT(4 * c + 2, bb0);
+        FS_FOLD_SLOT(4 * c + 3, bb1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair4(pb, sb, 2 * c + 3);
+        bias_slot_load(bb0, 4 * c + 6);
+        bias_slot_load(bb1, 4 * c + 7);
         __builtin_amdgcn_sched_barrier(0);
         h_store(buf ^ 1, Half0{});
         h_store(buf ^ 1, Half1{});
@@ -823,7 +859,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
     // Short contractions (fewer k-steps, or MXFP4 chunks, than slots): the
     // remaining slots.
-    for (int f = W4 ? 2 * (NC + (NC & 1)) : NC * kStepsPerChunk; f < kRB * kNoiseSlots; ++f) {
+    for (int f = !W4 ? NC * kStepsPerChunk : (Pipe::w4_long ? 4 * NC : 2 * (NC + (NC & 1)));
+         f < kRB * kNoiseSlots; ++f) {
       f32x4 bt = f32x4{0.f, 0.f, 0.f, 0.f};
       bias_slot_load(bt, f);
       FS_FOLD_SLOT(f, bt);

@@ -6,8 +6,9 @@ of 32 along D) against the oracle, through the C ABI.
   scale bit for bit, for every code in both nibble positions.
 * Logits within 2e-3 of the oracle's float64 logits; sampled indices equal
   the oracle's on every row whose top-2 perturbed-score gap exceeds 1e-3, for
-  every batch width, with and without a bias, an odd number of 256-k chunks,
-  several passes per wave, float32 and float64 noise.
+  every batch width, with and without a bias, D an odd multiple of 256 (in
+  both the 256-k and the 512-k chunk layouts), several passes per wave,
+  float32 and float64 noise.
 * Float64 noise: the fused draw equals the standalone sampler's over the
   path's own float32 logits, bit for bit.
 * Full size: the Qwen3-8B-shaped head (D = 4096, V = 151936) in MXFP4,
@@ -60,6 +61,7 @@ LOGIT_SHAPES = [
     (70, 768, 777),        # an odd number of 256-k chunks, two batch tiles
     (16, 4096, 2000),
     (1, 256, 5),
+    (32, 768, 3000),       # 32 columns in 512-k chunks, the last one half past D
 ]
 
 
@@ -98,6 +100,8 @@ MXFP4_CASES = [
     dict(B=64, D=512, V=3001),
     dict(B=64, D=256, V=170001, greedy_rows=(2, 40)),
     dict(B=20, D=256, V=170001, bias=True),
+    dict(B=30, D=768, V=4099, greedy_rows=(4,)),    # 512-k chunks, the last one half past D
+    dict(B=9, D=1280, V=2048, bias=True),           # 16 columns, bias, 512-k chunks
 ]
 
 
