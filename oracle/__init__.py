@@ -96,6 +96,14 @@ def _load():
         lib.oracle_sample_repeated_row.restype = None
         lib.oracle_sample_repeated_row.argtypes = [P, i64, ctypes.c_float, u64, u64, P,
                                                    i64, i32, P, P]
+        lib.oracle_filter_kept.restype = None
+        lib.oracle_filter_kept.argtypes = [P, i64, i64, P, P, P, P, P, P]
+        lib.oracle_sample_logits_filtered.restype = None
+        lib.oracle_sample_logits_filtered.argtypes = [P, i64, i64, P, P, P, P, u64, u64, P, i32,
+                                                      P, P, P]
+        lib.oracle_filtered_repeated_row.restype = None
+        lib.oracle_filtered_repeated_row.argtypes = [P, i64, ctypes.c_float, i32, ctypes.c_float,
+                                                     ctypes.c_float, u64, u64, P, i64, i32, P]
         _lib = lib
         return lib
 
@@ -373,3 +381,62 @@ def sample_repeated_row(row_f32, temp: float, *, seed: int, offset: int, row_ids
                                        _ptr(rid), rid.shape[0], int(fp64_noise), _ptr(out),
                                        _ptr(gap))
     return (out, gap) if with_gap else out
+
+
+def _filter_args(B, top_k, top_p, min_p):
+    """Per-row filter arrays (or None when a filter is off for every row)."""
+    def arr(v, dt):
+        if v is None:
+            return None
+        a = np.asarray(v, dtype=dt)
+        if a.ndim == 0:
+            a = np.full(B, a, dtype=dt)
+        a = np.ascontiguousarray(a.reshape(B))
+        return a
+    return arr(top_k, np.int32), arr(top_p, np.float32), arr(min_p, np.float32)
+
+
+def filter_kept(logits_f32, temp, *, top_k=None, top_p=None, min_p=None):
+    """(kept bool[B, V], margin float64[B]): the kept set of the filter chain
+    temperature -> top-k -> top-p -> min-p on each row, and each row's smallest
+    relative distance of a top-p or min-p decision from its boundary.  top_k,
+    top_p, min_p: a scalar for every row, a per-row array, or None (off)."""
+    x = np.ascontiguousarray(np.asarray(logits_f32, dtype=np.float32))
+    B, V = x.shape
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    k, p, m = _filter_args(B, top_k, top_p, min_p)
+    kept = np.zeros((B, V), dtype=np.uint8)
+    margin = np.zeros(B, dtype=np.float64)
+    _load().oracle_filter_kept(_ptr(x), B, V, _ptr(t), _ptr(k), _ptr(p), _ptr(m), _ptr(kept),
+                               _ptr(margin))
+    return kept.astype(bool), margin
+
+
+def sample_logits_filtered(logits_f32, temp, *, top_k=None, top_p=None, min_p=None, seed: int,
+                           offset: int, row_ids=None, fp64_noise: bool = False):
+    """(idx, gap, margin): filtered exact sampling over float32 logits[B,V]."""
+    x = np.ascontiguousarray(np.asarray(logits_f32, dtype=np.float32))
+    B, V = x.shape
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    k, p, m = _filter_args(B, top_k, top_p, min_p)
+    rid = _u32_or_none(row_ids, B)
+    idx = np.zeros(B, dtype=np.int64)
+    gap = np.zeros(B, dtype=np.float64)
+    margin = np.zeros(B, dtype=np.float64)
+    _load().oracle_sample_logits_filtered(_ptr(x), B, V, _ptr(t), _ptr(k), _ptr(p), _ptr(m),
+                                          seed, offset, _ptr(rid), int(fp64_noise), _ptr(idx),
+                                          _ptr(gap), _ptr(margin))
+    return idx, gap, margin
+
+
+def filtered_repeated_row(row_f32, temp: float, *, top_k: int = 0, top_p: float = 1.0,
+                          min_p: float = 0.0, seed: int, offset: int, row_ids,
+                          fp64_noise: bool = False):
+    """Filtered draws of many logical rows that all carry the logits row_f32[V]."""
+    x = np.ascontiguousarray(np.asarray(row_f32, dtype=np.float32).reshape(-1))
+    rid = np.ascontiguousarray(np.asarray(row_ids, dtype=np.uint32).reshape(-1))
+    out = np.zeros(rid.shape[0], dtype=np.int64)
+    _load().oracle_filtered_repeated_row(_ptr(x), x.shape[0], float(temp), int(top_k),
+                                         float(top_p), float(min_p), seed, offset, _ptr(rid),
+                                         rid.shape[0], int(fp64_noise), _ptr(out))
+    return out

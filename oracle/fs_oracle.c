@@ -35,6 +35,13 @@
  *         the k largest perturbed scores, proved in its appendix D); the
  *         result is the standard one of Kool, van Hoof and Welling, "Stochastic
  *         Beams and Where to Find Them", ICML 2019, section 3.
+ *   [SD]  spec-decode-ops kernel card: the description of its `sample`
+ *         pipeline (temperature -> top-k -> top-p -> min-p -> Gumbel-argmax
+ *         draw) and its "Semantics" section (the transformers processors'
+ *         order and boundaries: top-p keeps the smallest sorted prefix whose
+ *         probability reaches top_p, the crossing token included, over the
+ *         top-k prefix; min-p keeps p >= min_p * p_max; every filter keeps at
+ *         least one token).
  *
  * Definition computed (per batch row b, logical row id r = row_ids[b] or b):
  *   y_i   = sum_d H[b,d] * W[i,d]           float64, d ascending   [FS (1)]
@@ -54,6 +61,9 @@
  *   top-k (k draws without replacement) [GTK]: the indices of the k largest
  *         valid s_i, largest first, equal scores in increasing index order;
  *         -1 in the places past the number of valid scores.
+ *   filtered sampling [SD]: the draw above restricted to the kept set of
+ *         the filter chain on the row's logits (oracle_filter_kept below);
+ *         tokens outside it score -inf.
  *
  * Parity pins (tests marked "not gpu"): the Philox words against an
  * independent engine (the one PyTorch ships as a header); the uniform, E and
@@ -598,4 +608,199 @@ void oracle_sample_repeated_row(const float *logits, int64_t V, float temp,
         }
         free(s);
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* Filtered exact sampling [SD sample pipeline and Semantics].          */
+/* ------------------------------------------------------------------ */
+
+/* A logit and its index; sorted by value descending, ties in increasing
+ * index order. */
+typedef struct {
+    float v;
+    int64_t i;
+} vi_t;
+static int cmp_desc(const void *pa, const void *pb)
+{
+    const vi_t *a = (const vi_t *)pa, *b = (const vi_t *)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->i > b->i) - (a->i < b->i);
+}
+
+/* The kept set of one row of logits y[0..V) under temperature t and the
+ * filters top_k (off when k <= 0 or k >= the number of valid tokens), top_p
+ * (off when p >= 1 or NaN) and min_p (off when m <= 0 or NaN), applied in
+ * that order [SD].  Valid tokens are those whose logit is neither NaN nor
+ * -inf; no other token is ever kept.
+ *   probabilities: softmax of y/t over the tokens a filter sees, written
+ *     through the masses e_i = exp((y_i - M)/t) with M = the row's largest
+ *     valid logit (e = 1 on a +inf logit and 0 on the others when M = +inf);
+ *   top-k: the tokens whose logit is at least the k-th largest valid logit
+ *     (a tie at the k-th value keeps the whole tie class);
+ *   top-p: over the top-k survivors, a token is kept when the probability of
+ *     the strictly larger survivors is below p (the prefix up to and including
+ *     the crossing token; equal logits are kept or dropped together);
+ *   min-p: over the top-p survivors, a token is kept when e_i >= m, i.e.
+ *     p_i >= m * p_max (renormalising does not change that ratio);
+ *   each filter that would keep nothing keeps the largest logit's tie class.
+ * Greedy rows (!(t > 0)) keep the largest logit's tie class: their draw is the
+ * argmax whatever the filters.  Returns the kept mask and *margin, the
+ * smallest distance of a top-p or min-p decision from its boundary (relative:
+ * |A - pZ| / Z for top-p, |e_i - m| / m for min-p; +inf when neither decides
+ * anything), so that a comparison with another implementation can set aside
+ * the rows whose kept set rounding may decide. */
+static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
+                       float m, vi_t *order, double *e, uint8_t *kept,
+                       double *margin)
+{
+    int64_t n = 0;
+    for (int64_t i = 0; i < V; ++i) {
+        kept[i] = 0;
+        if (!isnan(y[i]) && y[i] != -INFINITY) {
+            order[n].v = y[i];
+            order[n].i = i;
+            ++n;
+        }
+    }
+    *margin = INFINITY;
+    if (n == 0) return;
+    qsort(order, (size_t)n, sizeof(vi_t), cmp_desc);
+    const double M = (double)order[0].v;
+    /* the largest logit's tie class: order[0 .. nmax) */
+    int64_t nmax = 1;
+    while (nmax < n && order[nmax].v == order[0].v) ++nmax;
+    if (!(t > 0.0)) {
+        for (int64_t j = 0; j < nmax; ++j) kept[order[j].i] = 1;
+        return;
+    }
+    for (int64_t j = 0; j < n; ++j) {
+        double v = (double)order[j].v;
+        if (M == INFINITY) e[j] = (v == INFINITY) ? 1.0 : 0.0;
+        else e[j] = exp((v - M) / t);
+    }
+    /* top-k: survivors order[0 .. n1) */
+    int64_t n1 = n;
+    if (k > 0 && (int64_t)k < n) {
+        const float theta = order[k - 1].v;
+        n1 = k;
+        while (n1 < n && order[n1].v == theta) ++n1;
+    }
+    /* top-p over the top-k survivors: order[0 .. n2) */
+    int64_t n2 = n1;
+    if (p < 1.0f) {                       /* NaN compares false: off */
+        double Z = 0.0;
+        for (int64_t j = 0; j < n1; ++j) Z += e[j];
+        const double target = (double)p * Z;
+        double above = 0.0;               /* mass of strictly larger logits */
+        n2 = 0;
+        int64_t j = 0;
+        while (j < n1) {
+            int64_t j2 = j + 1;           /* the tie class order[j .. j2) */
+            double cls = e[j];
+            while (j2 < n1 && order[j2].v == order[j].v) cls += e[j2++];
+            double d = fabs(above - target) / Z;
+            if (d < *margin) *margin = d;
+            if (!(above < target)) break;
+            n2 = j2;
+            above += cls;
+            j = j2;
+        }
+        if (n2 == 0) n2 = nmax;
+    }
+    /* min-p over the top-p survivors */
+    int64_t n3 = 0;
+    if (m > 0.0f) {                       /* NaN compares false: off */
+        for (int64_t j = 0; j < n2; ++j) {
+            double d = fabs(e[j] - (double)m) / (double)m;
+            if (d < *margin) *margin = d;
+            if (e[j] >= (double)m) {
+                kept[order[j].i] = 1;
+                ++n3;
+            }
+        }
+        if (n3 == 0)
+            for (int64_t j = 0; j < nmax; ++j) kept[order[j].i] = 1;
+    } else {
+        for (int64_t j = 0; j < n2; ++j) kept[order[j].i] = 1;
+    }
+}
+
+/* Kept sets of logits[B,V] (see filter_row): kept[B,V] (1 = kept) and
+ * margin[B].  top_k, top_p, min_p are per-row arrays or NULL (off). */
+void oracle_filter_kept(const float *logits, int64_t B, int64_t V, const float *temp,
+                        const int32_t *top_k, const float *top_p, const float *min_p,
+                        uint8_t *kept, double *margin)
+{
+    #pragma omp parallel
+    {
+        vi_t *order = (vi_t *)malloc((size_t)(V > 0 ? V : 1) * sizeof(vi_t));
+        double *e = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+        #pragma omp for schedule(dynamic)
+        for (int64_t b = 0; b < B; ++b)
+            filter_row(logits + b * V, V, (double)temp[b], top_k ? top_k[b] : 0,
+                       top_p ? top_p[b] : 1.0f, min_p ? min_p[b] : 0.0f, order, e,
+                       kept + b * V, &margin[b]);
+        free(e);
+        free(order);
+    }
+}
+
+/* Filtered exact sampling over float32 logits[B,V] [SD; FS prerequisites]:
+ * the kept set of oracle_filter_kept, then the standalone sampler's noise,
+ * transform and selection over the kept tokens only (the others score -inf).
+ * Outputs per row: the sampled index (-1 if none), the top-2 gap of the kept
+ * perturbed scores, and the filter margin. */
+void oracle_sample_logits_filtered(const float *logits, int64_t B, int64_t V,
+                                   const float *temp, const int32_t *top_k,
+                                   const float *top_p, const float *min_p,
+                                   uint64_t seed, uint64_t offset,
+                                   const uint32_t *row_ids, int fp64_noise,
+                                   int64_t *out_idx, double *out_gap,
+                                   double *out_margin)
+{
+    uint8_t *kept = (uint8_t *)malloc((size_t)(B * V > 0 ? B * V : 1));
+    double *s = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    oracle_filter_kept(logits, B, V, temp, top_k, top_p, min_p, kept, out_margin);
+    for (int64_t b = 0; b < B; ++b) {
+        uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        double t = (double)temp[b], best;
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i)
+            s[i] = kept[b * V + i]
+                       ? score_of((double)logits[b * V + i], 0.0, t, seed, offset, r, i,
+                                  fp64_noise)
+                       : -INFINITY;
+        select_row(s, V, &out_idx[b], &out_gap[b], &best);
+    }
+    free(s);
+    free(kept);
+}
+
+/* Filtered draws for many logical rows sharing one logits row (law tests):
+ * the kept set once, then one draw per logical row id. */
+void oracle_filtered_repeated_row(const float *logits, int64_t V, float temp,
+                                  int32_t top_k, float top_p, float min_p,
+                                  uint64_t seed, uint64_t offset,
+                                  const uint32_t *row_ids, int64_t n_rows,
+                                  int fp64_noise, int64_t *out_idx)
+{
+    uint8_t *kept = (uint8_t *)malloc((size_t)(V > 0 ? V : 1));
+    double margin;
+    oracle_filter_kept(logits, 1, V, &temp, &top_k, &top_p, &min_p, kept, &margin);
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+        #pragma omp for schedule(static)
+        for (int64_t q = 0; q < n_rows; ++q) {
+            double gap, best;
+            for (int64_t i = 0; i < V; ++i)
+                s[i] = kept[i] ? score_of((double)logits[i], 0.0, (double)temp, seed,
+                                          offset, row_ids[q], i, fp64_noise)
+                               : -INFINITY;
+            select_row(s, V, &out_idx[q], &gap, &best);
+        }
+        free(s);
+    }
+    free(kept);
 }
