@@ -649,7 +649,9 @@ static int cmp_desc(const void *pa, const void *pb)
  * smallest distance of a top-p or min-p decision from its boundary (relative:
  * |A - pZ| / Z for top-p, |e_i - m| / m for min-p; +inf when neither decides
  * anything), so that a comparison with another implementation can set aside
- * the rows whose kept set rounding may decide. */
+ * the rows whose kept set rounding may decide.  The largest logit's class has
+ * no such distance: its mass above is 0 and its mass ratio 1 exactly, and the
+ * filters keep it whatever p and m are. */
 static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
                        float m, vi_t *order, double *e, uint8_t *kept,
                        double *margin)
@@ -688,7 +690,9 @@ static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
     }
     /* top-p over the top-k survivors: order[0 .. n2) */
     int64_t n2 = n1;
-    if (p < 1.0f) {                       /* NaN compares false: off */
+    if (p < 1.0f && !(p > 0.0f)) {        /* keeps nothing: the largest class */
+        n2 = nmax;
+    } else if (p < 1.0f) {                /* NaN compares false: off */
         double Z = 0.0;
         for (int64_t j = 0; j < n1; ++j) Z += e[j];
         const double target = (double)p * Z;
@@ -699,8 +703,10 @@ static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
             int64_t j2 = j + 1;           /* the tie class order[j .. j2) */
             double cls = e[j];
             while (j2 < n1 && order[j2].v == order[j].v) cls += e[j2++];
-            double d = fabs(above - target) / Z;
-            if (d < *margin) *margin = d;
+            if (j > 0) {                  /* the largest class: above = 0 < pZ */
+                double d = fabs(above - target) / Z;
+                if (d < *margin) *margin = d;
+            }
             if (!(above < target)) break;
             n2 = j2;
             above += cls;
@@ -713,7 +719,7 @@ static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
     if (m > 0.0f) {                       /* NaN compares false: off */
         for (int64_t j = 0; j < n2; ++j) {
             double d = fabs(e[j] - (double)m) / (double)m;
-            if (d < *margin) *margin = d;
+            if (j >= nmax && d < *margin) *margin = d;
             if (e[j] >= (double)m) {
                 kept[order[j].i] = 1;
                 ++n3;

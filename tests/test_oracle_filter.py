@@ -107,6 +107,13 @@ def test_top_p_crossing_token_and_min_p_by_hand():
     # min-p keeps p >= m * 0.5
     for m, want in ((0.3, [1, 1, 1]), (0.5, [1, 1, 0]), (0.7, [1, 0, 0]), (2.0, [1, 0, 0])):
         np.testing.assert_array_equal(oracle.filter_kept(x, t, min_p=m)[0][0], np.array(want) > 0)
+    # margins: the distance of the closest decision from its boundary; the
+    # largest token's class decides nothing (mass above 0, mass ratio 1)
+    for kw, want in ((dict(top_p=0.6), 0.1), (dict(top_p=0.85), 0.05), (dict(top_p=0.05), 0.45),
+                     (dict(min_p=0.5), 0.2),
+                     (dict(min_p=1.0), 0.4), (dict(top_p=0.0), np.inf), (dict(top_k=2), np.inf)):
+        got = oracle.filter_kept(x, t, **kw)[1][0]
+        assert (got == want) if np.isinf(want) else abs(got - want) < 1e-6, (kw, got)
     # top-p after top-k renormalises over the top-k survivors: 0.5 / 0.8 = 0.625
     np.testing.assert_array_equal(oracle.filter_kept(x, t, top_k=2, top_p=0.6)[0][0], [1, 0, 0])
     np.testing.assert_array_equal(oracle.filter_kept(x, t, top_k=2, top_p=0.65)[0][0], [1, 1, 0])
