@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused", "sample_fused_w8",
     "sample_fused_topk", "sample_fused_mxfp4", "sample_logits", "sample_logits_topk",
-    "workspace_bytes", "debug_logits_mxfp4", "debug_philox_words", "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
+    "sample_logits_filtered", "workspace_bytes", "debug_logits_mxfp4", "debug_philox_words",
+    "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
     "KernelTimer",
 ]
 
@@ -95,6 +96,8 @@ def load_library():
         lib.fs_sample_fused_w8.argtypes = [P, P, P, i64, i64, i64, P, P, u64, u64, P, P, u32, P,
                                            sz, P]
         lib.fs_debug_logits_w8.restype = i32
+        lib.fs_sample_logits_filtered.restype = i32
+        lib.fs_sample_logits_filtered.argtypes = [P, i64, i64, P, P, P, P, u64, u64, i32, P, P, P]
         lib.fs_debug_logits_w8.argtypes = [P, P, P, i64, i64, i64, P, P]
         _lib = lib
         return lib
@@ -289,6 +292,47 @@ def sample_logits(logits: torch.Tensor, temp, *, seed: int, offset: int,
     st = lib.fs_sample_logits(_ptr(logits), B, V, _ptr(t), seed, offset, int(bool(fp64_noise)),
                               _ptr(out), _ptr(rid), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "fs_sample_logits")
+    return out
+
+
+def _filter_param(v, name: str, dtype, B: int, device):
+    """A per-row filter parameter: None (off), a Python scalar for every row, or
+    a [B] tensor of `dtype` on the device."""
+    if v is None:
+        return None
+    if isinstance(v, (int, float)):
+        return torch.full((B,), v, dtype=dtype, device=device)
+    _need(v, name, dtype, device, (B,))
+    return v
+
+
+def sample_logits_filtered(logits: torch.Tensor, temp, *, top_k=None, top_p=None, min_p=None,
+                           seed: int, offset: int, row_ids: torch.Tensor | None = None,
+                           fp64_noise: bool = False,
+                           out: torch.Tensor | None = None) -> torch.Tensor:
+    """One exact draw per row from softmax(logits / temp) restricted to the kept set of
+    the filters top-k, top-p, min-p (applied in that order) over float32 logits [B, V].
+    top_k (int32), top_p, min_p (float32): None, a scalar, or a [B] tensor."""
+    lib = load_library()
+    dev = logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    B, V = logits.shape
+    _need(logits, "logits", torch.float32, dev, (B, V))
+    t = _temp_tensor(temp, B, dev)
+    k = _filter_param(top_k, "top_k", torch.int32, B, dev)
+    p = _filter_param(top_p, "top_p", torch.float32, B, dev)
+    m = _filter_param(min_p, "min_p", torch.float32, B, dev)
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B,))
+    st = lib.fs_sample_logits_filtered(_ptr(logits), B, V, _ptr(t), _ptr(k), _ptr(p), _ptr(m),
+                                       seed, offset, int(bool(fp64_noise)), _ptr(out), _ptr(rid),
+                                       _stream(dev))
+    _check(st, "fs_sample_logits_filtered")
     return out
 
 

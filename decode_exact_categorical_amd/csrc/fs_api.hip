@@ -363,6 +363,40 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
   return FS_OK;
 }
 
+fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, const float* temp,
+                                    const int32_t* top_k, const float* top_p, const float* min_p,
+                                    uint64_t seed, uint64_t offset, int fp64_noise,
+                                    int64_t* out_idx, const uint32_t* row_ids, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_sizes(B, V);
+  if (s != FS_OK) return s;
+  if (B == 0) return FS_OK;
+  if (logits == nullptr || temp == nullptr || out_idx == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "logits, temp or out_idx is null");
+  if (((uintptr_t)logits & 3u) != 0) return fail(FS_ERR_UNSUPPORTED, "logits not 4-byte aligned");
+  if (B >= ((int64_t)1 << 31)) return fail(FS_ERR_INVALID_ARG, "B = %lld exceeds 2^31 - 1", (long long)B);
+
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  if (ev) (void)hipEventRecord(ev[0], st);
+  fs::FilterArgs a;
+  a.X = logits;
+  a.B = B;
+  a.V = V;
+  a.temp = temp;
+  a.row_ids = row_ids;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.min_p = min_p;
+  a.key = fs::make_key(seed, offset);
+  a.out = out_idx;
+  a.vec4 = aligned16(logits) && (V % 4 == 0);
+  hipError_t e = fs::launch_logits_filtered(a, fp64_noise != 0, st);
+  if (e != hipSuccess) return hip_fail(e, "filtered sampling launch");
+  if (ev) (void)hipEventRecord(ev[1], st);
+  return FS_OK;
+}
+
 fs_status fs_sample_logits_topk(const float* logits, int64_t B, int64_t V, const float* temp,
                                 uint64_t seed, uint64_t offset, int fp64_noise, int k,
                                 int64_t* out_idx, const uint32_t* row_ids, void* workspace,

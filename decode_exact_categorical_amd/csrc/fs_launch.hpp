@@ -76,6 +76,21 @@ struct LogitsArgs {
 hipError_t launch_logits_stage1(const LogitsArgs& a, bool fp64, hipStream_t stream);
 hipError_t launch_logits_topk(const LogitsArgs& a, bool fp64, hipStream_t stream);
 
+// Filtered sampling over materialised logits: one workgroup per row.
+struct FilterArgs {
+  const float* X;  // [B, V]
+  int64_t B, V;
+  const float* temp;
+  const uint32_t* row_ids;  // [B] or null: then row b has id b
+  const int32_t* top_k;     // [B] or null
+  const float* top_p;       // [B] or null
+  const float* min_p;       // [B] or null
+  NoiseKey key;
+  int64_t* out;  // [B]
+  int vec4;      // rows 16-byte aligned
+};
+hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t stream);
+
 // Test hook: the noise transforms applied to given words.
 hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,
                         hipStream_t stream);

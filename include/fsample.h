@@ -9,8 +9,9 @@
  *         (Stage 1 steps (1)-(6); Stage 2).
  *   [MG]  Megatron-LM pull request "fp64 sampling noise", sections "Problem"
  *         and "The change".
- *   [SD]  spec-decode-ops kernel card, sections "Usage", "API" and
- *         "Measured behavior" (determinism).
+ *   [SD]  spec-decode-ops kernel card: the description of its sample
+ *         pipeline, sections "Usage", "API", "Semantics" (the filter order and
+ *         boundaries) and "Measured behavior" (determinism).
  *   [SK]  "Write Triton Sampling Kernel" skill page, "Required reasoning
  *         process" items 3-4 and 10, "Correctness requirements".
  *   [OFP8] OCP 8-bit Floating Point Specification (OFP8), revision 1.0, the
@@ -193,6 +194,39 @@ fs_status fs_sample_logits(const float *logits, int64_t B, int64_t V, const floa
                            uint64_t seed, uint64_t offset, int fp64_noise,
                            int64_t *out_idx, const uint32_t *row_ids, void *workspace,
                            size_t workspace_bytes, fs_stream_t stream);
+
+/*
+ * Filtered exact sampling over materialised float32 logits [SD sample
+ * pipeline, "Semantics"]: per row, the kept set of the filter chain
+ * temperature -> top-k -> top-p -> min-p, then the draw of fs_sample_logits
+ * (same transform, noise stream, keys and tie rule) over the kept tokens only.
+ *   top_k    device, int32 [B] or NULL: keep the tokens whose logit is at
+ *            least the k-th largest valid logit (a tie at that value is kept
+ *            whole); off when k <= 0, k >= the row's number of valid logits,
+ *            or top_k is NULL
+ *   top_p    device, float [B] or NULL: over the top-k survivors with
+ *            probabilities softmax(y / t), keep a token when the survivors with
+ *            strictly larger logits carry less than p of their mass (the
+ *            smallest prefix that reaches p, the crossing token included;
+ *            equal logits are kept or dropped together); off when p >= 1, p is
+ *            NaN or top_p is NULL; p <= 0 keeps the largest logit's tie class
+ *   min_p    device, float [B] or NULL: over the top-p survivors, keep a token
+ *            when its probability is at least m times the largest one; off
+ *            when m <= 0, m is NaN or min_p is NULL; m >= 1 keeps the largest
+ *            logit's tie class
+ *   the other arguments as for fs_sample_logits (no workspace is needed).
+ * Valid logits are those neither NaN nor -inf; no other token is ever kept,
+ * and a row without one gets -1.  Greedy rows (t <= 0 or NaN) take the argmax
+ * whatever the filters (each keeps the largest logit).  A row whose filters
+ * are all off draws exactly what fs_sample_logits draws.  The top-p masses are
+ * summed in 64-bit fixed point (units of 2^-40 of the largest token's mass),
+ * so a call is reproducible bit for bit.
+ */
+fs_status fs_sample_logits_filtered(const float *logits, int64_t B, int64_t V,
+                                    const float *temp, const int32_t *top_k,
+                                    const float *top_p, const float *min_p, uint64_t seed,
+                                    uint64_t offset, int fp64_noise, int64_t *out_idx,
+                                    const uint32_t *row_ids, fs_stream_t stream);
 
 /*
  * Gumbel-top-k over materialised float32 logits [GTK]: k draws without

@@ -7,7 +7,8 @@ D = 4096, V = 128256 Llama-3-shaped head; D = 8192 wide head) and of the
 Megatron-LM tail-rate and chi-square tests.  Every draw uses a CPU
 ``torch.Generator`` with a fixed seed, so the oracle and the GPU path see
 identical bits.  Seeds: W = 0, H = 1, temperatures = 2, bias/mask = 3,
-chi-square row = 4.  Reading of "N(0, s)": s is the standard deviation.
+chi-square row = 4, materialised logits and filter settings = 5.  Reading of
+"N(0, s)": s is the standard deviation.
 """
 from __future__ import annotations
 
@@ -16,7 +17,7 @@ import math
 import numpy as np
 import torch
 
-SEED_W, SEED_H, SEED_T, SEED_BIAS, SEED_CHI2 = 0, 1, 2, 3, 4
+SEED_W, SEED_H, SEED_T, SEED_BIAS, SEED_CHI2, SEED_LOGITS = 0, 1, 2, 3, 4, 5
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -131,3 +132,25 @@ def tail_row(V: int, r: float) -> torch.Tensor:
 def row_ids(B: int, start: int = 0) -> torch.Tensor:
     """Logical row ids start..start+B-1 as int32 (bit pattern of uint32)."""
     return torch.arange(start, start + B, dtype=torch.int64).to(torch.int32)
+
+
+def logits(B: int, V: int, std: float = 3.0, seed: int = SEED_LOGITS) -> torch.Tensor:
+    """Materialised logits [B, V] float32 ~ N(0, std^2) (the standalone samplers'
+    input; std = 3 gives LM-like rows whose top-p sets hold from a few to a few
+    thousand tokens)."""
+    return (torch.randn((B, V), generator=_gen(seed)) * std).float()
+
+
+def filter_settings(B: int, V: int, seed: int = SEED_LOGITS + 100):
+    """Per-row filter parameters (top_k int32, top_p float32, min_p float32),
+    each row drawing which filters are on: top_k in [1, 200] or off (0), top_p
+    in [0.5, 0.99] or off (1), min_p in [0.01, 0.3] or off (0)."""
+    g = _gen(seed)
+    on = torch.rand((3, B), generator=g) < 0.6
+    k = torch.randint(1, min(200, V) + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    p = 0.5 + 0.49 * torch.rand((B,), generator=g)
+    m = 0.01 + 0.29 * torch.rand((B,), generator=g)
+    k = torch.where(on[0], k, torch.zeros_like(k))
+    p = torch.where(on[1], p, torch.ones_like(p)).float()
+    m = torch.where(on[2], m, torch.zeros_like(m)).float()
+    return k, p, m

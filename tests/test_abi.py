@@ -102,6 +102,25 @@ def test_logits_rejects_before_launch(kw, code):
     assert _logits(**kw) == code
 
 
+def _filtered(B=4, V=1000, X=FAKE, temp=FAKE, out=FAKE, k=None, p=None, m=None):
+    lib = fs.load_library()
+    return lib.fs_sample_logits_filtered(P(X), B, V, P(temp), k, p, m, 1, 0, 0, P(out), None,
+                                         None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-2), 1), (dict(V=0), 1), (dict(V=2**31), 1), (dict(X=0), 1), (dict(temp=0), 1),
+    (dict(out=0), 1), (dict(X=FAKE + 2), 2), (dict(B=2**31), 1),
+])
+def test_filtered_rejects_before_launch(kw, code):
+    assert _filtered(**kw) == code
+    assert fs.load_library().fs_last_error() != b""
+
+
+def test_filtered_empty_batch_is_a_noop():
+    assert _filtered(B=0, X=0, temp=0, out=0) == 0
+
+
 def test_debug_hooks_reject_before_launch():
     lib = fs.load_library()
     assert lib.fs_debug_philox_words(0, 0, None, -1, 4, P(FAKE), None) == 1

@@ -1,0 +1,200 @@
+"""GPU parity of filtered exact sampling (fs_sample_logits_filtered) against
+the oracle, through the C ABI.
+
+* Index parity: every row whose filter decisions are further than 2e-5 from
+  their boundaries (the oracle's margin, relative) and whose top-2 kept
+  perturbed-score gap exceeds 1e-3 draws the oracle's token; per-row mixes of
+  top-k, top-p and min-p, float32 and float64 noise, ragged V, greedy, masked
+  and NaN rows.
+* Every draw lies in the oracle's kept set, over many offsets.
+* A row with every filter off draws exactly what fs_sample_logits draws.
+* The law of the draws on a small row (chi-square against the softmax over the
+  kept set) and zero draws outside it.
+* Full size: the Qwen3-8B-shaped vocabulary (V = 151936), B = 64, every row
+  against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_exact_categorical_amd as fs
+import oracle
+import synthetic
+from gpu_common import check_index_parity, need_gpu, say
+from oracle import stats
+
+pytestmark = pytest.mark.gpu
+# The kernel's masses are float32 exp((y - M) * (1/t)): three float32 roundings
+# in the exponent x (relative error <= 3 * 2^-24 * |x|, at most 7e-6 for the
+# |x| <= 40 that carry mass above the 2^-40 fixed-point unit) and one ulp of
+# exp; the fixed-point sums lose at most V * 2^-40 of the largest token's mass.
+# A top-p or min-p decision further than 2e-5 (relative) from its boundary is
+# therefore taken the same way on both sides.
+MARGIN = 2e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def _run(dev, x, t, k, p, m, *, seed, offset, fp64=False, row_ids=None):
+    dx = x.to(dev)
+    dt = t.to(dev)
+    dk = None if k is None else k.to(dev)
+    dp = None if p is None else p.to(dev)
+    dm = None if m is None else m.to(dev)
+    drid = None if row_ids is None else row_ids.to(dev)
+    got = fs.sample_logits_filtered(dx, dt, top_k=dk, top_p=dp, min_p=dm, seed=seed, offset=offset,
+                                    row_ids=drid, fp64_noise=fp64)
+    torch.cuda.synchronize()
+    return got.cpu().numpy()
+
+
+def _oracle(x, t, k, p, m, *, seed, offset, fp64=False, row_ids=None):
+    npf = lambda v: None if v is None else v.numpy()
+    return oracle.sample_logits_filtered(x.numpy(), t.numpy(), top_k=npf(k), top_p=npf(p),
+                                         min_p=npf(m), seed=seed, offset=offset,
+                                         row_ids=None if row_ids is None else row_ids.numpy(),
+                                         fp64_noise=fp64)
+
+
+def _check(got, idx, gap, margin, what):
+    # rows whose kept set rounding may decide are compared like near ties
+    gap = np.where(margin > MARGIN, gap, 0.0)
+    near = check_index_parity(got, idx, gap, what)
+    assert near <= max(2, got.size // 4), f"{what}: {near} undecided rows"
+
+
+CASES = [
+    dict(B=37, V=1001),
+    dict(B=16, V=5003),              # V % 4 != 0: scalar loads
+    dict(B=8, V=32768),
+    dict(B=64, V=2048, std=1.0),     # flatter rows: large top-p sets
+    dict(B=5, V=7),
+    dict(B=3, V=1),
+]
+
+
+@pytest.mark.parametrize("fp64", [False, True])
+@pytest.mark.parametrize("case", CASES)
+def test_filtered_parity_mixed_settings(dev, case, fp64):
+    B, V = case["B"], case["V"]
+    say(f"filtered parity B={B} V={V} fp64={fp64}")
+    x = synthetic.logits(B, V, std=case.get("std", 3.0), seed=50 + V)
+    t = synthetic.temperatures(B, seed=51)
+    k, p, m = synthetic.filter_settings(B, V, seed=52 + B)
+    got = _run(dev, x, t, k, p, m, seed=99, offset=7, fp64=fp64)
+    idx, gap, margin = _oracle(x, t, k, p, m, seed=99, offset=7, fp64=fp64)
+    _check(got, idx, gap, margin, f"B={B} V={V} fp64={fp64}")
+
+
+@pytest.mark.parametrize("setting", [dict(top_k=1), dict(top_k=50), dict(top_p=0.9),
+                                     dict(min_p=0.05), dict(top_k=40, top_p=0.95, min_p=0.02),
+                                     dict(top_p=0.0), dict(min_p=1.0), dict(min_p=3.0),
+                                     dict(top_k=2000, top_p=0.3)])
+def test_filtered_parity_uniform_settings(dev, setting):
+    B, V = 48, 12345
+    say(f"filtered parity {setting}")
+    x = synthetic.logits(B, V, seed=60)
+    t = synthetic.temperatures(B, seed=61)
+    conv = {"top_k": torch.int32, "top_p": torch.float32, "min_p": torch.float32}
+    full = {n: (torch.full((B,), v, dtype=conv[n]) if n in setting else None)
+            for n, v in [("top_k", setting.get("top_k", 0)), ("top_p", setting.get("top_p", 1.0)),
+                         ("min_p", setting.get("min_p", 0.0))]}
+    got = _run(dev, x, t, full["top_k"], full["top_p"], full["min_p"], seed=3, offset=4)
+    idx, gap, margin = _oracle(x, t, full["top_k"], full["top_p"], full["min_p"], seed=3, offset=4)
+    _check(got, idx, gap, margin, str(setting))
+
+
+def test_filtered_special_rows(dev):
+    B, V = 12, 3000
+    x = synthetic.logits(B, V, seed=70)
+    x[0, :] = -float("inf")                      # nothing valid
+    x[1, ::2] = float("nan")
+    x[2, 10] = x[2, 2000] = float("inf")         # +inf holds all the mass
+    x[3, 100:200] = x[3].max() + 1.0             # a tie class at the top
+    x[4, :] = 0.5                                 # every logit equal
+    t = synthetic.temperatures(B, seed=71)
+    t[5], t[6], t[7] = 0.0, -2.0, float("nan")   # greedy
+    t[8] = float("inf")                           # uniform over the valid tokens
+    k = torch.full((B,), 20, dtype=torch.int32)
+    p = torch.full((B,), 0.8)
+    m = torch.full((B,), 0.1)
+    for fp64 in (False, True):
+        got = _run(dev, x, t, k, p, m, seed=8, offset=9, fp64=fp64)
+        idx, gap, margin = _oracle(x, t, k, p, m, seed=8, offset=9, fp64=fp64)
+        _check(got, idx, gap, margin, f"special rows fp64={fp64}")
+        assert got[0] == -1 and got[2] == 10
+        assert 100 <= got[3] < 200
+        assert got[5] == int(np.nanargmax(x[5].numpy()))
+
+
+def test_filters_off_equals_unfiltered(dev):
+    B, V = 40, 7001
+    x = synthetic.logits(B, V, seed=80)
+    x[1, 5] = float("nan")
+    x[2, :] = -float("inf")
+    t = synthetic.temperatures(B, seed=81)
+    t[3] = 0.0
+    dx, dt = x.to(dev), t.to(dev)
+    off_k = torch.zeros(B, dtype=torch.int32, device=dev)
+    off_p = torch.full((B,), 1.0, device=dev)
+    for fp64 in (False, True):
+        a = fs.sample_logits(dx, dt, seed=11, offset=12, fp64_noise=fp64)
+        b = fs.sample_logits_filtered(dx, dt, seed=11, offset=12, fp64_noise=fp64)
+        c = fs.sample_logits_filtered(dx, dt, top_k=off_k, top_p=off_p, seed=11, offset=12,
+                                      fp64_noise=fp64)
+        assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_draws_stay_in_the_kept_set(dev):
+    B, V = 32, 4096
+    x = synthetic.logits(B, V, seed=90)
+    t = synthetic.temperatures(B, seed=91)
+    k, p, m = synthetic.filter_settings(B, V, seed=92)
+    kept, margin = oracle.filter_kept(x.numpy(), t.numpy(), top_k=k.numpy(), top_p=p.numpy(),
+                                      min_p=m.numpy())
+    sure = margin > MARGIN
+    dx, dt, dk, dp, dm = (v.to(dev) for v in (x, t, k, p, m))
+    outs = torch.stack([fs.sample_logits_filtered(dx, dt, top_k=dk, top_p=dp, min_p=dm, seed=5,
+                                                  offset=o) for o in range(200)]).cpu().numpy()
+    for b in np.flatnonzero(sure):
+        assert kept[b, outs[:, b]].all(), f"row {b} drew outside its kept set"
+    # replays are bitwise reproducible
+    again = fs.sample_logits_filtered(dx, dt, top_k=dk, top_p=dp, min_p=dm, seed=5, offset=3)
+    assert np.array_equal(again.cpu().numpy(), outs[3])
+
+
+@pytest.mark.parametrize("fp64", [False, True])
+def test_filtered_law_chi_square(dev, fp64):
+    row = torch.tensor([2.0, 1.6, 1.5, 1.0, 0.9, 0.2, -0.3, -1.0, 0.7, 1.55])
+    t, k, p, m = 0.8, 7, 0.85, 0.08
+    n = 262144
+    x = row[None].repeat(n, 1)
+    kept, margin = oracle.filter_kept(row[None].numpy(), np.array([t], dtype=np.float32), top_k=k,
+                                      top_p=p, min_p=m)
+    assert margin[0] > MARGIN
+    z = row.double().numpy() / t
+    law = np.where(kept[0], np.exp(z - z.max()), 0.0)
+    law /= law.sum()
+    got = fs.sample_logits_filtered(x.to(dev), t, top_k=k, top_p=p, min_p=m, seed=21, offset=0,
+                                    row_ids=synthetic.row_ids(n).to(dev), fp64_noise=fp64)
+    counts = np.bincount(got.cpu().numpy(), minlength=row.numel())
+    assert counts[~kept[0]].sum() == 0
+    keep = np.flatnonzero(kept[0])
+    chi2 = stats.chi2_statistic(counts[keep], law[keep])
+    say(f"  filtered chi2 = {chi2:.2f} (dof {keep.size - 1})")
+    assert chi2 < stats.chi2_quantile(keep.size - 1, 1e-6)
+
+
+def test_filtered_qwen_vocabulary(dev):
+    B, V = 64, 151936
+    say("filtered parity at B=64 V=151936")
+    x = synthetic.logits(B, V, seed=100)
+    t = synthetic.temperatures(B, seed=101)
+    k, p, m = synthetic.filter_settings(B, V, seed=102)
+    for fp64 in (False, True):
+        got = _run(dev, x, t, k, p, m, seed=1234, offset=17, fp64=fp64)
+        idx, gap, margin = _oracle(x, t, k, p, m, seed=1234, offset=17, fp64=fp64)
+        _check(got, idx, gap, margin, f"qwen vocabulary fp64={fp64}")
