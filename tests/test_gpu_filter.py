@@ -92,7 +92,8 @@ def test_filtered_parity_mixed_settings(dev, case, fp64):
 @pytest.mark.parametrize("setting", [dict(top_k=1), dict(top_k=50), dict(top_p=0.9),
                                      dict(min_p=0.05), dict(top_k=40, top_p=0.95, min_p=0.02),
                                      dict(top_p=0.0), dict(min_p=1.0), dict(min_p=3.0),
-                                     dict(top_k=2000, top_p=0.3)])
+                                     dict(top_k=2000, top_p=0.3), dict(top_k=3000, min_p=0.3),
+                                     dict(top_k=9000), dict(top_k=9000, top_p=0.6)])
 def test_filtered_parity_uniform_settings(dev, setting):
     B, V = 48, 12345
     say(f"filtered parity {setting}")
@@ -128,6 +129,35 @@ def test_filtered_special_rows(dev):
         assert got[0] == -1 and got[2] == 10
         assert 100 <= got[3] < 200
         assert got[5] == int(np.nanargmax(x[5].numpy()))
+
+
+@pytest.mark.parametrize("fp64", [False, True])
+def test_filtered_many_candidates(dev, fp64):
+    """Rows where more tokens than the LDS holds can be kept: large tie classes
+    (which top-p and min-p keep or drop whole, far from their boundaries), an
+    infinite temperature, a top-k beyond the LDS capacity on nearly flat rows;
+    ordinary rows in the same launch."""
+    B, V = 10, 50000
+    say(f"filtered rows with many candidates fp64={fp64}")
+    g = torch.Generator().manual_seed(120)
+    x = torch.randn((B, V), generator=g) - 10.0
+    x[0, :20000] = 1.0                               # a tie class of 20000
+    x[2] = torch.randn((V,), generator=g) * 0.05     # nearly flat
+    x[3] = torch.randn((V,), generator=g) * 0.05
+    x[4, 5000:17000] = 2.0                           # a tie class of 12000
+    x[5, :9000] = 0.0                                # two close tie classes of 9000
+    x[5, 9000:18000] = -0.001
+    x[6:] = synthetic.logits(B - 6, V, seed=121)     # ordinary rows
+    t = synthetic.temperatures(B, seed=122)
+    t[1] = float("inf")
+    k = torch.tensor([0, 30000, 9000, 20000, 0, 0, 100, 0, 50, 0], dtype=torch.int32)
+    p = torch.tensor([0.9, 1.0, 1.0, 1.0, 1.0, 0.5, 1.0, 0.9, 0.95, 1.0])
+    m = torch.tensor([0.0, 0.0, 0.0, 0.5, 0.5, 0.0, 0.1, 0.0, 0.05, 0.2])
+    got = _run(dev, x, t, k, p, m, seed=12, offset=13, fp64=fp64)
+    idx, gap, margin = _oracle(x, t, k, p, m, seed=12, offset=13, fp64=fp64)
+    assert (margin[:6] > MARGIN).all(), margin
+    _check(got, idx, gap, margin, f"many candidates fp64={fp64}")
+    assert got[0] < 20000 and 5000 <= got[4] < 17000 and got[5] < 9000
 
 
 def test_filters_off_equals_unfiltered(dev):
