@@ -405,6 +405,53 @@ def main() -> int:
             del X
         result["standalone_sampler"] = sa
 
+        # Filtered sampling over float32 logits (temperature -> top-k -> top-p ->
+        # min-p -> draw): the settings of the spec-decode-ops card's example
+        # (top_k = 50, top_p = 0.95) at its latency vocabulary (V = 128256, B = 1
+        # and 8), at the Qwen3-8B vocabulary (B = 64, plus top-p and min-p alone)
+        # and at the tail-rate chunk shape; against the eager transformers chain
+        # (the card's comparison) on the same tensors.
+        log("timing the filtered sampler")
+        fl = {"settings": "top_k=50, top_p=0.95 unless named; logits N(0, 3^2), T = 0.8"}
+        try:
+            from transformers.generation.logits_process import (TemperatureLogitsWarper,
+                                                                TopKLogitsWarper, TopPLogitsWarper)
+        except Exception:           # the eager baseline needs transformers
+            TopKLogitsWarper = None
+        for (bl, vl, name, kw) in ((1, 128256, "", dict(top_k=50, top_p=0.95)),
+                                   (8, 128256, "", dict(top_k=50, top_p=0.95)),
+                                   (64, 151936, "", dict(top_k=50, top_p=0.95)),
+                                   (64, 151936, "_top_p_0.95", dict(top_p=0.95)),
+                                   (64, 151936, "_min_p_0.05", dict(min_p=0.05)),
+                                   (4096, 131072, "", dict(top_k=50, top_p=0.95))):
+            g = torch.Generator(device=dev).manual_seed(6)
+            X = torch.randn(bl, vl, generator=g, dtype=torch.float32, device=dev) * 3.0
+            Tl = torch.full((bl,), 0.8, dtype=torch.float32, device=dev)
+            ms, kms, pc = time_calls(
+                torch, fs, lambda s: fs.sample_logits_filtered(X, Tl, seed=98, offset=s, **kw),
+                max(20, args.steps // 4), 5)
+            lb = 4 * bl * vl + 12 * bl
+            key = f"B{bl}_V{vl}{name}"
+            fl[key] = {"us_per_call": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
+                       "alg_bytes": lb, "kernel_gbs": round(lb / (kms * 1e-3) / 1e9, 1),
+                       "kernel_frac": round(lb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if TopKLogitsWarper is not None and "top_k" in kw and bl <= 64:
+                wt = TemperatureLogitsWarper(0.8)
+                wk = TopKLogitsWarper(kw["top_k"])
+                wp = TopPLogitsWarper(kw["top_p"])
+
+                def eager(s):
+                    z = wp(None, wk(None, wt(None, X)))
+                    return torch.multinomial(torch.softmax(z, dim=-1), 1)
+
+                fl[key]["eager_transformers_chain_us"] = round(
+                    time_region(torch, eager, max(20, args.steps // 4), 5) * 1e3, 2)
+                fl[key]["speedup_vs_eager"] = round(
+                    fl[key]["eager_transformers_chain_us"] / fl[key]["us_per_call"], 2)
+            log(f"  {key}: {fl[key]}")
+            del X
+        result["filtered_sampler"] = fl
+
         # The large-batch end: the Llama-3-shaped head at the compute crossover
         # (H [256, 4096], W [128256, 4096], per-row temperature, fp32 bias with
         # 10% of each row masked), reported against both the MFMA and the HBM peak.

@@ -97,7 +97,10 @@ def load_library():
                                            sz, P]
         lib.fs_debug_logits_w8.restype = i32
         lib.fs_sample_logits_filtered.restype = i32
-        lib.fs_sample_logits_filtered.argtypes = [P, i64, i64, P, P, P, P, u64, u64, i32, P, P, P]
+        lib.fs_sample_logits_filtered.argtypes = [P, i64, i64, P, P, P, P, u64, u64, i32, P, P, P,
+                                                  sz, P]
+        lib.fs_workspace_bytes_filtered.restype = sz
+        lib.fs_workspace_bytes_filtered.argtypes = [i64, i64]
         lib.fs_debug_logits_w8.argtypes = [P, P, P, i64, i64, i64, P, P]
         _lib = lib
         return lib
@@ -329,9 +332,11 @@ def sample_logits_filtered(logits: torch.Tensor, temp, *, top_k=None, top_p=None
     if out is None:
         out = torch.empty((B,), dtype=torch.int64, device=dev)
     _need(out, "out", torch.int64, dev, (B,))
+    need = int(lib.fs_workspace_bytes_filtered(B, V)) if V > 0 else 0
+    ws = _workspace(dev, need) if need > 0 else None
     st = lib.fs_sample_logits_filtered(_ptr(logits), B, V, _ptr(t), _ptr(k), _ptr(p), _ptr(m),
                                        seed, offset, int(bool(fp64_noise)), _ptr(out), _ptr(rid),
-                                       _stream(dev))
+                                       _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(st, "fs_sample_logits_filtered")
     return out
 

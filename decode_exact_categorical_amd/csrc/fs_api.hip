@@ -363,10 +363,18 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
   return FS_OK;
 }
 
+size_t fs_workspace_bytes_filtered(int64_t B, int64_t V) {
+  if (B < 0 || V < 1 || V >= kMaxV) return 0;
+  const size_t words = fs::filtered_split_words(B, V);
+  if (words == 0) return 0;
+  return align_up((size_t)B * sizeof(uint32_t)) + words * sizeof(uint64_t);
+}
+
 fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, const float* temp,
                                     const int32_t* top_k, const float* top_p, const float* min_p,
                                     uint64_t seed, uint64_t offset, int fp64_noise,
-                                    int64_t* out_idx, const uint32_t* row_ids, fs_stream_t stream) {
+                                    int64_t* out_idx, const uint32_t* row_ids, void* workspace,
+                                    size_t workspace_bytes, fs_stream_t stream) {
   g_last_error[0] = 0;
   fs_status s = check_sizes(B, V);
   if (s != FS_OK) return s;
@@ -375,6 +383,13 @@ fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, c
     return fail(FS_ERR_INVALID_ARG, "logits, temp or out_idx is null");
   if (((uintptr_t)logits & 3u) != 0) return fail(FS_ERR_UNSUPPORTED, "logits not 4-byte aligned");
   if (B >= ((int64_t)1 << 31)) return fail(FS_ERR_INVALID_ARG, "B = %lld exceeds 2^31 - 1", (long long)B);
+  const size_t need = fs_workspace_bytes_filtered(B, V);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(FS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+      return fail(FS_ERR_WORKSPACE, "workspace not %zu-byte aligned", (size_t)kAlign);
+  }
 
   hipStream_t st = (hipStream_t)stream;
   hipEvent_t* ev = prof_slot();
@@ -391,6 +406,10 @@ fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, c
   a.key = fs::make_key(seed, offset);
   a.out = out_idx;
   a.vec4 = aligned16(logits) && (V % 4 == 0);
+  a.counters = need > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.split = need > 0 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) +
+                                                   align_up((size_t)B * sizeof(uint32_t)))
+                     : nullptr;
   hipError_t e = fs::launch_logits_filtered(a, fp64_noise != 0, st);
   if (e != hipSuccess) return hip_fail(e, "filtered sampling launch");
   if (ev) (void)hipEventRecord(ev[1], st);

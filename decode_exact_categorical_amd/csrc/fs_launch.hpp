@@ -88,7 +88,20 @@ struct FilterArgs {
   NoiseKey key;
   int64_t* out;  // [B]
   int vec4;      // rows 16-byte aligned
+  // Split rows (small batches): per-row completion counters (zero between
+  // calls) and filtered_split_words(B, V) 64-bit words of chunk headers and
+  // candidate lists; null selects one workgroup per row.
+  uint32_t* counters;
+  uint64_t* split;
 };
+// Rows a split launch takes: up to ~24 rows splitting wins (measured at
+// V = 151936: 46 against 90 us at B = 16); from B = 32 the per-row kernel
+// keeps up and from B = 64 it wins (the split kernel's LDS, sized for the
+// merge, holds one workgroup per CU).
+constexpr int kSplitMaxRows = 24;
+constexpr int kSplitMaxChunks = 32;   // chunks of a split row (V <= 262144)
+int filtered_split_chunks(int64_t B, int64_t V);  // 0: one workgroup per row
+size_t filtered_split_words(int64_t B, int64_t V);
 hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t stream);
 
 // Test hook: the noise transforms applied to given words.

@@ -214,7 +214,12 @@ fs_status fs_sample_logits(const float *logits, int64_t B, int64_t V, const floa
  *            when its probability is at least m times the largest one; off
  *            when m <= 0, m is NaN or min_p is NULL; m >= 1 keeps the largest
  *            logit's tie class
- *   the other arguments as for fs_sample_logits (no workspace is needed).
+ *   workspace, workspace_bytes  device, 256-byte aligned, at least
+ *            fs_workspace_bytes_filtered(B, V) bytes (NULL when that is 0); zero
+ *            it once before first use, as for fs_sample_fused: every call
+ *            leaves its counters at zero, and calls sharing one workspace are
+ *            serialised by their stream
+ *   the other arguments as for fs_sample_logits.
  * Valid logits are those neither NaN nor -inf; no other token is ever kept,
  * and a row without one gets -1.  Greedy rows (t <= 0 or NaN) take the argmax
  * whatever the filters (each keeps the largest logit).  A row whose filters
@@ -226,7 +231,17 @@ fs_status fs_sample_logits_filtered(const float *logits, int64_t B, int64_t V,
                                     const float *temp, const int32_t *top_k,
                                     const float *top_p, const float *min_p, uint64_t seed,
                                     uint64_t offset, int fp64_noise, int64_t *out_idx,
-                                    const uint32_t *row_ids, fs_stream_t stream);
+                                    const uint32_t *row_ids, void *workspace,
+                                    size_t workspace_bytes, fs_stream_t stream);
+
+/*
+ * Workspace bytes fs_sample_logits_filtered needs for (B, V): 0 when it runs
+ * one workgroup per row (no workspace; NULL is accepted), otherwise per-row
+ * completion counters and each row's chunk headers and candidate lists
+ * (small batches split each row over several workgroups).  0 for invalid
+ * sizes.
+ */
+size_t fs_workspace_bytes_filtered(int64_t B, int64_t V);
 
 /*
  * Gumbel-top-k over materialised float32 logits [GTK]: k draws without

@@ -102,15 +102,16 @@ def test_logits_rejects_before_launch(kw, code):
     assert _logits(**kw) == code
 
 
-def _filtered(B=4, V=1000, X=FAKE, temp=FAKE, out=FAKE, k=None, p=None, m=None):
+def _filtered(B=4, V=100000, X=FAKE, temp=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30):
     lib = fs.load_library()
-    return lib.fs_sample_logits_filtered(P(X), B, V, P(temp), k, p, m, 1, 0, 0, P(out), None,
-                                         None)
+    return lib.fs_sample_logits_filtered(P(X), B, V, P(temp), None, None, None, 1, 0, 0, P(out),
+                                         None, P(ws), wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-2), 1), (dict(V=0), 1), (dict(V=2**31), 1), (dict(X=0), 1), (dict(temp=0), 1),
     (dict(out=0), 1), (dict(X=FAKE + 2), 2), (dict(B=2**31), 1),
+    (dict(ws=0), 3), (dict(wsb=64), 3), (dict(ws=FAKE + 8), 3),
 ])
 def test_filtered_rejects_before_launch(kw, code):
     assert _filtered(**kw) == code
@@ -118,7 +119,19 @@ def test_filtered_rejects_before_launch(kw, code):
 
 
 def test_filtered_empty_batch_is_a_noop():
-    assert _filtered(B=0, X=0, temp=0, out=0) == 0
+    assert _filtered(B=0, X=0, temp=0, out=0, ws=0, wsb=0) == 0
+
+
+def test_filtered_workspace_bytes():
+    lib = fs.load_library()
+    # split rows for small batches of long rows: counters, chunk headers and lists
+    assert lib.fs_workspace_bytes_filtered(16, 151936) >= 16 * 19 * (8 + 512) * 8
+    assert lib.fs_workspace_bytes_filtered(1, 128256) > 0
+    # one workgroup per row (larger batches, short or very long rows): none
+    for B, V in ((4096, 131072), (64, 151936), (16, 8192), (8, 300000), (0, 151936)):
+        assert lib.fs_workspace_bytes_filtered(B, V) == 0, (B, V)
+    assert lib.fs_workspace_bytes_filtered(-1, 1000) == 0
+    assert lib.fs_workspace_bytes_filtered(4, 0) == 0
 
 
 def test_debug_hooks_reject_before_launch():

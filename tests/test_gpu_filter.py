@@ -8,10 +8,14 @@ the oracle, through the C ABI.
   and NaN rows.
 * Every draw lies in the oracle's kept set, over many offsets.
 * A row with every filter off draws exactly what fs_sample_logits draws.
+* Both launch shapes: one workgroup per row (large batches, short rows) and
+  rows split over several workgroups whose candidate lists the row's last
+  workgroup merges (small batches), including rows whose lists cannot hold
+  the kept set (the merge then runs the one-workgroup path).
 * The law of the draws on a small row (chi-square against the softmax over the
   kept set) and zero draws outside it.
-* Full size: the Qwen3-8B-shaped vocabulary (V = 151936), B = 64, every row
-  against the oracle.
+* Full size: the Qwen3-8B-shaped vocabulary (V = 151936), B = 8 (split rows)
+  and B = 64 (one workgroup per row), every row against the oracle.
 """
 import numpy as np
 import pytest
@@ -73,6 +77,9 @@ CASES = [
     dict(B=64, V=2048, std=1.0),     # flatter rows: large top-p sets
     dict(B=5, V=7),
     dict(B=3, V=1),
+    dict(B=600, V=9000),             # one workgroup per row
+    dict(B=24, V=20000),             # the most rows a split launch takes
+    dict(B=4, V=262144),             # the most chunks a split row has
 ]
 
 
@@ -108,8 +115,9 @@ def test_filtered_parity_uniform_settings(dev, setting):
     _check(got, idx, gap, margin, str(setting))
 
 
-def test_filtered_special_rows(dev):
-    B, V = 12, 3000
+@pytest.mark.parametrize("V", [3000, 20000])
+def test_filtered_special_rows(dev, V):
+    B = 12
     x = synthetic.logits(B, V, seed=70)
     x[0, :] = -float("inf")                      # nothing valid
     x[1, ::2] = float("nan")
@@ -160,8 +168,30 @@ def test_filtered_many_candidates(dev, fp64):
     assert got[0] < 20000 and 5000 <= got[4] < 17000 and got[5] < 9000
 
 
-def test_filters_off_equals_unfiltered(dev):
-    B, V = 40, 7001
+@pytest.mark.parametrize("V", [3000, 20000])
+def test_filtered_adjacent_floats(dev, V):
+    """The 100 largest logits are consecutive float32 values above 5: the
+    selections must resolve keys that differ only in their last bits."""
+    B = 4
+    x = synthetic.logits(B, V, std=1.0, seed=130) - 5.0
+    chain = np.nextafter(np.float32(5.0), np.float32(np.inf)) * np.ones(100, dtype=np.float32)
+    for j in range(1, 100):
+        chain[j] = np.nextafter(chain[j - 1], np.float32(np.inf))
+    for r in range(B):
+        x[r, torch.randperm(V, generator=torch.Generator().manual_seed(131 + r))[:100]] = \
+            torch.from_numpy(chain)
+    t = torch.full((B,), 0.9)
+    k = torch.tensor([37, 1, 0, 99], dtype=torch.int32)
+    p = torch.tensor([1.0, 1.0, 0.5, 0.3])
+    for fp64 in (False, True):
+        got = _run(dev, x, t, k, p, None, seed=14, offset=15, fp64=fp64)
+        idx, gap, margin = _oracle(x, t, k, p, None, seed=14, offset=15, fp64=fp64)
+        _check(got, idx, gap, margin, f"adjacent floats V={V} fp64={fp64}")
+
+
+@pytest.mark.parametrize("V", [7001, 40000])
+def test_filters_off_equals_unfiltered(dev, V):
+    B = 40
     x = synthetic.logits(B, V, seed=80)
     x[1, 5] = float("nan")
     x[2, :] = -float("inf")
@@ -179,7 +209,7 @@ def test_filters_off_equals_unfiltered(dev):
 
 
 def test_draws_stay_in_the_kept_set(dev):
-    B, V = 32, 4096
+    B, V = 32, 20000
     x = synthetic.logits(B, V, seed=90)
     t = synthetic.temperatures(B, seed=91)
     k, p, m = synthetic.filter_settings(B, V, seed=92)
@@ -218,9 +248,10 @@ def test_filtered_law_chi_square(dev, fp64):
     assert chi2 < stats.chi2_quantile(keep.size - 1, 1e-6)
 
 
-def test_filtered_qwen_vocabulary(dev):
-    B, V = 64, 151936
-    say("filtered parity at B=64 V=151936")
+@pytest.mark.parametrize("B", [8, 64])
+def test_filtered_qwen_vocabulary(dev, B):
+    V = 151936
+    say(f"filtered parity at B={B} V={V}")
     x = synthetic.logits(B, V, seed=100)
     t = synthetic.temperatures(B, seed=101)
     k, p, m = synthetic.filter_settings(B, V, seed=102)
