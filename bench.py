@@ -14,8 +14,9 @@ over the timed steps; p10/p50/p90 of the per-step times beside it);
 `roofline` prices that kernel's algorithmic HBM bytes against its own average
 duration, read from HIP events the library records around it on the stream it
 runs on, over the same timed region; `standalone_sampler` does the same for
-fs_sample_logits; `cpu_baseline` is the float64 CPU oracle computing the same
-step on this host's cores.
+fs_sample_logits, `filtered_sampler` for fs_sample_logits_filtered (top-k,
+top-p, min-p) beside the eager transformers chain; `cpu_baseline` is the
+float64 CPU oracle computing the same step on this host's cores.
 """
 from __future__ import annotations
 
