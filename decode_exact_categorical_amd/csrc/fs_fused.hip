@@ -173,14 +173,24 @@ struct Pipeline {
 };
 
 // Whether the noise is folded into the accumulators inside the k-loop: float32
-// noise over bf16 and MXFP4 weights is (MXFP4's block scales are applied as
-// the elements are widened, so the accumulator holds the logit itself).
-// Float64 noise, and any noise over FP8 weights (whose per-row scale
-// multiplies the sum only), is added after the k-loop, still in the same pass.
+// noise is over bf16 and MXFP4 weights (MXFP4's block scales are applied as
+// the elements are widened, so its accumulator holds the logit itself), and
+// over FP8 weights at 16 and 48 columns: FP8's row scale multiplies the
+// finished sum, so its fold adds (bias + t g) / scale and keeps the scales
+// live through the k-loop, which the 32- and 64-column FP8 kernels have no
+// registers for (measured: they spill and run slower; they add the noise
+// after the k-loop, as float64 noise does everywhere).  Rows whose scale is
+// zero or not finite fold nothing and are scored from their sums after the
+// k-loop.
 template <int NB, int EPI, bool HAS_BIAS, int WF>
 struct FoldNoise {
-  static constexpr bool value = EPI == kEpiSample32 && WF != kWFp8;
+  static constexpr bool value = EPI == kEpiSample32 && (WF != kWFp8 || (NB & 1) != 0);
 };
+
+// An FP8 row scale the fold can divide by: nonzero and finite.
+__device__ __forceinline__ bool fold_scale_ok(float s) {
+  return s != 0.0f && __builtin_fabsf(s) < __builtin_inff();
+}
 
 // BV4: the bias rows are 16-byte aligned (V % 4 == 0), so a fragment's four
 // biases come in one load.
@@ -390,6 +400,20 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // FP8 weights: the scales of the lane's 4 output rows in each row block
+    // (clamped, always valid addresses), for the finished sums; loaded here
+    // when the fold needs them inside the k-loop, else after it.
+    float wsc[kRB][4];
+    auto load_scales = [&]() {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wsc[rb][j] = a.w_scale[i0 + j < V ? i0 + j : V - 1];
+      }
+    };
+    if constexpr (W8 && kFold) load_scales();
+
     // Float32 noise of fragment slot f = 4*rb + cb (rb < kRB): bias + t * g of
     // the lane's 4 rows, or the bias alone for greedy and infinite-temperature
     // columns; the caller folds it into acc[rb][cb] (FS_FOLD_SLOT).  The bias
@@ -452,6 +476,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         dst[j] = a.bias[b * V + i];
       }
     };
+    // What a fold adds to row j of row block rb: the value itself, or over FP8
+    // weights the value divided by the row's scale (nothing for a scale the
+    // fold cannot divide by).
+    auto fold_value = [&](float v, int rb, int j) -> float {
+      if constexpr (W8) return fold_scale_ok(wsc[rb][j]) ? v / wsc[rb][j] : 0.0f;
+      return v;
+    };
 #define FS_FOLD_SLOT(F, BETA)                                            \
   do {                                                                   \
     const int f_ = (F);                                                  \
@@ -460,10 +491,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       _Pragma("unroll") for (int rb2 = 0; rb2 < kRB; ++rb2)              \
         _Pragma("unroll") for (int cb2 = 0; cb2 < NB; ++cb2)             \
           if (rb2 * kNoiseSlots + cb2 == f_) {                           \
-            acc[rb2][cb2][0] += n_.v[0];                                 \
-            acc[rb2][cb2][1] += n_.v[1];                                 \
-            acc[rb2][cb2][2] += n_.v[2];                                 \
-            acc[rb2][cb2][3] += n_.v[3];                                 \
+            acc[rb2][cb2][0] += fold_value(n_.v[0], rb2, 0);             \
+            acc[rb2][cb2][1] += fold_value(n_.v[1], rb2, 1);             \
+            acc[rb2][cb2][2] += fold_value(n_.v[2], rb2, 2);             \
+            acc[rb2][cb2][3] += fold_value(n_.v[3], rb2, 3);             \
           }                                                              \
     }                                                                    \
   } while (0)
@@ -750,15 +781,25 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         // The next chunk's H is loaded first and stored last: waiting for it
         // earlier would also wait for every W load issued before it (loads
         // complete in order), draining the pipe to one pair.
+        // Noise slots 4c + j are folded two per pair, their biases loaded a
+        // chunk ahead.
         h_load(cn, Half1{});
         __builtin_amdgcn_sched_barrier(0);
         mma8(pa, buf, 0);
+        FS_FOLD_SLOT(4 * c, ba0);
+        FS_FOLD_SLOT(4 * c + 1, ba1);
         __builtin_amdgcn_sched_barrier(0);
         load_pair(pa, 2 * c + 2);
+        bias_slot_load(ba0, 4 * c + 4);
+        bias_slot_load(ba1, 4 * c + 5);
         __builtin_amdgcn_sched_barrier(0);
         mma8(pb, buf, 128);
+        FS_FOLD_SLOT(4 * c + 2, bb0);
+        FS_FOLD_SLOT(4 * c + 3, bb1);
         __builtin_amdgcn_sched_barrier(0);
         load_pair(pb, 2 * c + 3);
+        bias_slot_load(bb0, 4 * c + 6);
+        bias_slot_load(bb1, 4 * c + 7);
         __builtin_amdgcn_sched_barrier(0);
         h_store(buf ^ 1, Half0{});
         h_store(buf ^ 1, Half1{});
@@ -859,7 +900,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
     // Short contractions (fewer k-steps, or MXFP4 chunks, than slots): the
     // remaining slots.
-    for (int f = !W4 ? NC * kStepsPerChunk : (Pipe::w4_long ? 4 * NC : 2 * (NC + (NC & 1)));
+    for (int f = W8 ? 4 * NC : (!W4 ? NC * kStepsPerChunk : (Pipe::w4_long ? 4 * NC : 2 * (NC + (NC & 1))));
          f < kRB * kNoiseSlots; ++f) {
       f32x4 bt = f32x4{0.f, 0.f, 0.f, 0.f};
       bias_slot_load(bt, f);
@@ -867,17 +908,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
 #undef FS_FOLD_SLOT
 
-    // FP8 weights: the scales of the lane's 4 output rows in each row block,
-    // applied to the finished dot products (clamped, always valid addresses).
-    float wsc[kRB][4];
-    if constexpr (W8) {
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wsc[rb][j] = a.w_scale[i0 + j < V ? i0 + j : V - 1];
-      }
-    }
+    if constexpr (W8 && !kFold) load_scales();
 
     // End of pass: scores of this wave's fragments.
     T bm[NB];
@@ -986,7 +1017,28 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           // past B are scored too and never published.
           float s[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[j] = y[j] * inv_t[cb];
+          for (int j = 0; j < 4; ++j) s[j] = (W8 ? y[j] * wsc[rb][j] : y[j]) * inv_t[cb];
+          if constexpr (W8) {
+            // Rows whose scale the fold could not divide by (zero or not
+            // finite) carry their bare sums: score them here (a wave-uniform
+            // branch, taken only when some lane has such a row).
+            bool bad = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bad |= !fold_scale_ok(wsc[rb][j]);
+            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+              const ColInfo ci = cols[16 * cb + col];
+              const int64_t bcol = bt0 + 16 * cb + col < B ? bt0 + 16 * cb + col : B - 1;
+              float beta[4];
+              load_bias4(a, bcol, i0, beta);
+              const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), ci.rid);
+              const float g[4] = {gumbel_f32(w.w0), gumbel_f32(w.w1), gumbel_f32(w.w2),
+                                  gumbel_f32(w.w3)};
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (!fold_scale_ok(wsc[rb][j]))
+                  s[j] = (y[j] * wsc[rb][j] + beta[j]) * ci.inv_t + (ci.mode == kGreedy ? 0.0f : g[j]);
+            }
+          }
           if (inf_any[cb]) {
             const ColInfo ci = cols[16 * cb + col];
             if (ci.mode == kInfT) {
@@ -1213,13 +1265,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   if (tid == 0) clear_counter(a.counters + btile);
 }
 
-// FP8 weights take no bias template: their noise is never folded, and the
-// bias is read after the k-loop whichever way.  bf16 and MXFP4 weights fold
-// the bias with the float32 noise.
+// Kernels that fold the float32 noise fold the bias with it (a bias
+// template); the others read the bias after the k-loop.
 template <int NB, int WF>
 hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream) {
   constexpr bool BF = WF == kWBf16;
-  constexpr bool FB = WF != kWFp8;
+  constexpr bool FB = FoldNoise<NB, kEpiSample32, false, WF>::value;
   switch (epi) {
     case kEpiSample32:
       if (a.bias && FB && a.bias_vec4)

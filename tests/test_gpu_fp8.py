@@ -149,6 +149,32 @@ def test_w8_sampling_parity(dev, case, fp64):
     check_index_parity(got.cpu().numpy(), ref, gap, f"fp8 B={B} V={V} fp64={fp64}")
 
 
+@pytest.mark.parametrize("B", [16, 20, 40])
+def test_w8_degenerate_scales(dev, B):
+    """Rows whose scale is zero (an all-zero row quantises so), negative or NaN,
+    at batch widths whose kernels fold the noise into the sums (16, 48 columns)
+    and one that adds it after the k-loop (32): the logit is the product of
+    the scale and the sum either way."""
+    D, V = 512, 3000
+    say(f"fp8 degenerate scales B={B}")
+    H, W8, scale, temp, bias = _case(B, D, V, bias=True, greedy_rows=(1,), seed_base=70)
+    scale = scale.clone()
+    scale[[5, 6, 77, 1500]] = 0.0
+    scale[[9, 2999]] = -scale[[9, 2999]]
+    scale[300] = float("nan")
+    # zero-scale tokens carry logit 0: with a large bias they must win
+    bias[0, [5, 6, 77, 1500]] = 100.0
+    bias[2, 77] = 200.0
+    Hd, W8d, sd, td, bd = to_dev(H, W8, scale, temp, bias, dev=dev)
+    got = fs.sample_fused_w8(Hd, W8d, sd, td, bd, seed=41, offset=42)
+    torch.cuda.synchronize()
+    ref, gap, _ = oracle.sample_fused_w8(H, W8.numpy(), scale.numpy(), temp.numpy(), bias.numpy(),
+                                         seed=41, offset=42)
+    got = got.cpu().numpy()
+    check_index_parity(got, ref, gap, f"fp8 degenerate scales B={B}")
+    assert got[0] in (5, 6, 77, 1500) and got[2] == 77
+
+
 def test_w8_fused_equals_standalone_on_its_logits(dev):
     say("fp8 fused vs standalone on the FP8 path's logits")
     B, D, V = 40, 512, 4096
