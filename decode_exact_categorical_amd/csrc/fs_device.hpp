@@ -156,10 +156,66 @@ __device__ __forceinline__ double neg_inf<double>() {
 
 constexpr int32_t kNoIndex = 0x7fffffff;
 
+// A 32-bit lane exchange by DPP (no LDS): quad_perm [1,0,3,2] and [2,3,0,1]
+// swap the lanes of xor 1 and xor 2; row_half_mirror pairs lane j with 7 - j
+// of each 8 and row_mirror lane j with 15 - j of each 16.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, 0xf, 0xf, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_val(float v) {
+  return __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(v)));
+}
+template <int kCtrl>
+__device__ __forceinline__ double dpp_val(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t r = (uint64_t)dpp_u32<kCtrl>((uint32_t)u) | ((uint64_t)dpp_u32<kCtrl>((uint32_t)(u >> 32)) << 32);
+  return __longlong_as_double((long long)r);
+}
+__device__ __forceinline__ float lane_val(float v, int l) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), l));
+}
+__device__ __forceinline__ double lane_val(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t r = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l) |
+                     ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l) << 32);
+  return __longlong_as_double((long long)r);
+}
+
 // Reduce (m, i) over the lanes of one wave64 that share `mask_bits` low lane
-// bits: xor-shuffles over the remaining bits from `lo_bit` to bit 5.
+// bits: xor-shuffles over the remaining bits from `lo_bit` to bit 5.  For the
+// whole wave (lo_bit = 0, every lane active) the best of each 16 lanes is
+// formed by DPP exchanges (each step pairs groups that already agree, so any
+// pairing gives the same best) and the four rows meet through readlane: no
+// LDS round trips.  The best under the total order is unique, so both ways
+// give the same result.
 template <typename T>
 __device__ __forceinline__ void wave_argmax_xor(T& m, int32_t& i, int lo_bit) {
+  if (lo_bit == 0) {
+    auto step = [&](T om, int32_t oi) {
+      const bool take = beats_nb(om, oi, m, i);
+      m = take ? om : m;
+      i = take ? oi : i;
+    };
+    step(dpp_val<0xb1>(m), (int32_t)dpp_u32<0xb1>((uint32_t)i));
+    step(dpp_val<0x4e>(m), (int32_t)dpp_u32<0x4e>((uint32_t)i));
+    step(dpp_val<0x141>(m), (int32_t)dpp_u32<0x141>((uint32_t)i));
+    step(dpp_val<0x140>(m), (int32_t)dpp_u32<0x140>((uint32_t)i));
+    T bm = lane_val(m, 0);
+    int32_t bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+      const T om = lane_val(m, 16 * r);
+      const int32_t oi = __builtin_amdgcn_readlane(i, 16 * r);
+      const bool take = beats_nb(om, oi, bm, bi);
+      bm = take ? om : bm;
+      bi = take ? oi : bi;
+    }
+    m = bm;
+    i = bi;
+    return;
+  }
   for (int b = lo_bit; b < 6; ++b) {
     const T om = __shfl_xor(m, 1 << b, 64);
     const int32_t oi = __shfl_xor(i, 1 << b, 64);

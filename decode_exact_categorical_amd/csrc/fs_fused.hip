@@ -1177,29 +1177,101 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
     wait_stores_complete();
 
-    // Stage 2: wave w takes rows w, w + 8, ... of the tile; a row's
-    // nT * kTopKMax candidates are read once (clamped addresses), then its
-    // places are picked one after the other.
+    // Stage 2: wave w takes rows w, w + 8, ... of the tile.  Lane l reads the
+    // whole sorted lists of tiles l, l + 64, l + 128, l + 192 (clamped
+    // addresses).  Among any k candidates the k-th best bounds the row's k-th
+    // place from below, so with theta the k-th best of the tile maxima, only
+    // candidates at or above theta can take a place: a prefix of each list,
+    // about k tiles' worth.  Those go to a per-wave LDS list (the H staging
+    // buffer is free now), and the places are picked from it, two candidates
+    // a lane; a row with more of them (rows with fewer than k valid scores)
+    // picks them from the lists themselves.
     if (!finish_last(a.counters + btile, (uint32_t)nT)) return;
-    constexpr int kPer = kMaxFusedTiles * kTopKMax / 64;
-    const int n = a.nT * kTopKMax;
+    constexpr int kTilesPerLane = kMaxFusedTiles / 64;
+    constexpr int kPer = kTilesPerLane * kTopKMax;
+    constexpr int kSurvPerLane = 2;
+    static_assert(kWaves * 64 * kSurvPerLane * sizeof(Cand<T>) <= sizeof(hs),
+                  "the survivors of every wave fit in the H staging buffer");
+    Cand<T>* const surv = reinterpret_cast<Cand<T>*>(&hs[0][0][0]) + wave * 64 * kSurvPerLane;
+    // The tile maxima (place 0 of each list) of row b, clamped addresses.
+    auto load_maxima = [&](Cand<T> (&mx)[kTilesPerLane], int64_t b) {
+      const Cand<T>* rc = reinterpret_cast<const Cand<T>*>(a.cand) + b * a.nT * kTopKMax;
+#pragma unroll
+      for (int j = 0; j < kTilesPerLane; ++j) {
+        const int t = lane + 64 * j;
+        mx[j] = load_cand(rc + (t < a.nT ? t * kTopKMax : 0));
+        if (t >= a.nT) mx[j] = Cand<T>{neg_inf<T>(), kNoIndex};
+      }
+    };
+    // A row's maxima are requested with the previous row's list loads, so each
+    // row costs one round trip to the coherence point.
+    Cand<T> mxn[kTilesPerLane];
+    if (bt0 + wave < B) load_maxima(mxn, bt0 + wave);
 #pragma unroll 1
     for (int i = wave; i < kTile; i += kWaves) {
       const int64_t b = bt0 + i;
       if (b >= B) break;
       const Cand<T>* rc = reinterpret_cast<const Cand<T>*>(a.cand) + b * a.nT * kTopKMax;
+      // theta is the k-th place among the tile maxima.
+      Cand<T> mx[kTilesPerLane];
+#pragma unroll
+      for (int j = 0; j < kTilesPerLane; ++j) mx[j] = mxn[j];
+      if (i + kWaves < kTile && b + kWaves < B) load_maxima(mxn, b + kWaves);
+      Cand<T> th = Cand<T>{neg_inf<T>(), kNoIndex};
+#pragma unroll 1
+      for (int r = 0; r < a.k; ++r) th = next_place(mx, r == 0, th.m, th.idx);
+      // Then the rest of the lists whose maximum is at or above theta (the
+      // others cannot hold a survivor).
       Cand<T> c[kPer];
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int e = lane + 64 * q;
-        c[q] = load_cand(rc + (e < n ? e : n - 1));
-        if (e >= n) c[q] = Cand<T>{neg_inf<T>(), kNoIndex};
+      for (int j = 0; j < kTilesPerLane; ++j) {
+        const int t = lane + 64 * j;
+        const bool live = t < a.nT && !after(mx[j].m, mx[j].idx, th.m, th.idx);
+        c[j * kTopKMax] = mx[j];
+#pragma unroll
+        for (int p = 1; p < kTopKMax; ++p) {
+          c[j * kTopKMax + p] = Cand<T>{neg_inf<T>(), kNoIndex};
+          if (live) c[j * kTopKMax + p] = load_cand(rc + t * kTopKMax + p);
+        }
       }
+      // The survivors (at or above theta) and this lane's offset among them.
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) cnt += after(c[q].m, c[q].idx, th.m, th.idx) ? 0u : 1u;
+      uint32_t off = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(off, o);
+        if (lane >= o) off += v;
+      }
+      const uint32_t total = __shfl(off, 63);
+      off -= cnt;
       Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
+      if (total <= 64u * kSurvPerLane) {
+#pragma unroll
+        for (int q = 0; q < kPer; ++q)
+          if (!after(c[q].m, c[q].idx, th.m, th.idx)) surv[off++] = c[q];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        Cand<T> c2[kSurvPerLane];
+#pragma unroll
+        for (int q = 0; q < kSurvPerLane; ++q)
+          c2[q] = (uint32_t)(lane + 64 * q) < total ? surv[lane + 64 * q] : Cand<T>{neg_inf<T>(), kNoIndex};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll 1
-      for (int r = 0; r < a.k; ++r) {
-        pl = next_place(c, r == 0, pl.m, pl.idx);
-        if (lane == 0) a.out[b * a.k + r] = pl.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)pl.idx;
+        for (int r = 0; r < a.k; ++r) {
+          pl = next_place(c2, r == 0, pl.m, pl.idx);
+          if (lane == 0) a.out[b * a.k + r] = pl.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)pl.idx;
+        }
+      } else {
+#pragma unroll 1
+        for (int r = 0; r < a.k; ++r) {
+          pl = next_place(c, r == 0, pl.m, pl.idx);
+          if (lane == 0) a.out[b * a.k + r] = pl.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)pl.idx;
+        }
       }
     }
     if (tid == 0) clear_counter(a.counters + btile);
