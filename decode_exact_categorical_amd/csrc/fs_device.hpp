@@ -346,6 +346,39 @@ __device__ __forceinline__ void topk_insert(T (&m)[K], int32_t (&id)[K], T s, in
   id[0] = top ? i : id[0];
 }
 
+// The top kTopKMax of two lists of kTopKMax places, each sorted best first
+// and holding distinct candidates: a bitonic merge.  The best of a[j] and
+// b[K-1-j] for every j is a bitonic sequence holding the top K of both lists;
+// three half-cleaner stages sort it best first.  Compares use the place
+// order (larger score, then smaller index), so the result is the unique
+// sorted top K; (-inf, kNoIndex) fillers stay at the end.
+template <typename T>
+__device__ __forceinline__ void merge_top(T (&am)[kTopKMax], int32_t (&ai)[kTopKMax],
+                                          const T (&bm)[kTopKMax], const int32_t (&bi)[kTopKMax]) {
+  static_assert(kTopKMax == 8, "three half-cleaner stages");
+#pragma unroll
+  for (int j = 0; j < kTopKMax; ++j) {
+    const T om = bm[kTopKMax - 1 - j];
+    const int32_t oi = bi[kTopKMax - 1 - j];
+    const bool take = beats_nb(om, oi, am[j], ai[j]);
+    am[j] = take ? om : am[j];
+    ai[j] = take ? oi : ai[j];
+  }
+#pragma unroll
+  for (int d = kTopKMax / 2; d >= 1; d >>= 1)
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j)
+      if ((j & d) == 0) {
+        const bool sw = beats_nb(am[j + d], ai[j + d], am[j], ai[j]);
+        const T tm = am[j];
+        const int32_t ti = ai[j];
+        am[j] = sw ? am[j + d] : am[j];
+        ai[j] = sw ? ai[j + d] : ai[j];
+        am[j + d] = sw ? tm : am[j + d];
+        ai[j + d] = sw ? ti : ai[j + d];
+      }
+}
+
 // The next place after (pm, pi) among a wave's candidates: every lane offers
 // its best candidate that comes after the previous place (first: any), and
 // the lanes that differ only in bits lo_bit..5 of the lane id pick the best

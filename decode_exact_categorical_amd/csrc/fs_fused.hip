@@ -970,17 +970,47 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           for (int j = 0; j < 4; ++j)
             topk_insert(lm, li, i0 + j < r1 ? s[j] : neg_inf<T>(), (int32_t)(i0 + j));
         }
-        Cand<T> c[2 * kTopKMax];
+        // The column's running places (held by its row-group-0 lane), then
+        // the other row groups' lists (lanes 16 and 32 apart), merged in:
+        // bitonic merges of sorted lists with float32 scores; with float64
+        // scores (whose exchanged lists would need more registers than the
+        // 64-column kernel has) place by place.
+        if constexpr (EPI == kEpiTopK64) {
+          Cand<T> c[2 * kTopKMax];
 #pragma unroll
-        for (int j = 0; j < kTopKMax; ++j) {
-          c[j] = Cand<T>{lm[j], li[j]};
-          c[kTopKMax + j] = grp == 0 ? tkc[wave][16 * cb + col][j] : Cand<T>{neg_inf<T>(), kNoIndex};
-        }
-        Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
+          for (int j = 0; j < kTopKMax; ++j) {
+            c[j] = Cand<T>{lm[j], li[j]};
+            c[kTopKMax + j] = grp == 0 ? tkc[wave][16 * cb + col][j] : Cand<T>{neg_inf<T>(), kNoIndex};
+          }
+          Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
 #pragma unroll 1
-        for (int r = 0; r < kTopKMax; ++r) {
-          pl = next_place(c, r == 0, pl.m, pl.idx, 4);
-          if (grp == 0) tkc[wave][16 * cb + col][r] = pl;
+          for (int r = 0; r < kTopKMax; ++r) {
+            pl = next_place(c, r == 0, pl.m, pl.idx, 4);
+            if (grp == 0) tkc[wave][16 * cb + col][r] = pl;
+          }
+        } else {
+          T om[kTopKMax];
+          int32_t oi[kTopKMax];
+#pragma unroll
+          for (int j = 0; j < kTopKMax; ++j) {
+            const Cand<T> o = grp == 0 ? tkc[wave][16 * cb + col][j] : Cand<T>{neg_inf<T>(), kNoIndex};
+            om[j] = o.m;
+            oi[j] = o.idx;
+          }
+          merge_top(lm, li, om, oi);
+#pragma unroll
+          for (int x = 16; x <= 32; x <<= 1) {
+#pragma unroll
+            for (int j = 0; j < kTopKMax; ++j) {
+              om[j] = __shfl_xor(lm[j], x, 64);
+              oi[j] = __shfl_xor(li[j], x, 64);
+            }
+            merge_top(lm, li, om, oi);
+          }
+          if (grp == 0) {
+#pragma unroll
+            for (int j = 0; j < kTopKMax; ++j) tkc[wave][16 * cb + col][j] = Cand<T>{lm[j], li[j]};
+          }
         }
       }
     } else if (EPI == kEpiStore || kFold) {
