@@ -104,6 +104,13 @@ def _load():
         lib.oracle_filtered_repeated_row.restype = None
         lib.oracle_filtered_repeated_row.argtypes = [P, i64, ctypes.c_float, i32, ctypes.c_float,
                                                      ctypes.c_float, u64, u64, P, i64, i32, P]
+        lib.oracle_accept_uniform.restype = ctypes.c_double
+        lib.oracle_accept_uniform.argtypes = [u64, u64, u32]
+        lib.oracle_verify.restype = None
+        lib.oracle_verify.argtypes = [P, P, P, i64, i64, i64, P, u64, u64, P, i32, P, P, P, P]
+        lib.oracle_verify_repeated.restype = None
+        lib.oracle_verify_repeated.argtypes = [P, P, P, i64, i64, ctypes.c_float, u64, u64, P,
+                                               i64, i32, P, P]
         _lib = lib
         return lib
 
@@ -440,3 +447,52 @@ def filtered_repeated_row(row_f32, temp: float, *, top_k: int = 0, top_p: float 
                                          float(top_p), float(min_p), seed, offset, _ptr(rid),
                                          rid.shape[0], int(fp64_noise), _ptr(out))
     return out
+
+
+def accept_uniform(seed: int, pos: int, row_id: int) -> float:
+    """The acceptance uniform of verification position `pos` (offset + i) of
+    logical row `row_id`."""
+    return float(_load().oracle_accept_uniform(seed, pos, row_id))
+
+
+def verify(target_f32, draft_f32, tokens, temp, *, seed: int, offset: int, row_ids=None,
+           fp64_noise: bool = False):
+    """(accept_len int64[B], out int64[B, K+1], margin float64[B], gap float64[B]):
+    speculative-decoding verification of draft tokens[B, K] against target
+    logits[B, K+1, V] and draft logits[B, K, V] (float32)."""
+    tg = np.ascontiguousarray(np.asarray(target_f32, dtype=np.float32))
+    dr = np.ascontiguousarray(np.asarray(draft_f32, dtype=np.float32))
+    B, K1, V = tg.shape
+    K = K1 - 1
+    assert dr.shape == (B, K, V)
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).reshape(B, K))
+    t = np.ascontiguousarray(np.broadcast_to(np.asarray(temp, dtype=np.float32), (B,)).copy())
+    rid = _u32_or_none(row_ids, B)
+    acc = np.zeros(B, dtype=np.int64)
+    out = np.zeros((B, K + 1), dtype=np.int64)
+    margin = np.zeros(B, dtype=np.float64)
+    gap = np.zeros(B, dtype=np.float64)
+    _load().oracle_verify(_ptr(tg), _ptr(dr), _ptr(tok), B, K, V, _ptr(t), seed, offset,
+                          _ptr(rid), int(fp64_noise), _ptr(acc), _ptr(out), _ptr(margin),
+                          _ptr(gap))
+    return acc, out, margin, gap
+
+
+def verify_repeated(target_f32, draft_f32, tokens, temp: float, *, seed: int, offset: int,
+                    row_ids, fp64_noise: bool = False):
+    """(accept_len, out) for many logical rows sharing one target block
+    [K+1, V] and one draft block [K, V], with draft tokens[n, K] and ids
+    row_ids[n]."""
+    tg = np.ascontiguousarray(np.asarray(target_f32, dtype=np.float32))
+    dr = np.ascontiguousarray(np.asarray(draft_f32, dtype=np.float32))
+    K1, V = tg.shape
+    K = K1 - 1
+    assert dr.shape == (K, V)
+    rid = np.ascontiguousarray(np.asarray(row_ids, dtype=np.uint32).reshape(-1))
+    n = rid.shape[0]
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).reshape(n, K))
+    acc = np.zeros(n, dtype=np.int64)
+    out = np.zeros((n, K + 1), dtype=np.int64)
+    _load().oracle_verify_repeated(_ptr(tg), _ptr(dr), _ptr(tok), K, V, float(temp), seed,
+                                   offset, _ptr(rid), n, int(fp64_noise), _ptr(acc), _ptr(out))
+    return acc, out

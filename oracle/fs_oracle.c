@@ -42,6 +42,12 @@
  *         probability reaches top_p, the crossing token included, over the
  *         top-k prefix; min-p keeps p >= min_p * p_max; every filter keeps at
  *         least one token).
+ *   [SPV] spec-decode-ops kernel card: its description and usage example of
+ *         `verify` (speculative-decoding rejection sampling after Leviathan,
+ *         Kalman, Matias, ICML 2023, and Chen et al. 2023: accept the draft
+ *         token with probability min(1, p_t / p_d), replace the first
+ *         rejection by a draw from max(p_t - p_d, 0) renormalised, append a
+ *         bonus draw from the target's last position when all are accepted).
  *
  * Definition computed (per batch row b, logical row id r = row_ids[b] or b):
  *   y_i   = sum_d H[b,d] * W[i,d]           float64, d ascending   [FS (1)]
@@ -64,6 +70,7 @@
  *   filtered sampling [SD]: the draw above restricted to the kept set of
  *         the filter chain on the row's logits (oracle_filter_kept below);
  *         tokens outside it score -inf.
+ *   verification [SPV]: see the block comment above oracle_verify.
  *
  * Parity pins (tests marked "not gpu"): the Philox words against an
  * independent engine (the one PyTorch ships as a header); the uniform, E and
@@ -809,4 +816,253 @@ void oracle_filtered_repeated_row(const float *logits, int64_t V, float temp,
         free(s);
     }
     free(kept);
+}
+
+/* ------------------------------------------------------------------ */
+/* Speculative-decoding verification [SPV]: the spec-decode-ops card's  */
+/* description of `verify` (rejection sampling after Leviathan et al.   */
+/* 2023 and Chen et al. 2023) and its usage example (target logits     */
+/* [B, K+1, V], draft logits [B, K, V], draft tokens [B, K]; the tokens */
+/* out[b, 0 .. accept_len] are emitted).                                */
+/*                                                                      */
+/* Per row b (logical id r) and position i < K, with p_t and p_d the    */
+/* temperature softmaxes of target row i and draft row i:               */
+/*   u_i  = the 52-bit midpoint uniform of Philox counter               */
+/*          (2^32 - 1, r, offset + i): words 0 and 1, as the fp64 noise */
+/*          takes them.  Vocabulary words never reach that counter      */
+/*          value, so u_i is independent of every noise value;          */
+/*   accept x_i iff u_i * p_d(x_i) < p_t(x_i), i.e. with probability    */
+/*          min(1, p_t(x_i) / p_d(x_i)) (a token outside [0, V) has     */
+/*          probability 0 under both and is rejected);                  */
+/*   accept_len = the first rejected position, or K.                    */
+/* out[j] = x_j for j < accept_len; -1 past accept_len; and out at      */
+/* accept_len is                                                         */
+/*   a rejected position: a draw from max(p_t - p_d, 0) renormalised,   */
+/*          as the Gumbel-max of log r_j with the noise of counter      */
+/*          position offset + accept_len (the standalone sampler's      */
+/*          stream at that offset); if the residual is all zero (p_t    */
+/*          equals p_d), the draw from p_t itself;                      */
+/*   K accepted: the bonus draw from target row K, which is the         */
+/*          standalone sampler's draw on that row at offset + K.        */
+/* Greedy rows (!(t > 0)): p is one-hot on the row's first largest      */
+/* valid logit; the draw at a rejected position is the target argmax.   */
+/* ------------------------------------------------------------------ */
+
+/* Temperature softmax of one row, p[0..V), over its valid logits (neither
+ * NaN nor -inf): e_j = exp((y_j - M)/t) with M the largest valid logit, or,
+ * when M = +inf, e_j = 1 on the +inf logits and 0 elsewhere (the limit of
+ * softmax); p_j = e_j / sum e.  Greedy rows: one-hot on the first largest
+ * valid logit.  No valid logit: p = 0.  z[j] receives (y_j - M)/t on rows
+ * whose probabilities go through exp (0 otherwise), for the error bounds
+ * below. */
+static void row_probs(const float *y, int64_t V, double t, double *p, double *z)
+{
+    int64_t am = -1;
+    for (int64_t j = 0; j < V; ++j) {
+        p[j] = 0.0;
+        z[j] = 0.0;
+        if (isnan(y[j]) || y[j] == -INFINITY) continue;
+        if (am < 0 || y[j] > y[am]) am = j;
+    }
+    if (am < 0) return;
+    const double M = (double)y[am];
+    if (!(t > 0.0)) {
+        p[am] = 1.0;
+        return;
+    }
+    double Z = 0.0;
+    for (int64_t j = 0; j < V; ++j) {
+        if (isnan(y[j]) || y[j] == -INFINITY) continue;
+        if (M == INFINITY) {
+            p[j] = (y[j] == INFINITY) ? 1.0 : 0.0;
+        } else {
+            z[j] = ((double)y[j] - M) / t;
+            p[j] = exp(z[j]);
+        }
+        Z += p[j];
+    }
+    for (int64_t j = 0; j < V; ++j) p[j] /= Z;
+}
+
+/* The acceptance uniform of position `pos` (= offset + i) of logical row r. */
+static double accept_uniform(uint64_t seed, uint64_t pos, uint32_t r)
+{
+    uint32_t x[4];
+    words_for(seed, pos, r, 0xFFFFFFFFu, x);
+    uint64_t k = (((uint64_t)x[0] << 32) | (uint64_t)x[1]) >> 12;
+    return ((double)k + 0.5) / 4503599627370496.0;           /* 2^52 */
+}
+
+double oracle_accept_uniform(uint64_t seed, uint64_t pos, uint32_t r)
+{
+    return accept_uniform(seed, pos, r);
+}
+
+/* Relative error allowed to another implementation's probability of token j
+ * when it computes p in float32 (rounding of (y - M) * (1/t), of the exp and
+ * of the normaliser): it grows with |z|.  Used only for the margins. */
+static double prob_tol(double z) { return 4e-7 * (4.0 + fabs(z)); }
+
+typedef struct {
+    double *pt, *pd, *zt, *zd, *s, *g;
+} verify_buf_t;
+
+static int verify_buf_alloc(verify_buf_t *w, int64_t V)
+{
+    size_t n = (size_t)(V > 0 ? V : 1) * sizeof(double);
+    w->pt = (double *)malloc(n);
+    w->pd = (double *)malloc(n);
+    w->zt = (double *)malloc(n);
+    w->zd = (double *)malloc(n);
+    w->s = (double *)malloc(n);
+    w->g = (double *)malloc(n);
+    return w->pt && w->pd && w->zt && w->zd && w->s && w->g;
+}
+
+static void verify_buf_free(verify_buf_t *w)
+{
+    free(w->pt);
+    free(w->pd);
+    free(w->zt);
+    free(w->zd);
+    free(w->s);
+    free(w->g);
+}
+
+/* One row of the verification (see the block comment above).  tg: K+1 rows
+ * of V target logits, dr: K rows of draft logits, tok: K draft tokens.
+ * Writes *accept_len, out[0..K], and two margins for comparisons with
+ * another implementation:
+ *   *margin: the smallest relative distance |u q - a| / max(a, q) of an
+ *     acceptance decision from its boundary over the decided positions
+ *     (0 when a and q are both below 1e-30, where float32 underflow decides);
+ *   *gap: the margin of the draw at accept_len: the plain top-2 gap of the
+ *     perturbed scores for the bonus and fallback draws (+inf on greedy
+ *     rows); for the residual draw, the winner's score lowered by its error
+ *     bound minus the best other score raised by its own, where token j's
+ *     residual may move by prob_tol * (p_t + p_d) (so rows whose draw rests
+ *     on a residual of rounding size get a negative gap). */
+static void verify_row(const float *tg, const float *dr, const int64_t *tok, int64_t K,
+                       int64_t V, double t, uint64_t seed, uint64_t offset, uint32_t r,
+                       int fp64, verify_buf_t *w, int64_t *accept_len, int64_t *out,
+                       double *margin, double *gap)
+{
+    *margin = INFINITY;
+    int64_t L = K;
+    for (int64_t i = 0; i < K; ++i) {
+        row_probs(tg + i * V, V, t, w->pt, w->zt);
+        row_probs(dr + i * V, V, t, w->pd, w->zd);
+        const int64_t x = tok[i];
+        double a = 0.0, q = 0.0;
+        if (x >= 0 && x < V) {
+            a = w->pt[x];
+            q = w->pd[x];
+        }
+        const double u = accept_uniform(seed, offset + (uint64_t)i, r);
+        if (a > 0.0 || q > 0.0) {
+            double d = (fmax(a, q) < 1e-30) ? 0.0 : fabs(u * q - a) / fmax(a, q);
+            if (d < *margin) *margin = d;
+        }
+        if (!(u * q < a)) {
+            L = i;
+            break;
+        }
+    }
+    *accept_len = L;
+    for (int64_t j = 0; j <= K; ++j) out[j] = (j < L) ? tok[j] : -1;
+    const uint64_t pos = offset + (uint64_t)L;
+    const float *y = tg + L * V;
+    double best;
+    if (L == K || !(t > 0.0)) {
+        /* the bonus draw, or a greedy row's target argmax */
+        for (int64_t j = 0; j < V; ++j)
+            w->s[j] = score_of((double)y[j], 0.0, t, seed, pos, r, j, fp64);
+        select_row(w->s, V, &out[L], gap, &best);
+        if (!(t > 0.0)) *gap = INFINITY;
+        return;
+    }
+    /* residual max(p_t - p_d, 0) of position L (pt, pd hold its rows) */
+    int any = 0;
+    for (int64_t j = 0; j < V; ++j) {
+        double d = w->pt[j] - w->pd[j];
+        w->s[j] = d > 0.0 ? d : 0.0;
+        any |= d > 0.0;
+    }
+    if (!any) {
+        for (int64_t j = 0; j < V; ++j)
+            w->s[j] = score_of((double)y[j], 0.0, t, seed, pos, r, j, fp64);
+        select_row(w->s, V, &out[L], gap, &best);
+        return;
+    }
+    for (int64_t j = 0; j < V; ++j) {
+        w->g[j] = gumbel_of(uniform_for(seed, pos, r, j, fp64));
+        double rr = w->s[j];
+        w->s[j] = rr > 0.0 ? log(rr) + w->g[j] : -INFINITY;
+    }
+    double plain;
+    int64_t win;
+    select_row(w->s, V, &win, &plain, &best);
+    out[L] = win;
+    double lo = -INFINITY, hi_other = -INFINITY;
+    for (int64_t j = 0; j < V; ++j) {
+        double mass = w->pt[j] + w->pd[j];
+        if (!(mass > 0.0)) continue;
+        double rr = w->pt[j] - w->pd[j];
+        if (rr < 0.0) rr = 0.0;
+        double tol = fmax(prob_tol(w->zt[j]), prob_tol(w->zd[j])) * mass;
+        if (j == win) {
+            if (rr - tol > 0.0) lo = log(rr - tol) + w->g[j];
+        } else if (rr + tol > 0.0) {
+            double ub = log(rr + tol) + w->g[j];
+            if (ub > hi_other) hi_other = ub;
+        }
+    }
+    *gap = (hi_other == -INFINITY) ? INFINITY : lo - hi_other;
+}
+
+/* Verification of B rows: target[B, K+1, V], draft[B, K, V], tokens[B, K],
+ * temp[B]; accept_len[B], out[B, K+1], margin[B], gap[B]. */
+void oracle_verify(const float *target, const float *draft, const int64_t *tokens,
+                   int64_t B, int64_t K, int64_t V, const float *temp, uint64_t seed,
+                   uint64_t offset, const uint32_t *row_ids, int fp64_noise,
+                   int64_t *accept_len, int64_t *out, double *margin, double *gap)
+{
+    #pragma omp parallel
+    {
+        verify_buf_t w;
+        int ok = verify_buf_alloc(&w, V);
+        #pragma omp for schedule(dynamic)
+        for (int64_t b = 0; b < B; ++b) {
+            if (!ok) continue;
+            uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+            verify_row(target + b * (K + 1) * V, draft + b * K * V, tokens + b * K, K, V,
+                       (double)temp[b], seed, offset, r, fp64_noise, &w, &accept_len[b],
+                       out + b * (K + 1), &margin[b], &gap[b]);
+        }
+        verify_buf_free(&w);
+    }
+}
+
+/* Many logical rows that share one target block [K+1, V] and one draft block
+ * [K, V], each with its own draft tokens tokens[q, 0..K) and logical id
+ * row_ids[q] (law tests). */
+void oracle_verify_repeated(const float *target, const float *draft, const int64_t *tokens,
+                            int64_t K, int64_t V, float temp, uint64_t seed, uint64_t offset,
+                            const uint32_t *row_ids, int64_t n_rows, int fp64_noise,
+                            int64_t *accept_len, int64_t *out)
+{
+    #pragma omp parallel
+    {
+        verify_buf_t w;
+        int ok = verify_buf_alloc(&w, V);
+        #pragma omp for schedule(static)
+        for (int64_t q = 0; q < n_rows; ++q) {
+            if (!ok) continue;
+            double margin, gap;
+            verify_row(target, draft, tokens + q * K, K, V, (double)temp, seed, offset,
+                       row_ids[q], fp64_noise, &w, &accept_len[q], out + q * (K + 1), &margin,
+                       &gap);
+        }
+        verify_buf_free(&w);
+    }
 }
