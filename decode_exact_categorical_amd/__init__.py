@@ -101,6 +101,10 @@ def load_library():
                                                   sz, P]
         lib.fs_workspace_bytes_filtered.restype = sz
         lib.fs_workspace_bytes_filtered.argtypes = [i64, i64]
+        lib.fs_verify.restype = i32
+        lib.fs_verify.argtypes = [P, P, P, i64, i64, i64, P, u64, u64, i32, P, P, P, P, sz, P]
+        lib.fs_workspace_bytes_verify.restype = sz
+        lib.fs_workspace_bytes_verify.argtypes = [i64, i64, i64]
         lib.fs_debug_logits_w8.argtypes = [P, P, P, i64, i64, i64, P, P]
         _lib = lib
         return lib
@@ -339,6 +343,42 @@ def sample_logits_filtered(logits: torch.Tensor, temp, *, top_k=None, top_p=None
                                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(st, "fs_sample_logits_filtered")
     return out
+
+
+def verify(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens: torch.Tensor,
+           temp, *, seed: int, offset: int, row_ids: torch.Tensor | None = None,
+           fp64_noise: bool = False, accept_len: torch.Tensor | None = None,
+           out: torch.Tensor | None = None):
+    """Speculative-decoding verification: (accept_len int64 [B], out int64 [B, K+1]).
+    target_logits float32 [B, K+1, V], draft_logits float32 [B, K, V], draft_tokens int64
+    [B, K]; out[b, :accept_len[b] + 1] are the emitted tokens, distributed as the target's
+    own draws; offset is the absolute position of the first draft token."""
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("target_logits must be a GPU tensor")
+    if target_logits.dim() != 3 or target_logits.shape[1] < 1:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    _need(target_logits, "target_logits", torch.float32, dev, (B, K + 1, V))
+    _need(draft_logits, "draft_logits", torch.float32, dev, (B, K, V))
+    _need(draft_tokens, "draft_tokens", torch.int64, dev, (B, K))
+    t = _temp_tensor(temp, B, dev)
+    rid = _row_ids(row_ids, B, dev)
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int64, device=dev)
+    if out is None:
+        out = torch.empty((B, K + 1), dtype=torch.int64, device=dev)
+    _need(accept_len, "accept_len", torch.int64, dev, (B,))
+    _need(out, "out", torch.int64, dev, (B, K + 1))
+    need = int(lib.fs_workspace_bytes_verify(B, K, V))
+    ws = _workspace(dev, need)
+    st = lib.fs_verify(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), B, K, V,
+                       _ptr(t), seed, offset, int(bool(fp64_noise)), _ptr(accept_len), _ptr(out),
+                       _ptr(rid), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "fs_verify")
+    return accept_len, out
 
 
 def sample_fused_topk(H: torch.Tensor, W: torch.Tensor, temp, bias: torch.Tensor | None = None, *,

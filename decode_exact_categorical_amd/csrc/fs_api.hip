@@ -97,10 +97,13 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 // Workspace layout: a fixed region of kCounterWords completion counters at the
 // start (one per batch tile of the fused kernel, one per row of a standalone
 // launch), then the [B, tiles] candidates (tiles = the larger tile count of the
-// two samplers, at the most CUs the library uses).  Candidates of any call
-// never overlap the counters, so the counters stay zero between calls whatever
-// shapes share the workspace.
+// two samplers, at the most CUs the library uses).  Every entry point (the
+// fused and standalone samplers, Gumbel-top-k, the filtered sampler's split
+// rows, verification) keeps its counters in that region and its other data
+// after it, so no call's data overlaps another's counters: the counters stay
+// zero between calls whatever entry points and shapes share the workspace.
 constexpr int64_t kCounterWords = 65536;
+constexpr int64_t kVerifyMaxB = kCounterWords;  // one counter per sequence
 constexpr size_t kCounterBytes = (size_t)kCounterWords * sizeof(uint32_t);
 
 size_t cand_region_bytes(int64_t B, int64_t V, uint32_t flags) {
@@ -367,7 +370,7 @@ size_t fs_workspace_bytes_filtered(int64_t B, int64_t V) {
   if (B < 0 || V < 1 || V >= kMaxV) return 0;
   const size_t words = fs::filtered_split_words(B, V);
   if (words == 0) return 0;
-  return align_up((size_t)B * sizeof(uint32_t)) + words * sizeof(uint64_t);
+  return kCounterBytes + words * sizeof(uint64_t);
 }
 
 fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, const float* temp,
@@ -407,11 +410,75 @@ fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, c
   a.out = out_idx;
   a.vec4 = aligned16(logits) && (V % 4 == 0);
   a.counters = need > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
-  a.split = need > 0 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) +
-                                                   align_up((size_t)B * sizeof(uint32_t)))
+  a.split = need > 0 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kCounterBytes)
                      : nullptr;
   hipError_t e = fs::launch_logits_filtered(a, fp64_noise != 0, st);
   if (e != hipSuccess) return hip_fail(e, "filtered sampling launch");
+  if (ev) (void)hipEventRecord(ev[1], st);
+  return FS_OK;
+}
+
+size_t fs_workspace_bytes_verify(int64_t B, int64_t K, int64_t V) {
+  if (B < 0 || B > kVerifyMaxB || K < 0 || K > FS_VERIFY_MAX_K || V < 1 || V >= kMaxV) return 0;
+  const int64_t nC = (V + fs::kVerifyChunk - 1) / fs::kVerifyChunk;  // most chunks of a row
+  return kCounterBytes + align_up((size_t)B * 2 * K * nC * fs::verify_stat_bytes()) +
+         align_up((size_t)B * nC * 16) + align_up((size_t)B * 2 * nC * 16);
+}
+
+fs_status fs_verify(const float* target, const float* draft, const int64_t* tokens, int64_t B,
+                    int64_t K, int64_t V, const float* temp, uint64_t seed, uint64_t offset,
+                    int fp64_noise, int64_t* accept_len, int64_t* out, const uint32_t* row_ids,
+                    void* workspace, size_t workspace_bytes, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_sizes(B, V);
+  if (s != FS_OK) return s;
+  if (B > kVerifyMaxB) return fail(FS_ERR_INVALID_ARG, "B = %lld exceeds %lld", (long long)B, (long long)kVerifyMaxB);
+  if (K < 0 || K > FS_VERIFY_MAX_K)
+    return fail(FS_ERR_INVALID_ARG, "K = %lld outside [0, %d]", (long long)K, FS_VERIFY_MAX_K);
+  if (B == 0) return FS_OK;
+  if (target == nullptr || temp == nullptr || accept_len == nullptr || out == nullptr ||
+      (K > 0 && (draft == nullptr || tokens == nullptr)))
+    return fail(FS_ERR_INVALID_ARG, "target, draft, tokens, temp, accept_len or out is null");
+  if (((uintptr_t)target & 3u) != 0 || ((uintptr_t)draft & 3u) != 0)
+    return fail(FS_ERR_UNSUPPORTED, "target or draft not 4-byte aligned");
+  const size_t need = fs_workspace_bytes_verify(B, K, V);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(FS_ERR_WORKSPACE, "workspace not %zu-byte aligned", (size_t)kAlign);
+
+  fs::VerifyArgs a;
+  a.target = target;
+  a.draft = draft;
+  a.tokens = tokens;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.temp = temp;
+  a.row_ids = row_ids;
+  a.seed = seed;
+  a.offset = offset;
+  fs::verify_chunks(B, K, V, &a.chunk, &a.nC, &a.chunk2, &a.nC2);
+  if (B * (2 * K + 1) * a.nC >= ((int64_t)1 << 31) || B * a.nC2 >= ((int64_t)1 << 31))
+    return fail(FS_ERR_INVALID_ARG, "B, K, V give more than 2^31 workgroups");
+  char* w = static_cast<char*>(workspace);
+  const int64_t nCmax = (V + fs::kVerifyChunk - 1) / fs::kVerifyChunk;
+  a.counters = counters_of(workspace);
+  w += kCounterBytes;
+  a.stats = w;
+  w += align_up((size_t)B * 2 * K * nCmax * fs::verify_stat_bytes());
+  a.bonus = w;
+  w += align_up((size_t)B * nCmax * 16);
+  a.resid = w;
+  a.accept_len = accept_len;
+  a.out = out;
+  a.vec4 = aligned16(target) && (K == 0 || aligned16(draft)) && (V % 4 == 0);
+
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  if (ev) (void)hipEventRecord(ev[0], st);
+  hipError_t e = fs::launch_verify(a, fp64_noise != 0, st);
+  if (e != hipSuccess) return hip_fail(e, "verify launch");
   if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }

@@ -104,6 +104,34 @@ int filtered_split_chunks(int64_t B, int64_t V);  // 0: one workgroup per row
 size_t filtered_split_words(int64_t B, int64_t V);
 hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t stream);
 
+// Speculative-decoding verification over materialised target logits
+// [B, K+1, V] and draft logits [B, K, V]: a statistics launch over every row,
+// then a decision and draw launch.
+constexpr int kVerifyMaxK = 32;          // draft tokens per sequence
+constexpr int kVerifyChunk = 2048;       // fewest logits per workgroup (sizes the workspace)
+constexpr int kVerifyChunkMax = 32768;   // most logits per workgroup
+struct VerifyArgs {
+  const float* target;     // [B, K+1, V]
+  const float* draft;      // [B, K, V]
+  const int64_t* tokens;   // [B, K]
+  int64_t B, K, V;
+  const float* temp;       // [B]
+  const uint32_t* row_ids; // [B] or null: then row b has id b
+  uint64_t seed, offset;   // position i's noise and uniform use offset + i
+  int chunk, nC;           // statistics launch: logits per workgroup, chunks per row
+  int chunk2, nC2;         // draw launch: the same
+  void* stats;             // [B, 2K, nC] softmax partials (verify_stat_bytes each)
+  void* bonus;             // [B, nC] candidates of the target's row K
+  void* resid;             // [B, 2, nC2] residual and fallback candidates
+  uint32_t* counters;      // [B] completion counters, zero between calls
+  int64_t* accept_len;     // [B]
+  int64_t* out;            // [B, K+1]
+  int vec4;                // rows 16-byte aligned
+};
+size_t verify_stat_bytes();
+void verify_chunks(int64_t B, int64_t K, int64_t V, int* chunk, int* nC, int* chunk2, int* nC2);
+hipError_t launch_verify(const VerifyArgs& a, bool fp64, hipStream_t stream);
+
 // Test hook: the noise transforms applied to given words.
 hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,
                         hipStream_t stream);

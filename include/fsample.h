@@ -24,6 +24,10 @@
  *         work name the top-k extension (k draws without replacement, the k
  *         largest perturbed scores; its appendix D proves it); the standard
  *         statement is Kool, van Hoof and Welling, ICML 2019, section 3.
+ *   [SPV] spec-decode-ops kernel card: the description of its `verify`
+ *         (speculative-decoding rejection sampling after Leviathan, Kalman and
+ *         Matias, ICML 2023, and Chen et al. 2023), its "Speculative
+ *         verification" usage example and its "API" table.
  *
  * Conventions shared by every entry point
  *   Pointers.   Arguments documented as "device" are device (HBM) pointers the
@@ -236,12 +240,69 @@ fs_status fs_sample_logits_filtered(const float *logits, int64_t B, int64_t V,
 
 /*
  * Workspace bytes fs_sample_logits_filtered needs for (B, V): 0 when it runs
- * one workgroup per row (no workspace; NULL is accepted), otherwise per-row
- * completion counters and each row's chunk headers and candidate lists
- * (small batches split each row over several workgroups).  0 for invalid
- * sizes.
+ * one workgroup per row (no workspace; NULL is accepted), otherwise the
+ * library's fixed completion-counter region (the same leading 256 KiB every
+ * entry point keeps its counters in, so one workspace can serve them all)
+ * followed by each row's chunk headers and candidate lists (small batches
+ * split each row over several workgroups).  0 for invalid sizes.
  */
 size_t fs_workspace_bytes_filtered(int64_t B, int64_t V);
+
+/*
+ * Speculative-decoding verification over materialised float32 logits [SPV].
+ * Per sequence b (logical row id r = row_ids[b], or b) and position i < K,
+ * with p_t and p_d the temperature softmaxes of target row i and draft row i
+ * (over the valid logits, those neither NaN nor -inf; a +inf maximum shares
+ * the mass among the +inf logits; greedy rows, t <= 0 or NaN, are one-hot on
+ * the first largest valid logit):
+ *   the draft token x_i is accepted iff u_i * p_d(x_i) < p_t(x_i), i.e. with
+ *   probability min(1, p_t(x_i) / p_d(x_i)); u_i = (k + 1/2) / 2^52 with k the
+ *   top 52 bits of words 0 and 1 of Philox counter (2^32 - 1, r,
+ *   offset + i) under the seed key (no noise value uses that counter); a
+ *   token outside [0, V) has probability 0 under both and is rejected;
+ *   accept_len[b] = the first rejected position, or K;
+ *   out[b, j] = x_j for j < accept_len[b], -1 for j > accept_len[b], and at
+ *   j = accept_len[b]:
+ *     after a rejection, a draw from max(p_t - p_d, 0) renormalised (the
+ *     Gumbel-max of log max(p_t - p_d, 0) with the noise fs_sample_logits
+ *     uses at offset + j and row id r); if that residual is all zero, the
+ *     draw fs_sample_logits makes from target row j at offset + j; on greedy
+ *     rows, the target argmax;
+ *     after K acceptances, the bonus draw: exactly fs_sample_logits on target
+ *     row K at offset + K.
+ * The tokens out[b, 0 .. accept_len[b]] are then distributed as the target
+ * model's own draws.  Position i's noise and uniform use offset + i, the
+ * absolute position: advance offset by at least the tokens emitted.
+ *   target    device, float [B, K+1, V], 4-byte aligned (16-byte aligned
+ *             rows with V % 4 == 0 take vector loads)
+ *   draft     device, float [B, K, V]
+ *   tokens    device, int64 [B, K] draft tokens
+ *   B, K, V   host: 0 <= B <= 65536, 0 <= K <= FS_VERIFY_MAX_K, 1 <= V < 2^31
+ *             (K = 0 is a plain draw from target row 0)
+ *   temp      device, float [B]
+ *   seed, offset, fp64_noise, row_ids   as for fs_sample_logits (fp64_noise
+ *             selects the float64 noise of the residual and bonus draws; the
+ *             acceptance uniforms are always 52-bit)
+ *   accept_len  device, int64 [B];  out  device, int64 [B, K+1]
+ *   workspace, workspace_bytes  device, 256-byte aligned, at least
+ *             fs_workspace_bytes_verify(B, K, V) bytes, zeroed once before
+ *             first use (every call leaves its counters at zero; calls sharing
+ *             one workspace are serialised by their stream)
+ * The softmax normalisers are float32 sums of float32 exponentials merged in
+ * float64; the acceptance test runs in float64; the residual is formed in
+ * float32.  Two launches on `stream`; deterministic for fixed arguments.
+ */
+#define FS_VERIFY_MAX_K 32
+fs_status fs_verify(const float *target, const float *draft, const int64_t *tokens,
+                    int64_t B, int64_t K, int64_t V, const float *temp, uint64_t seed,
+                    uint64_t offset, int fp64_noise, int64_t *accept_len, int64_t *out,
+                    const uint32_t *row_ids, void *workspace, size_t workspace_bytes,
+                    fs_stream_t stream);
+
+/*
+ * Workspace bytes fs_verify needs for (B, K, V); 0 for invalid sizes.
+ */
+size_t fs_workspace_bytes_verify(int64_t B, int64_t K, int64_t V);
 
 /*
  * Gumbel-top-k over materialised float32 logits [GTK]: k draws without

@@ -7,7 +7,8 @@ D = 4096, V = 128256 Llama-3-shaped head; D = 8192 wide head) and of the
 Megatron-LM tail-rate and chi-square tests.  Every draw uses a CPU
 ``torch.Generator`` with a fixed seed, so the oracle and the GPU path see
 identical bits.  Seeds: W = 0, H = 1, temperatures = 2, bias/mask = 3,
-chi-square row = 4, materialised logits and filter settings = 5.  Reading of
+chi-square row = 4, materialised logits and filter settings = 5, speculative
+verification inputs = 6.  Reading of
 "N(0, s)": s is the standard deviation.
 """
 from __future__ import annotations
@@ -17,7 +18,7 @@ import math
 import numpy as np
 import torch
 
-SEED_W, SEED_H, SEED_T, SEED_BIAS, SEED_CHI2, SEED_LOGITS = 0, 1, 2, 3, 4, 5
+SEED_W, SEED_H, SEED_T, SEED_BIAS, SEED_CHI2, SEED_LOGITS, SEED_SPEC = 0, 1, 2, 3, 4, 5, 6
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -154,3 +155,20 @@ def filter_settings(B: int, V: int, seed: int = SEED_LOGITS + 100):
     p = torch.where(on[1], p, torch.ones_like(p)).float()
     m = torch.where(on[2], m, torch.zeros_like(m)).float()
     return k, p, m
+
+
+def spec_decode(B: int, K: int, V: int, std: float = 3.0, draft_noise: float = 1.0,
+                temp: float = 0.8, seed: int = SEED_SPEC):
+    """Inputs of speculative verification: target logits [B, K+1, V] ~ N(0, std^2),
+    draft logits [B, K, V] = the target's first K rows + N(0, draft_noise^2) (a draft
+    model that mostly agrees with the target), and draft tokens [B, K] int64 drawn
+    from the draft's own softmax at temperature `temp` (torch.multinomial), as a draft
+    model's sampler would propose them."""
+    g = _gen(seed)
+    target = (torch.randn((B, K + 1, V), generator=g) * std).float()
+    draft = (target[:, :K] + torch.randn((B, K, V), generator=g) * draft_noise).float().contiguous()
+    if K == 0 or B == 0:
+        return target, draft, torch.zeros((B, K), dtype=torch.int64)
+    probs = torch.softmax(draft.double().reshape(B * K, V) / temp, dim=-1)
+    tokens = torch.multinomial(probs, 1, generator=g).reshape(B, K)
+    return target, draft, tokens.to(torch.int64).contiguous()

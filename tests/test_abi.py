@@ -134,6 +134,51 @@ def test_filtered_workspace_bytes():
     assert lib.fs_workspace_bytes_filtered(4, 0) == 0
 
 
+def _verify(B=4, K=4, V=100000, T=FAKE, D=FAKE, tok=FAKE, temp=FAKE, acc=FAKE, out=FAKE,
+            ws=FAKE, wsb=1 << 30):
+    lib = fs.load_library()
+    return lib.fs_verify(P(T), P(D), P(tok), B, K, V, P(temp), 1, 0, 0, P(acc), P(out), None,
+                         P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), 1), (dict(V=0), 1), (dict(V=2**31), 1), (dict(K=-1), 1), (dict(K=33), 1),
+    (dict(B=65537), 1), (dict(T=0), 1), (dict(D=0), 1), (dict(tok=0), 1), (dict(temp=0), 1),
+    (dict(acc=0), 1), (dict(out=0), 1), (dict(T=FAKE + 2), 2), (dict(D=FAKE + 6), 2),
+    (dict(ws=0), 3), (dict(wsb=1024), 3), (dict(ws=FAKE + 16), 3),
+])
+def test_verify_rejects_before_launch(kw, code):
+    assert _verify(**kw) == code
+    assert fs.load_library().fs_last_error() != b""
+
+
+def test_verify_sizes_and_workspace():
+    lib = fs.load_library()
+    assert _verify(B=0, T=0, D=0, tok=0, temp=0, acc=0, out=0, ws=0, wsb=0) == 0
+    # K = 0 needs no draft rows or tokens (a plain draw from target row 0): only
+    # the workspace is missing here
+    assert _verify(K=0, D=0, tok=0, ws=0, wsb=0) == 3
+    # the leading counter region, then the per-chunk softmax partials of 2K rows,
+    # the bonus row's candidates and the residual candidates
+    nC = (151936 + 2047) // 2048
+    assert lib.fs_workspace_bytes_verify(64, 4, 151936) >= 256 * 1024 + 64 * nC * (8 * 16 + 16 + 32)
+    assert lib.fs_workspace_bytes_verify(1, 0, 10) > 0
+    for B, K, V in ((-1, 4, 100), (4, 33, 100), (4, -1, 100), (4, 4, 0), (65537, 1, 100)):
+        assert lib.fs_workspace_bytes_verify(B, K, V) == 0, (B, K, V)
+
+
+def test_every_workspace_keeps_its_counters_in_the_leading_region():
+    """One workspace may serve every entry point in turn (the Python binding
+    caches one per stream): each keeps its completion counters in the first
+    256 KiB and its other data after them, so no call's data lands on another's
+    counters.  The filtered sampler's split rows and verification reserve the
+    whole region."""
+    lib = fs.load_library()
+    assert lib.fs_workspace_bytes_filtered(1, 151936) >= 256 * 1024 + 8 * 8
+    assert lib.fs_workspace_bytes_verify(1, 1, 8) >= 256 * 1024
+    assert lib.fs_workspace_bytes(1, 8, 0) >= 256 * 1024
+
+
 def test_debug_hooks_reject_before_launch():
     lib = fs.load_library()
     assert lib.fs_debug_philox_words(0, 0, None, -1, 4, P(FAKE), None) == 1
