@@ -15,7 +15,9 @@ over the timed steps; p10/p50/p90 of the per-step times beside it);
 duration, read from HIP events the library records around it on the stream it
 runs on, over the same timed region; `standalone_sampler` does the same for
 fs_sample_logits, `filtered_sampler` for fs_sample_logits_filtered (top-k,
-top-p, min-p) beside the eager transformers chain; `cpu_baseline` is the
+top-p, min-p) beside the eager transformers chain, `verify` for fs_verify
+(speculative-decoding rejection sampling, K = 4) beside an eager PyTorch
+rejection sampler; `cpu_baseline` is the
 float64 CPU oracle computing the same step on this host's cores.
 """
 from __future__ import annotations
@@ -128,6 +130,15 @@ def logits_alg_bytes(B: int, V: int, cand: int = 8) -> int:
     temperatures, candidates written and read back once, the indices written."""
     n_tiles = (V + LOGITS_CHUNK - 1) // LOGITS_CHUNK
     return 4 * B * V + 4 * B + 2 * cand * B * n_tiles + 8 * B
+
+
+def verify_alg_bytes(B: int, K: int, V: int, residual_rows: int) -> int:
+    """What one verification call must move: every float32 target and draft row
+    once (the softmax normalisers and the bonus draw), the two rows of the
+    rejected position again for each row whose residual draw runs (its scores
+    need both normalisers), the draft tokens, temperatures and outputs; the
+    small per-chunk partials are left out."""
+    return 4 * B * (2 * K + 1) * V + 8 * V * residual_rows + 8 * B * K + 4 * B + 8 * B * (K + 2)
 
 
 def percentiles(xs, qs=(10, 50, 90)):
@@ -452,6 +463,54 @@ def main() -> int:
             log(f"  {key}: {fl[key]}")
             del X
         result["filtered_sampler"] = fl
+
+        # Speculative-decoding verification over float32 target [B, K+1, V] and
+        # draft [B, K, V] logits, K = 4 (the spec-decode-ops card's acceptance
+        # length test), at the Qwen3-8B vocabulary: the draft is the target plus
+        # N(0, 1) noise and proposes from its own softmax (T = 0.8).  Against an
+        # eager PyTorch rejection sampler on the same tensors (softmaxes of every
+        # row materialised, the residual of every position formed, multinomial).
+        log("timing speculative verification")
+        vf = {"settings": "K=4, target N(0, 3^2), draft = target + N(0, 1), T = 0.8"}
+        KV = 4
+        for bl in (1, 8, 64):
+            g = torch.Generator(device=dev).manual_seed(8)
+            TG = torch.randn(bl, KV + 1, VOCAB, generator=g, device=dev) * 3.0
+            DR = (TG[:, :KV] + torch.randn(bl, KV, VOCAB, generator=g, device=dev)).contiguous()
+            Tv = torch.full((bl,), 0.8, dtype=torch.float32, device=dev)
+            TOK = torch.multinomial(torch.softmax(DR.reshape(-1, VOCAB) / 0.8, dim=-1), 1,
+                                    generator=g).reshape(bl, KV).contiguous()
+            ms, kms, pc = time_calls(
+                torch, fs, lambda s: fs.verify(TG, DR, TOK, Tv, seed=97, offset=s),
+                max(20, args.steps // 4), 5)
+            acc, _ = fs.verify(TG, DR, TOK, Tv, seed=97, offset=0)
+            n_res = int((acc < KV).sum().item())     # rows whose residual pass ran
+            lb = verify_alg_bytes(bl, KV, VOCAB, n_res)
+            key = f"B{bl}_K{KV}_V{VOCAB}"
+            vf[key] = {"us_per_call": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
+                       "residual_rows": n_res, "alg_bytes": lb,
+                       "kernel_gbs": round(lb / (kms * 1e-3) / 1e9, 1),
+                       "kernel_frac": round(lb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+            def eager(s):
+                pt = torch.softmax(TG / Tv[:, None, None], dim=-1)
+                pd = torch.softmax(DR / Tv[:, None, None], dim=-1)
+                a = pt[:, :KV].gather(2, TOK[..., None])[..., 0]
+                q = pd.gather(2, TOK[..., None])[..., 0]
+                ok = torch.rand(bl, KV, device=dev) * q < a
+                L = ok.int().cumprod(dim=1).sum(dim=1)
+                res = (pt[:, :KV] - pd).clamp_min(0)
+                row = res[torch.arange(bl, device=dev), L.clamp(max=KV - 1)]
+                r_tok = torch.multinomial(row / row.sum(-1, keepdim=True), 1)[:, 0]
+                b_tok = torch.multinomial(pt[:, KV], 1)[:, 0]
+                return L, torch.where(L == KV, b_tok, r_tok)
+
+            vf[key]["eager_torch_us"] = round(
+                time_region(torch, eager, max(20, args.steps // 4), 5) * 1e3, 2)
+            vf[key]["speedup_vs_eager"] = round(vf[key]["eager_torch_us"] / vf[key]["us_per_call"], 2)
+            log(f"  {key}: {vf[key]}")
+            del TG, DR
+        result["verify"] = vf
 
         # The large-batch end: the Llama-3-shaped head at the compute crossover
         # (H [256, 4096], W [128256, 4096], per-row temperature, fp32 bias with

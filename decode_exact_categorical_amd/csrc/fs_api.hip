@@ -422,7 +422,7 @@ size_t fs_workspace_bytes_verify(int64_t B, int64_t K, int64_t V) {
   if (B < 0 || B > kVerifyMaxB || K < 0 || K > FS_VERIFY_MAX_K || V < 1 || V >= kMaxV) return 0;
   const int64_t nC = (V + fs::kVerifyChunk - 1) / fs::kVerifyChunk;  // most chunks of a row
   return kCounterBytes + align_up((size_t)B * 2 * K * nC * fs::verify_stat_bytes()) +
-         align_up((size_t)B * nC * 16) + align_up((size_t)B * 2 * nC * 16);
+         align_up((size_t)B * nC * 16) + align_up((size_t)B * nC * 16);
 }
 
 fs_status fs_verify(const float* target, const float* draft, const int64_t* tokens, int64_t B,

@@ -109,7 +109,7 @@ hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t st
 // then a decision and draw launch.
 constexpr int kVerifyMaxK = 32;          // draft tokens per sequence
 constexpr int kVerifyChunk = 2048;       // fewest logits per workgroup (sizes the workspace)
-constexpr int kVerifyChunkMax = 32768;   // most logits per workgroup
+constexpr int kVerifyChunkMax = 8192;    // most logits per workgroup
 struct VerifyArgs {
   const float* target;     // [B, K+1, V]
   const float* draft;      // [B, K, V]
@@ -122,7 +122,7 @@ struct VerifyArgs {
   int chunk2, nC2;         // draw launch: the same
   void* stats;             // [B, 2K, nC] softmax partials (verify_stat_bytes each)
   void* bonus;             // [B, nC] candidates of the target's row K
-  void* resid;             // [B, 2, nC2] residual and fallback candidates
+  void* resid;             // [B, nC2] residual candidates
   uint32_t* counters;      // [B] completion counters, zero between calls
   int64_t* accept_len;     // [B]
   int64_t* out;            // [B, K+1]

@@ -22,9 +22,10 @@
 //    merge the bonus candidates, greedy rows emit the target argmax, and only
 //    rows with a sampled rejection stream their two position-L rows once more
 //    for the residual draw: Gumbel-max over log max(p_t - p_d, 0) with the
-//    noise of position offset + L, plus the plain target draw with the same
-//    noise for a residual that is all zero.  The last workgroup of a row
-//    merges the chunks (finish_last).
+//    noise of position offset + L.  The last workgroup of a row merges the
+//    chunks (finish_last); a residual that is all zero (p_t equal to p_d) is
+//    replaced by the plain target draw with the same noise, which that
+//    workgroup then makes alone.
 //
 // The acceptance uniform of position i is the 52-bit midpoint value of words
 // 0 and 1 of Philox counter (2^32 - 1, row id, offset + i): vocabulary words
@@ -53,24 +54,18 @@ __device__ __forceinline__ float rel_mass(float a, float m, float c) {
   return __builtin_amdgcn_exp2f((a - m) * c);
 }
 
-// Online (max, normaliser, first argmax) of the valid logits a thread meets
-// in increasing index order.
+// exp2 scale of a row's masses: log2(e) / t (floored at 1e-30 so that t = +inf
+// gives masses of 1 rather than NaN at -inf logits; greedy rows use no masses).
+__device__ __forceinline__ float mass_scale(float t, bool greedy) {
+  return greedy ? kLog2e : __builtin_fmaxf(kLog2e / t, 1e-30f);
+}
+
+// (max, normaliser, first argmax) of the valid logits a thread has met.
 struct Stat {
   float m;
   float z;
   int32_t idx;
 };
-
-__device__ __forceinline__ void stat_add(Stat& s, float y, int32_t j, float c) {
-  if (!valid_logit(y)) return;
-  if (y > s.m) {
-    s.z = s.z * rel_mass(s.m, y, c) + 1.0f;
-    s.m = y;
-    s.idx = j;
-  } else {
-    s.z += rel_mass(y, s.m, c);
-  }
-}
 
 // Merge of two partials: larger max wins, equal maxima keep the smaller index.
 __device__ __forceinline__ Stat stat_merge(float am, float az, int32_t ai, float bm, float bz,
@@ -195,17 +190,47 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(VerifyArgs a) {
     return;
   }
 
-  // Softmax partial of a target or draft row of position < K.
-  const float cexp = greedy ? kLog2e : kLog2e / t;
-  Stat st{-__builtin_inff(), 0.0f, kNoIndex};
+  // Softmax partial of a target or draft row of position < K.  Per step of
+  // 4 kInFlight logits: their maximum first (NaN read as -inf), the running
+  // normaliser rescaled only when it grows, then one exp2 per logit.
+  const float cexp = mass_scale(t, greedy);
+  constexpr float kInf = __builtin_inff();
+  Stat st{-kInf, 0.0f, kNoIndex};
   for (int64_t i0 = lo + 4 * (int64_t)threadIdx.x; i0 < hi; i0 += kStride * kInFlight) {
     float y[kInFlight][4];
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) load4(x, i0 + kStride * u, hi, vec4, y[u]);
+    float mx = -kInf;
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) stat_add(st, y[u][j], (int32_t)(i0 + kStride * u + j), cexp);
+      for (int j = 0; j < 4; ++j) {
+        y[u][j] = __builtin_fmaxf(y[u][j], -kInf);  // NaN -> -inf
+        mx = __builtin_fmaxf(mx, y[u][j]);
+      }
+    if (mx > st.m) {
+      int32_t id = kNoIndex;  // the first index attaining mx
+#pragma unroll
+      for (int u = kInFlight - 1; u >= 0; --u)
+#pragma unroll
+        for (int j = 3; j >= 0; --j)
+          if (y[u][j] == mx) id = (int32_t)(i0 + kStride * u + j);
+      st.z *= rel_mass(st.m, mx, cexp);
+      st.m = mx;
+      st.idx = id;
+    }
+    if (st.m == kInf) {  // +inf maximum: the mass is shared among the +inf logits
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st.z += y[u][j] == kInf ? 1.0f : 0.0f;
+    } else if (st.m != -kInf) {
+      const float m = st.m;
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st.z += __builtin_amdgcn_exp2f((y[u][j] - m) * cexp);
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -246,43 +271,55 @@ __global__ __launch_bounds__(kThreads) void verify_draw_kernel(VerifyArgs a) {
   const bool greedy = !(t > 0.0f);
   const uint32_t rid = row_id_of(a, b);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float cexp = greedy ? kLog2e : kLog2e / t;
+  const float cexp = mass_scale(t, greedy);
 
-  // Merged softmax of the 2K rows (wave w merges rows w, w + 4, ...).
+  // The draft tokens and their two logits (wave 0, lane i: position i), issued
+  // before the partials are merged so that the two wait together.
+  int64_t xtok = -1;
+  float ytx = -__builtin_inff(), ydx = -__builtin_inff();
+  if (wave == 0 && lane < K) {
+    xtok = a.tokens[b * K + lane];
+    if (xtok >= 0 && xtok < V) {
+      ytx = a.target[(b * (K + 1) + lane) * V + xtok];
+      ydx = a.draft[(b * K + lane) * V + xtok];
+    }
+  }
+
+  // Merged softmax of the 2K rows (wave w merges rows w, w + 4, ...): one
+  // online pass over the chunk partials, then the lanes' merge.
   __shared__ float s_m[2 * kVerifyMaxK];
   __shared__ int32_t s_am[2 * kVerifyMaxK];
   __shared__ double s_z[2 * kVerifyMaxK];
   __shared__ int s_len;
   for (int64_t r = wave; r < 2 * K; r += kThreads / 64) {
     const RowStat* p = reinterpret_cast<const RowStat*>(a.stats) + (b * 2 * K + r) * a.nC;
-    Stat st{-__builtin_inff(), 0.0f, kNoIndex};
+    float m = -__builtin_inff();
+    int32_t idx = kNoIndex;
     double z = 0.0;
-    // first the row's max and argmax, then the normaliser rescaled to it
     for (int cc = lane; cc < a.nC; cc += 64) {
       const RowStat e = p[cc];
-      if (e.m > st.m || (e.m == st.m && e.idx < st.idx)) {
-        st.m = e.m;
-        st.idx = e.idx;
-      }
+      const bool first = e.m > m || (e.m == m && e.idx < idx);
+      const float nm = first ? e.m : m;
+      z = z * (double)rel_mass(m, nm, cexp) + e.z * (double)rel_mass(e.m, nm, cexp);
+      if (nm == -__builtin_inff()) z = 0.0;
+      m = nm;
+      idx = first ? e.idx : idx;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-      const float om = __shfl_xor(st.m, o);
-      const int32_t oi = __shfl_xor(st.idx, o);
-      if (om > st.m || (om == st.m && oi < st.idx)) {
-        st.m = om;
-        st.idx = oi;
-      }
+      const float om = __shfl_xor(m, o);
+      const int32_t oi = __shfl_xor(idx, o);
+      const double oz = __shfl_xor(z, o);
+      const bool first = om > m || (om == m && oi < idx);
+      const float nm = first ? om : m;
+      z = z * (double)rel_mass(m, nm, cexp) + oz * (double)rel_mass(om, nm, cexp);
+      if (nm == -__builtin_inff()) z = 0.0;
+      m = nm;
+      idx = first ? oi : idx;
     }
-    for (int cc = lane; cc < a.nC; cc += 64) {
-      const RowStat e = p[cc];
-      if (e.z > 0.0) z += e.z * (double)rel_mass(e.m, st.m, cexp);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
     if (lane == 0) {
-      s_m[r] = st.m;
-      s_am[r] = st.idx;
+      s_m[r] = m;
+      s_am[r] = idx;
       s_z[r] = z;
     }
   }
@@ -292,13 +329,10 @@ __global__ __launch_bounds__(kThreads) void verify_draw_kernel(VerifyArgs a) {
   if (wave == 0) {
     bool acc = true;
     if (lane < K) {
-      const int64_t x = a.tokens[b * K + lane];
       double pt = 0.0, pq = 0.0;
-      if (x >= 0 && x < V) {
-        const float yt = a.target[(b * (K + 1) + lane) * V + x];
-        const float yd = a.draft[(b * K + lane) * V + x];
-        pt = prob_of(yt, x, greedy, (double)t, s_m[lane], s_am[lane], s_z[lane]);
-        pq = prob_of(yd, x, greedy, (double)t, s_m[K + lane], s_am[K + lane], s_z[K + lane]);
+      if (xtok >= 0 && xtok < V) {
+        pt = prob_of(ytx, xtok, greedy, (double)t, s_m[lane], s_am[lane], s_z[lane]);
+        pq = prob_of(ydx, xtok, greedy, (double)t, s_m[K + lane], s_am[K + lane], s_z[K + lane]);
       }
       const NoiseKey key = make_key(a.seed, a.offset + (uint64_t)lane);
       const Words w = noise_words(key, kAcceptCounter, rid);
@@ -330,8 +364,7 @@ __global__ __launch_bounds__(kThreads) void verify_draw_kernel(VerifyArgs a) {
     return;
   }
 
-  // Residual draw at position L: scores log(max(p_t - p_d, 0)) + g and, for a
-  // residual that is all zero, the target's own y / t + g, with the same noise.
+  // Residual draw at position L: scores log(max(p_t - p_d, 0)) + g.
   const float* xt = a.target + (b * (K + 1) + L) * V;
   const float* xd = a.draft + (b * K + L) * V;
   const float mt = s_m[L], md = s_m[K + L];
@@ -343,8 +376,8 @@ __global__ __launch_bounds__(kThreads) void verify_draw_kernel(VerifyArgs a) {
   const int64_t hi = lo + a.chunk2 < V ? lo + a.chunk2 : V;
   constexpr int64_t kStride = 4 * kThreads;
   const bool vec4 = a.vec4 != 0;
-  T rm = neg_inf<T>(), fm = neg_inf<T>();
-  int32_t ri = kNoIndex, fi = kNoIndex;
+  T rm = neg_inf<T>();
+  int32_t ri = kNoIndex;
   for (int64_t i0 = lo + 4 * (int64_t)threadIdx.x; i0 < hi; i0 += kStride * kInFlight) {
     float yt[kInFlight][4], yd[kInFlight][4];
 #pragma unroll
@@ -377,45 +410,56 @@ __global__ __launch_bounds__(kThreads) void verify_draw_kernel(VerifyArgs a) {
         const float pd = valid_logit(yd[u][j]) ? rel_mass(yd[u][j], md, cexp) * izd : 0.0f;
         const float r = pt - pd;
         const T sr = r > 0.0f ? T(kLn2f * __builtin_amdgcn_logf(r)) + g[j] : neg_inf<T>();
-        const T sf = (sizeof(T) == 4 ? T(yt[u][j] * (float)inv_t) : T(yt[u][j]) * inv_t) + g[j];
-        if (j0 + j < hi) {
-          if (sr > rm) {
-            rm = sr;
-            ri = (int32_t)(j0 + j);
-          }
-          if (sf > fm) {
-            fm = sf;
-            fi = (int32_t)(j0 + j);
-          }
+        if (j0 + j < hi && sr > rm) {
+          rm = sr;
+          ri = (int32_t)(j0 + j);
         }
       }
     }
   }
   wave_argmax_xor(rm, ri, 0);
-  wave_argmax_xor(fm, fi, 0);
-  __shared__ Cand<T> wres[kThreads / 64], wfb[kThreads / 64];
-  if (lane == 0) {
-    wres[wave] = Cand<T>{rm, ri};
-    wfb[wave] = Cand<T>{fm, fi};
-  }
+  __shared__ Cand<T> wres[kThreads / 64];
+  __shared__ int64_t s_tok;
+  if (lane == 0) wres[wave] = Cand<T>{rm, ri};
   __syncthreads();
-  Cand<T>* cres = reinterpret_cast<Cand<T>*>(a.resid) + b * 2 * a.nC2;
+  Cand<T>* cres = reinterpret_cast<Cand<T>*>(a.resid) + b * a.nC2;
   if (threadIdx.x == 0) {
-    Cand<T> br = wres[0], bf = wfb[0];
+    Cand<T> br = wres[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) {
+    for (int w = 1; w < kThreads / 64; ++w)
       if (beats(wres[w].m, wres[w].idx, br.m, br.idx)) br = wres[w];
-      if (beats(wfb[w].m, wfb[w].idx, bf.m, bf.idx)) bf = wfb[w];
-    }
     store_cand(cres + c, br);
-    store_cand(cres + a.nC2 + c, bf);
     wait_stores_complete();
   }
   if (!finish_last(a.counters + b, (uint32_t)a.nC2)) return;
+  // row_winner gives -1 when the best residual score is -inf (all zero)
   if (wave == 0) {
-    // row_winner gives -1 when the best residual score is -inf (all zero)
-    int64_t tok_L = row_winner(cres, a.nC2, lane);
-    if (tok_L < 0) tok_L = row_winner(cres + a.nC2, a.nC2, lane);
+    const int64_t w = row_winner(cres, a.nC2, lane);
+    if (lane == 0) s_tok = w;
+  }
+  __syncthreads();
+  int64_t tok_L = s_tok;
+  if (tok_L < 0) {
+    // A residual that is all zero (p_t equals p_d): the draw from p_t itself,
+    // the standalone sampler's on target row L at offset + L, by this
+    // workgroup alone (a rare case).
+    T bm = neg_inf<T>();
+    int32_t bi = kNoIndex;
+    for (int64_t i0 = 4 * (int64_t)threadIdx.x; i0 < V; i0 += kStride) {
+      float y[4];
+      load4(xt, i0, V, vec4, y);
+      sample4<T>(key, false, inv_t, rid, i0, V, y, bm, bi);
+    }
+    wave_argmax_xor(bm, bi, 0);
+    if (lane == 0) wres[wave] = Cand<T>{bm, bi};
+    __syncthreads();
+    Cand<T> best = wres[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w)
+      if (beats(wres[w].m, wres[w].idx, best.m, best.idx)) best = wres[w];
+    tok_L = best.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)best.idx;
+  }
+  if (wave == 0) {
     for (int64_t j = lane; j <= K; j += 64)
       a.out[b * (K + 1) + j] = j < L ? a.tokens[b * K + j] : (j == L ? tok_L : (int64_t)-1);
     if (lane == 0) a.accept_len[b] = L;

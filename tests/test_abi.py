@@ -161,7 +161,7 @@ def test_verify_sizes_and_workspace():
     # the leading counter region, then the per-chunk softmax partials of 2K rows,
     # the bonus row's candidates and the residual candidates
     nC = (151936 + 2047) // 2048
-    assert lib.fs_workspace_bytes_verify(64, 4, 151936) >= 256 * 1024 + 64 * nC * (8 * 16 + 16 + 32)
+    assert lib.fs_workspace_bytes_verify(64, 4, 151936) >= 256 * 1024 + 64 * nC * (8 * 16 + 16 + 16)
     assert lib.fs_workspace_bytes_verify(1, 0, 10) > 0
     for B, K, V in ((-1, 4, 100), (4, 33, 100), (4, -1, 100), (4, 4, 0), (65537, 1, 100)):
         assert lib.fs_workspace_bytes_verify(B, K, V) == 0, (B, K, V)
