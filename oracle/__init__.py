@@ -104,6 +104,8 @@ def _load():
         lib.oracle_filtered_repeated_row.restype = None
         lib.oracle_filtered_repeated_row.argtypes = [P, i64, ctypes.c_float, i32, ctypes.c_float,
                                                      ctypes.c_float, u64, u64, P, i64, i32, P]
+        lib.oracle_filter_logits.restype = None
+        lib.oracle_filter_logits.argtypes = [P, i64, i64, P, P, P, P, P, P]
         lib.oracle_accept_uniform.restype = ctypes.c_double
         lib.oracle_accept_uniform.argtypes = [u64, u64, u32]
         lib.oracle_verify.restype = None
@@ -417,6 +419,20 @@ def filter_kept(logits_f32, temp, *, top_k=None, top_p=None, min_p=None):
     _load().oracle_filter_kept(_ptr(x), B, V, _ptr(t), _ptr(k), _ptr(p), _ptr(m), _ptr(kept),
                                _ptr(margin))
     return kept.astype(bool), margin
+
+
+def filter_logits(logits_f32, temp, *, top_k=None, top_p=None, min_p=None):
+    """(out float64[B, V], margin float64[B]): the filter chain's masked,
+    temperature-scaled logits (y / t on the kept tokens, -inf elsewhere)."""
+    x = np.ascontiguousarray(np.asarray(logits_f32, dtype=np.float32))
+    B, V = x.shape
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    k, p, m = _filter_args(B, top_k, top_p, min_p)
+    out = np.zeros((B, V), dtype=np.float64)
+    margin = np.zeros(B, dtype=np.float64)
+    _load().oracle_filter_logits(_ptr(x), B, V, _ptr(t), _ptr(k), _ptr(p), _ptr(m), _ptr(out),
+                                 _ptr(margin))
+    return out, margin
 
 
 def sample_logits_filtered(logits_f32, temp, *, top_k=None, top_p=None, min_p=None, seed: int,

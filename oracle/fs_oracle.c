@@ -759,6 +759,26 @@ void oracle_filter_kept(const float *logits, int64_t B, int64_t V, const float *
     }
 }
 
+/* The filter chain's output [SD API table: filter_logits]: out[b, i] =
+ * logits[b, i] / t on the kept tokens of oracle_filter_kept and -inf
+ * elsewhere; greedy rows (!(t > 0)) keep the largest logit's tie class
+ * unscaled.  margin[b] as in oracle_filter_kept. */
+void oracle_filter_logits(const float *logits, int64_t B, int64_t V, const float *temp,
+                          const int32_t *top_k, const float *top_p, const float *min_p,
+                          double *out, double *margin)
+{
+    uint8_t *kept = (uint8_t *)malloc((size_t)(B * V > 0 ? B * V : 1));
+    oracle_filter_kept(logits, B, V, temp, top_k, top_p, min_p, kept, margin);
+    for (int64_t b = 0; b < B; ++b) {
+        double t = (double)temp[b];
+        for (int64_t i = 0; i < V; ++i) {
+            double y = (double)logits[b * V + i];
+            out[b * V + i] = kept[b * V + i] ? ((t > 0.0) ? y / t : y) : -INFINITY;
+        }
+    }
+    free(kept);
+}
+
 /* Filtered exact sampling over float32 logits[B,V] [SD; FS prerequisites]:
  * the kept set of oracle_filter_kept, then the standalone sampler's noise,
  * transform and selection over the kept tokens only (the others score -inf).

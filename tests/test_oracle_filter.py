@@ -12,7 +12,9 @@ code:
   kept set (chi-square), with no draw outside it;
 * special cases that reduce to other pinned results: every filter off equals
   the unfiltered sampler draw for draw, top_k = 1 is numpy's argmax, greedy
-  rows, masks and NaN.
+  rows, masks and NaN;
+* the filtered logits (filter_logits) against the processors' own output
+  values: -inf at the same tokens, y / t elsewhere.
 """
 import numpy as np
 import pytest
@@ -206,3 +208,39 @@ def test_law_chi_square(fp64):
     chi2 = stats.chi2_statistic(counts[keep], law[keep])
     thr = stats.chi2_quantile(keep.size - 1, 1e-6)
     assert chi2 < thr, (chi2, thr)
+
+
+@pytest.mark.parametrize("setting", SETTINGS[:6] + [dict()])
+def test_filter_logits_match_processor_output(setting):
+    """The processors return the masked, temperature-scaled logits themselves."""
+    rng = np.random.default_rng(16)
+    B, V = 40, 300
+    x = (rng.standard_normal((B, V)) * rng.uniform(0.5, 4.0, size=(B, 1))).astype(np.float32)
+    t = rng.uniform(0.3, 1.5, size=B).astype(np.float32)
+    out, margin = oracle.filter_logits(x, t, **setting)
+    from transformers.generation.logits_process import (MinPLogitsWarper, TemperatureLogitsWarper,
+                                                        TopKLogitsWarper, TopPLogitsWarper)
+    checked = 0
+    for b in range(B):
+        if margin[b] <= MARGIN:
+            continue
+        z = TemperatureLogitsWarper(float(t[b]))(None, torch.as_tensor(x[b])[None].clone())
+        if "top_k" in setting:
+            z = TopKLogitsWarper(setting["top_k"])(None, z)
+        if "top_p" in setting:
+            z = TopPLogitsWarper(setting["top_p"])(None, z)
+        if "min_p" in setting:
+            z = MinPLogitsWarper(setting["min_p"])(None, z)
+        z = z[0].double().numpy()
+        np.testing.assert_array_equal(np.isinf(out[b]) & (out[b] < 0), np.isinf(z) & (z < 0))
+        fin = np.isfinite(z)
+        np.testing.assert_allclose(out[b][fin], z[fin], rtol=2e-7)
+        checked += 1
+    assert checked >= 0.8 * B
+
+
+def test_filter_logits_greedy_and_masks():
+    x = np.array([[1.0, 3.0, np.nan, 3.0, -np.inf], [0.5, -1.0, 2.0, 1.0, 0.0]], dtype=np.float32)
+    out, _ = oracle.filter_logits(x, [0.0, 2.0], top_k=2)
+    np.testing.assert_array_equal(out[0], [-np.inf, 3.0, -np.inf, 3.0, -np.inf])
+    np.testing.assert_array_equal(out[1], [-np.inf, -np.inf, 1.0, 0.5, -np.inf])
