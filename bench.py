@@ -460,6 +460,14 @@ def main() -> int:
                     time_region(torch, eager, max(20, args.steps // 4), 5) * 1e3, 2)
                 fl[key]["speedup_vs_eager"] = round(
                     fl[key]["eager_transformers_chain_us"] / fl[key]["us_per_call"], 2)
+            if bl == 64 and not name:
+                # the chain's masked, temperature-scaled logits (filter_logits)
+                Y = torch.empty_like(X)
+                fms, fkms, _ = time_calls(
+                    torch, fs, lambda s: fs.filter_logits(X, Tl, out=Y, **kw),
+                    max(20, args.steps // 4), 5)
+                fl[key]["filter_logits_kernel_us"] = round(fkms * 1e3, 2)
+                del Y
             log(f"  {key}: {fl[key]}")
             del X
         result["filtered_sampler"] = fl

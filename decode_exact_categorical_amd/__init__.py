@@ -101,6 +101,8 @@ def load_library():
                                                   sz, P]
         lib.fs_workspace_bytes_filtered.restype = sz
         lib.fs_workspace_bytes_filtered.argtypes = [i64, i64]
+        lib.fs_filter_logits.restype = i32
+        lib.fs_filter_logits.argtypes = [P, i64, i64, P, P, P, P, P, P]
         lib.fs_verify.restype = i32
         lib.fs_verify.argtypes = [P, P, P, i64, i64, i64, P, u64, u64, i32, P, P, P, P, sz, P]
         lib.fs_workspace_bytes_verify.restype = sz
@@ -342,6 +344,33 @@ def sample_logits_filtered(logits: torch.Tensor, temp, *, top_k=None, top_p=None
                                        seed, offset, int(bool(fp64_noise)), _ptr(out), _ptr(rid),
                                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(st, "fs_sample_logits_filtered")
+    return out
+
+
+def filter_logits(logits: torch.Tensor, temp, *, top_k=None, top_p=None, min_p=None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """The masked, temperature-scaled logits of the filter chain top-k, top-p, min-p over
+    float32 logits [B, V]: y / temp on the kept tokens, -inf elsewhere."""
+    lib = load_library()
+    dev = logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    B, V = logits.shape
+    _need(logits, "logits", torch.float32, dev, (B, V))
+    t = _temp_tensor(temp, B, dev)
+    k = _filter_param(top_k, "top_k", torch.int32, B, dev)
+    p = _filter_param(top_p, "top_p", torch.float32, B, dev)
+    m = _filter_param(min_p, "min_p", torch.float32, B, dev)
+    if out is None:
+        out = torch.empty((B, V), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, (B, V))
+    if out.data_ptr() == logits.data_ptr() and B * V > 0:
+        raise ValueError("out may not alias logits")
+    st = lib.fs_filter_logits(_ptr(logits), B, V, _ptr(t), _ptr(k), _ptr(p), _ptr(m), _ptr(out),
+                              _stream(dev))
+    _check(st, "fs_filter_logits")
     return out
 
 

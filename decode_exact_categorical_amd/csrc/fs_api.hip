@@ -412,8 +412,45 @@ fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, c
   a.counters = need > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
   a.split = need > 0 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kCounterBytes)
                      : nullptr;
+  a.Y = nullptr;
   hipError_t e = fs::launch_logits_filtered(a, fp64_noise != 0, st);
   if (e != hipSuccess) return hip_fail(e, "filtered sampling launch");
+  if (ev) (void)hipEventRecord(ev[1], st);
+  return FS_OK;
+}
+
+fs_status fs_filter_logits(const float* logits, int64_t B, int64_t V, const float* temp,
+                           const int32_t* top_k, const float* top_p, const float* min_p,
+                           float* out_logits, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_sizes(B, V);
+  if (s != FS_OK) return s;
+  if (B >= ((int64_t)1 << 31)) return fail(FS_ERR_INVALID_ARG, "B = %lld exceeds 2^31 - 1", (long long)B);
+  if (B == 0) return FS_OK;
+  if (logits == nullptr || temp == nullptr || out_logits == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "logits, temp or out_logits is null");
+  if (((uintptr_t)logits & 3u) != 0 || ((uintptr_t)out_logits & 3u) != 0)
+    return fail(FS_ERR_UNSUPPORTED, "logits or out_logits not 4-byte aligned");
+  fs::FilterArgs a;
+  a.X = logits;
+  a.B = B;
+  a.V = V;
+  a.temp = temp;
+  a.row_ids = nullptr;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.min_p = min_p;
+  a.key = fs::make_key(0, 0);
+  a.out = nullptr;
+  a.vec4 = aligned16(logits) && aligned16(out_logits) && (V % 4 == 0);
+  a.counters = nullptr;
+  a.split = nullptr;
+  a.Y = out_logits;
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  if (ev) (void)hipEventRecord(ev[0], st);
+  hipError_t e = fs::launch_filter_logits(a, st);
+  if (e != hipSuccess) return hip_fail(e, "filter_logits launch");
   if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }

@@ -318,8 +318,10 @@ struct FilterShared {
 };
 
 // Row b filtered and drawn by one workgroup (steps 1-4 above): the sampled
-// index, or -1, in every thread.
-template <bool FP64, int Cap>
+// index, or -1, in every thread.  STORE: instead of the draw, the row's
+// filtered logits go to a.Y: y / t on the kept tokens, -inf elsewhere (greedy
+// rows keep the largest logit's tie class, unscaled); returns 0.
+template <bool FP64, int Cap, bool STORE = false>
 __device__ __forceinline__ int64_t filter_row_single(
     const FilterArgs& a, int64_t b,
     FilterShared<typename std::conditional<FP64, double, float>::type, Cap>& sh) {
@@ -565,18 +567,21 @@ __device__ __forceinline__ int64_t filter_row_single(
         kappa = kappa > km ? kappa : km;
         use_m = false;
       }
-      // The draw over the kept candidates.
-      for (int q = tid; q < n; q += kFThreads) {
-        const float y = cval[q];
-        if (order_key(y) < kappa || (use_m && !(mass_of(y, M, inv_tf) >= min_p))) continue;
-        const int32_t i = cidx[q];
-        const T s = score1(y, i);
-        if (beats(s, i, bm, bi)) {
-          bm = s;
-          bi = i;
+      // The draw over the kept candidates (the store variant writes the
+      // whole row below).
+      if constexpr (!STORE) {
+        for (int q = tid; q < n; q += kFThreads) {
+          const float y = cval[q];
+          if (order_key(y) < kappa || (use_m && !(mass_of(y, M, inv_tf) >= min_p))) continue;
+          const int32_t i = cidx[q];
+          const T s = score1(y, i);
+          if (beats(s, i, bm, bi)) {
+            bm = s;
+            bi = i;
+          }
         }
+        done = true;
       }
-      done = true;
     } else {
       // 4. Too many candidates: the same selections over the row.
       auto visit_row = [&](auto&& f) {
@@ -614,6 +619,44 @@ __device__ __forceinline__ int64_t filter_row_single(
     }
   }
 
+  if constexpr (STORE) {
+    // The filtered logits: every valid token with key >= kappa that passes the
+    // min-p test, scaled by 1/t; greedy rows keep the largest logit's class.
+    if (greedy) {
+      float lm = neg_inf<float>();
+      for_row(x, V, vec4, [&](int64_t, const float (&y)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (valid_logit(y[j])) lm = fmaxf(lm, y[j]);
+      });
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) lm = fmaxf(lm, __shfl_xor(lm, o));
+      if (lane == 0) red_f[wave] = lm;
+      __syncthreads();
+      M = neg_inf<float>();
+#pragma unroll
+      for (int w = 0; w < kFWaves; ++w) M = fmaxf(M, red_f[w]);
+      kappa = valid_logit(M) ? order_key(M) : 0xFFFFFFFFu;
+    }
+    float* const yo = a.Y + b * V;
+    for_row(x, V, vec4, [&](int64_t i0, const float (&y)[4]) {
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool keep = valid_logit(y[j]) && order_key(y[j]) >= kappa &&
+                          (!use_m || mass_of(y[j], M, inv_tf) >= min_p);
+        o[j] = keep ? y[j] * inv_tf : neg_inf<float>();
+      }
+      if (vec4) {
+        *reinterpret_cast<float4*>(yo + i0) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (i0 + j < V) yo[i0 + j] = o[j];
+      }
+    });
+    return 0;
+  }
   if (!done) {
     // The draw over the row: every valid token with key >= kappa that passes
     // the min-p test (every valid token when no filter is on).
@@ -1059,6 +1102,20 @@ __global__ __launch_bounds__(kFThreads) void logits_filtered_split_kernel(Filter
 }
 
 }  // namespace
+
+namespace {
+
+__global__ __launch_bounds__(kFThreads) void logits_filter_store_kernel(FilterArgs a) {
+  __shared__ FilterShared<float, kCap> sh;
+  (void)filter_row_single<false, kCap, true>(a, (int64_t)blockIdx.x, sh);
+}
+
+}  // namespace
+
+hipError_t launch_filter_logits(const FilterArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(logits_filter_store_kernel, dim3((unsigned)a.B), dim3(kFThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 int filtered_split_chunks(int64_t B, int64_t V) {
   const int64_t G = (V + kChunk - 1) / kChunk;

@@ -93,6 +93,9 @@ struct FilterArgs {
   // candidate lists; null selects one workgroup per row.
   uint32_t* counters;
   uint64_t* split;
+  // Filtered logits (launch_filter_logits): [B, V] out; vec4 then also
+  // covers this buffer.
+  float* Y;
 };
 // Rows a split launch takes: up to ~24 rows splitting wins (measured at
 // V = 151936: 46 against 90 us at B = 16); from B = 32 the per-row kernel
@@ -103,6 +106,9 @@ constexpr int kSplitMaxChunks = 32;   // chunks of a split row (V <= 262144)
 int filtered_split_chunks(int64_t B, int64_t V);  // 0: one workgroup per row
 size_t filtered_split_words(int64_t B, int64_t V);
 hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t stream);
+// The filter chain's output instead of a draw: a.Y[b, i] = y / t on the kept
+// tokens, -inf elsewhere (one workgroup per row).
+hipError_t launch_filter_logits(const FilterArgs& a, hipStream_t stream);
 
 // Speculative-decoding verification over materialised target logits
 // [B, K+1, V] and draft logits [B, K, V]: a statistics launch over every row,

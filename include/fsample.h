@@ -239,6 +239,23 @@ fs_status fs_sample_logits_filtered(const float *logits, int64_t B, int64_t V,
                                     size_t workspace_bytes, fs_stream_t stream);
 
 /*
+ * The filter chain's output [SD API table, filter_logits; Semantics]: the
+ * masked, temperature-scaled logits of fs_sample_logits_filtered's kept set,
+ *   out_logits[b, i] = logits[b, i] * (1 / t)   for the kept tokens,
+ *                      -inf                      elsewhere (NaN included);
+ * greedy rows (t <= 0 or NaN) keep the largest valid logit's tie class,
+ * unscaled.  With the same filters applied to a target's and a draft's
+ * logits, fs_verify at temperature 1 on the two outputs verifies against the
+ * filtered distributions (the card's filtered speculative decoding).
+ *   out_logits  device, float [B, V], 4-byte aligned (may not alias logits)
+ *   the other arguments as for fs_sample_logits_filtered; no workspace, one
+ *   workgroup per row.
+ */
+fs_status fs_filter_logits(const float *logits, int64_t B, int64_t V, const float *temp,
+                           const int32_t *top_k, const float *top_p, const float *min_p,
+                           float *out_logits, fs_stream_t stream);
+
+/*
  * Workspace bytes fs_sample_logits_filtered needs for (B, V): 0 when it runs
  * one workgroup per row (no workspace; NULL is accepted), otherwise the
  * library's fixed completion-counter region (the same leading 256 KiB every

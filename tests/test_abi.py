@@ -134,6 +134,19 @@ def test_filtered_workspace_bytes():
     assert lib.fs_workspace_bytes_filtered(4, 0) == 0
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), 1), (dict(V=0), 1), (dict(X=0), 1), (dict(temp=0), 1), (dict(Y=0), 1),
+    (dict(X=FAKE + 2), 2), (dict(Y=FAKE + 6), 2),
+])
+def test_filter_logits_rejects_before_launch(kw, code):
+    args = dict(B=4, V=1000, X=FAKE, temp=FAKE, Y=FAKE)
+    args.update(kw)
+    lib = fs.load_library()
+    assert lib.fs_filter_logits(P(args["X"]), args["B"], args["V"], P(args["temp"]), None, None,
+                                None, P(args["Y"]), None) == code
+    assert lib.fs_filter_logits(None, 0, 10, None, None, None, None, None, None) == 0
+
+
 def _verify(B=4, K=4, V=100000, T=FAKE, D=FAKE, tok=FAKE, temp=FAKE, acc=FAKE, out=FAKE,
             ws=FAKE, wsb=1 << 30):
     lib = fs.load_library()
