@@ -31,8 +31,19 @@
 namespace fs {
 namespace {
 
-constexpr int kFThreads = 512;
+// Threads of a workgroup (the most; arrays are sized for it).  The split
+// kernel always runs 16 waves.  The one-row-per-workgroup kernels run 16 waves
+// while the rows do not fill the chip: a row's passes are VALU-bound on its one
+// CU (exp2 for the masses, Philox and the Gumbel transform for the draw), and
+// four waves a SIMD hide the transcendental latency that two do not (measured
+// 97.6 -> 76.3 us at B = 64, V = 151936, top-k 50 + top-p 0.95).  With more
+// rows than CUs they run 8 waves, two rows a CU, whose serial phases then
+// overlap each other's streaming (953 against 1140 us at 4096 x 131072).
+// The row helpers below take the thread count from blockDim.
+constexpr int kFThreads = 1024;
 constexpr int kFWaves = kFThreads / 64;
+constexpr int kRowThreadsWide = 512;  // one-row kernels when B exceeds kRowsNarrow
+constexpr int64_t kRowsNarrow = 256;  // rows up to about one per CU
 constexpr float kMassUnit = 0x1p40f;  // fixed-point scale of the masses
 
 // Larger floats have larger keys (NaN is never keyed: it is never kept).
@@ -62,7 +73,7 @@ __device__ __forceinline__ unsigned long long mass_fixed(float e) {
 constexpr int kRowInFlight = 8;
 template <typename F>
 __device__ __forceinline__ void for_row(const float* x, int64_t V, bool vec4, F&& f) {
-  constexpr int64_t kStride = 4 * kFThreads;
+  const int64_t kStride = 4 * (int64_t)blockDim.x;
   int64_t i0 = 4 * (int64_t)threadIdx.x;
   if (vec4) {  // V % 4 == 0, rows 16-byte aligned
     for (; i0 + (kRowInFlight - 1) * kStride < V; i0 += kRowInFlight * kStride) {
@@ -159,7 +170,7 @@ __device__ __forceinline__ RadixStart radix_start(Visit&& visit, bool narrow, ui
   lo = 0xffffffffu;
   hi = 0u;
 #pragma unroll
-  for (int w = 0; w < kFWaves; ++w) {
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
     lo = min(lo, red[2 * w]);
     hi = max(hi, red[2 * w + 1]);
   }
@@ -295,7 +306,7 @@ __device__ __forceinline__ void wave_then_block_best(T& bm, int32_t& bi, Cand<T>
   __syncthreads();
   Cand<T> best = wbest[0];
 #pragma unroll
-  for (int w = 1; w < kFWaves; ++w)
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w)
     if (beats(wbest[w].m, wbest[w].idx, best.m, best.idx)) best = wbest[w];
   bm = best.m;
   bi = best.idx;
@@ -401,7 +412,7 @@ __device__ __forceinline__ int64_t filter_row_single(
     __syncthreads();
     uint32_t n_valid = 0;
 #pragma unroll
-    for (int w = 0; w < kFWaves; ++w) {
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
       M = fmaxf(M, red_f[w]);
       n_valid += red_u[w];
     }
@@ -538,7 +549,7 @@ __device__ __forceinline__ int64_t filter_row_single(
       __syncthreads();
       const int n = (int)(n_cand < (uint32_t)Cap ? n_cand : (uint32_t)Cap);
       auto visit_all = [&](auto&& f) {
-        for (int q = tid; q < n; q += kFThreads) f(order_key(cval[q]), cval[q]);
+        for (int q = tid; q < n; q += (int)blockDim.x) f(order_key(cval[q]), cval[q]);
       };
       // Top-k binds only when the candidates reach its bin; then they hold
       // every logit down to the k-th largest.
@@ -550,7 +561,7 @@ __device__ __forceinline__ int64_t filter_row_single(
           key_p = order_key(M);
         } else {
           auto visit_s1 = [&](auto&& f) {
-            for (int q = tid; q < n; q += kFThreads) {
+            for (int q = tid; q < n; q += (int)blockDim.x) {
               const uint32_t key = order_key(cval[q]);
               if (key >= key_k) f(key, cval[q]);
             }
@@ -570,7 +581,7 @@ __device__ __forceinline__ int64_t filter_row_single(
       // The draw over the kept candidates (the store variant writes the
       // whole row below).
       if constexpr (!STORE) {
-        for (int q = tid; q < n; q += kFThreads) {
+        for (int q = tid; q < n; q += (int)blockDim.x) {
           const float y = cval[q];
           if (order_key(y) < kappa || (use_m && !(mass_of(y, M, inv_tf) >= min_p))) continue;
           const int32_t i = cidx[q];
@@ -635,7 +646,7 @@ __device__ __forceinline__ int64_t filter_row_single(
       __syncthreads();
       M = neg_inf<float>();
 #pragma unroll
-      for (int w = 0; w < kFWaves; ++w) M = fmaxf(M, red_f[w]);
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) M = fmaxf(M, red_f[w]);
       kappa = valid_logit(M) ? order_key(M) : 0xFFFFFFFFu;
     }
     float* const yo = a.Y + b * V;
@@ -1113,7 +1124,8 @@ __global__ __launch_bounds__(kFThreads) void logits_filter_store_kernel(FilterAr
 }  // namespace
 
 hipError_t launch_filter_logits(const FilterArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(logits_filter_store_kernel, dim3((unsigned)a.B), dim3(kFThreads), 0, stream, a);
+  const int nthr = a.B > kRowsNarrow ? kRowThreadsWide : kFThreads;
+  hipLaunchKernelGGL(logits_filter_store_kernel, dim3((unsigned)a.B), dim3(nthr), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1138,10 +1150,11 @@ hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t st
     return hipGetLastError();
   }
   const dim3 grid((unsigned)a.B);
+  const dim3 block(a.B > kRowsNarrow ? kRowThreadsWide : kFThreads);
   if (fp64)
-    hipLaunchKernelGGL(logits_filtered_kernel<true>, grid, dim3(kFThreads), 0, stream, a);
+    hipLaunchKernelGGL(logits_filtered_kernel<true>, grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(logits_filtered_kernel<false>, grid, dim3(kFThreads), 0, stream, a);
+    hipLaunchKernelGGL(logits_filtered_kernel<false>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
