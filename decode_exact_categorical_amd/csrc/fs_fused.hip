@@ -194,6 +194,111 @@ __device__ __forceinline__ bool fold_scale_ok(float s) {
 
 // BV4: the bias rows are 16-byte aligned (V % 4 == 0), so a fragment's four
 // biases come in one load.
+// ---------------------------------------------------------------------------
+// Gumbel-top-k Stage 2 of one row, by one wave.  Lane l reads the sorted
+// lists of tiles l, l + 64, l + 128, l + 192 (clamped addresses).  Among any k
+// candidates the k-th best bounds the row's k-th place from below, so with
+// theta the k-th best of the tile maxima (place 0 of each list), only
+// candidates at or above theta can take a place: a prefix of each list, about
+// k tiles' worth.  So the maxima come first, then only the lists whose maximum
+// is at or above theta; the survivors go to the wave's LDS list and the places
+// are picked from it, two candidates a lane.  A row with more survivors (rows
+// with fewer than k valid scores) picks them from the lists themselves.
+// ---------------------------------------------------------------------------
+constexpr int kS2TilesPerLane = kMaxFusedTiles / 64;
+constexpr int kS2SurvPerLane = 2;
+constexpr int kS2SurvPerWave = 64 * kS2SurvPerLane;
+constexpr int64_t kStage2InKernelRows = 16;  // widest tile whose Stage 2 runs in the fused kernel
+
+template <typename T>
+__device__ __forceinline__ void topk_load_maxima(const FusedArgs& a, int64_t b, int lane,
+                                                 Cand<T> (&mx)[kS2TilesPerLane]) {
+  const Cand<T>* rc = reinterpret_cast<const Cand<T>*>(a.cand) + b * a.nT * kTopKMax;
+#pragma unroll
+  for (int j = 0; j < kS2TilesPerLane; ++j) {
+    const int t = lane + 64 * j;
+    mx[j] = load_cand(rc + (t < a.nT ? t * kTopKMax : 0));
+    if (t >= a.nT) mx[j] = Cand<T>{neg_inf<T>(), kNoIndex};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void topk_row_places(const FusedArgs& a, int64_t b, int lane,
+                                                const Cand<T> (&mx)[kS2TilesPerLane],
+                                                Cand<T>* surv) {
+  constexpr int kPer = kS2TilesPerLane * kTopKMax;
+  const Cand<T>* rc = reinterpret_cast<const Cand<T>*>(a.cand) + b * a.nT * kTopKMax;
+  // theta is the k-th place among the tile maxima.
+  Cand<T> th = Cand<T>{neg_inf<T>(), kNoIndex};
+#pragma unroll 1
+  for (int r = 0; r < a.k; ++r) th = next_place(mx, r == 0, th.m, th.idx);
+  // Then the rest of the lists whose maximum is at or above theta (the others
+  // cannot hold a survivor).
+  Cand<T> c[kPer];
+#pragma unroll
+  for (int j = 0; j < kS2TilesPerLane; ++j) {
+    const int t = lane + 64 * j;
+    const bool live = t < a.nT && !after(mx[j].m, mx[j].idx, th.m, th.idx);
+    c[j * kTopKMax] = mx[j];
+#pragma unroll
+    for (int p = 1; p < kTopKMax; ++p) {
+      c[j * kTopKMax + p] = Cand<T>{neg_inf<T>(), kNoIndex};
+      if (live) c[j * kTopKMax + p] = load_cand(rc + t * kTopKMax + p);
+    }
+  }
+  // The survivors (at or above theta) and this lane's offset among them.
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) cnt += after(c[q].m, c[q].idx, th.m, th.idx) ? 0u : 1u;
+  uint32_t off = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(off, o);
+    if (lane >= o) off += v;
+  }
+  const uint32_t total = __shfl(off, 63);
+  off -= cnt;
+  Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
+  if (total <= (uint32_t)kS2SurvPerWave) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if (!after(c[q].m, c[q].idx, th.m, th.idx)) surv[off++] = c[q];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    Cand<T> c2[kS2SurvPerLane];
+#pragma unroll
+    for (int q = 0; q < kS2SurvPerLane; ++q)
+      c2[q] = (uint32_t)(lane + 64 * q) < total ? surv[lane + 64 * q] : Cand<T>{neg_inf<T>(), kNoIndex};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 1
+    for (int r = 0; r < a.k; ++r) {
+      pl = next_place(c2, r == 0, pl.m, pl.idx);
+      if (lane == 0) a.out[b * a.k + r] = pl.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)pl.idx;
+    }
+  } else {
+#pragma unroll 1
+    for (int r = 0; r < a.k; ++r) {
+      pl = next_place(c, r == 0, pl.m, pl.idx);
+      if (lane == 0) a.out[b * a.k + r] = pl.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)pl.idx;
+    }
+  }
+}
+
+// Stage 2 as its own launch: one wave per row, four rows a workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void topk_stage2_kernel(FusedArgs a) {
+  __shared__ Cand<T> surv[4][kS2SurvPerWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t b = (int64_t)blockIdx.x * 4 + wave;
+  if (b >= a.B) return;  // whole waves; nothing below waits on another wave
+  Cand<T> mx[kS2TilesPerLane];
+  topk_load_maxima(a, b, lane, mx);
+  topk_row_places(a, b, lane, mx, surv[wave]);
+}
+
 template <int NB, int EPI, bool HAS_BIAS, int WF, bool BV4 = false>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
@@ -1207,105 +1312,33 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
     wait_stores_complete();
 
-    // Stage 2: wave w takes rows w, w + 8, ... of the tile.  Lane l reads the
-    // whole sorted lists of tiles l, l + 64, l + 128, l + 192 (clamped
-    // addresses).  Among any k candidates the k-th best bounds the row's k-th
-    // place from below, so with theta the k-th best of the tile maxima, only
-    // candidates at or above theta can take a place: a prefix of each list,
-    // about k tiles' worth.  Those go to a per-wave LDS list (the H staging
-    // buffer is free now), and the places are picked from it, two candidates
-    // a lane; a row with more of them (rows with fewer than k valid scores)
-    // picks them from the lists themselves.
+    // Stage 2 (topk_row_places above), here for tiles of at most
+    // kStage2InKernelRows rows: wave w takes rows w, w + 8, ... of the tile,
+    // each row's maxima requested with the previous row's list loads.  Wider
+    // tiles leave it to a launch of one wave per row (topk_stage2_kernel, made
+    // by launch_fused_stage1), since here a tile's rows would queue 8 to a wave.
+    if constexpr (16 * NB > kStage2InKernelRows) {
+      return;
+    } else {
     if (!finish_last(a.counters + btile, (uint32_t)nT)) return;
-    constexpr int kTilesPerLane = kMaxFusedTiles / 64;
-    constexpr int kPer = kTilesPerLane * kTopKMax;
-    constexpr int kSurvPerLane = 2;
-    static_assert(kWaves * 64 * kSurvPerLane * sizeof(Cand<T>) <= sizeof(hs),
+    static_assert(kWaves * kS2SurvPerWave * sizeof(Cand<T>) <= sizeof(hs),
                   "the survivors of every wave fit in the H staging buffer");
-    Cand<T>* const surv = reinterpret_cast<Cand<T>*>(&hs[0][0][0]) + wave * 64 * kSurvPerLane;
-    // The tile maxima (place 0 of each list) of row b, clamped addresses.
-    auto load_maxima = [&](Cand<T> (&mx)[kTilesPerLane], int64_t b) {
-      const Cand<T>* rc = reinterpret_cast<const Cand<T>*>(a.cand) + b * a.nT * kTopKMax;
-#pragma unroll
-      for (int j = 0; j < kTilesPerLane; ++j) {
-        const int t = lane + 64 * j;
-        mx[j] = load_cand(rc + (t < a.nT ? t * kTopKMax : 0));
-        if (t >= a.nT) mx[j] = Cand<T>{neg_inf<T>(), kNoIndex};
-      }
-    };
-    // A row's maxima are requested with the previous row's list loads, so each
-    // row costs one round trip to the coherence point.
-    Cand<T> mxn[kTilesPerLane];
-    if (bt0 + wave < B) load_maxima(mxn, bt0 + wave);
+    Cand<T>* const surv = reinterpret_cast<Cand<T>*>(&hs[0][0][0]) + wave * kS2SurvPerWave;
+    Cand<T> mxn[kS2TilesPerLane];
+    if (bt0 + wave < B) topk_load_maxima(a, bt0 + wave, lane, mxn);
 #pragma unroll 1
     for (int i = wave; i < kTile; i += kWaves) {
       const int64_t b = bt0 + i;
       if (b >= B) break;
-      const Cand<T>* rc = reinterpret_cast<const Cand<T>*>(a.cand) + b * a.nT * kTopKMax;
-      // theta is the k-th place among the tile maxima.
-      Cand<T> mx[kTilesPerLane];
+      Cand<T> mx[kS2TilesPerLane];
 #pragma unroll
-      for (int j = 0; j < kTilesPerLane; ++j) mx[j] = mxn[j];
-      if (i + kWaves < kTile && b + kWaves < B) load_maxima(mxn, b + kWaves);
-      Cand<T> th = Cand<T>{neg_inf<T>(), kNoIndex};
-#pragma unroll 1
-      for (int r = 0; r < a.k; ++r) th = next_place(mx, r == 0, th.m, th.idx);
-      // Then the rest of the lists whose maximum is at or above theta (the
-      // others cannot hold a survivor).
-      Cand<T> c[kPer];
-#pragma unroll
-      for (int j = 0; j < kTilesPerLane; ++j) {
-        const int t = lane + 64 * j;
-        const bool live = t < a.nT && !after(mx[j].m, mx[j].idx, th.m, th.idx);
-        c[j * kTopKMax] = mx[j];
-#pragma unroll
-        for (int p = 1; p < kTopKMax; ++p) {
-          c[j * kTopKMax + p] = Cand<T>{neg_inf<T>(), kNoIndex};
-          if (live) c[j * kTopKMax + p] = load_cand(rc + t * kTopKMax + p);
-        }
-      }
-      // The survivors (at or above theta) and this lane's offset among them.
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) cnt += after(c[q].m, c[q].idx, th.m, th.idx) ? 0u : 1u;
-      uint32_t off = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_up(off, o);
-        if (lane >= o) off += v;
-      }
-      const uint32_t total = __shfl(off, 63);
-      off -= cnt;
-      Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
-      if (total <= 64u * kSurvPerLane) {
-#pragma unroll
-        for (int q = 0; q < kPer; ++q)
-          if (!after(c[q].m, c[q].idx, th.m, th.idx)) surv[off++] = c[q];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        Cand<T> c2[kSurvPerLane];
-#pragma unroll
-        for (int q = 0; q < kSurvPerLane; ++q)
-          c2[q] = (uint32_t)(lane + 64 * q) < total ? surv[lane + 64 * q] : Cand<T>{neg_inf<T>(), kNoIndex};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 1
-        for (int r = 0; r < a.k; ++r) {
-          pl = next_place(c2, r == 0, pl.m, pl.idx);
-          if (lane == 0) a.out[b * a.k + r] = pl.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)pl.idx;
-        }
-      } else {
-#pragma unroll 1
-        for (int r = 0; r < a.k; ++r) {
-          pl = next_place(c, r == 0, pl.m, pl.idx);
-          if (lane == 0) a.out[b * a.k + r] = pl.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)pl.idx;
-        }
-      }
+      for (int j = 0; j < kS2TilesPerLane; ++j) mx[j] = mxn[j];
+      if (i + kWaves < kTile && b + kWaves < B) topk_load_maxima(a, b + kWaves, lane, mxn);
+      topk_row_places(a, b, lane, mx, surv);
     }
     if (tid == 0) clear_counter(a.counters + btile);
     return;
+    }
   }
 
   // Across the waves, in wave order, through LDS.
@@ -1455,7 +1488,15 @@ hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) 
     int nb = fused_column_blocks(a.B, true, false);  // tiles of at most 64 columns
     if (epi == kEpiTopK64 && nb > 1) nb = 4;
     const dim3 grid((unsigned)a.nT, (unsigned)((a.B + 16 * nb - 1) / (16 * nb)));
-    return launch_w<kWBf16>(a, epi, grid, nb, stream);
+    hipError_t e = launch_w<kWBf16>(a, epi, grid, nb, stream);
+    // Tiles wider than kStage2InKernelRows rows: Stage 2 in a launch of its own.
+    if (e != hipSuccess || 16 * nb <= kStage2InKernelRows) return e;
+    const dim3 g2((unsigned)((a.B + 3) / 4));
+    if (epi == kEpiTopK64)
+      hipLaunchKernelGGL(topk_stage2_kernel<double>, g2, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(topk_stage2_kernel<float>, g2, dim3(256), 0, stream, a);
+    return hipGetLastError();
   }
   const bool narrow = a.W8 != nullptr || a.W4 != nullptr;
   const int nb = fused_column_blocks(a.B, narrow, epi == kEpiSample64);
