@@ -745,19 +745,26 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-template <bool FP64>
+// MODE kSplitOne: chunks and merge in one launch (the merge in the row's last
+// workgroup).  kSplitChunks / kSplitMerge: the same two halves as two
+// launches, so that the chunk workgroups hold only their chunk in LDS (two a
+// CU) and every row's merge starts at once (batches past kSplitMaxRows).
+enum SplitMode { kSplitOne = 0, kSplitChunks = 1, kSplitMerge = 2 };
+
+template <bool FP64, int MODE>
 __global__ __launch_bounds__(kFThreads) void logits_filtered_split_kernel(FilterArgs a) {
   typedef typename std::conditional<FP64, double, float>::type T;
-  __shared__ FilterShared<T, kSplitCap> sh;
+  __shared__ FilterShared<T, MODE == kSplitChunks ? kChunk : kSplitCap> sh;
   __shared__ float gM[kSplitMaxChunks];
   __shared__ unsigned long long gZ[kSplitMaxChunks];
   __shared__ uint32_t gN[kSplitMaxChunks], gTau[kSplitMaxChunks], gList[kSplitMaxChunks],
       gBase[kSplitMaxChunks + 1];
   __shared__ Cand<T> gBest[kSplitMaxChunks];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = blockIdx.x, G = gridDim.x;
   const int64_t b = blockIdx.y;
   const int64_t V = a.V;
+  const int g = blockIdx.x;
+  const int G = MODE == kSplitMerge ? (int)((V + kChunk - 1) / kChunk) : (int)gridDim.x;
   const float* x = a.X + b * V;
   const float t = a.temp[b];
   const bool greedy = !(t > 0.0f);
@@ -776,6 +783,7 @@ __global__ __launch_bounds__(kFThreads) void logits_filtered_split_kernel(Filter
   uint64_t* const hdr = a.split + ((b * G + g) * (kHdrWords + kListCap));
   uint64_t* const lst = hdr + kHdrWords;
 
+  if constexpr (MODE != kSplitMerge) {
   // 1. The chunk into LDS; its largest valid logit and count.
   if (a.vec4) {  // V % 4 == 0 and kChunk % 4 == 0: n % 4 == 0, aligned
     for (int q = 4 * tid; q < n; q += 4 * kFThreads) {
@@ -951,9 +959,15 @@ __global__ __launch_bounds__(kFThreads) void logits_filtered_split_kernel(Filter
   }
   if (tid == 0) cand_store_u64(hdr + 0, (uint64_t)__float_as_uint(Mg) | ((uint64_t)nvg << 32));
   wait_stores_complete();
+  }
 
-  // 4. The row's last workgroup merges.
-  if (!finish_last(a.counters + b, (uint32_t)G)) return;
+  // 4. The row's last workgroup merges (or the merge launch's workgroup).
+  if constexpr (MODE == kSplitChunks) {
+    return;
+  } else {
+  if constexpr (MODE == kSplitOne) {
+    if (!finish_last(a.counters + b, (uint32_t)G)) return;
+  }
   if (tid < G) {
     const uint64_t* h = a.split + ((b * G + tid) * (kHdrWords + kListCap));
     const uint64_t h0 = cand_load_u64(h + 0);
@@ -1110,6 +1124,7 @@ __global__ __launch_bounds__(kFThreads) void logits_filtered_split_kernel(Filter
     a.out[b] = out;
     clear_counter(a.counters + b);
   }
+  }
 }
 
 }  // namespace
@@ -1131,7 +1146,7 @@ hipError_t launch_filter_logits(const FilterArgs& a, hipStream_t stream) {
 
 int filtered_split_chunks(int64_t B, int64_t V) {
   const int64_t G = (V + kChunk - 1) / kChunk;
-  return (B <= kSplitMaxRows && G >= 2 && G <= kSplitMaxChunks) ? (int)G : 0;
+  return (B <= kSplitTwoLaunchMaxRows && G >= 2 && G <= kSplitMaxChunks) ? (int)G : 0;
 }
 
 size_t filtered_split_words(int64_t B, int64_t V) {
@@ -1141,12 +1156,23 @@ size_t filtered_split_words(int64_t B, int64_t V) {
 
 hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t stream) {
   const int G = a.split ? filtered_split_chunks(a.B, a.V) : 0;
-  if (G) {
+  if (G && a.B <= kSplitMaxRows) {
     const dim3 grid((unsigned)G, (unsigned)a.B);
     if (fp64)
-      hipLaunchKernelGGL(logits_filtered_split_kernel<true>, grid, dim3(kFThreads), 0, stream, a);
+      hipLaunchKernelGGL((logits_filtered_split_kernel<true, kSplitOne>), grid, dim3(kFThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(logits_filtered_split_kernel<false>, grid, dim3(kFThreads), 0, stream, a);
+      hipLaunchKernelGGL((logits_filtered_split_kernel<false, kSplitOne>), grid, dim3(kFThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (G) {
+    const dim3 grid((unsigned)G, (unsigned)a.B), grid2(1u, (unsigned)a.B);
+    if (fp64) {
+      hipLaunchKernelGGL((logits_filtered_split_kernel<true, kSplitChunks>), grid, dim3(kFThreads), 0, stream, a);
+      hipLaunchKernelGGL((logits_filtered_split_kernel<true, kSplitMerge>), grid2, dim3(kFThreads), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((logits_filtered_split_kernel<false, kSplitChunks>), grid, dim3(kFThreads), 0, stream, a);
+      hipLaunchKernelGGL((logits_filtered_split_kernel<false, kSplitMerge>), grid2, dim3(kFThreads), 0, stream, a);
+    }
     return hipGetLastError();
   }
   const dim3 grid((unsigned)a.B);

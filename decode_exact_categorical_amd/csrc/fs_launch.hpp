@@ -102,6 +102,11 @@ struct FilterArgs {
 // keeps up and from B = 64 it wins (the split kernel's LDS, sized for the
 // merge, holds one workgroup per CU).
 constexpr int kSplitMaxRows = 24;
+// Up to this many rows the chunks and the merges run as two launches (chunk
+// workgroups two a CU, every row's merge at once); beyond it, one workgroup
+// per row (measured at V = 151936, top-k 50 + top-p 0.95: 46.5 against 73.1 us
+// at B = 32, 57.8 against 78.3 at B = 64, even at 128, behind from 256).
+constexpr int kSplitTwoLaunchMaxRows = 96;
 constexpr int kSplitMaxChunks = 32;   // chunks of a split row (V <= 262144)
 int filtered_split_chunks(int64_t B, int64_t V);  // 0: one workgroup per row
 size_t filtered_split_words(int64_t B, int64_t V);
