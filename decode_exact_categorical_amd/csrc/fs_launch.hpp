@@ -97,11 +97,11 @@ struct FilterArgs {
   // covers this buffer.
   float* Y;
 };
-// Rows a split launch takes: up to ~24 rows splitting wins (measured at
-// V = 151936: 46 against 90 us at B = 16); from B = 32 the per-row kernel
-// keeps up and from B = 64 it wins (the split kernel's LDS, sized for the
-// merge, holds one workgroup per CU).
-constexpr int kSplitMaxRows = 24;
+// Split rows up to this many run chunks and merge in one launch (the merge in
+// each row's last workgroup): at B <= 8 that saves the second launch's gap;
+// from B = 16 two launches win (40.1 against 44.5 us at B = 16, 40.5 against
+// 55 at B = 24; V = 151936, top-k 50 + top-p 0.95).
+constexpr int kSplitMaxRows = 8;
 // Up to this many rows the chunks and the merges run as two launches (chunk
 // workgroups two a CU, every row's merge at once); beyond it, one workgroup
 // per row (measured at V = 151936, top-k 50 + top-p 0.95: 46.5 against 73.1 us

@@ -127,7 +127,7 @@ def test_filtered_workspace_bytes():
     # split rows for small batches of long rows: counters, chunk headers and lists
     assert lib.fs_workspace_bytes_filtered(16, 151936) >= 16 * 19 * (8 + 512) * 8
     assert lib.fs_workspace_bytes_filtered(1, 128256) > 0
-    # batches past 24 rows run the chunks and the merges as two launches
+    # batches of 9 to 96 rows run the chunks and the merges as two launches
     assert lib.fs_workspace_bytes_filtered(64, 151936) >= 256 * 1024 + 64 * 19 * (8 + 512) * 8
     # one workgroup per row (large batches, short or very long rows): none
     for B, V in ((4096, 131072), (97, 151936), (16, 8192), (8, 300000), (0, 151936)):

@@ -8,14 +8,16 @@ the oracle, through the C ABI.
   and NaN rows.
 * Every draw lies in the oracle's kept set, over many offsets.
 * A row with every filter off draws exactly what fs_sample_logits draws.
-* Both launch shapes: one workgroup per row (large batches, short rows) and
-  rows split over several workgroups whose candidate lists the row's last
-  workgroup merges (small batches), including rows whose lists cannot hold
-  the kept set (the merge then runs the one-workgroup path).
+* Every launch shape: one workgroup per row (large batches, short rows) and
+  rows split over several workgroups whose candidate lists are merged per
+  row, in the row's last workgroup (B <= 8) or in a second launch (9 to 96
+  rows), including rows whose lists cannot hold the kept set (the merge then
+  runs the one-workgroup path).
 * The law of the draws on a small row (chi-square against the softmax over the
   kept set) and zero draws outside it.
-* Full size: the Qwen3-8B-shaped vocabulary (V = 151936), B = 8 (split rows)
-  and B = 64 (one workgroup per row), every row against the oracle.
+* Full size: the Qwen3-8B-shaped vocabulary (V = 151936), B = 8 (split rows,
+  one launch) and B = 64 (split rows, two launches), every row against the
+  oracle.
 """
 import numpy as np
 import pytest
@@ -78,8 +80,12 @@ CASES = [
     dict(B=5, V=7),
     dict(B=3, V=1),
     dict(B=600, V=9000),             # one workgroup per row
-    dict(B=24, V=20000),             # the most rows a split launch takes
+    dict(B=8, V=20000),              # the most rows split in one launch
+    dict(B=24, V=20000),             # split rows, chunks and merges in two launches
+    dict(B=96, V=20000),             # the most rows split in two launches
+    dict(B=97, V=20000),             # one workgroup per row again
     dict(B=4, V=262144),             # the most chunks a split row has
+    dict(B=40, V=262144),            # ... in two launches
 ]
 
 
