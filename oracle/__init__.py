@@ -104,6 +104,8 @@ def _load():
         lib.oracle_filtered_repeated_row.restype = None
         lib.oracle_filtered_repeated_row.argtypes = [P, i64, ctypes.c_float, i32, ctypes.c_float,
                                                      ctypes.c_float, u64, u64, P, i64, i32, P]
+        lib.oracle_repetition_penalty.restype = None
+        lib.oracle_repetition_penalty.argtypes = [P, i64, i64, P, i64, P, P]
         lib.oracle_filter_logits.restype = None
         lib.oracle_filter_logits.argtypes = [P, i64, i64, P, P, P, P, P, P]
         lib.oracle_accept_uniform.restype = ctypes.c_double
@@ -419,6 +421,18 @@ def filter_kept(logits_f32, temp, *, top_k=None, top_p=None, min_p=None):
     _load().oracle_filter_kept(_ptr(x), B, V, _ptr(t), _ptr(k), _ptr(p), _ptr(m), _ptr(kept),
                                _ptr(margin))
     return kept.astype(bool), margin
+
+
+def repetition_penalty(logits_f32, prev_tokens, penalty) -> np.ndarray:
+    """float32[B, V]: logits with the repetition penalty applied to the tokens of
+    prev_tokens[B, L] (entries outside [0, V) are padding); penalty scalar or [B]."""
+    x = np.ascontiguousarray(np.asarray(logits_f32, dtype=np.float32))
+    B, V = x.shape
+    prev = np.ascontiguousarray(np.asarray(prev_tokens, dtype=np.int64).reshape(B, -1))
+    pen = np.ascontiguousarray(np.broadcast_to(np.asarray(penalty, dtype=np.float32), (B,)).copy())
+    out = np.empty_like(x)
+    _load().oracle_repetition_penalty(_ptr(x), B, V, _ptr(prev), prev.shape[1], _ptr(pen), _ptr(out))
+    return out
 
 
 def filter_logits(logits_f32, temp, *, top_k=None, top_p=None, min_p=None):

@@ -759,6 +759,30 @@ void oracle_filter_kept(const float *logits, int64_t B, int64_t V, const float *
     }
 }
 
+/* Repetition penalty [SD sample pipeline: the penalty comes before the
+ * temperature; the transformers processor's rule]: every token that occurs in
+ * row b's previous tokens prev[b, 0..L) (entries outside [0, V) are padding)
+ * has its logit y replaced by y * penalty when y < 0 and by y / penalty
+ * otherwise; the other logits are unchanged.  A row whose penalty is not
+ * positive (or NaN) is unchanged.  Computed in float64 and rounded to float32
+ * (for a product or a quotient of two float32 values this is the correctly
+ * rounded float32 result). */
+void oracle_repetition_penalty(const float *logits, int64_t B, int64_t V, const int64_t *prev,
+                               int64_t L, const float *penalty, float *out)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < V; ++i) out[b * V + i] = logits[b * V + i];
+        double p = (double)penalty[b];
+        if (!(p > 0.0)) continue;
+        for (int64_t j = 0; j < L; ++j) {
+            int64_t x = prev[b * L + j];
+            if (x < 0 || x >= V) continue;
+            double y = (double)logits[b * V + x];
+            out[b * V + x] = (float)((y < 0.0) ? y * p : y / p);
+        }
+    }
+}
+
 /* The filter chain's output [SD API table: filter_logits]: out[b, i] =
  * logits[b, i] / t on the kept tokens of oracle_filter_kept and -inf
  * elsewhere; greedy rows (!(t > 0)) keep the largest logit's tie class

@@ -14,7 +14,10 @@ code:
   the unfiltered sampler draw for draw, top_k = 1 is numpy's argmax, greedy
   rows, masks and NaN;
 * the filtered logits (filter_logits) against the processors' own output
-  values: -inf at the same tokens, y / t elsewhere.
+  values: -inf at the same tokens, y / t elsewhere;
+* the repetition penalty against the transformers processor
+  (RepetitionPenaltyLogitsProcessor) bit for bit, duplicates and padding
+  included.
 """
 import numpy as np
 import pytest
@@ -244,3 +247,29 @@ def test_filter_logits_greedy_and_masks():
     out, _ = oracle.filter_logits(x, [0.0, 2.0], top_k=2)
     np.testing.assert_array_equal(out[0], [-np.inf, 3.0, -np.inf, 3.0, -np.inf])
     np.testing.assert_array_equal(out[1], [-np.inf, -np.inf, 1.0, 0.5, -np.inf])
+
+
+def test_repetition_penalty_matches_transformers():
+    from transformers.generation.logits_process import RepetitionPenaltyLogitsProcessor
+    rng = np.random.default_rng(17)
+    B, V, L = 12, 500, 40
+    x = (rng.standard_normal((B, V)) * 3).astype(np.float32)
+    x[0, :5] = 0.0
+    x[1, 7] = -np.inf
+    prev = rng.integers(0, V, (B, L))
+    prev[:, 1] = prev[:, 0]                       # duplicates count once
+    prev[0, :5] = np.arange(5)                    # zero logits: 0 / p
+    prev[1, 0] = 7
+    for pen in (1.3, 0.7, 2.0):
+        ref = RepetitionPenaltyLogitsProcessor(pen)(torch.from_numpy(prev),
+                                                    torch.from_numpy(x.copy())).numpy()
+        got = oracle.repetition_penalty(x, prev, pen)
+        np.testing.assert_array_equal(got, ref)
+    # padding outside [0, V) is ignored; a penalty that is not positive is off
+    pp = prev.copy()
+    pp[:, L // 2:] = -1
+    pp[:, -1] = V
+    ref = RepetitionPenaltyLogitsProcessor(1.5)(torch.from_numpy(prev[:, :L // 2]),
+                                                torch.from_numpy(x.copy())).numpy()
+    np.testing.assert_array_equal(oracle.repetition_penalty(x, pp, 1.5), ref)
+    np.testing.assert_array_equal(oracle.repetition_penalty(x, prev, 0.0), x)
