@@ -101,6 +101,8 @@ def load_library():
                                                   sz, P]
         lib.fs_workspace_bytes_filtered.restype = sz
         lib.fs_workspace_bytes_filtered.argtypes = [i64, i64]
+        lib.fs_repetition_penalty.restype = i32
+        lib.fs_repetition_penalty.argtypes = [P, i64, i64, P, i64, P, P, P]
         lib.fs_filter_logits.restype = i32
         lib.fs_filter_logits.argtypes = [P, i64, i64, P, P, P, P, P, P]
         lib.fs_verify.restype = i32
@@ -345,6 +347,48 @@ def sample_logits_filtered(logits: torch.Tensor, temp, *, top_k=None, top_p=None
                                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(st, "fs_sample_logits_filtered")
     return out
+
+
+def repetition_penalty(logits: torch.Tensor, prev_tokens: torch.Tensor, penalty, *,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """Logits [B, V] float32 with the repetition penalty applied to the tokens of
+    prev_tokens [B, L] int64 (entries outside [0, V) are padding): y * penalty where
+    y < 0, y / penalty elsewhere.  penalty: a float or a [B] tensor; out may be logits."""
+    lib = load_library()
+    dev = logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dim() != 2 or prev_tokens.dim() != 2:
+        raise ValueError("logits must be [B, V] and prev_tokens [B, L]")
+    B, V = logits.shape
+    L = prev_tokens.shape[1]
+    _need(logits, "logits", torch.float32, dev, (B, V))
+    _need(prev_tokens, "prev_tokens", torch.int64, dev, (B, L))
+    pen = _temp_tensor(penalty, B, dev)
+    if out is None:
+        out = torch.empty_like(logits)
+    _need(out, "out", torch.float32, dev, (B, V))
+    st = lib.fs_repetition_penalty(_ptr(logits), B, V, _ptr(prev_tokens) if L > 0 else None, L,
+                                   _ptr(pen), _ptr(out), _stream(dev))
+    _check(st, "fs_repetition_penalty")
+    return out
+
+
+_penalise = repetition_penalty  # `sample` takes an argument of that name
+
+
+def sample(logits: torch.Tensor, temperature, *, top_k=None, top_p=None, min_p=None,
+           repetition_penalty=None, prev_tokens: torch.Tensor | None = None, seed: int,
+           offset: int, row_ids: torch.Tensor | None = None, fp64_noise: bool = False):
+    """The spec-decode-ops sample pipeline: repetition penalty (when repetition_penalty
+    and prev_tokens are given), temperature, top-k, top-p, min-p, then the exact draw.
+    One int64 token per row."""
+    x = logits
+    if repetition_penalty is not None and prev_tokens is not None:
+        x = _penalise(logits, prev_tokens, repetition_penalty)
+    return sample_logits_filtered(x, temperature, top_k=top_k, top_p=top_p, min_p=min_p,
+                                  seed=seed, offset=offset, row_ids=row_ids,
+                                  fp64_noise=fp64_noise)
 
 
 def filter_logits(logits: torch.Tensor, temp, *, top_k=None, top_p=None, min_p=None,

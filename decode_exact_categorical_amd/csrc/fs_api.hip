@@ -419,6 +419,38 @@ fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, c
   return FS_OK;
 }
 
+fs_status fs_repetition_penalty(const float* logits, int64_t B, int64_t V,
+                                const int64_t* prev_tokens, int64_t L, const float* penalty,
+                                float* out_logits, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_sizes(B, V);
+  if (s != FS_OK) return s;
+  if (B > 65535) return fail(FS_ERR_INVALID_ARG, "B = %lld exceeds 65535", (long long)B);
+  if (L < 0) return fail(FS_ERR_INVALID_ARG, "L = %lld is negative", (long long)L);
+  if (B == 0) return FS_OK;
+  if (logits == nullptr || penalty == nullptr || out_logits == nullptr ||
+      (L > 0 && prev_tokens == nullptr))
+    return fail(FS_ERR_INVALID_ARG, "logits, prev_tokens, penalty or out_logits is null");
+  if (((uintptr_t)logits & 3u) != 0 || ((uintptr_t)out_logits & 3u) != 0)
+    return fail(FS_ERR_UNSUPPORTED, "logits or out_logits not 4-byte aligned");
+  fs::PenaltyArgs a;
+  a.X = logits;
+  a.Y = out_logits;
+  a.B = B;
+  a.V = V;
+  a.prev = prev_tokens;
+  a.L = L;
+  a.penalty = penalty;
+  a.vec4 = aligned16(logits) && aligned16(out_logits) && (V % 4 == 0);
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = prof_slot();
+  if (ev) (void)hipEventRecord(ev[0], st);
+  hipError_t e = fs::launch_repetition_penalty(a, st);
+  if (e != hipSuccess) return hip_fail(e, "repetition penalty launch");
+  if (ev) (void)hipEventRecord(ev[1], st);
+  return FS_OK;
+}
+
 fs_status fs_filter_logits(const float* logits, int64_t B, int64_t V, const float* temp,
                            const int32_t* top_k, const float* top_p, const float* min_p,
                            float* out_logits, fs_stream_t stream) {

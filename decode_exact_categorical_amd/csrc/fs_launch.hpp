@@ -143,6 +143,20 @@ size_t verify_stat_bytes();
 void verify_chunks(int64_t B, int64_t K, int64_t V, int* chunk, int* nC, int* chunk2, int* nC2);
 hipError_t launch_verify(const VerifyArgs& a, bool fp64, hipStream_t stream);
 
+// Repetition penalty over materialised logits: Y = X with the previous
+// tokens' logits penalised (Y may be X).  One workgroup per chunk of a row.
+constexpr int kPenaltyChunk = 8192;
+struct PenaltyArgs {
+  const float* X;          // [B, V]
+  float* Y;                // [B, V]
+  int64_t B, V;
+  const int64_t* prev;     // [B, L]; entries outside [0, V) are padding
+  int64_t L;
+  const float* penalty;    // [B]
+  int vec4;                // X and Y rows 16-byte aligned
+};
+hipError_t launch_repetition_penalty(const PenaltyArgs& a, hipStream_t stream);
+
 // Test hook: the noise transforms applied to given words.
 hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,
                         hipStream_t stream);

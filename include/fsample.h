@@ -239,6 +239,26 @@ fs_status fs_sample_logits_filtered(const float *logits, int64_t B, int64_t V,
                                     size_t workspace_bytes, fs_stream_t stream);
 
 /*
+ * Repetition penalty [SD sample pipeline and Semantics: the penalty comes
+ * before the temperature]: out_logits = logits, except that every token
+ * occurring in row b's previous tokens has its logit y replaced by
+ * y * penalty[b] when y < 0 and by y / penalty[b] otherwise (float32,
+ * correctly rounded; a token occurring several times is penalised once).
+ * Rows whose penalty is not positive (or NaN) are copied unchanged.
+ *   logits       device, float [B, V], 4-byte aligned
+ *   prev_tokens  device, int64 [B, L]; entries outside [0, V) are padding
+ *                (NULL when L = 0)
+ *   penalty      device, float [B]
+ *   out_logits   device, float [B, V]; may be logits itself (in place)
+ *   B, V, L      host: 0 <= B <= 65535, 1 <= V < 2^31, L >= 0
+ * Followed by fs_sample_logits_filtered at the row temperatures, this is the
+ * card's sample pipeline (penalty, temperature, top-k, top-p, min-p, draw).
+ */
+fs_status fs_repetition_penalty(const float *logits, int64_t B, int64_t V,
+                                const int64_t *prev_tokens, int64_t L, const float *penalty,
+                                float *out_logits, fs_stream_t stream);
+
+/*
  * The filter chain's output [SD API table, filter_logits; Semantics]: the
  * masked, temperature-scaled logits of fs_sample_logits_filtered's kept set,
  *   out_logits[b, i] = logits[b, i] * (1 / t)   for the kept tokens,

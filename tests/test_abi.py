@@ -136,6 +136,16 @@ def test_filtered_workspace_bytes():
     assert lib.fs_workspace_bytes_filtered(4, 0) == 0
 
 
+def test_repetition_penalty_rejects_before_launch():
+    lib = fs.load_library()
+    call = lambda B=4, V=100, prev=FAKE, L=3, pen=FAKE, X=FAKE, Y=FAKE: lib.fs_repetition_penalty(
+        P(X), B, V, P(prev), L, P(pen), P(Y), None)
+    assert call(B=-1) == 1 and call(V=0) == 1 and call(L=-1) == 1 and call(B=65536) == 1
+    assert call(X=0) == 1 and call(Y=0) == 1 and call(pen=0) == 1 and call(prev=0) == 1
+    assert call(X=FAKE + 2) == 2 and call(Y=FAKE + 6) == 2
+    assert call(B=0, X=0, Y=0, pen=0, prev=0) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), 1), (dict(V=0), 1), (dict(X=0), 1), (dict(temp=0), 1), (dict(Y=0), 1),
     (dict(X=FAKE + 2), 2), (dict(Y=FAKE + 6), 2),
