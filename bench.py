@@ -467,7 +467,17 @@ def main() -> int:
                     torch, fs, lambda s: fs.filter_logits(X, Tl, out=Y, **kw),
                     max(20, args.steps // 4), 5)
                 fl[key]["filter_logits_kernel_us"] = round(fkms * 1e3, 2)
-                del Y
+                # the card's whole pipeline: repetition penalty over 256 previous
+                # tokens a row, then the filtered draw (two launches)
+                prev = torch.randint(0, vl, (bl, 256), generator=g, device=dev)
+                pen = torch.full((bl,), 1.3, dtype=torch.float32, device=dev)
+                pms, pkms, _ = time_calls(
+                    torch, fs, lambda s: fs.sample(X, Tl, repetition_penalty=pen, prev_tokens=prev,
+                                                   seed=98, offset=s, **kw),
+                    max(20, args.steps // 4), 5)
+                fl[key]["pipeline_with_penalty_us"] = round(pms * 1e3, 2)
+                fl[key]["pipeline_with_penalty_kernels_us"] = round(pkms * 1e3, 2)
+                del Y, prev, pen
             log(f"  {key}: {fl[key]}")
             del X
         result["filtered_sampler"] = fl
