@@ -784,346 +784,346 @@ __global__ __launch_bounds__(kFThreads) void logits_filtered_split_kernel(Filter
   uint64_t* const lst = hdr + kHdrWords;
 
   if constexpr (MODE != kSplitMerge) {
-  // 1. The chunk into LDS; its largest valid logit and count.
-  if (a.vec4) {  // V % 4 == 0 and kChunk % 4 == 0: n % 4 == 0, aligned
-    for (int q = 4 * tid; q < n; q += 4 * kFThreads) {
-      const float4 v = *reinterpret_cast<const float4*>(x + c0 + q);
-      sh.cval[q] = v.x;
-      sh.cval[q + 1] = v.y;
-      sh.cval[q + 2] = v.z;
-      sh.cval[q + 3] = v.w;
+    // 1. The chunk into LDS; its largest valid logit and count.
+    if (a.vec4) {  // V % 4 == 0 and kChunk % 4 == 0: n % 4 == 0, aligned
+      for (int q = 4 * tid; q < n; q += 4 * kFThreads) {
+        const float4 v = *reinterpret_cast<const float4*>(x + c0 + q);
+        sh.cval[q] = v.x;
+        sh.cval[q + 1] = v.y;
+        sh.cval[q + 2] = v.z;
+        sh.cval[q + 3] = v.w;
+      }
+    } else {
+      for (int q = tid; q < n; q += kFThreads) sh.cval[q] = x[c0 + q];
     }
-  } else {
-    for (int q = tid; q < n; q += kFThreads) sh.cval[q] = x[c0 + q];
-  }
-  __syncthreads();
-  float lm = neg_inf<float>();
-  uint32_t nv = 0;
-  for (int q = tid; q < n; q += kFThreads)
-    if (valid_logit(sh.cval[q])) {
-      lm = fmaxf(lm, sh.cval[q]);
-      ++nv;
+    __syncthreads();
+    float lm = neg_inf<float>();
+    uint32_t nv = 0;
+    for (int q = tid; q < n; q += kFThreads)
+      if (valid_logit(sh.cval[q])) {
+        lm = fmaxf(lm, sh.cval[q]);
+        ++nv;
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lm = fmaxf(lm, __shfl_xor(lm, o));
+    nv = wave_sum(nv);
+    if (lane == 0) {
+      sh.red_f[wave] = lm;
+      sh.red_u[wave] = nv;
     }
+    __syncthreads();
+    float Mg = neg_inf<float>();
+    uint32_t nvg = 0;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lm = fmaxf(lm, __shfl_xor(lm, o));
-  nv = wave_sum(nv);
-  if (lane == 0) {
-    sh.red_f[wave] = lm;
-    sh.red_u[wave] = nv;
-  }
-  __syncthreads();
-  float Mg = neg_inf<float>();
-  uint32_t nvg = 0;
-#pragma unroll
-  for (int w = 0; w < kFWaves; ++w) {
-    Mg = fmaxf(Mg, sh.red_f[w]);
-    nvg += sh.red_u[w];
-  }
+    for (int w = 0; w < kFWaves; ++w) {
+      Mg = fmaxf(Mg, sh.red_f[w]);
+      nvg += sh.red_u[w];
+    }
 
-  if (!filtered) {
-    // 2a. The chunk's unfiltered best: groups of 4 in increasing index order
-    // per thread, the unfiltered sampler's scores.
-    T bm = neg_inf<T>();
-    int32_t bi = kNoIndex;
-    for (int q = 4 * tid; q < n; q += 4 * kFThreads) {
-      const int64_t i0 = c0 + q;
-      float y[4];
+    if (!filtered) {
+      // 2a. The chunk's unfiltered best: groups of 4 in increasing index order
+      // per thread, the unfiltered sampler's scores.
+      T bm = neg_inf<T>();
+      int32_t bi = kNoIndex;
+      for (int q = 4 * tid; q < n; q += 4 * kFThreads) {
+        const int64_t i0 = c0 + q;
+        float y[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = q + j < n ? sh.cval[q + j] : neg_inf<float>();
-      T s[4];
-      if (greedy) {
+        for (int j = 0; j < 4; ++j) y[j] = q + j < n ? sh.cval[q + j] : neg_inf<float>();
+        T s[4];
+        if (greedy) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[j] = T(y[j]);
-      } else if constexpr (!FP64) {
-        const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), rid);
-        s[0] = T(y[0] * (float)inv_t) + T(gumbel_f32(w.w0));
-        s[1] = T(y[1] * (float)inv_t) + T(gumbel_f32(w.w1));
-        s[2] = T(y[2] * (float)inv_t) + T(gumbel_f32(w.w2));
-        s[3] = T(y[3] * (float)inv_t) + T(gumbel_f32(w.w3));
-      } else {
-        const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), rid);
-        const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, rid);
-        s[0] = T(y[0]) * inv_t + T(gumbel_f64(w0.w0, w0.w1));
-        s[1] = T(y[1]) * inv_t + T(gumbel_f64(w0.w2, w0.w3));
-        s[2] = T(y[2]) * inv_t + T(gumbel_f64(w1.w0, w1.w1));
-        s[3] = T(y[3]) * inv_t + T(gumbel_f64(w1.w2, w1.w3));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (valid_logit(y[j]) && s[j] > bm) {
-          bm = s[j];
-          bi = (int32_t)(i0 + j);
+          for (int j = 0; j < 4; ++j) s[j] = T(y[j]);
+        } else if constexpr (!FP64) {
+          const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), rid);
+          s[0] = T(y[0] * (float)inv_t) + T(gumbel_f32(w.w0));
+          s[1] = T(y[1] * (float)inv_t) + T(gumbel_f32(w.w1));
+          s[2] = T(y[2] * (float)inv_t) + T(gumbel_f32(w.w2));
+          s[3] = T(y[3] * (float)inv_t) + T(gumbel_f32(w.w3));
+        } else {
+          const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), rid);
+          const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, rid);
+          s[0] = T(y[0]) * inv_t + T(gumbel_f64(w0.w0, w0.w1));
+          s[1] = T(y[1]) * inv_t + T(gumbel_f64(w0.w2, w0.w3));
+          s[2] = T(y[2]) * inv_t + T(gumbel_f64(w1.w0, w1.w1));
+          s[3] = T(y[3]) * inv_t + T(gumbel_f64(w1.w2, w1.w3));
         }
-    }
-    wave_then_block_best(bm, bi, sh.wbest);
-    if (tid == 0) {
-      cand_store_u64(hdr + 3, FP64 ? (uint64_t)__double_as_longlong((double)bm)
-                                   : (uint64_t)__float_as_uint((float)bm));
-      cand_store_u64(hdr + 4, (uint64_t)(uint32_t)bi);
-      cand_store_u64(hdr + 2, 0ull);
-      cand_store_u64(hdr + 1, 0ull);
-    }
-  } else {
-    // 2b. The chunk's z-histogram relative to its own largest logit.
-    if (tid < 256) {
-      sh.hcount[tid] = 0u;
-      sh.hmass[tid] = 0ull;
-    }
-    __syncthreads();
-    for (int q = tid; q < n; q += kFThreads) {
-      const float y = sh.cval[q];
-      if (valid_logit(y)) {
-        const int bin = z_bin(y, Mg, inv_tf);
-        atomicAdd(&sh.hcount[bin], 1u);
-        atomicAdd(&sh.hmass[bin], mass_fixed(mass_of(y, Mg, inv_tf)));
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // The listed bins 0 .. cut: the longest prefix holding at most kListCap
-      // logits (cut = -1 when bin 0 alone holds more), and no further than the
-      // chunk's own bounds: with top-k on, the bin of its k-th largest logit
-      // (the row's top-k lie within the chunks' top-k, and top-p then needs
-      // only those); with min-p on, the bins whose mass relative to the
-      // chunk's largest logit can reach min_p (the row's largest is larger).
-      uint32_t c[4], cs = 0;
-      unsigned long long ws = 0ull;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = sh.hcount[4 * lane + j];
-        cs += c[j];
-        ws += sh.hmass[4 * lane + j];
+        for (int j = 0; j < 4; ++j)
+          if (valid_logit(y[j]) && s[j] > bm) {
+            bm = s[j];
+            bi = (int32_t)(i0 + j);
+          }
       }
-      uint32_t cc = wave_exclusive_scan(cs, lane);
-      int mine = -1, kbin = 256;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        cc += c[j];
-        if (cc <= (uint32_t)kListCap) mine = 4 * lane + j;
-        if (kbin == 256 && use_k && cc >= (uint32_t)top_k) kbin = 4 * lane + j;
+      wave_then_block_best(bm, bi, sh.wbest);
+      if (tid == 0) {
+        cand_store_u64(hdr + 3, FP64 ? (uint64_t)__double_as_longlong((double)bm)
+                                     : (uint64_t)__float_as_uint((float)bm));
+        cand_store_u64(hdr + 4, (uint64_t)(uint32_t)bi);
+        cand_store_u64(hdr + 2, 0ull);
+        cand_store_u64(hdr + 1, 0ull);
       }
-      int cut = mine;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        cut = max(cut, __shfl_xor(cut, o));
-        kbin = min(kbin, __shfl_xor(kbin, o));
+    } else {
+      // 2b. The chunk's z-histogram relative to its own largest logit.
+      if (tid < 256) {
+        sh.hcount[tid] = 0u;
+        sh.hmass[tid] = 0ull;
       }
-      if (use_k && kbin < cut) cut = kbin;
-      if (use_m) {
-        int mbin = 0;
-        if (min_p < 1.0f) {
-          const double zmax = -log((double)min_p) * (1.0 + 1e-5) + 1e-5;
-          mbin = zmax < (double)kZTop ? (int)(zmax * kBinsPerNat) : 255;
+      __syncthreads();
+      for (int q = tid; q < n; q += kFThreads) {
+        const float y = sh.cval[q];
+        if (valid_logit(y)) {
+          const int bin = z_bin(y, Mg, inv_tf);
+          atomicAdd(&sh.hcount[bin], 1u);
+          atomicAdd(&sh.hmass[bin], mass_fixed(mass_of(y, Mg, inv_tf)));
         }
-        if (mbin < cut) cut = mbin;
       }
-      const unsigned long long zg = wave_sum(ws);
-      if (lane == 0) {
-        sh.bin_cut = cut;
-        sh.z_all = zg;
-        sh.n_cand = 0u;
-      }
-    }
-    __syncthreads();
-    const int cut = sh.bin_cut;
-    // 3. The listed logits out; the largest unlisted key gives tau_g.
-    uint32_t unl = 0u;
-    bool any_unl = false;
-    for (int q = tid; q < n; q += kFThreads) {
-      const float y = sh.cval[q];
-      if (!valid_logit(y)) continue;
-      if (z_bin(y, Mg, inv_tf) <= cut) {
-        const uint32_t slot = atomicAdd(&sh.n_cand, 1u);
-        cand_store_u64(lst + slot,
-                       (uint64_t)__float_as_uint(y) | ((uint64_t)(uint32_t)(c0 + q) << 32));
-      } else {
-        const uint32_t k = order_key(y);
-        unl = any_unl ? (unl > k ? unl : k) : k;
-        any_unl = true;
-      }
-    }
-    // tau_g = largest unlisted key + 1 (0 when every valid logit is listed);
-    // keys of valid logits are below 0xff800001, so the sum cannot wrap.
-    uint32_t tg = any_unl ? unl + 1u : 0u;
+      __syncthreads();
+      if (wave == 0) {
+        // The listed bins 0 .. cut: the longest prefix holding at most kListCap
+        // logits (cut = -1 when bin 0 alone holds more), and no further than the
+        // chunk's own bounds: with top-k on, the bin of its k-th largest logit
+        // (the row's top-k lie within the chunks' top-k, and top-p then needs
+        // only those); with min-p on, the bins whose mass relative to the
+        // chunk's largest logit can reach min_p (the row's largest is larger).
+        uint32_t c[4], cs = 0;
+        unsigned long long ws = 0ull;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tg = max(tg, __shfl_xor(tg, o));
-    if (lane == 0) sh.red_u[wave] = tg;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t tau = 0u;
+        for (int j = 0; j < 4; ++j) {
+          c[j] = sh.hcount[4 * lane + j];
+          cs += c[j];
+          ws += sh.hmass[4 * lane + j];
+        }
+        uint32_t cc = wave_exclusive_scan(cs, lane);
+        int mine = -1, kbin = 256;
 #pragma unroll
-      for (int w = 0; w < kFWaves; ++w) tau = tau > sh.red_u[w] ? tau : sh.red_u[w];
-      cand_store_u64(hdr + 1, sh.z_all);
-      cand_store_u64(hdr + 2, (uint64_t)tau | ((uint64_t)sh.n_cand << 32));
+        for (int j = 0; j < 4; ++j) {
+          cc += c[j];
+          if (cc <= (uint32_t)kListCap) mine = 4 * lane + j;
+          if (kbin == 256 && use_k && cc >= (uint32_t)top_k) kbin = 4 * lane + j;
+        }
+        int cut = mine;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          cut = max(cut, __shfl_xor(cut, o));
+          kbin = min(kbin, __shfl_xor(kbin, o));
+        }
+        if (use_k && kbin < cut) cut = kbin;
+        if (use_m) {
+          int mbin = 0;
+          if (min_p < 1.0f) {
+            const double zmax = -log((double)min_p) * (1.0 + 1e-5) + 1e-5;
+            mbin = zmax < (double)kZTop ? (int)(zmax * kBinsPerNat) : 255;
+          }
+          if (mbin < cut) cut = mbin;
+        }
+        const unsigned long long zg = wave_sum(ws);
+        if (lane == 0) {
+          sh.bin_cut = cut;
+          sh.z_all = zg;
+          sh.n_cand = 0u;
+        }
+      }
+      __syncthreads();
+      const int cut = sh.bin_cut;
+      // 3. The listed logits out; the largest unlisted key gives tau_g.
+      uint32_t unl = 0u;
+      bool any_unl = false;
+      for (int q = tid; q < n; q += kFThreads) {
+        const float y = sh.cval[q];
+        if (!valid_logit(y)) continue;
+        if (z_bin(y, Mg, inv_tf) <= cut) {
+          const uint32_t slot = atomicAdd(&sh.n_cand, 1u);
+          cand_store_u64(lst + slot,
+                         (uint64_t)__float_as_uint(y) | ((uint64_t)(uint32_t)(c0 + q) << 32));
+        } else {
+          const uint32_t k = order_key(y);
+          unl = any_unl ? (unl > k ? unl : k) : k;
+          any_unl = true;
+        }
+      }
+      // tau_g = largest unlisted key + 1 (0 when every valid logit is listed);
+      // keys of valid logits are below 0xff800001, so the sum cannot wrap.
+      uint32_t tg = any_unl ? unl + 1u : 0u;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) tg = max(tg, __shfl_xor(tg, o));
+      if (lane == 0) sh.red_u[wave] = tg;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t tau = 0u;
+#pragma unroll
+        for (int w = 0; w < kFWaves; ++w) tau = tau > sh.red_u[w] ? tau : sh.red_u[w];
+        cand_store_u64(hdr + 1, sh.z_all);
+        cand_store_u64(hdr + 2, (uint64_t)tau | ((uint64_t)sh.n_cand << 32));
+      }
     }
-  }
-  if (tid == 0) cand_store_u64(hdr + 0, (uint64_t)__float_as_uint(Mg) | ((uint64_t)nvg << 32));
-  wait_stores_complete();
+    if (tid == 0) cand_store_u64(hdr + 0, (uint64_t)__float_as_uint(Mg) | ((uint64_t)nvg << 32));
+    wait_stores_complete();
   }
 
   // 4. The row's last workgroup merges (or the merge launch's workgroup).
   if constexpr (MODE == kSplitChunks) {
     return;
   } else {
-  if constexpr (MODE == kSplitOne) {
-    if (!finish_last(a.counters + b, (uint32_t)G)) return;
-  }
-  if (tid < G) {
-    const uint64_t* h = a.split + ((b * G + tid) * (kHdrWords + kListCap));
-    const uint64_t h0 = cand_load_u64(h + 0);
-    gM[tid] = __uint_as_float((uint32_t)h0);
-    gN[tid] = (uint32_t)(h0 >> 32);
-    gZ[tid] = cand_load_u64(h + 1);
-    const uint64_t h2 = cand_load_u64(h + 2);
-    gTau[tid] = (uint32_t)h2;
-    gList[tid] = (uint32_t)(h2 >> 32);
-    if (!filtered) {
-      const uint64_t m = cand_load_u64(h + 3);
-      gBest[tid] = Cand<T>{FP64 ? T(__longlong_as_double((long long)m)) : T(__uint_as_float((uint32_t)m)),
-                           (int32_t)(uint32_t)cand_load_u64(h + 4)};
+    if constexpr (MODE == kSplitOne) {
+      if (!finish_last(a.counters + b, (uint32_t)G)) return;
     }
-  }
-  __syncthreads();
-  int64_t out = -1;
-  if (!filtered) {
+    if (tid < G) {
+      const uint64_t* h = a.split + ((b * G + tid) * (kHdrWords + kListCap));
+      const uint64_t h0 = cand_load_u64(h + 0);
+      gM[tid] = __uint_as_float((uint32_t)h0);
+      gN[tid] = (uint32_t)(h0 >> 32);
+      gZ[tid] = cand_load_u64(h + 1);
+      const uint64_t h2 = cand_load_u64(h + 2);
+      gTau[tid] = (uint32_t)h2;
+      gList[tid] = (uint32_t)(h2 >> 32);
+      if (!filtered) {
+        const uint64_t m = cand_load_u64(h + 3);
+        gBest[tid] = Cand<T>{FP64 ? T(__longlong_as_double((long long)m)) : T(__uint_as_float((uint32_t)m)),
+                             (int32_t)(uint32_t)cand_load_u64(h + 4)};
+      }
+    }
+    __syncthreads();
+    int64_t out = -1;
+    if (!filtered) {
+      if (tid == 0) {
+        Cand<T> best = Cand<T>{neg_inf<T>(), kNoIndex};
+        for (int q = 0; q < G; ++q)
+          if (beats(gBest[q].m, gBest[q].idx, best.m, best.idx)) best = gBest[q];
+        a.out[b] = best.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)best.idx;
+        clear_counter(a.counters + b);
+      }
+      return;
+    }
+    float M = neg_inf<float>();
+    uint32_t n_valid = 0u, tau = 0u;
+    for (int q = 0; q < G; ++q) {
+      M = fmaxf(M, gM[q]);
+      n_valid += gN[q];
+      tau = tau > gTau[q] ? tau : gTau[q];
+    }
     if (tid == 0) {
-      Cand<T> best = Cand<T>{neg_inf<T>(), kNoIndex};
-      for (int q = 0; q < G; ++q)
-        if (beats(gBest[q].m, gBest[q].idx, best.m, best.idx)) best = gBest[q];
-      a.out[b] = best.m == neg_inf<T>() ? (int64_t)-1 : (int64_t)best.idx;
+      uint32_t base = 0u;
+      for (int q = 0; q < G; ++q) {
+        gBase[q] = base;
+        base += gList[q];
+      }
+      gBase[G] = base;
+    }
+    __syncthreads();
+    bool covered = n_valid > 0u;
+    if ((int64_t)top_k >= (int64_t)n_valid) use_k = false;
+    if (!(use_k || use_p || use_m)) covered = false;  // nothing filters: the full row is kept
+    // The survivors' total mass without top-k: every chunk's fixed-point mass
+    // rescaled to the row's largest logit (float64; the units stay 2^-40).
+    double z_total = 0.0;
+    for (int q = 0; q < G; ++q) {
+      if (gN[q] == 0u) continue;
+      if (M == __builtin_inff())
+        z_total += gM[q] == M ? (double)gZ[q] : 0.0;
+      else
+        z_total += (double)gZ[q] * exp((double)(gM[q] - M) * (double)inv_tf);
+    }
+    // The union of the lists into LDS: each thread takes union entries
+    // tid, tid + kFThreads, ... (chunk q holds entries gBase[q] .. gBase[q+1]),
+    // so all of its loads are in flight together.
+    const int nu = (int)gBase[G];
+    {
+      constexpr int kPer = kSplitCap / kFThreads;
+      uint64_t v[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * kFThreads;
+        if (e >= nu) break;
+        int q = 0;
+        while (q + 1 < G && (int)gBase[q + 1] <= e) ++q;
+        v[u] = cand_load_u64(a.split + ((b * G + q) * (kHdrWords + kListCap)) + kHdrWords +
+                             (e - (int)gBase[q]));
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * kFThreads;
+        if (e >= nu) break;
+        sh.cval[e] = __uint_as_float((uint32_t)v[u]);
+        sh.cidx[e] = (int32_t)(uint32_t)(v[u] >> 32);
+      }
+    }
+    __syncthreads();
+    auto visit_u = [&](auto&& f) {
+      for (int q = tid; q < nu; q += kFThreads) f(order_key(sh.cval[q]), sh.cval[q]);
+    };
+    uint32_t key_k = 0u, key_p = 0u;
+    if (covered && use_k) {
+      // the union's top top_k are the row's when it holds that many above tau
+      uint32_t ca = 0u;
+      for (int q = tid; q < nu; q += kFThreads) ca += order_key(sh.cval[q]) >= tau ? 1u : 0u;
+      ca = wave_sum(ca);
+      if (lane == 0) sh.red_u[wave] = ca;
+      __syncthreads();
+      uint32_t above = 0u;
+#pragma unroll
+      for (int w = 0; w < kFWaves; ++w) above += sh.red_u[w];
+      __syncthreads();
+      if (above >= (uint32_t)top_k)
+        key_k = kth_largest_key(visit_u, (uint32_t)top_k, sh.hcount, sh.sel, true);
+      else
+        covered = false;
+    }
+    if (covered && use_p) {
+      if (!(top_p > 0.0f)) {
+        key_p = order_key(M);
+      } else {
+        auto visit_s1 = [&](auto&& f) {
+          for (int q = tid; q < nu; q += kFThreads) {
+            const uint32_t key = order_key(sh.cval[q]);
+            if (key >= key_k) f(key, sh.cval[q]);
+          }
+        };
+        key_p = top_p_key(visit_s1, M, inv_tf, top_p, use_k ? 0.0 : z_total, sh.hcount, sh.hmass,
+                          sh.sel, &sh.sel_above, true);
+        if (key_p < tau) covered = false;  // the crossing may lie among unlisted logits
+      }
+    }
+    uint32_t kappa = key_k > key_p ? key_k : key_p;
+    if (use_m && !(min_p < 1.0f)) {
+      const uint32_t km = order_key(M);
+      kappa = kappa > km ? kappa : km;
+      use_m = false;
+    }
+    // Logits below tau are unlisted: the kept set must lie above it.
+    if (covered && kappa < tau && !(use_m && mass_of(key_float(tau - 1u), M, inv_tf) < min_p))
+      covered = false;
+    if (covered) {
+      T bm = neg_inf<T>();
+      int32_t bi = kNoIndex;
+      for (int q = tid; q < nu; q += kFThreads) {
+        const float y = sh.cval[q];
+        if (order_key(y) < kappa || (use_m && !(mass_of(y, M, inv_tf) >= min_p))) continue;
+        const int32_t i = sh.cidx[q];
+        T s;
+        if constexpr (!FP64) {
+          const Words w = noise_words(a.key, (uint32_t)(i >> 2), rid);
+          const uint32_t r = i & 3;
+          const uint32_t word = r == 0 ? w.w0 : (r == 1 ? w.w1 : (r == 2 ? w.w2 : w.w3));
+          s = T(y * (float)inv_t) + T(gumbel_f32(word));
+        } else {
+          const Words w = noise_words(a.key, (uint32_t)(i >> 1), rid);
+          s = (i & 1) ? T(y) * inv_t + T(gumbel_f64(w.w2, w.w3)) : T(y) * inv_t + T(gumbel_f64(w.w0, w.w1));
+        }
+        if (beats(s, i, bm, bi)) {
+          bm = s;
+          bi = i;
+        }
+      }
+      wave_then_block_best(bm, bi, sh.wbest);
+      out = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
+    } else {
+      out = filter_row_single<FP64, kSplitCap>(a, b, sh);
+    }
+    if (tid == 0) {
+      a.out[b] = out;
       clear_counter(a.counters + b);
     }
-    return;
-  }
-  float M = neg_inf<float>();
-  uint32_t n_valid = 0u, tau = 0u;
-  for (int q = 0; q < G; ++q) {
-    M = fmaxf(M, gM[q]);
-    n_valid += gN[q];
-    tau = tau > gTau[q] ? tau : gTau[q];
-  }
-  if (tid == 0) {
-    uint32_t base = 0u;
-    for (int q = 0; q < G; ++q) {
-      gBase[q] = base;
-      base += gList[q];
-    }
-    gBase[G] = base;
-  }
-  __syncthreads();
-  bool covered = n_valid > 0u;
-  if ((int64_t)top_k >= (int64_t)n_valid) use_k = false;
-  if (!(use_k || use_p || use_m)) covered = false;  // nothing filters: the full row is kept
-  // The survivors' total mass without top-k: every chunk's fixed-point mass
-  // rescaled to the row's largest logit (float64; the units stay 2^-40).
-  double z_total = 0.0;
-  for (int q = 0; q < G; ++q) {
-    if (gN[q] == 0u) continue;
-    if (M == __builtin_inff())
-      z_total += gM[q] == M ? (double)gZ[q] : 0.0;
-    else
-      z_total += (double)gZ[q] * exp((double)(gM[q] - M) * (double)inv_tf);
-  }
-  // The union of the lists into LDS: each thread takes union entries
-  // tid, tid + kFThreads, ... (chunk q holds entries gBase[q] .. gBase[q+1]),
-  // so all of its loads are in flight together.
-  const int nu = (int)gBase[G];
-  {
-    constexpr int kPer = kSplitCap / kFThreads;
-    uint64_t v[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kFThreads;
-      if (e >= nu) break;
-      int q = 0;
-      while (q + 1 < G && (int)gBase[q + 1] <= e) ++q;
-      v[u] = cand_load_u64(a.split + ((b * G + q) * (kHdrWords + kListCap)) + kHdrWords +
-                           (e - (int)gBase[q]));
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kFThreads;
-      if (e >= nu) break;
-      sh.cval[e] = __uint_as_float((uint32_t)v[u]);
-      sh.cidx[e] = (int32_t)(uint32_t)(v[u] >> 32);
-    }
-  }
-  __syncthreads();
-  auto visit_u = [&](auto&& f) {
-    for (int q = tid; q < nu; q += kFThreads) f(order_key(sh.cval[q]), sh.cval[q]);
-  };
-  uint32_t key_k = 0u, key_p = 0u;
-  if (covered && use_k) {
-    // the union's top top_k are the row's when it holds that many above tau
-    uint32_t ca = 0u;
-    for (int q = tid; q < nu; q += kFThreads) ca += order_key(sh.cval[q]) >= tau ? 1u : 0u;
-    ca = wave_sum(ca);
-    if (lane == 0) sh.red_u[wave] = ca;
-    __syncthreads();
-    uint32_t above = 0u;
-#pragma unroll
-    for (int w = 0; w < kFWaves; ++w) above += sh.red_u[w];
-    __syncthreads();
-    if (above >= (uint32_t)top_k)
-      key_k = kth_largest_key(visit_u, (uint32_t)top_k, sh.hcount, sh.sel, true);
-    else
-      covered = false;
-  }
-  if (covered && use_p) {
-    if (!(top_p > 0.0f)) {
-      key_p = order_key(M);
-    } else {
-      auto visit_s1 = [&](auto&& f) {
-        for (int q = tid; q < nu; q += kFThreads) {
-          const uint32_t key = order_key(sh.cval[q]);
-          if (key >= key_k) f(key, sh.cval[q]);
-        }
-      };
-      key_p = top_p_key(visit_s1, M, inv_tf, top_p, use_k ? 0.0 : z_total, sh.hcount, sh.hmass,
-                        sh.sel, &sh.sel_above, true);
-      if (key_p < tau) covered = false;  // the crossing may lie among unlisted logits
-    }
-  }
-  uint32_t kappa = key_k > key_p ? key_k : key_p;
-  if (use_m && !(min_p < 1.0f)) {
-    const uint32_t km = order_key(M);
-    kappa = kappa > km ? kappa : km;
-    use_m = false;
-  }
-  // Logits below tau are unlisted: the kept set must lie above it.
-  if (covered && kappa < tau && !(use_m && mass_of(key_float(tau - 1u), M, inv_tf) < min_p))
-    covered = false;
-  if (covered) {
-    T bm = neg_inf<T>();
-    int32_t bi = kNoIndex;
-    for (int q = tid; q < nu; q += kFThreads) {
-      const float y = sh.cval[q];
-      if (order_key(y) < kappa || (use_m && !(mass_of(y, M, inv_tf) >= min_p))) continue;
-      const int32_t i = sh.cidx[q];
-      T s;
-      if constexpr (!FP64) {
-        const Words w = noise_words(a.key, (uint32_t)(i >> 2), rid);
-        const uint32_t r = i & 3;
-        const uint32_t word = r == 0 ? w.w0 : (r == 1 ? w.w1 : (r == 2 ? w.w2 : w.w3));
-        s = T(y * (float)inv_t) + T(gumbel_f32(word));
-      } else {
-        const Words w = noise_words(a.key, (uint32_t)(i >> 1), rid);
-        s = (i & 1) ? T(y) * inv_t + T(gumbel_f64(w.w2, w.w3)) : T(y) * inv_t + T(gumbel_f64(w.w0, w.w1));
-      }
-      if (beats(s, i, bm, bi)) {
-        bm = s;
-        bi = i;
-      }
-    }
-    wave_then_block_best(bm, bi, sh.wbest);
-    out = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
-  } else {
-    out = filter_row_single<FP64, kSplitCap>(a, b, sh);
-  }
-  if (tid == 0) {
-    a.out[b] = out;
-    clear_counter(a.counters + b);
-  }
   }
 }
 
@@ -1154,24 +1154,23 @@ size_t filtered_split_words(int64_t B, int64_t V) {
   return G ? (size_t)B * G * (kHdrWords + kListCap) : 0;
 }
 
+template <int MODE>
+static void launch_split(const FilterArgs& a, bool fp64, dim3 grid, hipStream_t stream) {
+  if (fp64)
+    hipLaunchKernelGGL((logits_filtered_split_kernel<true, MODE>), grid, dim3(kFThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((logits_filtered_split_kernel<false, MODE>), grid, dim3(kFThreads), 0, stream, a);
+}
+
 hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t stream) {
   const int G = a.split ? filtered_split_chunks(a.B, a.V) : 0;
-  if (G && a.B <= kSplitMaxRows) {
-    const dim3 grid((unsigned)G, (unsigned)a.B);
-    if (fp64)
-      hipLaunchKernelGGL((logits_filtered_split_kernel<true, kSplitOne>), grid, dim3(kFThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((logits_filtered_split_kernel<false, kSplitOne>), grid, dim3(kFThreads), 0, stream, a);
-    return hipGetLastError();
-  }
   if (G) {
-    const dim3 grid((unsigned)G, (unsigned)a.B), grid2(1u, (unsigned)a.B);
-    if (fp64) {
-      hipLaunchKernelGGL((logits_filtered_split_kernel<true, kSplitChunks>), grid, dim3(kFThreads), 0, stream, a);
-      hipLaunchKernelGGL((logits_filtered_split_kernel<true, kSplitMerge>), grid2, dim3(kFThreads), 0, stream, a);
+    const dim3 chunks((unsigned)G, (unsigned)a.B), rows(1u, (unsigned)a.B);
+    if (a.B <= kSplitMaxRows) {
+      launch_split<kSplitOne>(a, fp64, chunks, stream);
     } else {
-      hipLaunchKernelGGL((logits_filtered_split_kernel<false, kSplitChunks>), grid, dim3(kFThreads), 0, stream, a);
-      hipLaunchKernelGGL((logits_filtered_split_kernel<false, kSplitMerge>), grid2, dim3(kFThreads), 0, stream, a);
+      launch_split<kSplitChunks>(a, fp64, chunks, stream);
+      launch_split<kSplitMerge>(a, fp64, rows, stream);
     }
     return hipGetLastError();
   }

@@ -1320,24 +1320,24 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     if constexpr (16 * NB > kStage2InKernelRows) {
       return;
     } else {
-    if (!finish_last(a.counters + btile, (uint32_t)nT)) return;
-    static_assert(kWaves * kS2SurvPerWave * sizeof(Cand<T>) <= sizeof(hs),
-                  "the survivors of every wave fit in the H staging buffer");
-    Cand<T>* const surv = reinterpret_cast<Cand<T>*>(&hs[0][0][0]) + wave * kS2SurvPerWave;
-    Cand<T> mxn[kS2TilesPerLane];
-    if (bt0 + wave < B) topk_load_maxima(a, bt0 + wave, lane, mxn);
+      if (!finish_last(a.counters + btile, (uint32_t)nT)) return;
+      static_assert(kWaves * kS2SurvPerWave * sizeof(Cand<T>) <= sizeof(hs),
+                    "the survivors of every wave fit in the H staging buffer");
+      Cand<T>* const surv = reinterpret_cast<Cand<T>*>(&hs[0][0][0]) + wave * kS2SurvPerWave;
+      Cand<T> mxn[kS2TilesPerLane];
+      if (bt0 + wave < B) topk_load_maxima(a, bt0 + wave, lane, mxn);
 #pragma unroll 1
-    for (int i = wave; i < kTile; i += kWaves) {
-      const int64_t b = bt0 + i;
-      if (b >= B) break;
-      Cand<T> mx[kS2TilesPerLane];
+      for (int i = wave; i < kTile; i += kWaves) {
+        const int64_t b = bt0 + i;
+        if (b >= B) break;
+        Cand<T> mx[kS2TilesPerLane];
 #pragma unroll
-      for (int j = 0; j < kS2TilesPerLane; ++j) mx[j] = mxn[j];
-      if (i + kWaves < kTile && b + kWaves < B) topk_load_maxima(a, b + kWaves, lane, mxn);
-      topk_row_places(a, b, lane, mx, surv);
-    }
-    if (tid == 0) clear_counter(a.counters + btile);
-    return;
+        for (int j = 0; j < kS2TilesPerLane; ++j) mx[j] = mxn[j];
+        if (i + kWaves < kTile && b + kWaves < B) topk_load_maxima(a, b + kWaves, lane, mxn);
+        topk_row_places(a, b, lane, mx, surv);
+      }
+      if (tid == 0) clear_counter(a.counters + btile);
+      return;
     }
   }
 
