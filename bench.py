@@ -15,7 +15,7 @@ over the timed steps; p10/p50/p90 of the per-step times beside it);
 duration, read from HIP events the library records around it on the stream it
 runs on, over the same timed region; `standalone_sampler` does the same for
 fs_sample_logits, `filtered_sampler` for fs_sample_logits_filtered (top-k,
-top-p, min-p) beside the eager transformers chain, `verify` for fs_verify
+top-p, min-p) beside the eager transformers chain, `wide_head` the D = 8192, V = 262144 head with float64 noise, `verify` for fs_verify
 (speculative-decoding rejection sampling, K = 4) beside an eager PyTorch
 rejection sampler; `cpu_baseline` is the
 float64 CPU oracle computing the same step on this host's cores.
@@ -557,6 +557,34 @@ def main() -> int:
         }
         log(f"  {result['large_batch']}")
         del WL, HL, biasL
+
+        # The wide head (D = 8192, V = 262144, 4 GiB of bf16 W) with float64 noise,
+        # T = 0.7, B = 1, 16, 128; the unfused GEMM + fp64-noise sampler beside B = 128.
+        log("timing the wide head (D=8192, V=262144, fp64 noise)")
+        gw = torch.Generator(device=dev).manual_seed(9)
+        VW, DW = 262144, 8192
+        WW = (torch.randn(VW, DW, generator=gw, device=dev) * 0.015).to(torch.bfloat16)
+        wide = {"workload": "D=8192, V=262144 bf16 W, T = 0.7, fp64 noise"}
+        for bw in (1, 16, 128):
+            HW = torch.randn(bw, DW, generator=gw, device=dev).to(torch.bfloat16)
+            TW = torch.full((bw,), 0.7, dtype=torch.float32, device=dev)
+            ms, kms, pc = time_calls(
+                torch, fs, lambda s: fs.sample_fused(HW, WW, TW, seed=5, offset=s, fp64_noise=True),
+                max(20, args.steps // 8), 5)
+            lb = kernel_alg_bytes(bw, DW, VW, fused_tiles(VW, cus), cand=16)
+            wide[f"B{bw}"] = {"us_per_call": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
+                              "alg_bytes": lb,
+                              "hbm_frac": round(lb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if bw == 128:
+                def unfused_wide(s):
+                    y = torch.matmul(HW, WW.t())
+                    return fs.sample_logits(y.float(), TW, seed=5, offset=s, fp64_noise=True)
+                wide[f"B{bw}"]["unfused_us"] = round(
+                    time_region(torch, unfused_wide, max(20, args.steps // 8), 5) * 1e3, 2)
+            log(f"  B={bw}: {wide[f'B{bw}']}")
+            del HW
+        result["wide_head"] = wide
+        del WW
 
         # Baselines on the same data: (1) unfused: rocBLAS/hipBLASLt GEMM writes bf16
         # logits to HBM, then the standalone sampler; (2) softmax + multinomial.
