@@ -75,9 +75,14 @@ def measured_traffic():
         return None
 
 
-def fused_tiles(V: int, cus: int) -> int:
-    """Vocabulary tiles of the fused Stage 1 (one workgroup per CU, 8-row units)."""
-    return max(1, min((V + 7) // 8, cus))
+def fused_tiles(V: int, cus: int, row_bytes: int = 0) -> int:
+    """Vocabulary tiles of the fused Stage 1 (one workgroup per CU, 8-row units;
+    four fewer when every workgroup's W range would start on a 16 MiB boundary)."""
+    nunits = (V + 7) // 8
+    g = min(cus, 256)
+    if row_bytes > 0 and g > 8 and (-(-nunits // g) * 8 * row_bytes) % (16 << 20) == 0:
+        g -= 4
+    return max(1, min(nunits, g))
 
 
 def kernel_alg_bytes(B: int, D: int, V: int, n_tiles: int, bias: bool = False, cand: int = 8,
@@ -571,7 +576,8 @@ def main() -> int:
             ms, kms, pc = time_calls(
                 torch, fs, lambda s: fs.sample_fused(HW, WW, TW, seed=5, offset=s, fp64_noise=True),
                 max(20, args.steps // 8), 5)
-            lb = kernel_alg_bytes(bw, DW, VW, fused_tiles(VW, cus), cand=16)
+            lb = kernel_alg_bytes(bw, DW, VW, fused_tiles(VW, cus, 2 * DW if bw <= 64 else 0),
+                                  cand=16)
             wide[f"B{bw}"] = {"us_per_call": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
                               "alg_bytes": lb,
                               "hbm_frac": round(lb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -193,7 +193,8 @@ fs_status sample_fused(const fs_bf16* H, const void* W, int fmt, const void* sca
   int cus = 0;
   s = device_cus(&cus);
   if (s != FS_OK) return s;
-  const int nT = fs::fused_num_tiles(V, cus);
+  // (128-column tiles stream W in passes of 32 rows, which 256 tiles divide evenly)
+  const int nT = fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, fmt) : 0);
   s = check_span(V, D, nT, fmt);
   if (s != FS_OK) return s;
   const bool fp64 = (flags & FS_FP64_NOISE) != 0;
@@ -235,7 +236,8 @@ fs_status debug_logits(const fs_bf16* H, const void* W, int fmt, const void* sca
   int cus = 0;
   s = device_cus(&cus);
   if (s != FS_OK) return s;
-  const int nT = fs::fused_num_tiles(V, cus);
+  // (128-column tiles stream W in passes of 32 rows, which 256 tiles divide evenly)
+  const int nT = fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, fmt) : 0);
   s = check_span(V, D, nT, fmt);
   if (s != FS_OK) return s;
   fs::FusedArgs a;

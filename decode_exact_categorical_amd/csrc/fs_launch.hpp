@@ -45,7 +45,9 @@ enum FusedEpilogue {
 // kMaxFusedTiles / 64 loads per lane).
 constexpr int kMaxFusedTiles = 256;
 static_assert(kMaxFusedTiles % 64 == 0, "whole waves of candidates");
-int fused_num_tiles(int64_t V, int num_cus);
+// row_bytes (bytes of one W row; 0: unknown) lets it avoid splits whose
+// workgroup ranges all start on 16 MiB boundaries.
+int fused_num_tiles(int64_t V, int num_cus, int64_t row_bytes = 0);
 // MFMA column blocks of 16 per batch tile: up to 4 (64 columns) for B <= 64
 // or FP8 / MXFP4 weights, else 8 (tiles of 128 columns).
 int fused_column_blocks(int64_t B, bool fp8_weights, bool fp64_noise);
