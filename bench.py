@@ -77,11 +77,11 @@ def measured_traffic():
 
 def fused_tiles(V: int, cus: int, row_bytes: int = 0) -> int:
     """Vocabulary tiles of the fused Stage 1 (one workgroup per CU, 8-row units;
-    four fewer when every workgroup's W range would start on a 16 MiB boundary)."""
+    one fewer when every workgroup's W range would start on a 16 MiB boundary)."""
     nunits = (V + 7) // 8
     g = min(cus, 256)
     if row_bytes > 0 and g > 8 and (-(-nunits // g) * 8 * row_bytes) % (16 << 20) == 0:
-        g -= 4
+        g -= 1
     return max(1, min(nunits, g))
 
 

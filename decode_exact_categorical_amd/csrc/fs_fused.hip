@@ -1468,12 +1468,12 @@ int fused_num_tiles(int64_t V, int num_cus, int64_t row_bytes) {
   const int64_t nunits = (V + 7) >> 3;
   int64_t g = num_cus < kMaxFusedTiles ? num_cus : kMaxFusedTiles;  // one workgroup per CU
   // Workgroup W ranges that all start on 16 MiB boundaries stream markedly
-  // slower (D = 8192, V = 262144: 980 us with 256 tiles, 810 with 252; the
-  // neighbouring shapes stream at 5.3-6.1 TB/s), so such a split gives up four
-  // CUs to move the range starts off those boundaries.
+  // slower (D = 8192, V = 262144, B = 1: 980 us with 256 tiles, 731 with 255,
+  // 792 with 252; the neighbouring shapes stream at 5.3-6.1 TB/s), so such a
+  // split gives up one CU to move the range starts off those boundaries.
   if (row_bytes > 0 && g > 8) {
     const int64_t stride = (nunits + g - 1) / g * 8 * row_bytes;
-    if (stride % ((int64_t)16 << 20) == 0) g -= 4;
+    if (stride % ((int64_t)16 << 20) == 0) g -= 1;
   }
   if (g > nunits) g = nunits;
   if (g < 1) g = 1;
