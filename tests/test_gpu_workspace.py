@@ -116,3 +116,33 @@ def test_logits_batch_beyond_one_launch(dev):
                                        row_ids=rows.astype(np.uint32))
     check_index_parity(a[rows], ref, gap, f"standalone B={B} sampled rows")
     assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
+
+
+def test_one_workspace_serves_every_entry_point(dev):
+    """The binding keeps one cached workspace per stream for every entry point.
+    Split-row filtered sampling and verification write their chunk data after
+    the counter region, never inside it, so the standalone sampler's per-row
+    counters (here 200 rows: past the first 256 bytes) and the fused sampler's
+    stay zero whatever ran before them."""
+    say("filtered (split rows) -> verify -> standalone B=200 -> fused, one workspace")
+    B, V = 200, 20000
+    X = synthetic.logits(B, V, seed=80)
+    t = synthetic.temperatures(B, seed=81)
+    Xd, td = X.to(dev), t.to(dev)
+    fs.sample_logits_filtered(Xd[:8].contiguous(), td[:8].contiguous(), top_k=50, top_p=0.9,
+                              seed=1, offset=2)          # split rows, one launch
+    fs.sample_logits_filtered(Xd[:40].contiguous(), td[:40].contiguous(), top_p=0.9, seed=1,
+                              offset=2)                  # split rows, two launches
+    tg, dr, tok = synthetic.spec_decode(4, 2, V, seed=82)
+    fs.verify(tg.to(dev), dr.to(dev), tok.to(dev), td[:4].contiguous(), seed=3, offset=4)
+    got = fs.sample_logits(Xd, td, seed=5, offset=6)
+    torch.cuda.synchronize()
+    ref, gap, _ = oracle.sample_logits(X.numpy(), t.numpy(), seed=5, offset=6)
+    check_index_parity(got.cpu().numpy(), ref, gap, "standalone after the other entry points")
+    H = synthetic.hidden(70, 512, seed=83)
+    W = synthetic.weight(3000, 512, std=0.3, seed=84)
+    t2 = synthetic.temperatures(70, seed=85)
+    got = fs.sample_fused(H.to(dev), W.to(dev), t2.to(dev), seed=7, offset=8)
+    torch.cuda.synchronize()
+    ref, gap, _ = oracle.sample_fused(H, W, t2.numpy(), seed=7, offset=8)
+    check_index_parity(got.cpu().numpy(), ref, gap, "fused after the other entry points")
