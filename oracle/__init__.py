@@ -58,6 +58,8 @@ def _load():
         lib.oracle_philox_block.argtypes = [P, u32, u32, P]
         lib.oracle_noise_at.restype = None
         lib.oracle_noise_at.argtypes = [u64, u64, u32, i64, i32, P, P, P]
+        lib.oracle_noise_row.restype = None
+        lib.oracle_noise_row.argtypes = [u64, u64, u32, i64, i32, P]
         lib.oracle_noise_of_uniform.restype = None
         lib.oracle_noise_of_uniform.argtypes = [ctypes.c_double, P, P]
         lib.oracle_noise_grid.restype = None
@@ -171,6 +173,13 @@ def noise_at(seed: int, offset: int, row_id: int, i: int, fp64: bool):
     _load().oracle_noise_at(seed, offset, row_id, i, int(fp64),
                             ctypes.byref(u), ctypes.byref(E), ctypes.byref(g))
     return u.value, E.value, g.value
+
+
+def noise_row(seed: int, offset: int, row_id: int, V: int, fp64: bool) -> np.ndarray:
+    """float64[V]: the Gumbel noise g_i of every vocabulary index of logical row row_id."""
+    g = np.zeros(V, dtype=np.float64)
+    _load().oracle_noise_row(seed, offset, row_id, V, int(fp64), _ptr(g))
+    return g
 
 
 def noise_of_uniform(u: float):

@@ -256,6 +256,15 @@ void oracle_noise_at(uint64_t seed, uint64_t offset, uint32_t r, int64_t i,
     *g = -log(ee);
 }
 
+/* g_i for i = 0 .. V-1 of logical row r: the Gumbel noise of a whole row
+ * [MG change; FS (3)]. */
+void oracle_noise_row(uint64_t seed, uint64_t offset, uint32_t r, int64_t V, int fp64,
+                      double *g)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < V; ++i) g[i] = gumbel_of(uniform_for(seed, offset, r, i, fp64));
+}
+
 /* Noise transforms of a given uniform (for the decimal-arithmetic pin). */
 void oracle_noise_of_uniform(double u, double *E, double *g)
 {
@@ -896,15 +905,12 @@ void oracle_filtered_repeated_row(const float *logits, int64_t V, float temp,
  * NaN nor -inf): e_j = exp((y_j - M)/t) with M the largest valid logit, or,
  * when M = +inf, e_j = 1 on the +inf logits and 0 elsewhere (the limit of
  * softmax); p_j = e_j / sum e.  Greedy rows: one-hot on the first largest
- * valid logit.  No valid logit: p = 0.  z[j] receives (y_j - M)/t on rows
- * whose probabilities go through exp (0 otherwise), for the error bounds
- * below. */
-static void row_probs(const float *y, int64_t V, double t, double *p, double *z)
+ * valid logit.  No valid logit: p = 0. */
+static void row_probs(const float *y, int64_t V, double t, double *p)
 {
     int64_t am = -1;
     for (int64_t j = 0; j < V; ++j) {
         p[j] = 0.0;
-        z[j] = 0.0;
         if (isnan(y[j]) || y[j] == -INFINITY) continue;
         if (am < 0 || y[j] > y[am]) am = j;
     }
@@ -917,12 +923,10 @@ static void row_probs(const float *y, int64_t V, double t, double *p, double *z)
     double Z = 0.0;
     for (int64_t j = 0; j < V; ++j) {
         if (isnan(y[j]) || y[j] == -INFINITY) continue;
-        if (M == INFINITY) {
+        if (M == INFINITY)
             p[j] = (y[j] == INFINITY) ? 1.0 : 0.0;
-        } else {
-            z[j] = ((double)y[j] - M) / t;
-            p[j] = exp(z[j]);
-        }
+        else
+            p[j] = exp(((double)y[j] - M) / t);
         Z += p[j];
     }
     for (int64_t j = 0; j < V; ++j) p[j] /= Z;
@@ -942,13 +946,8 @@ double oracle_accept_uniform(uint64_t seed, uint64_t pos, uint32_t r)
     return accept_uniform(seed, pos, r);
 }
 
-/* Relative error allowed to another implementation's probability of token j
- * when it computes p in float32 (rounding of (y - M) * (1/t), of the exp and
- * of the normaliser): it grows with |z|.  Used only for the margins. */
-static double prob_tol(double z) { return 4e-7 * (4.0 + fabs(z)); }
-
 typedef struct {
-    double *pt, *pd, *zt, *zd, *s, *g;
+    double *pt, *pd, *s;
 } verify_buf_t;
 
 static int verify_buf_alloc(verify_buf_t *w, int64_t V)
@@ -956,21 +955,15 @@ static int verify_buf_alloc(verify_buf_t *w, int64_t V)
     size_t n = (size_t)(V > 0 ? V : 1) * sizeof(double);
     w->pt = (double *)malloc(n);
     w->pd = (double *)malloc(n);
-    w->zt = (double *)malloc(n);
-    w->zd = (double *)malloc(n);
     w->s = (double *)malloc(n);
-    w->g = (double *)malloc(n);
-    return w->pt && w->pd && w->zt && w->zd && w->s && w->g;
+    return w->pt && w->pd && w->s;
 }
 
 static void verify_buf_free(verify_buf_t *w)
 {
     free(w->pt);
     free(w->pd);
-    free(w->zt);
-    free(w->zd);
     free(w->s);
-    free(w->g);
 }
 
 /* One row of the verification (see the block comment above).  tg: K+1 rows
@@ -980,12 +973,9 @@ static void verify_buf_free(verify_buf_t *w)
  *   *margin: the smallest relative distance |u q - a| / max(a, q) of an
  *     acceptance decision from its boundary over the decided positions
  *     (0 when a and q are both below 1e-30, where float32 underflow decides);
- *   *gap: the margin of the draw at accept_len: the plain top-2 gap of the
- *     perturbed scores for the bonus and fallback draws (+inf on greedy
- *     rows); for the residual draw, the winner's score lowered by its error
- *     bound minus the best other score raised by its own, where token j's
- *     residual may move by prob_tol * (p_t + p_d) (so rows whose draw rests
- *     on a residual of rounding size get a negative gap). */
+ *   *gap: the top-2 gap of the perturbed scores of the draw at accept_len
+ *     (the bonus or fallback draw's scores, or the residual draw's
+ *     log r_j + g_j); +inf on greedy rows. */
 static void verify_row(const float *tg, const float *dr, const int64_t *tok, int64_t K,
                        int64_t V, double t, uint64_t seed, uint64_t offset, uint32_t r,
                        int fp64, verify_buf_t *w, int64_t *accept_len, int64_t *out,
@@ -994,8 +984,8 @@ static void verify_row(const float *tg, const float *dr, const int64_t *tok, int
     *margin = INFINITY;
     int64_t L = K;
     for (int64_t i = 0; i < K; ++i) {
-        row_probs(tg + i * V, V, t, w->pt, w->zt);
-        row_probs(dr + i * V, V, t, w->pd, w->zd);
+        row_probs(tg + i * V, V, t, w->pt);
+        row_probs(dr + i * V, V, t, w->pd);
         const int64_t x = tok[i];
         double a = 0.0, q = 0.0;
         if (x >= 0 && x < V) {
@@ -1039,29 +1029,10 @@ static void verify_row(const float *tg, const float *dr, const int64_t *tok, int
         return;
     }
     for (int64_t j = 0; j < V; ++j) {
-        w->g[j] = gumbel_of(uniform_for(seed, pos, r, j, fp64));
         double rr = w->s[j];
-        w->s[j] = rr > 0.0 ? log(rr) + w->g[j] : -INFINITY;
+        w->s[j] = rr > 0.0 ? log(rr) + gumbel_of(uniform_for(seed, pos, r, j, fp64)) : -INFINITY;
     }
-    double plain;
-    int64_t win;
-    select_row(w->s, V, &win, &plain, &best);
-    out[L] = win;
-    double lo = -INFINITY, hi_other = -INFINITY;
-    for (int64_t j = 0; j < V; ++j) {
-        double mass = w->pt[j] + w->pd[j];
-        if (!(mass > 0.0)) continue;
-        double rr = w->pt[j] - w->pd[j];
-        if (rr < 0.0) rr = 0.0;
-        double tol = fmax(prob_tol(w->zt[j]), prob_tol(w->zd[j])) * mass;
-        if (j == win) {
-            if (rr - tol > 0.0) lo = log(rr - tol) + w->g[j];
-        } else if (rr + tol > 0.0) {
-            double ub = log(rr + tol) + w->g[j];
-            if (ub > hi_other) hi_other = ub;
-        }
-    }
-    *gap = (hi_other == -INFINITY) ? INFINITY : lo - hi_other;
+    select_row(w->s, V, &out[L], gap, &best);
 }
 
 /* Verification of B rows: target[B, K+1, V], draft[B, K, V], tokens[B, K],

@@ -5,7 +5,10 @@ oracle, through the C ABI.
   acceptance decisions are at least 1e-4 (relative) from their boundaries;
   the token at the first rejection (or the bonus token) equals the oracle's
   where its draw's margin exceeds 1e-3; every row has the emitted-prefix
-  structure.  Shapes: several chunks per row and a ragged tail, V % 4 != 0
+  structure, and a floor on the number of compared draws keeps the token
+  check from passing vacuously.  The draw's margin is the oracle's plain
+  top-2 gap, except for residual draws, whose set-aside margin this file
+  derives (draw_margin below) from the kernel's float32 probabilities.  Shapes: several chunks per row and a ragged tail, V % 4 != 0
   (scalar loads), K from 0 to 32, close and mismatched drafts, greedy rows,
   float32 and float64 noise.
 * Reductions to the standalone sampler, bit for bit: identical target and
@@ -37,6 +40,73 @@ pytestmark = pytest.mark.gpu
 DECISION_MARGIN = 1e-4
 
 
+def prob_tol(z):
+    """Relative error bound of the kernel's float32 probability of a token whose
+    scaled logit is z = (y - M) / t: three roundings in the exponent's argument
+    ((y - M), the product with 1/t) grow with |z|, plus an ulp or two of exp2
+    and of the normaliser's sum; 4e-7 (4 + |z|) covers them."""
+    return 4e-7 * (4.0 + np.abs(z))
+
+
+def _probs(y, t):
+    """(z, p) of one row's temperature softmax over its valid logits, float64
+    (the verification semantics: a +inf maximum shares the mass among the +inf
+    logits; z is 0 where p does not go through exp)."""
+    y = np.asarray(y, dtype=np.float64)
+    valid = ~np.isnan(y) & (y != -np.inf)
+    z = np.zeros_like(y)
+    p = np.zeros_like(y)
+    if not valid.any():
+        return z, p
+    M = y[valid].max()
+    if M == np.inf:
+        p[valid & (y == np.inf)] = 1.0
+    else:
+        z[valid] = (y[valid] - M) / t
+        p[valid] = np.exp(z[valid])
+    return z, p / p.sum()
+
+
+def draw_margin(target, draft, temp, ref, *, seed, offset, row_ids=None, fp64=False):
+    """Per row, the margin of the draw at the oracle's accept_len.  Bonus,
+    fallback and greedy draws: the oracle's plain top-2 gap.  Residual draws
+    (a sampled rejection with a nonzero residual): the kernel forms each
+    probability in float32, so its residual r_j = max(p_t - p_d, 0) may move by
+    prob_tol(z) (p_t + p_d); the margin is the winner's score log r_j + g_j with
+    its residual lowered by that bound, minus the best other score with its
+    residual raised by its own (negative when the draw rests on a residual of
+    rounding size)."""
+    r_acc, r_out, _, gap = ref
+    target = np.asarray(target, dtype=np.float32)
+    draft = np.asarray(draft, dtype=np.float32)
+    temp = np.asarray(temp, dtype=np.float64)
+    B, K1, V = target.shape
+    K = K1 - 1
+    gap = gap.copy()
+    for b in range(B):
+        L, t = int(r_acc[b]), float(temp[b])
+        if L == K or not (t > 0.0):
+            continue
+        zt, pt = _probs(target[b, L], t)
+        zd, pd = _probs(draft[b, L], t)
+        rr = np.maximum(pt - pd, 0.0)
+        if not (rr > 0.0).any():
+            continue                        # the fallback draw: its plain gap stands
+        rid = b if row_ids is None else int(row_ids[b])
+        g = oracle.noise_row(seed, offset + L, rid, V, fp64)
+        mass = pt + pd
+        tol = np.maximum(prob_tol(zt), prob_tol(zd)) * mass
+        win = int(r_out[b, L])
+        lo = np.log(rr[win] - tol[win]) + g[win] if rr[win] - tol[win] > 0.0 else -np.inf
+        other = mass > 0.0
+        other[win] = False
+        up = rr + tol
+        other &= up > 0.0
+        hi = (np.log(up[other]) + g[other]).max() if other.any() else -np.inf
+        gap[b] = np.inf if hi == -np.inf else lo - hi
+    return gap
+
+
 @pytest.fixture(scope="module")
 def dev():
     return need_gpu()
@@ -50,9 +120,10 @@ def _run(dev, target, draft, tokens, temp, *, seed, offset, row_ids=None, fp64=F
     return acc.cpu().numpy(), out.cpu().numpy()
 
 
-def _check(acc, out, tokens, ref, what, min_decided=0.75):
-    """The parity rule; returns (rows compared, tokens compared)."""
-    r_acc, r_out, margin, gap = ref
+def _check(acc, out, tokens, ref, what, gap, min_decided=0.75, min_drawn=0.9):
+    """The parity rule, with `gap` the draws' margins (draw_margin); returns
+    (rows compared, tokens compared)."""
+    r_acc, r_out, margin, _ = ref
     tokens = np.asarray(tokens)
     B, K1 = out.shape
     K = K1 - 1
@@ -73,6 +144,7 @@ def _check(acc, out, tokens, ref, what, min_decided=0.75):
     assert bad.size == 0, (f"{what}: emitted tokens differ on rows {bad[:5]}: got "
                            f"{out[bad[:5], acc[bad[:5]]]} oracle {r_out[bad[:5], r_acc[bad[:5]]]} "
                            f"gap {gap[bad[:5]]}")
+    assert rows.size >= min_drawn * B, (f"{what}: only {rows.size} of {B} drawn tokens compared")
     return decided.sum(), rows.size
 
 
@@ -104,7 +176,9 @@ def test_verify_parity(dev, case, fp64):
                     fp64=fp64)
     ref = oracle.verify(target.numpy(), draft.numpy(), tokens.numpy(), temp.numpy(), seed=4321,
                         offset=1000, row_ids=rid, fp64_noise=fp64)
-    n_rows, n_tok = _check(acc, out, tokens.numpy(), ref, f"B={B} K={K} V={V}")
+    gap = draw_margin(target.numpy(), draft.numpy(), temp.numpy(), ref, seed=4321, offset=1000,
+                      row_ids=rid, fp64=fp64)
+    n_rows, n_tok = _check(acc, out, tokens.numpy(), ref, f"B={B} K={K} V={V}", gap)
     say(f"  compared {n_rows} rows, {n_tok} drawn tokens; mean accept {acc.mean():.2f}")
 
 
@@ -153,12 +227,13 @@ def test_edge_rows(dev):
     acc, out = _run(dev, target, draft, tokens, temp, seed=9, offset=3)
     ref = oracle.verify(target.numpy(), draft.numpy(), tokens.numpy(), temp.numpy(), seed=9,
                         offset=3)
+    gap = draw_margin(target.numpy(), draft.numpy(), temp.numpy(), ref, seed=9, offset=3)
     assert (acc[:6] == 0).all() and (ref[0][:6] == 0).all()
     assert out[4, 0] == -1 and ref[1][4, 0] == -1
     assert out[5, 0] in (17, 900)
     for b in (0, 1, 2, 3):
         assert out[b, 0] != tokens[b, 0]
-    _check(acc, out, tokens.numpy(), ref, "edge rows", min_decided=0.5)
+    _check(acc, out, tokens.numpy(), ref, "edge rows", gap, min_decided=0.5, min_drawn=0.5)
     # V = 1 and K = 0
     t1 = torch.zeros((3, 3, 1))
     d1 = torch.zeros((3, 2, 1))
@@ -233,5 +308,6 @@ def test_verify_qwen_vocabulary(dev, B):
     say("  oracle")
     ref = oracle.verify(target.numpy(), draft.numpy(), tokens.numpy(), temp.numpy(), seed=1234,
                         offset=17)
-    n_rows, n_tok = _check(acc, out, tokens.numpy(), ref, f"qwen B={B}", min_decided=0.7)
+    gap = draw_margin(target.numpy(), draft.numpy(), temp.numpy(), ref, seed=1234, offset=17)
+    n_rows, n_tok = _check(acc, out, tokens.numpy(), ref, f"qwen B={B}", gap, min_decided=0.7)
     say(f"  compared {n_rows} rows, {n_tok} drawn tokens; mean accept {acc.mean():.2f}")

@@ -88,3 +88,13 @@ def test_offset_and_row_change_the_stream():
     d = [oracle.noise_at(2, 0, 0, i, False)[0] for i in range(64)]
     assert a != b and a != c and a != d
     assert a == [oracle.noise_at(1, 0, 0, i, False)[0] for i in range(64)]
+
+
+@pytest.mark.parametrize("fp64", [False, True])
+def test_noise_row_is_the_per_index_noise(fp64):
+    # the whole-row export (used to price residual draws in the verification
+    # tests) is the per-index noise of the same row, index by index
+    V = 1031
+    g = oracle.noise_row(77, 12, 5, V, fp64)
+    ref = np.array([oracle.noise_at(77, 12, 5, i, fp64)[2] for i in range(V)])
+    assert np.array_equal(g, ref)
