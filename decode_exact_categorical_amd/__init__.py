@@ -19,11 +19,14 @@ import threading
 import torch
 
 __all__ = [
-    "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused", "sample_fused_w8",
+    "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused",
+    "sample_fused_w8",
     "sample_fused_topk", "sample_fused_mxfp4", "sample_logits", "sample_logits_topk",
     "sample_logits_filtered", "workspace_bytes", "debug_logits_mxfp4", "debug_philox_words",
     "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
     "KernelTimer",
+    "fused_tiles",
+    "debug_stream_read",
 ]
 
 FS_FP64_NOISE = 0x1
@@ -76,6 +79,12 @@ def load_library():
         lib.fs_profile_begin.argtypes = []
         lib.fs_profile_end.restype = i32
         lib.fs_profile_end.argtypes = [P, P]
+        lib.fs_profile_end_detail.restype = i32
+        lib.fs_profile_end_detail.argtypes = [P, P, P, P, i64]
+        lib.fs_fused_tiles.restype = i32
+        lib.fs_fused_tiles.argtypes = [i64, i64, i64, i32]
+        lib.fs_debug_stream_read.restype = i32
+        lib.fs_debug_stream_read.argtypes = [P, sz, P, P]
         lib.fs_debug_noise.restype = i32
         lib.fs_debug_noise.argtypes = [P, i64, i32, P, P, P]
         lib.fs_debug_logits.restype = i32
@@ -516,19 +525,63 @@ def sample_logits_topk(logits: torch.Tensor, temp, *, k: int, seed: int, offset:
 class KernelTimer:
     """Context manager: summed kernel milliseconds of the sampling calls made inside
     it (one launch per call), from HIP events the library records on each call's
-    stream."""
+    stream.  With per_call=True it also keeps each call's kernel milliseconds
+    (`launch_ms`) and the milliseconds from each call's start to the next one's
+    (`start_to_start_ms`, one fewer)."""
+
+    _CAP = 4096
+
+    def __init__(self, per_call: bool = False):
+        self.per_call = per_call
 
     def __enter__(self):
         _check(load_library().fs_profile_begin(), "fs_profile_begin")
         self.kernel_ms = 0.0
         self.calls = 0
+        self.launch_ms = []
+        self.start_to_start_ms = []
         return self
 
     def __exit__(self, *exc):
         a, n = ctypes.c_double(), ctypes.c_int64()
-        _check(load_library().fs_profile_end(ctypes.byref(a), ctypes.byref(n)), "fs_profile_end")
+        if not self.per_call:
+            _check(load_library().fs_profile_end(ctypes.byref(a), ctypes.byref(n)),
+                   "fs_profile_end")
+            self.kernel_ms, self.calls = a.value, n.value
+            return False
+        lm = (ctypes.c_float * self._CAP)()
+        ss = (ctypes.c_float * self._CAP)()
+        _check(load_library().fs_profile_end_detail(ctypes.byref(a), ctypes.byref(n), lm, ss,
+                                                    self._CAP), "fs_profile_end_detail")
         self.kernel_ms, self.calls = a.value, n.value
+        k = min(self.calls, self._CAP)
+        self.launch_ms = list(lm[:k])
+        self.start_to_start_ms = list(ss[:max(0, k - 1)])
         return False
+
+
+def fused_tiles(B: int, D: int, V: int, weight_format: str = "bf16") -> int:
+    """Vocabulary tiles the fused calls use for (B, D, V) on the current device."""
+    fmt = {"bf16": 0, "fp8": 1, "mxfp4": 2}[weight_format]
+    n = int(load_library().fs_fused_tiles(B, D, V, fmt))
+    if n < 0:
+        raise ValueError(f"fs_fused_tiles: {load_library().fs_last_error().decode()}")
+    return n
+
+
+def debug_stream_read(buf: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One plain streaming read of a contiguous device tensor (a multiple of 16
+    bytes), xor-folded into out (int64 [1] on the same device)."""
+    lib = load_library()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.zeros((1,), dtype=torch.int64, device=buf.device)
+    _need(out, "out", torch.int64, buf.device, (1,))
+    _check(lib.fs_debug_stream_read(_ptr(buf), nbytes, _ptr(out), _stream(buf.device)),
+           "fs_debug_stream_read")
+    return out
 
 
 def debug_philox_words(seed: int, offset: int, B: int, n_ctr: int, *,

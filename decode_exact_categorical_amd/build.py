@@ -31,18 +31,40 @@ def sources():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libfsample.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + sources()
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    """Compile every HIP source into libfsample.so (always recompiles): one hipcc
+    process per source, run side by side, then one link."""
     # the host pass does not know the fp32 feature name and says so; that is harmless
     noise = "packed-fp32-ops' is not a recognized feature"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    tag = "%d" % os.getpid()
+    objs, procs = [], []
+    for src in sources():
+        obj = os.path.join(CSRC, os.path.basename(src) + ".o" + tag)
+        cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                                                 src, "-o", obj]
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
+        objs.append(obj)
+    msgs, failed = [], []
+    for src, p in procs:
+        out, _ = p.communicate()
+        msgs += [ln for ln in out.splitlines() if noise not in ln]
+        if p.returncode != 0:
+            failed.append(os.path.basename(src))
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed on " + ", ".join(failed) + ":\n" + "\n".join(msgs))
+        tmp = LIB + ".tmp" + tag
+        res = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs,
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + res.stdout + res.stderr)
+        if verbose and msgs:
+            print("\n".join(msgs))
+        os.replace(tmp, LIB)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return LIB
 
 

@@ -12,6 +12,13 @@
 #include "fs_launch.hpp"
 #include "fsample.h"
 
+namespace fs {
+LaunchTiming& launch_timing() {
+  static thread_local LaunchTiming t;
+  return t;
+}
+}  // namespace fs
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -58,6 +65,25 @@ hipEvent_t* prof_slot() {
   ++g_prof.used;
   return slot;
 }
+
+// A timed call: the call's events go to its launches through launch_timing()
+// (fs_launch.hpp).  If the call launched nothing, the events are recorded on
+// the stream at the end, so that every timed call has both.
+struct ProfScope {
+  hipEvent_t* ev;
+  hipStream_t st;
+  explicit ProfScope(hipStream_t stream) : ev(prof_slot()), st(stream) {
+    if (ev) fs::launch_timing() = fs::LaunchTiming{ev[0], ev[1]};
+  }
+  ~ProfScope() {
+    if (!ev) return;
+    if (fs::launch_timing().start != nullptr) {
+      (void)hipEventRecord(ev[0], st);
+      (void)hipEventRecord(ev[1], st);
+    }
+    fs::launch_timing() = fs::LaunchTiming{};
+  }
+};
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -172,6 +198,12 @@ void set_weights(fs::FusedArgs& a, const void* W, int fmt, const void* scale) {
   a.w4_scale = fmt == kFmtMxfp4 ? static_cast<const uint8_t*>(scale) : nullptr;
 }
 
+fs_status launch_sampling(const fs_bf16* H, const void* W, int fmt, const void* scale, int64_t B,
+                          int64_t D, int64_t V, const float* temp, const float* bias,
+                          uint64_t seed, uint64_t offset, int64_t* out_idx,
+                          const uint32_t* row_ids, uint32_t flags, void* cand,
+                          uint32_t* counters, int nT, fs_stream_t stream, int k);
+
 // k = 0: one draw per row; 1 <= k <= kTopKMax: Gumbel-top-k (bf16 weights).
 fs_status sample_fused(const fs_bf16* H, const void* W, int fmt, const void* scale, int64_t B,
                        int64_t D, int64_t V, const float* temp, const float* bias, uint64_t seed,
@@ -197,6 +229,18 @@ fs_status sample_fused(const fs_bf16* H, const void* W, int fmt, const void* sca
   const int nT = fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, fmt) : 0);
   s = check_span(V, D, nT, fmt);
   if (s != FS_OK) return s;
+  return launch_sampling(H, W, fmt, scale, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
+                         flags, candidates_of(workspace), counters_of(workspace), nT, stream, k);
+}
+
+// The launch of a fused sampling call whose arguments have been checked: the
+// per-tile candidates go to `cand`, the batch tiles' completion counters
+// (zero on entry, left zero) are `counters`.
+fs_status launch_sampling(const fs_bf16* H, const void* W, int fmt, const void* scale, int64_t B,
+                          int64_t D, int64_t V, const float* temp, const float* bias,
+                          uint64_t seed, uint64_t offset, int64_t* out_idx,
+                          const uint32_t* row_ids, uint32_t flags, void* cand,
+                          uint32_t* counters, int nT, fs_stream_t stream, int k) {
   const bool fp64 = (flags & FS_FP64_NOISE) != 0;
   fs::FusedArgs a;
   memset(&a, 0, sizeof a);
@@ -209,9 +253,9 @@ fs_status sample_fused(const fs_bf16* H, const void* W, int fmt, const void* sca
   a.bias = bias;
   a.row_ids = row_ids;
   a.key = fs::make_key(seed, offset);
-  a.cand = candidates_of(workspace);
+  a.cand = cand;
   a.nT = nT;
-  a.counters = counters_of(workspace);  // ceil(B / 64) <= 65536 words (B <= 2^22)
+  a.counters = counters;  // ceil(B / 16) words at most
   a.out = out_idx;
   a.Y = nullptr;
   a.bias_vec4 = bias != nullptr && aligned16(bias) && (V % 4 == 0);
@@ -219,11 +263,9 @@ fs_status sample_fused(const fs_bf16* H, const void* W, int fmt, const void* sca
   const int epi = k > 0 ? (fp64 ? fs::kEpiTopK64 : fs::kEpiTopK32)
                         : (fp64 ? fs::kEpiSample64 : fs::kEpiSample32);
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = prof_slot();
-  if (ev) (void)hipEventRecord(ev[0], st);
+  ProfScope prof(st);
   hipError_t e = fs::launch_fused_stage1(a, epi, st);
   if (e != hipSuccess) return hip_fail(e, "fused sampling launch");
-  if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }
 
@@ -342,8 +384,7 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
   // One launch per run of at most kCounterWords rows (one counter per row);
   // the launches follow each other on the stream and reuse the workspace.
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = prof_slot();
-  if (ev) (void)hipEventRecord(ev[0], st);
+  ProfScope prof(st);
   for (int64_t b0 = 0; b0 < B; b0 += kCounterWords) {
     const int64_t nb = B - b0 < kCounterWords ? B - b0 : kCounterWords;
     fs::LogitsArgs a;
@@ -364,7 +405,6 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
     hipError_t e = fs::launch_logits_stage1(a, fp64_noise != 0, st);
     if (e != hipSuccess) return hip_fail(e, "logits sampling launch");
   }
-  if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }
 
@@ -397,8 +437,7 @@ fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, c
   }
 
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = prof_slot();
-  if (ev) (void)hipEventRecord(ev[0], st);
+  ProfScope prof(st);
   fs::FilterArgs a;
   a.X = logits;
   a.B = B;
@@ -417,7 +456,6 @@ fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, c
   a.Y = nullptr;
   hipError_t e = fs::launch_logits_filtered(a, fp64_noise != 0, st);
   if (e != hipSuccess) return hip_fail(e, "filtered sampling launch");
-  if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }
 
@@ -445,11 +483,9 @@ fs_status fs_repetition_penalty(const float* logits, int64_t B, int64_t V,
   a.penalty = penalty;
   a.vec4 = aligned16(logits) && aligned16(out_logits) && (V % 4 == 0);
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = prof_slot();
-  if (ev) (void)hipEventRecord(ev[0], st);
+  ProfScope prof(st);
   hipError_t e = fs::launch_repetition_penalty(a, st);
   if (e != hipSuccess) return hip_fail(e, "repetition penalty launch");
-  if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }
 
@@ -481,11 +517,9 @@ fs_status fs_filter_logits(const float* logits, int64_t B, int64_t V, const floa
   a.split = nullptr;
   a.Y = out_logits;
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = prof_slot();
-  if (ev) (void)hipEventRecord(ev[0], st);
+  ProfScope prof(st);
   hipError_t e = fs::launch_filter_logits(a, st);
   if (e != hipSuccess) return hip_fail(e, "filter_logits launch");
-  if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }
 
@@ -546,11 +580,9 @@ fs_status fs_verify(const float* target, const float* draft, const int64_t* toke
   a.vec4 = aligned16(target) && (K == 0 || aligned16(draft)) && (V % 4 == 0);
 
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = prof_slot();
-  if (ev) (void)hipEventRecord(ev[0], st);
+  ProfScope prof(st);
   hipError_t e = fs::launch_verify(a, fp64_noise != 0, st);
   if (e != hipSuccess) return hip_fail(e, "verify launch");
-  if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }
 
@@ -576,8 +608,7 @@ fs_status fs_sample_logits_topk(const float* logits, int64_t B, int64_t V, const
   if (s != FS_OK) return s;
 
   hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = prof_slot();
-  if (ev) (void)hipEventRecord(ev[0], st);
+  ProfScope prof(st);
   for (int64_t b0 = 0; b0 < B; b0 += kCounterWords) {
     const int64_t nb = B - b0 < kCounterWords ? B - b0 : kCounterWords;
     fs::LogitsArgs a;
@@ -598,7 +629,6 @@ fs_status fs_sample_logits_topk(const float* logits, int64_t B, int64_t V, const
     hipError_t e = fs::launch_logits_topk(a, fp64_noise != 0, st);
     if (e != hipSuccess) return hip_fail(e, "logits top-k launch");
   }
-  if (ev) (void)hipEventRecord(ev[1], st);
   return FS_OK;
 }
 
@@ -610,27 +640,65 @@ fs_status fs_profile_begin(void) {
   return FS_OK;
 }
 
-fs_status fs_profile_end(double* kernel_ms, int64_t* calls) {
+fs_status fs_profile_end_detail(double* kernel_ms, int64_t* calls, float* launch_ms,
+                                float* start_to_start_ms, int64_t cap) {
   g_last_error[0] = 0;
   std::lock_guard<std::mutex> lock(g_prof.mu);
   double total = 0.0;
   fs_status status = FS_OK;
   for (size_t c = 0; c < g_prof.used; ++c) {
     hipEvent_t* ev = &g_prof.pool[2 * c];
-    float ms = 0.f;
+    float ms = 0.f, gap = 0.f;
     hipError_t e = hipEventSynchronize(ev[1]);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+    if (e == hipSuccess && start_to_start_ms && (int64_t)c + 1 < cap && c + 1 < g_prof.used) {
+      e = hipEventSynchronize(ev[3]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&gap, ev[0], ev[2]);
+    }
     if (e != hipSuccess) {
       status = hip_fail(e, "profile events");
       break;
     }
     total += ms;
+    if (launch_ms && (int64_t)c < cap) launch_ms[c] = ms;
+    if (start_to_start_ms && (int64_t)c + 1 < cap && c + 1 < g_prof.used) start_to_start_ms[c] = gap;
   }
   if (kernel_ms) *kernel_ms = total;
   if (calls) *calls = (int64_t)g_prof.used;
   g_prof.on = false;
   g_prof.used = 0;
   return status;
+}
+
+fs_status fs_profile_end(double* kernel_ms, int64_t* calls) {
+  return fs_profile_end_detail(kernel_ms, calls, nullptr, nullptr, 0);
+}
+
+int fs_fused_tiles(int64_t B, int64_t D, int64_t V, int weight_format) {
+  g_last_error[0] = 0;
+  if (B < 0 || D < 1 || V < 1 || V >= kMaxV || weight_format < 0 || weight_format > 2) {
+    fail(FS_ERR_INVALID_ARG, "fs_fused_tiles: invalid sizes or weight format");
+    return -1;
+  }
+  int cus = 0;
+  if (device_cus(&cus) != FS_OK) return -1;
+  return fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, weight_format) : 0);
+}
+
+fs_status fs_debug_stream_read(const void* buf, size_t bytes, uint64_t* out, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  if (out == nullptr || (bytes > 0 && buf == nullptr))
+    return fail(FS_ERR_INVALID_ARG, "buf or out is null");
+  if (!aligned16(buf) || (bytes & 15u) != 0)
+    return fail(FS_ERR_UNSUPPORTED, "buf must be 16-byte aligned and a multiple of 16 bytes");
+  int cus = 0;
+  fs_status s = device_cus(&cus);
+  if (s != FS_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  ProfScope prof(st);
+  hipError_t e = fs::launch_stream_read(buf, bytes, cus, out, st);
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return FS_OK;
 }
 
 fs_status fs_debug_philox_words(uint64_t seed, uint64_t offset, const uint32_t* row_ids,

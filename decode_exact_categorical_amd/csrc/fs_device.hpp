@@ -278,7 +278,13 @@ __device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_wait
 
 // True, in every thread, for the workgroup that completes its group of
 // `group_size` workgroups on `counter`.  Writer threads call store_cand and
-// wait_stores_complete before this.
+// wait_stores_complete before this.  The workgroup that counts last takes an
+// agent-scope acquire fence before it reads the group's candidates: on the
+// reading side that is what the memory model asks for, and it costs one cache
+// invalidation per group, not per workgroup.  The writing side keeps the
+// hardware guarantee stated above (write-through atomic stores, completed
+// before the count) instead of a release, whose L2 write-back every workgroup
+// would pay.
 __device__ __forceinline__ bool finish_last(uint32_t* counter, uint32_t group_size) {
   __shared__ uint32_t last;
   __syncthreads();  // every writer's stores have completed
@@ -288,7 +294,9 @@ __device__ __forceinline__ bool finish_last(uint32_t* counter, uint32_t group_si
                ? 1u
                : 0u;
   __syncthreads();
-  return last != 0u;
+  if (last == 0u) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
 }
 
 // Leave a group's counter at zero for the next call (one thread, after the

@@ -1140,7 +1140,7 @@ __global__ __launch_bounds__(kFThreads) void logits_filter_store_kernel(FilterAr
 
 hipError_t launch_filter_logits(const FilterArgs& a, hipStream_t stream) {
   const int nthr = a.B > kRowsNarrow ? kRowThreadsWide : kFThreads;
-  hipLaunchKernelGGL(logits_filter_store_kernel, dim3((unsigned)a.B), dim3(nthr), 0, stream, a);
+  launch(logits_filter_store_kernel, dim3((unsigned)a.B), dim3(nthr), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1157,9 +1157,9 @@ size_t filtered_split_words(int64_t B, int64_t V) {
 template <int MODE>
 static void launch_split(const FilterArgs& a, bool fp64, dim3 grid, hipStream_t stream) {
   if (fp64)
-    hipLaunchKernelGGL((logits_filtered_split_kernel<true, MODE>), grid, dim3(kFThreads), 0, stream, a);
+    launch((logits_filtered_split_kernel<true, MODE>), grid, dim3(kFThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((logits_filtered_split_kernel<false, MODE>), grid, dim3(kFThreads), 0, stream, a);
+    launch((logits_filtered_split_kernel<false, MODE>), grid, dim3(kFThreads), 0, stream, a);
 }
 
 hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t stream) {
@@ -1177,9 +1177,9 @@ hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t st
   const dim3 grid((unsigned)a.B);
   const dim3 block(a.B > kRowsNarrow ? kRowThreadsWide : kFThreads);
   if (fp64)
-    hipLaunchKernelGGL(logits_filtered_kernel<true>, grid, block, 0, stream, a);
+    launch(logits_filtered_kernel<true>, grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(logits_filtered_kernel<false>, grid, block, 0, stream, a);
+    launch(logits_filtered_kernel<false>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1409,23 +1409,23 @@ hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream)
   switch (epi) {
     case kEpiSample32:
       if (a.bias && FB && a.bias_vec4)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, FB, WF, FB>), grid, dim3(kThreads),
+        launch((fused_stage1_kernel<NB, kEpiSample32, FB, WF, FB>), grid, dim3(kThreads),
                            0, stream, a);
       else if (a.bias && FB)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, FB, WF>), grid, dim3(kThreads), 0,
+        launch((fused_stage1_kernel<NB, kEpiSample32, FB, WF>), grid, dim3(kThreads), 0,
                            stream, a);
       else
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample32, false, WF>), grid, dim3(kThreads),
+        launch((fused_stage1_kernel<NB, kEpiSample32, false, WF>), grid, dim3(kThreads),
                            0, stream, a);
       break;
     case kEpiSample64:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiSample64, false, WF>), grid, dim3(kThreads), 0,
+      launch((fused_stage1_kernel<NB, kEpiSample64, false, WF>), grid, dim3(kThreads), 0,
                          stream, a);
       break;
     case kEpiTopK32:
       // Gumbel-top-k: tiles of at most 64 columns, bf16 weights.
       if constexpr (NB <= 4 && BF)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK32, false, kWBf16>), grid,
+        launch((fused_stage1_kernel<NB, kEpiTopK32, false, kWBf16>), grid,
                            dim3(kThreads), 0, stream, a);
       else
         return hipErrorInvalidValue;
@@ -1434,13 +1434,13 @@ hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream)
       // Float64 scores: tiles of 16 or 64 columns (the 32- and 48-column
       // layouts run out of registers).
       if constexpr ((NB == 1 || NB == 4) && BF)
-        hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiTopK64, false, kWBf16>), grid,
+        launch((fused_stage1_kernel<NB, kEpiTopK64, false, kWBf16>), grid,
                            dim3(kThreads), 0, stream, a);
       else
         return hipErrorInvalidValue;
       break;
     default:
-      hipLaunchKernelGGL((fused_stage1_kernel<NB, kEpiStore, false, WF>), grid, dim3(kThreads), 0,
+      launch((fused_stage1_kernel<NB, kEpiStore, false, WF>), grid, dim3(kThreads), 0,
                          stream, a);
       break;
   }
@@ -1501,9 +1501,9 @@ hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) 
     if (e != hipSuccess || 16 * nb <= kStage2InKernelRows) return e;
     const dim3 g2((unsigned)((a.B + 3) / 4));
     if (epi == kEpiTopK64)
-      hipLaunchKernelGGL(topk_stage2_kernel<double>, g2, dim3(256), 0, stream, a);
+      launch(topk_stage2_kernel<double>, g2, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(topk_stage2_kernel<float>, g2, dim3(256), 0, stream, a);
+      launch(topk_stage2_kernel<float>, g2, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   const bool narrow = a.W8 != nullptr || a.W4 != nullptr;

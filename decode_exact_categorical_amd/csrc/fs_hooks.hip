@@ -31,12 +31,63 @@ __global__ __launch_bounds__(256) void noise_kernel(const uint32_t* words, int64
   }
 }
 
+// A plain streaming read: every workgroup takes a contiguous slice of the
+// buffer and each thread keeps four 16-byte loads in flight per step, with
+// the slice's lines read in order (the access shape the fused kernels' W
+// stream has).  What one launch achieves is the practical read rate an
+// HBM-bound kernel can aim for.
+constexpr int kStreamThreads = 512;
+constexpr int kStreamUnroll = 4;
+
+__global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4* p, int64_t n16,
+                                                                    uint64_t* out) {
+  const int64_t nwg = gridDim.x;
+  const int64_t lo = n16 * (int64_t)blockIdx.x / nwg;
+  const int64_t hi = n16 * ((int64_t)blockIdx.x + 1) / nwg;
+  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+  const int64_t step = (int64_t)kStreamThreads * kStreamUnroll;
+  int64_t i = lo + threadIdx.x;
+  for (; i + (kStreamUnroll - 1) * kStreamThreads < hi; i += step) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = p[i + u * kStreamThreads];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      acc.x ^= v[u].x;
+      acc.y ^= v[u].y;
+      acc.z ^= v[u].z;
+      acc.w ^= v[u].w;
+    }
+  }
+  for (; i < hi; i += kStreamThreads) {
+    const uint4 v = p[i];
+    acc.x ^= v.x;
+    acc.y ^= v.y;
+    acc.z ^= v.z;
+    acc.w ^= v.w;
+  }
+  uint64_t x = ((uint64_t)(acc.x ^ acc.z) << 32) | (uint64_t)(acc.y ^ acc.w);
+  for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o, 64);
+  if ((threadIdx.x & 63) == 0 && x != 0) atomicXor((unsigned long long*)out, (unsigned long long)x);
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, int cus, uint64_t* out,
+                              hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  int64_t wgs = (int64_t)cus * 2;
+  if (wgs > n16) wgs = n16;
+  launch(stream_read_kernel, dim3((unsigned)wgs), dim3(kStreamThreads), 0, stream,
+                     static_cast<const uint4*>(buf), n16, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,
                         hipStream_t stream) {
   const dim3 grid((unsigned)((n + 255) / 256));
-  hipLaunchKernelGGL(noise_kernel, grid, dim3(256), 0, stream, words, n, fp64, E, g);
+  launch(noise_kernel, grid, dim3(256), 0, stream, words, n, fp64, E, g);
   return hipGetLastError();
 }
 
@@ -44,7 +95,7 @@ hipError_t launch_philox_words(NoiseKey key, const uint32_t* row_ids, int64_t B,
                                uint32_t* out, hipStream_t stream) {
   const int64_t n = B * n_ctr;
   const dim3 grid((unsigned)((n + 255) / 256));
-  hipLaunchKernelGGL(philox_words_kernel, grid, dim3(256), 0, stream, key, row_ids, B, n_ctr, out);
+  launch(philox_words_kernel, grid, dim3(256), 0, stream, key, row_ids, B, n_ctr, out);
   return hipGetLastError();
 }
 

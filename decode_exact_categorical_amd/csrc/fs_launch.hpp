@@ -2,12 +2,36 @@
 // the public C ABI is include/fsample.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "fs_device.hpp"
 
 namespace fs {
+
+// Kernel timing events of the library call being launched on this thread
+// (set by the entry point while its calls are being timed, else null).  The
+// first launch of a call carries the start event and every launch the stop
+// event, both through the launch packet itself (hipExtLaunchKernelGGL), so
+// timing adds no packet of its own between kernels.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+template <typename F, typename... Args>
+inline void launch(F kernel, const dim3& grid, const dim3& block, uint32_t shmem,
+                   hipStream_t stream, Args... args) {
+  LaunchTiming& t = launch_timing();
+  if (t.start != nullptr || t.stop != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, t.start, t.stop, 0u, args...);
+    t.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+  }
+}
 
 // Fused sampling kernel (Stage 1: matmul + transform + noise + per-tile argmax;
 // Stage 2 in the last workgroup of each batch tile) and its logits-store twin.
@@ -158,6 +182,11 @@ struct PenaltyArgs {
   int vec4;                // X and Y rows 16-byte aligned
 };
 hipError_t launch_repetition_penalty(const PenaltyArgs& a, hipStream_t stream);
+
+// Measurement hook: one plain read of `bytes` (16-byte loads, a multiple of
+// 16), xor-folded into *out so no load is dead (out is not cleared first).
+hipError_t launch_stream_read(const void* buf, size_t bytes, int cus, uint64_t* out,
+                              hipStream_t stream);
 
 // Test hook: the noise transforms applied to given words.
 hipError_t launch_noise(const uint32_t* words, int64_t n, bool fp64, double* E, double* g,

@@ -140,9 +140,9 @@ int logits_chunk(int64_t B, int64_t V) {
 hipError_t launch_logits_stage1(const LogitsArgs& a, bool fp64, hipStream_t stream) {
   const dim3 grid((unsigned)(a.B * a.nT));
   if (fp64)
-    hipLaunchKernelGGL(logits_stage1_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+    launch(logits_stage1_kernel<true>, grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(logits_stage1_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+    launch(logits_stage1_kernel<false>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kPThreads) void repetition_penalty_kernel(PenaltyAr
 
 hipError_t launch_repetition_penalty(const PenaltyArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((a.V + kPenaltyChunk - 1) / kPenaltyChunk), (unsigned)a.B);
-  hipLaunchKernelGGL(repetition_penalty_kernel, grid, dim3(kPThreads), 0, stream, a);
+  launch(repetition_penalty_kernel, grid, dim3(kPThreads), 0, stream, a);
   return hipGetLastError();
 }
 

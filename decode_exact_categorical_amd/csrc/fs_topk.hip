@@ -148,9 +148,9 @@ __global__ __launch_bounds__(kThreads) void logits_topk_kernel(LogitsArgs a) {
 hipError_t launch_logits_topk(const LogitsArgs& a, bool fp64, hipStream_t stream) {
   const dim3 grid((unsigned)(a.B * a.nT));
   if (fp64)
-    hipLaunchKernelGGL(logits_topk_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+    launch(logits_topk_kernel<true>, grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(logits_topk_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+    launch(logits_topk_kernel<false>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

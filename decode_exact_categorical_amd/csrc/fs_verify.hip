@@ -489,11 +489,11 @@ void verify_chunks(int64_t B, int64_t K, int64_t V, int* chunk, int* nC, int* ch
 hipError_t launch_verify(const VerifyArgs& a, bool fp64, hipStream_t stream) {
   const dim3 g1((unsigned)(a.B * (2 * a.K + 1) * a.nC)), g2((unsigned)(a.B * a.nC2));
   if (fp64) {
-    hipLaunchKernelGGL(verify_stats_kernel<true>, g1, dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(verify_draw_kernel<true>, g2, dim3(kThreads), 0, stream, a);
+    launch(verify_stats_kernel<true>, g1, dim3(kThreads), 0, stream, a);
+    launch(verify_draw_kernel<true>, g2, dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(verify_stats_kernel<false>, g1, dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(verify_draw_kernel<false>, g2, dim3(kThreads), 0, stream, a);
+    launch(verify_stats_kernel<false>, g1, dim3(kThreads), 0, stream, a);
+    launch(verify_draw_kernel<false>, g2, dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

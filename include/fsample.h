@@ -425,6 +425,41 @@ fs_status fs_sample_fused_topk(const fs_bf16 *H, const fs_bf16 *W, int64_t B, in
 fs_status fs_profile_begin(void);
 fs_status fs_profile_end(double *kernel_ms, int64_t *calls);
 
+/*
+ * fs_profile_end with the per-call figures as well (host memory, NULL to
+ * skip): launch_ms[c] = call c's kernel duration (its two events) for
+ * c < min(calls, cap); start_to_start_ms[c] = the time from call c's first
+ * event to call c + 1's first event for c < min(calls - 1, cap - 1) -- with
+ * calls issued back to back on one stream, the per-call step time.
+ */
+fs_status fs_profile_end_detail(double *kernel_ms, int64_t *calls, float *launch_ms,
+                                float *start_to_start_ms, int64_t cap);
+
+/* Weight formats for fs_fused_tiles. */
+#define FS_WEIGHT_BF16 0
+#define FS_WEIGHT_FP8 1
+#define FS_WEIGHT_MXFP4 2
+
+/*
+ * Vocabulary tiles (workgroups along the vocabulary, one per CU) the fused
+ * calls split V into for B rows of D-dimensional hidden states on the
+ * current device: the count of per-tile candidates each row publishes
+ * [FS Stage 1 step (6)], which a caller needs to price a call's candidate
+ * traffic.  Host only (queries the device's CU count once); -1 on invalid
+ * arguments (fs_last_error() says why).
+ */
+int fs_fused_tiles(int64_t B, int64_t D, int64_t V, int weight_format);
+
+/*
+ * Measurement hook: reads `bytes` of device memory at `buf` once with a
+ * plain streaming kernel (16-byte loads, every workgroup a contiguous slice)
+ * and xors what it read into *out (device uint64, not cleared).  Its duration
+ * prices the read rate an HBM-bound kernel can practically reach on the
+ * device; it is timed by fs_profile_begin/end like the sampling calls.
+ * buf 16-byte aligned, bytes a multiple of 16.
+ */
+fs_status fs_debug_stream_read(const void *buf, size_t bytes, uint64_t *out, fs_stream_t stream);
+
 /* Static description of a status code. */
 const char *fs_status_string(fs_status status);
 

@@ -7,6 +7,13 @@ times (the C ABI's fused entry point on torch's current stream).
   fp32 bias ~ N(0, 1) with 10% of each row masked to -inf; oracle on 8 sampled rows.
 * Wide head: D = 8192, V = 262144, B in {1, 16, 128}, T = 0.7, float64 noise;
   oracle on sampled rows; batch-permutation invariance at B = 16.
+* The 128-column tiles (B > 64) at both of those heads (B = 128 with float64
+  noise, B = 256 with the bias and mask): non-default row ids (around 10^9)
+  against the oracle on sampled rows, a batch permutation carried with its row
+  ids bitwise equal to the unpermuted draws, and single-row calls equal to the
+  batched draws on those rows (where the oracle's gap exceeds the parity gap:
+  a single row runs 16-column tiles, whose k rotation differs, so its float32
+  logits may differ in the last bits).
 """
 import numpy as np
 import pytest
@@ -15,7 +22,7 @@ import torch
 import decode_exact_categorical_amd as fs
 import oracle
 import synthetic
-from gpu_common import LOGIT_TOL, check_index_parity, need_gpu, say
+from gpu_common import GAP, LOGIT_TOL, check_index_parity, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -57,14 +64,21 @@ def test_qwen_head_logits_sampled_rows(dev, qwen_head):
         assert err <= LOGIT_TOL
 
 
-def test_llama_head_b256_bias_mask(dev):
+@pytest.fixture(scope="module")
+def llama_head(dev):
     B, D, V = 256, 4096, 128256
     say("generating the D=4096 V=128256 head with bias")
     W = synthetic.weight(V, D, std=0.02)
     H = synthetic.hidden(B, D)
     temp = synthetic.temperatures(B)
     bias = synthetic.bias_with_mask(B, V, 0.1)
-    got = fs.sample_fused(H.to(dev), W.to(dev), temp.to(dev), bias.to(dev), seed=1234, offset=3)
+    return H, W, temp, bias, W.to(dev)
+
+
+def test_llama_head_b256_bias_mask(dev, llama_head):
+    H, W, temp, bias, Wd = llama_head
+    B = H.shape[0]
+    got = fs.sample_fused(H.to(dev), Wd, temp.to(dev), bias.to(dev), seed=1234, offset=3)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
     rows = np.array([0, 1, 63, 64, 127, 128, 200, 255])
@@ -75,12 +89,17 @@ def test_llama_head_b256_bias_mask(dev):
     assert np.all(np.isfinite(bias[np.arange(B), got].numpy()))      # never a masked token
 
 
-def test_wide_head_fp64_noise(dev):
+@pytest.fixture(scope="module")
+def wide_head(dev):
     D, V = 8192, 262144
     say("generating the D=8192 V=262144 head (4 GiB)")
     W = synthetic.weight(V, D, std=0.015)
     H = synthetic.hidden(128, D)
-    Wd = W.to(dev)
+    return H, W, W.to(dev)
+
+
+def test_wide_head_fp64_noise(dev, wide_head):
+    H, W, Wd = wide_head
     temp = torch.full((128,), 0.7)
     rows = np.array([0, 5, 15, 77, 127])
     say(f"oracle rows {rows.tolist()} at D=8192 V=262144")
