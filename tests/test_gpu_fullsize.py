@@ -120,3 +120,55 @@ def test_wide_head_fp64_noise(dev, wide_head):
             p = fs.sample_fused(Hd[perm.to(dev)].contiguous(), Wd, temp[:16].to(dev), seed=99,
                                 offset=123, row_ids=ids.to(dev), fp64_noise=True)
             assert np.array_equal(p.cpu().numpy(), got[perm.numpy()])
+
+
+def _wide_tile_checks(dev, H, W, Wd, temp, bias, *, seed, offset, fp64, rows, singles, what):
+    """Row ids around 10^9 against the oracle on `rows`; a permutation carried
+    with its ids, bitwise; single-row calls on `singles` against the batch."""
+    B = H.shape[0]
+    ids = (10**9 + 7 * np.arange(B)).astype(np.uint32)
+    Hd, td = H.to(dev), temp.to(dev)
+    bd = None if bias is None else bias.to(dev)
+    idd = torch.from_numpy(ids.view(np.int32)).to(dev)
+    say(f"{what}: B={B} with row ids 10^9 + 7b")
+    got = fs.sample_fused(Hd, Wd, td, bd, seed=seed, offset=offset, row_ids=idd,
+                          fp64_noise=fp64).cpu().numpy()
+    say(f"  oracle rows {rows.tolist()}")
+    ref, gap, _ = oracle.sample_fused(H[rows], W, temp[rows].numpy(),
+                                      None if bias is None else bias[rows].numpy(), seed=seed,
+                                      offset=offset, row_ids=ids[rows], fp64_noise=fp64)
+    check_index_parity(got[rows], ref, gap, f"{what} ids 10^9")
+    say("  permuted batch with its ids")
+    perm = torch.randperm(B, generator=torch.Generator().manual_seed(5))
+    pd = perm.to(dev)
+    p = fs.sample_fused(Hd[pd].contiguous(), Wd, td[pd].contiguous(),
+                        None if bd is None else bd[pd].contiguous(), seed=seed, offset=offset,
+                        row_ids=idd[pd].contiguous(), fp64_noise=fp64).cpu().numpy()
+    assert np.array_equal(p, got[perm.numpy()]), f"{what}: permuted draws differ"
+    compared = 0
+    for r in singles:
+        say(f"  single row {r}")
+        s1 = fs.sample_fused(Hd[r:r + 1].contiguous(), Wd, td[r:r + 1].contiguous(),
+                             None if bd is None else bd[r:r + 1].contiguous(), seed=seed,
+                             offset=offset, row_ids=idd[r:r + 1].contiguous(),
+                             fp64_noise=fp64).item()
+        j = int(np.flatnonzero(rows == r)[0])
+        if gap[j] > GAP:
+            assert s1 == got[r] == ref[j], (what, r, s1, got[r], ref[j])
+            compared += 1
+    assert compared >= len(singles) - 1, f"{what}: single-row checks all near ties"
+
+
+def test_wide_tiles_wide_head_b128(dev, wide_head):
+    H, W, Wd = wide_head
+    temp = torch.full((128,), 0.7)
+    _wide_tile_checks(dev, H, W, Wd, temp, None, seed=41, offset=2**40 + 9, fp64=True,
+                      rows=np.array([0, 33, 64, 100, 127]), singles=(0, 64, 127),
+                      what="wide head fp64")
+
+
+def test_wide_tiles_llama_head_b256(dev, llama_head):
+    H, W, temp, bias, Wd = llama_head
+    _wide_tile_checks(dev, H, W, Wd, temp, bias, seed=42, offset=77, fp64=False,
+                      rows=np.array([1, 90, 128, 191, 254]), singles=(1, 128, 254),
+                      what="llama head bias")
