@@ -19,7 +19,7 @@ import threading
 import torch
 
 __all__ = [
-    "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused",
+    "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused", "sample_fused_noalloc",
     "sample_fused_w8",
     "sample_fused_topk", "sample_fused_mxfp4", "sample_logits", "sample_logits_topk",
     "sample_logits_filtered", "workspace_bytes", "debug_logits_mxfp4", "debug_philox_words",
@@ -81,6 +81,8 @@ def load_library():
         lib.fs_profile_end.argtypes = [P, P]
         lib.fs_profile_end_detail.restype = i32
         lib.fs_profile_end_detail.argtypes = [P, P, P, P, i64]
+        lib.fs_sample_fused_noalloc.restype = i32
+        lib.fs_sample_fused_noalloc.argtypes = [P, P, i64, i64, i64, P, P, u64, u64, P, P, u32, P]
         lib.fs_fused_tiles.restype = i32
         lib.fs_fused_tiles.argtypes = [i64, i64, i64, i32]
         lib.fs_debug_stream_read.restype = i32
@@ -208,6 +210,36 @@ def sample_fused(H: torch.Tensor, W: torch.Tensor, temp, bias: torch.Tensor | No
     st = lib.fs_sample_fused(_ptr(H), _ptr(W), B, D, V, _ptr(t), _ptr(bias), seed, offset,
                              _ptr(out), _ptr(rid), flags, _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "fs_sample_fused")
+    return out
+
+
+def sample_fused_noalloc(H: torch.Tensor, W: torch.Tensor, temp, bias: torch.Tensor | None = None,
+                         *, seed: int, offset: int, row_ids: torch.Tensor | None = None,
+                         fp64_noise: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+    """sample_fused without a workspace: the library's built-in per-GPU scratch
+    (B <= 1024; calls that overlap on one GPU race on it).  `out` given, the
+    call allocates nothing."""
+    lib = load_library()
+    dev = H.device
+    if dev.type != "cuda":
+        raise ValueError("H must be a GPU tensor")
+    if H.dim() != 2 or W.dim() != 2:
+        raise ValueError("H must be [B, D] and W [V, D]")
+    B, D = H.shape
+    V = W.shape[0]
+    _need(H, "H", torch.bfloat16, dev, (B, D))
+    _need(W, "W", torch.bfloat16, dev, (V, D))
+    _need(temp, "temp", torch.float32, dev, (B,))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (B, V))
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B,))
+    flags = FS_FP64_NOISE if fp64_noise else 0
+    st = lib.fs_sample_fused_noalloc(_ptr(H), _ptr(W), B, D, V, _ptr(temp), _ptr(bias), seed,
+                                     offset, _ptr(out), _ptr(rid), flags, _stream(dev))
+    _check(st, "fs_sample_fused_noalloc")
     return out
 
 

@@ -296,9 +296,82 @@ fs_status debug_logits(const fs_bf16* H, const void* W, int fmt, const void* sca
   return FS_OK;
 }
 
+// ---- the entry point that allocates nothing (fs_sample_fused_noalloc) ----
+// Its scratch memory is this file-scope device array: a counter region, then
+// the per-tile candidates of at most kNoAllocMaxB rows (16-byte candidates,
+// kMaxFusedTiles tiles).  Each GPU holds its own copy for the life of the
+// process; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (the array's name on the host is not a
+// device address).
+constexpr int64_t kNoAllocMaxB = 1024;
+constexpr size_t kNoAllocCounterBytes = 4096;  // ceil(B / 16) <= 64 counters
+constexpr size_t kNoAllocCandBytes = (size_t)kNoAllocMaxB * fs::kMaxFusedTiles * 16;
+constexpr size_t kNoAllocBytes = kNoAllocCounterBytes + kNoAllocCandBytes;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+__global__ void clear_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The current device's scratch address, looked up (and its counter region
+// cleared, by a kernel on `stream`) on the first call on that device.
+fs_status noalloc_scratch(hipStream_t stream, unsigned char** out) {
+  static unsigned char* ptrs[kMaxDevices] = {nullptr};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FS_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(FS_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    const int64_t words = (int64_t)(kNoAllocCounterBytes / sizeof(uint32_t));
+    fs::launch(clear_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+    ptrs[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = ptrs[dev];
+  return FS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+fs_status fs_sample_fused_noalloc(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D,
+                                  int64_t V, const float* temp, const float* bias, uint64_t seed,
+                                  uint64_t offset, int64_t* out_idx, const uint32_t* row_ids,
+                                  uint32_t flags, fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_fused(H, W, kFmtBf16, nullptr, B, D, V);
+  if (s != FS_OK) return s;
+  if (flags & ~FS_FP64_NOISE) return fail(FS_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (B > kNoAllocMaxB)
+    return fail(FS_ERR_UNSUPPORTED, "B = %lld exceeds the %lld rows of the built-in scratch",
+                (long long)B, (long long)kNoAllocMaxB);
+  if (B == 0) return FS_OK;
+  if (temp == nullptr || out_idx == nullptr) return fail(FS_ERR_INVALID_ARG, "temp or out_idx is null");
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != FS_OK) return s;
+  const int nT = fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, kFmtBf16) : 0);
+  s = check_span(V, D, nT, kFmtBf16);
+  if (s != FS_OK) return s;
+  if ((size_t)B * (size_t)nT * cand_bytes(flags) > kNoAllocCandBytes)
+    return fail(FS_ERR_UNSUPPORTED, "B * tiles exceeds the built-in scratch");
+  unsigned char* p = nullptr;
+  s = noalloc_scratch((hipStream_t)stream, &p);
+  if (s != FS_OK) return s;
+  return launch_sampling(H, W, kFmtBf16, nullptr, B, D, V, temp, bias, seed, offset, out_idx,
+                         row_ids, flags, p + kNoAllocCounterBytes, reinterpret_cast<uint32_t*>(p),
+                         nT, stream, 0);
+}
 
 size_t fs_workspace_bytes(int64_t B, int64_t V, uint32_t flags) {
   if (B < 0 || V < 1 || V >= kMaxV) return 0;

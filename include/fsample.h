@@ -153,6 +153,26 @@ fs_status fs_sample_fused(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t
                           size_t workspace_bytes, fs_stream_t stream);
 
 /*
+ * fs_sample_fused for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, rule and results as fs_sample_fused, without the workspace:
+ * the per-tile candidates and completion counters live in a scratch array
+ * built into the library, one per GPU, of 4 MiB + 4 KiB (held until the
+ * process ends), sized for
+ *   B <= 1024 rows (FS_ERR_UNSUPPORTED beyond; B = 0 is a no-op).
+ * The first call on a device looks up that device's copy of the array and
+ * clears its counters with a small kernel on `stream`; no call allocates
+ * (no hipMalloc, hipFree or allocating library routine).  Every call on a GPU
+ * shares that GPU's array and leaves its counters at zero: calls that can
+ * overlap on one GPU (other streams, other threads) race on it and must be
+ * serialised by the caller.  bf16 weights, one draw per row.
+ */
+fs_status fs_sample_fused_noalloc(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t D,
+                                  int64_t V, const float *temp, const float *bias,
+                                  uint64_t seed, uint64_t offset, int64_t *out_idx,
+                                  const uint32_t *row_ids, uint32_t flags, fs_stream_t stream);
+
+/*
  * Fused LM-head + exact sampling with FP8 weights: W8 holds OCP FP8 E4M3 codes
  * [OFP8] (sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities;
  * 0x7F and 0xFF are NaN) and row i of the weight is w_scale[i] * W8[i, :].

@@ -218,3 +218,21 @@ def test_python_binding_checks_without_gpu():
     with pytest.raises(ValueError):
         fs.sample_fused(torch.zeros(2, 8, dtype=torch.bfloat16),
                         torch.zeros(3, 8, dtype=torch.bfloat16), 1.0, seed=0, offset=0)
+
+
+def _noalloc(B=4, D=512, V=1000, H=FAKE, W=FAKE, temp=FAKE, out=FAKE, flags=0):
+    lib = fs.load_library()
+    return lib.fs_sample_fused_noalloc(P(H), P(W), B, D, V, P(temp), None, 1, 0, P(out), None,
+                                       flags, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), 1), (dict(V=0), 1), (dict(D=0), 1), (dict(H=0), 1), (dict(temp=0), 1),
+    (dict(out=0), 1), (dict(flags=2), 1), (dict(D=12), 2), (dict(W=FAKE + 8), 2),
+    (dict(B=1025), 2),
+])
+def test_noalloc_rejects_before_launch(kw, code):
+    # sizes past the built-in scratch (B > 1024) are refused like any other
+    # argument error: on the host, before any HIP call
+    assert _noalloc(**kw) == code
+    assert fs.load_library().fs_last_error() != b""
