@@ -100,6 +100,9 @@ def _load():
                                                    i64, i32, P, P]
         lib.oracle_filter_kept.restype = None
         lib.oracle_filter_kept.argtypes = [P, i64, i64, P, P, P, P, P, P]
+        lib.oracle_sample_fused_filtered.restype = None
+        lib.oracle_sample_fused_filtered.argtypes = [P, P, i64, i64, i64, P, P, P, P, u64, u64,
+                                                     P, i32, P, P, P, P]
         lib.oracle_sample_logits_filtered.restype = None
         lib.oracle_sample_logits_filtered.argtypes = [P, i64, i64, P, P, P, P, u64, u64, P, i32,
                                                       P, P, P]
@@ -473,6 +476,29 @@ def sample_logits_filtered(logits_f32, temp, *, top_k=None, top_p=None, min_p=No
                                           seed, offset, _ptr(rid), int(fp64_noise), _ptr(idx),
                                           _ptr(gap), _ptr(margin))
     return idx, gap, margin
+
+
+def sample_fused_filtered(H, W, temp, *, top_k=None, top_p=None, min_p=None, seed: int,
+                          offset: int, row_ids=None, fp64_noise: bool = False):
+    """(idx, gap, margin, vmargin): filtered exact sampling of the logits H W^T
+    (H[B,D], W[V,D] bf16, summed in float64): the filter chain over those
+    logits, then the fused draw over the kept tokens.  margin: the smallest
+    relative distance of a top-p or min-p decision from its boundary; vmargin:
+    the smallest logit gap at a top-k or top-p cut."""
+    h, w = _bf16_bits(H), _bf16_bits(W)
+    B, D = h.shape
+    V = w.shape[0]
+    t = np.ascontiguousarray(np.asarray(temp, dtype=np.float32).reshape(B))
+    k, p, m = _filter_args(B, top_k, top_p, min_p)
+    rid = _u32_or_none(row_ids, B)
+    idx = np.zeros(B, dtype=np.int64)
+    gap = np.zeros(B, dtype=np.float64)
+    margin = np.zeros(B, dtype=np.float64)
+    vmargin = np.zeros(B, dtype=np.float64)
+    _load().oracle_sample_fused_filtered(_ptr(h), _ptr(w), B, D, V, _ptr(t), _ptr(k), _ptr(p),
+                                         _ptr(m), seed, offset, _ptr(rid), int(fp64_noise),
+                                         _ptr(idx), _ptr(gap), _ptr(margin), _ptr(vmargin))
+    return idx, gap, margin, vmargin
 
 
 def filtered_repeated_row(row_f32, temp: float, *, top_k: int = 0, top_p: float = 1.0,

@@ -633,7 +633,7 @@ void oracle_sample_repeated_row(const float *logits, int64_t V, float temp,
 /* A logit and its index; sorted by value descending, ties in increasing
  * index order. */
 typedef struct {
-    float v;
+    double v;
     int64_t i;
 } vi_t;
 static int cmp_desc(const void *pa, const void *pb)
@@ -661,16 +661,22 @@ static int cmp_desc(const void *pa, const void *pb)
  *     p_i >= m * p_max (renormalising does not change that ratio);
  *   each filter that would keep nothing keeps the largest logit's tie class.
  * Greedy rows (!(t > 0)) keep the largest logit's tie class: their draw is the
- * argmax whatever the filters.  Returns the kept mask and *margin, the
- * smallest distance of a top-p or min-p decision from its boundary (relative:
- * |A - pZ| / Z for top-p, |e_i - m| / m for min-p; +inf when neither decides
- * anything), so that a comparison with another implementation can set aside
- * the rows whose kept set rounding may decide.  The largest logit's class has
- * no such distance: its mass above is 0 and its mass ratio 1 exactly, and the
- * filters keep it whatever p and m are. */
-static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
+ * argmax whatever the filters.  The logits are float64 (float32 rows convert
+ * exactly).  Returns the kept mask and two margins, so that a comparison with
+ * another implementation can set aside the rows whose kept set rounding may
+ * decide:
+ *   *margin, the smallest distance of a top-p or min-p decision from its
+ *     boundary (relative: |A - pZ| / Z for top-p, |e_i - m| / m for min-p;
+ *     +inf when neither decides anything).  The largest logit's class has no
+ *     such distance: its mass above is 0 and its mass ratio 1 exactly, and
+ *     the filters keep it whatever p and m are;
+ *   *vmargin, the logit gap at each cut the top-k and top-p filters make
+ *     (the last kept value minus the first dropped value; +inf when neither
+ *     cuts): a smaller perturbation of the logits cannot reorder the tokens
+ *     on either side of a cut. */
+static void filter_row(const double *y, int64_t V, double t, int32_t k, float p,
                        float m, vi_t *order, double *e, uint8_t *kept,
-                       double *margin)
+                       double *margin, double *vmargin)
 {
     int64_t n = 0;
     for (int64_t i = 0; i < V; ++i) {
@@ -682,6 +688,7 @@ static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
         }
     }
     *margin = INFINITY;
+    *vmargin = INFINITY;
     if (n == 0) return;
     qsort(order, (size_t)n, sizeof(vi_t), cmp_desc);
     const double M = (double)order[0].v;
@@ -700,9 +707,10 @@ static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
     /* top-k: survivors order[0 .. n1) */
     int64_t n1 = n;
     if (k > 0 && (int64_t)k < n) {
-        const float theta = order[k - 1].v;
+        const double theta = order[k - 1].v;
         n1 = k;
         while (n1 < n && order[n1].v == theta) ++n1;
+        if (n1 < n) *vmargin = fmin(*vmargin, order[n1 - 1].v - order[n1].v);
     }
     /* top-p over the top-k survivors: order[0 .. n2) */
     int64_t n2 = n1;
@@ -729,6 +737,7 @@ static void filter_row(const float *y, int64_t V, double t, int32_t k, float p,
             j = j2;
         }
         if (n2 == 0) n2 = nmax;
+        if (n2 < n1) *vmargin = fmin(*vmargin, order[n2 - 1].v - order[n2].v);
     }
     /* min-p over the top-p survivors */
     int64_t n3 = 0;
@@ -758,14 +767,56 @@ void oracle_filter_kept(const float *logits, int64_t B, int64_t V, const float *
     {
         vi_t *order = (vi_t *)malloc((size_t)(V > 0 ? V : 1) * sizeof(vi_t));
         double *e = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+        double *y = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
         #pragma omp for schedule(dynamic)
-        for (int64_t b = 0; b < B; ++b)
-            filter_row(logits + b * V, V, (double)temp[b], top_k ? top_k[b] : 0,
+        for (int64_t b = 0; b < B; ++b) {
+            double vm;
+            for (int64_t i = 0; i < V; ++i) y[i] = (double)logits[b * V + i];
+            filter_row(y, V, (double)temp[b], top_k ? top_k[b] : 0,
                        top_p ? top_p[b] : 1.0f, min_p ? min_p[b] : 0.0f, order, e,
-                       kept + b * V, &margin[b]);
+                       kept + b * V, &margin[b], &vm);
+        }
+        free(y);
         free(e);
         free(order);
     }
+}
+
+/* Fused filtered exact sampling [SD sample pipeline and Semantics; FS
+ * algorithm details step (1)]: per row, the logits y = H W^T in float64 (the
+ * sum of oracle_logits), the kept set of filter_row over them, then the draw
+ * of oracle_sample_fused (no bias) over the kept tokens only.  Outputs per
+ * row: the sampled index (-1 if none), the top-2 gap of the kept perturbed
+ * scores, and filter_row's two margins. */
+void oracle_sample_fused_filtered(const uint16_t *H, const uint16_t *W, int64_t B, int64_t D,
+                                  int64_t V, const float *temp, const int32_t *top_k,
+                                  const float *top_p, const float *min_p, uint64_t seed,
+                                  uint64_t offset, const uint32_t *row_ids, int fp64_noise,
+                                  int64_t *out_idx, double *out_gap, double *out_margin,
+                                  double *out_vmargin)
+{
+    double *y = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    double *s = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    double *e = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    vi_t *order = (vi_t *)malloc((size_t)(V > 0 ? V : 1) * sizeof(vi_t));
+    uint8_t *kept = (uint8_t *)malloc((size_t)(V > 0 ? V : 1));
+    for (int64_t b = 0; b < B; ++b) {
+        const uint32_t r = row_ids ? row_ids[b] : (uint32_t)b;
+        const double t = (double)temp[b];
+        oracle_logits(H + b * D, W, 1, D, V, y);
+        filter_row(y, V, t, top_k ? top_k[b] : 0, top_p ? top_p[b] : 1.0f,
+                   min_p ? min_p[b] : 0.0f, order, e, kept, &out_margin[b], &out_vmargin[b]);
+        double best;
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < V; ++i)
+            s[i] = kept[i] ? score_of(y[i], 0.0, t, seed, offset, r, i, fp64_noise) : -INFINITY;
+        select_row(s, V, &out_idx[b], &out_gap[b], &best);
+    }
+    free(kept);
+    free(order);
+    free(e);
+    free(s);
+    free(y);
 }
 
 /* Repetition penalty [SD sample pipeline: the penalty comes before the
