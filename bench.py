@@ -551,6 +551,37 @@ def main() -> int:
             del X
         result["filtered_sampler"] = fl
 
+        # Filtered sampling fused into the LM head (fs_sample_fused_filtered) at
+        # the card's settings (top_k 50 + top_p 0.95) on the Qwen3-8B head, and
+        # top-p or min-p alone at B = 64 (flat rows send top-p-alone rows through
+        # the exact fallback); against the GEMM + fs_sample_logits_filtered.
+        log("timing fused filtered sampling")
+        ff = {"workload": "W [151936, 4096] bf16, per-row T ~ U[0.5,1.2], fp32 noise"}
+        for (bl, name, kw) in ((1, "", dict(top_k=50, top_p=0.95)),
+                               (8, "", dict(top_k=50, top_p=0.95)),
+                               (64, "", dict(top_k=50, top_p=0.95)),
+                               (64, "_top_p_0.95", dict(top_p=0.95)),
+                               (64, "_min_p_0.05", dict(min_p=0.05))):
+            Hs, Ts = H[:bl].contiguous(), temp[:bl].contiguous()
+            ms, kms, pc = time_calls(
+                torch, fs, lambda s: fs.sample_fused_filtered(Hs, W, Ts, seed=1234, offset=s, **kw),
+                max(20, args.steps // 4), 5)
+
+            def unfused_filtered(s):
+                y = torch.matmul(Hs, W.t()).float()
+                return fs.sample_logits_filtered(y, Ts, seed=1234, offset=s, **kw)
+
+            unf = time_region(torch, unfused_filtered, max(20, args.steps // 4), 5)
+            nTf = fs.fused_tiles(bl, D_MODEL, VOCAB)
+            kb = VOCAB * D_MODEL * 2 + bl * D_MODEL * 2 + 2 * 128 * bl * nTf + 16 * bl
+            key = f"B{bl}{name}"
+            ff[key] = {"us_per_call": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
+                       "alg_bytes": kb, "kernel_frac": round(kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "unfused_gemm_filtered_us": round(unf * 1e3, 2),
+                       "speedup_vs_unfused": round(unf / ms, 3)}
+            log(f"  {key}: {ff[key]}")
+        result["fused_filtered"] = ff
+
         # Speculative-decoding verification over float32 target [B, K+1, V] and
         # draft [B, K, V] logits, K = 4 (the spec-decode-ops card's acceptance
         # length test), at the Qwen3-8B vocabulary: the draft is the target plus

@@ -22,7 +22,8 @@ __all__ = [
     "FS_FP64_NOISE", "FS_TOPK_MAX", "FSampleError", "sample_fused", "sample_fused_noalloc",
     "sample_fused_w8",
     "sample_fused_topk", "sample_fused_mxfp4", "sample_logits", "sample_logits_topk",
-    "sample_logits_filtered", "workspace_bytes", "debug_logits_mxfp4", "debug_philox_words",
+    "sample_logits_filtered", "sample_fused_filtered", "workspace_bytes", "debug_logits_mxfp4",
+    "debug_philox_words",
     "debug_logits", "debug_logits_w8", "debug_noise", "library_path", "load_library",
     "KernelTimer",
     "fused_tiles",
@@ -81,6 +82,11 @@ def load_library():
         lib.fs_profile_end.argtypes = [P, P]
         lib.fs_profile_end_detail.restype = i32
         lib.fs_profile_end_detail.argtypes = [P, P, P, P, i64]
+        lib.fs_workspace_bytes_fused_filtered.restype = sz
+        lib.fs_workspace_bytes_fused_filtered.argtypes = [i64, i64]
+        lib.fs_sample_fused_filtered.restype = i32
+        lib.fs_sample_fused_filtered.argtypes = [P, P, i64, i64, i64, P, P, P, P, u64, u64, P, P,
+                                                 u32, P, sz, P]
         lib.fs_sample_fused_noalloc.restype = i32
         lib.fs_sample_fused_noalloc.argtypes = [P, P, i64, i64, i64, P, P, u64, u64, P, P, u32, P]
         lib.fs_fused_tiles.restype = i32
@@ -387,6 +393,43 @@ def sample_logits_filtered(logits: torch.Tensor, temp, *, top_k=None, top_p=None
                                        seed, offset, int(bool(fp64_noise)), _ptr(out), _ptr(rid),
                                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(st, "fs_sample_logits_filtered")
+    return out
+
+
+def sample_fused_filtered(H: torch.Tensor, W: torch.Tensor, temp, *, top_k=None, top_p=None,
+                          min_p=None, seed: int, offset: int, row_ids: torch.Tensor | None = None,
+                          fp64_noise: bool = False,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    """Filtered exact sampling fused into the LM head: per row, the draw
+    sample_logits_filtered makes over the float32 logits H W^T, without writing
+    them (a row the tiles' lists cannot resolve is computed again and drawn
+    exactly inside the same call).  top_k (int32), top_p, min_p (float32):
+    None, a scalar, or a [B] tensor."""
+    lib = load_library()
+    dev = H.device
+    if dev.type != "cuda":
+        raise ValueError("H must be a GPU tensor")
+    if H.dim() != 2 or W.dim() != 2:
+        raise ValueError("H must be [B, D] and W [V, D]")
+    B, D = H.shape
+    V = W.shape[0]
+    _need(H, "H", torch.bfloat16, dev, (B, D))
+    _need(W, "W", torch.bfloat16, dev, (V, D))
+    t = _temp_tensor(temp, B, dev)
+    k = _filter_param(top_k, "top_k", torch.int32, B, dev)
+    p = _filter_param(top_p, "top_p", torch.float32, B, dev)
+    m = _filter_param(min_p, "min_p", torch.float32, B, dev)
+    rid = _row_ids(row_ids, B, dev)
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, dev, (B,))
+    need = int(lib.fs_workspace_bytes_fused_filtered(B, V)) if V > 0 else 0
+    ws = _workspace(dev, need)
+    st = lib.fs_sample_fused_filtered(_ptr(H), _ptr(W), B, D, V, _ptr(t), _ptr(k), _ptr(p),
+                                      _ptr(m), seed, offset, _ptr(out), _ptr(rid),
+                                      FS_FP64_NOISE if fp64_noise else 0, _ptr(ws), ws.numel(),
+                                      _stream(dev))
+    _check(st, "fs_sample_fused_filtered")
     return out
 
 

@@ -481,6 +481,95 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
   return FS_OK;
 }
 
+// Workspace of the fused filtered sampler: the counter region (its word 0
+// counts the rows flagged for the fallback, words 1 .. B are the rows' flags;
+// like every counter they are zero between calls), the per-(row, tile)
+// records, then the fallback logits [B, V] (written only for flagged rows).
+constexpr int64_t kFusedFilteredMaxB = kCounterWords - 1;
+struct FusedFilteredLayout {
+  size_t records, logits, total;
+};
+FusedFilteredLayout fused_filtered_layout(int64_t B, int64_t V) {
+  FusedFilteredLayout L;
+  L.records = kCounterBytes;
+  L.logits = L.records + align_up((size_t)B * fs::kMaxFusedTiles * fs::kFiltRecBytes);
+  L.total = L.logits + align_up((size_t)B * (size_t)V * sizeof(float));
+  return L;
+}
+
+size_t fs_workspace_bytes_fused_filtered(int64_t B, int64_t V) {
+  if (B < 0 || B > kFusedFilteredMaxB || V < 1 || V >= kMaxV) return 0;
+  return fused_filtered_layout(B, V).total;
+}
+
+fs_status fs_sample_fused_filtered(const fs_bf16* H, const fs_bf16* W, int64_t B, int64_t D,
+                                   int64_t V, const float* temp, const int32_t* top_k,
+                                   const float* top_p, const float* min_p, uint64_t seed,
+                                   uint64_t offset, int64_t* out_idx, const uint32_t* row_ids,
+                                   uint32_t flags, void* workspace, size_t workspace_bytes,
+                                   fs_stream_t stream) {
+  g_last_error[0] = 0;
+  fs_status s = check_fused(H, W, kFmtBf16, nullptr, B, D, V);
+  if (s != FS_OK) return s;
+  if (flags & ~FS_FP64_NOISE) return fail(FS_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (B > kFusedFilteredMaxB)
+    return fail(FS_ERR_UNSUPPORTED, "B = %lld > %lld", (long long)B, (long long)kFusedFilteredMaxB);
+  if (B == 0) return FS_OK;
+  if (temp == nullptr || out_idx == nullptr) return fail(FS_ERR_INVALID_ARG, "temp or out_idx is null");
+  const FusedFilteredLayout L = fused_filtered_layout(B, V);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(FS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(FS_ERR_WORKSPACE, "workspace not %zu-byte aligned", (size_t)kAlign);
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != FS_OK) return s;
+  const int nT = fs::fused_num_tiles(V, cus, row_bytes(D, kFmtBf16));
+  s = check_span(V, D, nT, kFmtBf16);
+  if (s != FS_OK) return s;
+  const bool fp64 = (flags & FS_FP64_NOISE) != 0;
+  char* ws = static_cast<char*>(workspace);
+  fs::FusedArgs a;
+  memset(&a, 0, sizeof a);
+  a.H = H;
+  a.W = W;
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.temp = temp;
+  a.row_ids = row_ids;
+  a.key = fs::make_key(seed, offset);
+  a.cand = ws + L.records;
+  a.nT = nT;
+  a.counters = counters_of(workspace);
+  a.out = out_idx;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.min_p = min_p;
+  a.flag_count = counters_of(workspace);
+  a.row_flags = counters_of(workspace) + 1;
+  fs::FilterArgs fa;
+  memset(&fa, 0, sizeof fa);
+  fa.X = reinterpret_cast<const float*>(ws + L.logits);
+  fa.B = B;
+  fa.V = V;
+  fa.temp = temp;
+  fa.row_ids = row_ids;
+  fa.top_k = top_k;
+  fa.top_p = top_p;
+  fa.min_p = min_p;
+  fa.key = a.key;
+  fa.out = out_idx;
+  fa.vec4 = (V % 4 == 0);
+  fa.row_flags = a.row_flags;
+  fa.flag_count = a.flag_count;
+  hipStream_t st = (hipStream_t)stream;
+  ProfScope prof(st);
+  hipError_t e = fs::launch_fused_filtered(a, fp64, fa, st);
+  if (e != hipSuccess) return hip_fail(e, "fused filtered sampling launch");
+  return FS_OK;
+}
+
 size_t fs_workspace_bytes_filtered(int64_t B, int64_t V) {
   if (B < 0 || V < 1 || V >= kMaxV) return 0;
   const size_t words = fs::filtered_split_words(B, V);
@@ -527,6 +616,8 @@ fs_status fs_sample_logits_filtered(const float* logits, int64_t B, int64_t V, c
   a.split = need > 0 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kCounterBytes)
                      : nullptr;
   a.Y = nullptr;
+  a.row_flags = nullptr;
+  a.flag_count = nullptr;
   hipError_t e = fs::launch_logits_filtered(a, fp64_noise != 0, st);
   if (e != hipSuccess) return hip_fail(e, "filtered sampling launch");
   return FS_OK;
@@ -589,6 +680,8 @@ fs_status fs_filter_logits(const float* logits, int64_t B, int64_t V, const floa
   a.counters = nullptr;
   a.split = nullptr;
   a.Y = out_logits;
+  a.row_flags = nullptr;
+  a.flag_count = nullptr;
   hipStream_t st = (hipStream_t)stream;
   ProfScope prof(st);
   hipError_t e = fs::launch_filter_logits(a, st);

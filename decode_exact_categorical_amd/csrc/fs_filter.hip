@@ -717,8 +717,17 @@ template <bool FP64>
 __global__ __launch_bounds__(kFThreads) void logits_filtered_kernel(FilterArgs a) {
   typedef typename std::conditional<FP64, double, float>::type T;
   __shared__ FilterShared<T, kCap> sh;
+  if (a.row_flags) {
+    // Only the flagged rows (the fused filtered sampler's fallback): the
+    // previous launches have read the flag count, so it is cleared here.
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.flag_count = 0u;
+    if (a.row_flags[blockIdx.x] == 0u) return;
+  }
   const int64_t o = filter_row_single<FP64, kCap>(a, (int64_t)blockIdx.x, sh);
-  if (threadIdx.x == 0) a.out[blockIdx.x] = o;
+  if (threadIdx.x == 0) {
+    a.out[blockIdx.x] = o;
+    if (a.row_flags) a.row_flags[blockIdx.x] = 0u;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1163,7 +1172,7 @@ static void launch_split(const FilterArgs& a, bool fp64, dim3 grid, hipStream_t 
 }
 
 hipError_t launch_logits_filtered(const FilterArgs& a, bool fp64, hipStream_t stream) {
-  const int G = a.split ? filtered_split_chunks(a.B, a.V) : 0;
+  const int G = a.split && !a.row_flags ? filtered_split_chunks(a.B, a.V) : 0;
   if (G) {
     const dim3 chunks((unsigned)G, (unsigned)a.B), rows(1u, (unsigned)a.B);
     if (a.B <= kSplitMaxRows) {

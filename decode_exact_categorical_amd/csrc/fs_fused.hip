@@ -85,6 +85,10 @@ template <>
 struct ScoreType<kEpiTopK64> {
   typedef double type;
 };
+template <>
+struct ScoreType<kEpiFilt64> {
+  typedef double type;
+};
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -153,7 +157,8 @@ struct Pipeline {
   static constexpr bool narrow = WF != kWBf16;  // FP8 or MXFP4 weights
   // Noise added after the k-loop (float64 noise, Gumbel-top-k): the same
   // register budget as float64 noise.
-  static constexpr bool late_noise = EPI == kEpiSample64 || EPI == kEpiTopK32 || EPI == kEpiTopK64;
+  static constexpr bool late_noise = EPI == kEpiSample64 || EPI == kEpiTopK32 || EPI == kEpiTopK64 ||
+                                     EPI == kEpiFilt32 || EPI == kEpiFilt64;
   static constexpr bool wide = NB > 4;
   static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || late_noise);
   static constexpr bool ring1 = !narrow && !wide && NB >= 3 && !wide_extra;
@@ -305,7 +310,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   constexpr bool W8 = WF == kWFp8, W4 = WF == kWFp4;
   constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS, WF>::value;
   constexpr bool kTopK = EPI == kEpiTopK32 || EPI == kEpiTopK64;
+  constexpr bool kFilt = EPI == kEpiFilt32 || EPI == kEpiFilt64;
   typedef Pipeline<NB, EPI, HAS_BIAS, WF> Pipe;
+  // The fallback store of the filtered sampler: nothing to do when Stage 2
+  // resolved every row.
+  if (EPI == kEpiStore && a.flag_count != nullptr && *a.flag_count == 0u) return;
   // W element bytes, and k per 16-byte lane load (one MFMA k-step of bf16,
   // two of FP8).
   // A lane's 16-byte load holds 8 bf16, 16 FP8 or 32 FP4 values of its row;
@@ -420,6 +429,30 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
         for (int j = 0; j < kTopKMax; ++j) tkc[wave][16 * cb + col][j] = Cand<T>{neg_inf<T>(), kNoIndex};
+    }
+  }
+
+  // Filtered sampling: each batch column's running top-kFiltList logits and
+  // its running best score, mass and count, per wave across its passes.
+  struct FiltAux {
+    T bs;
+    float by;
+    int32_t bi;
+    float mm;
+    uint32_t nv;
+    double zz;
+  };
+  constexpr int kFLW = kFilt ? kWaves : 1, kFLC = kFilt ? 16 * NB : 1, kFLK = kFilt ? kFiltList : 1;
+  __shared__ Cand<float> flc[kFLW][kFLC][kFLK];
+  __shared__ FiltAux fla[kFLW][kFLC];
+  if constexpr (kFilt) {
+    if (grp == 0) {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+#pragma unroll
+        for (int j = 0; j < kFiltList; ++j) flc[wave][16 * cb + col][j] = Cand<float>{neg_inf<float>(), kNoIndex};
+        fla[wave][16 * cb + col] = FiltAux{neg_inf<T>(), neg_inf<float>(), kNoIndex, neg_inf<float>(), 0u, 0.0};
+      }
     }
   }
 
@@ -1118,6 +1151,142 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           }
         }
       }
+    } else if constexpr (kFilt) {
+      // Filtered sampling, column block by column block: each lane's rows of
+      // the pass (in increasing index order) update its sorted list of the
+      // kFiltList largest valid logits, its best perturbed score (the
+      // unfiltered sampler's arithmetic: y / t + g, greedy y), its running
+      // mass exp((y - mm) / t) relative to its largest logit mm, and its count
+      // of valid logits; then the column's four row groups (lanes 16 apart)
+      // and the column's running state (LDS) merge into the new running state.
+#pragma unroll 1
+      for (int cb = 0; cb < NB; ++cb) {
+        float lm[kFiltList];
+        int32_t li[kFiltList];
+#pragma unroll
+        for (int j = 0; j < kFiltList; ++j) {
+          lm[j] = neg_inf<float>();
+          li[j] = kNoIndex;
+        }
+        T bs = neg_inf<T>();
+        int32_t bi = kNoIndex;
+        float by = neg_inf<float>();
+        float mm = neg_inf<float>(), mz = 0.0f;
+        uint32_t nv = 0u;
+        const ColInfo ci = cols[16 * cb + col];
+        const bool greedy = ci.mode == kGreedy;
+        const float inv_tf = greedy ? 1.0f : 1.0f / ci.t;
+        const T inv_t = greedy ? T(1) : T(1) / T(ci.t);
+        // mass of logit y relative to a larger-or-equal logit m
+        auto rel_mass = [&](float y, float m) -> float {
+          if (m == __builtin_inff()) return y == m ? 1.0f : 0.0f;
+          return expf((y - m) * inv_tf);
+        };
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          if (rb >= nrb) break;
+          f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c2 = 0; c2 < NB; ++c2)
+            if (c2 == cb) y = acc[rb][c2];
+          const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+          bool ok[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ok[j] = (i0 + j < r1) & (y[j] == y[j]) & (y[j] != neg_inf<float>());
+          T sc[4];
+          if (greedy) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[j] = T(y[j]);
+          } else if constexpr (EPI == kEpiFilt32) {
+            const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), ci.rid);
+            sc[0] = T(y[0] * inv_tf) + T(gumbel_f32(w.w0));
+            sc[1] = T(y[1] * inv_tf) + T(gumbel_f32(w.w1));
+            sc[2] = T(y[2] * inv_tf) + T(gumbel_f32(w.w2));
+            sc[3] = T(y[3] * inv_tf) + T(gumbel_f32(w.w3));
+          } else {
+            const Words w0 = noise_words(a.key, (uint32_t)(i0 >> 1), ci.rid);
+            const Words w1 = noise_words(a.key, (uint32_t)(i0 >> 1) + 1u, ci.rid);
+            sc[0] = T(y[0]) * inv_t + T(gumbel_f64(w0.w0, w0.w1));
+            sc[1] = T(y[1]) * inv_t + T(gumbel_f64(w0.w2, w0.w3));
+            sc[2] = T(y[2]) * inv_t + T(gumbel_f64(w1.w0, w1.w1));
+            sc[3] = T(y[3]) * inv_t + T(gumbel_f64(w1.w2, w1.w3));
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int32_t i = (int32_t)(i0 + j);
+            // rows past the wave's last one and invalid logits enter as -inf,
+            // which never takes a place (no branch around the insert)
+            topk_insert(lm, li, ok[j] ? y[j] : neg_inf<float>(), i);
+            if (ok[j]) {
+              ++nv;
+              if (y[j] > mm) {
+                mz = mm == neg_inf<float>() ? 1.0f : mz * rel_mass(mm, y[j]) + 1.0f;
+                mm = y[j];
+              } else {
+                mz += rel_mass(y[j], mm);
+              }
+              if (sc[j] > bs) {  // increasing index order: ties keep the smaller
+                bs = sc[j];
+                bi = i;
+                by = y[j];
+              }
+            }
+          }
+        }
+        double zz = (double)mz;
+        // the column's running state (row group 0 only), then the other row
+        // groups' (lanes 16 and 32 apart)
+        auto merge_aux = [&](T os, int32_t oi, float oy, float om, double oz, uint32_t on) {
+          if (beats(os, oi, bs, bi)) {
+            bs = os;
+            bi = oi;
+            by = oy;
+          }
+          if (om > mm) {
+            zz = (mm == neg_inf<float>() ? 0.0 : zz * (double)rel_mass(mm, om)) + oz;
+            mm = om;
+          } else if (om != neg_inf<float>()) {
+            zz += oz * (double)rel_mass(om, mm);
+          }
+          nv += on;
+        };
+        {
+          float om[kFiltList];
+          int32_t oi[kFiltList];
+#pragma unroll
+          for (int j = 0; j < kFiltList; ++j) {
+            const Cand<float> o = grp == 0 ? flc[wave][16 * cb + col][j] : Cand<float>{neg_inf<float>(), kNoIndex};
+            om[j] = o.m;
+            oi[j] = o.idx;
+          }
+          merge_top(lm, li, om, oi);
+          if (grp == 0) {
+            const FiltAux o = fla[wave][16 * cb + col];
+            merge_aux(o.bs, o.bi, o.by, o.mm, o.zz, o.nv);
+          }
+#pragma unroll
+          for (int x = 16; x <= 32; x <<= 1) {
+#pragma unroll
+            for (int j = 0; j < kFiltList; ++j) {
+              om[j] = __shfl_xor(lm[j], x, 64);
+              oi[j] = __shfl_xor(li[j], x, 64);
+            }
+            merge_top(lm, li, om, oi);
+            const T os = __shfl_xor(bs, x, 64);
+            const int32_t obi = __shfl_xor(bi, x, 64);
+            const float oy = __shfl_xor(by, x, 64);
+            const float omm = __shfl_xor(mm, x, 64);
+            const double oz = __shfl_xor(zz, x, 64);
+            const uint32_t on = (uint32_t)__shfl_xor((int)nv, x, 64);
+            merge_aux(os, obi, oy, omm, oz, on);
+          }
+        }
+        if (grp == 0) {
+#pragma unroll
+          for (int j = 0; j < kFiltList; ++j) flc[wave][16 * cb + col][j] = Cand<float>{lm[j], li[j]};
+          fla[wave][16 * cb + col] = FiltAux{bs, by, bi, mm, nv, zz};
+        }
+      }
     } else if (EPI == kEpiStore || kFold) {
       const int32_t r1s = (int32_t)r1;  // V < 2^31
       // Per column: 1 / t (1 for greedy) and whether any column of the wave
@@ -1142,6 +1311,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           if (EPI == kEpiStore) {
             if (!col_ok[cb]) continue;
             const int64_t b = bt0 + 16 * cb + col;
+            if (a.row_flags != nullptr && a.row_flags[b] == 0u) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               if (i0 + j < r1) a.Y[b * V + i0 + j] = W8 ? y[j] * wsc[rb][j] : y[j];
@@ -1276,7 +1446,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           }
       }
     }
-    if (EPI != kEpiStore && !kTopK) {
+    if (EPI != kEpiStore && !kTopK && !kFilt) {
       // Lanes that share a column (the 4 row groups) -> one value per column,
       // merged into the wave's running best.
 #pragma unroll
@@ -1291,6 +1461,78 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   }
 
   if (EPI == kEpiStore) return;
+
+  if constexpr (kFilt) {
+    // Per column, its record: the kFiltList places among the 8 waves' lists
+    // (one candidate a lane: lane l holds place l % 8 of wave l / 8), lane r
+    // keeping place r; the waves' best scores, masses and counts merged by
+    // lanes 0-7.  Stage 2 is a launch of its own.
+    __syncthreads();
+    static_assert(kWaves * kFiltList == 64, "one candidate per lane");
+#pragma unroll 1
+    for (int c = wave; c < 16 * NB; c += kWaves) {
+      const int64_t b = bt0 + c;
+      Cand<float> it[1];
+      it[0] = flc[lane / kFiltList][c][lane % kFiltList];
+      Cand<float> pl = Cand<float>{neg_inf<float>(), kNoIndex};
+      float my = neg_inf<float>();
+      int32_t mi = kNoIndex;
+#pragma unroll 1
+      for (int r = 0; r < kFiltList; ++r) {
+        pl = next_place(it, r == 0, pl.m, pl.idx);
+        if (lane == r) {
+          my = pl.m;
+          mi = pl.idx;
+        }
+      }
+      const ColInfo ci = cols[c];
+      const float inv_tf = ci.mode == kGreedy ? 1.0f : 1.0f / ci.t;
+      auto rel_mass = [&](float y, float m) -> float {
+        if (m == __builtin_inff()) return y == m ? 1.0f : 0.0f;
+        return expf((y - m) * inv_tf);
+      };
+      FiltAux x = lane < kWaves ? fla[lane][c]
+                                : FiltAux{neg_inf<T>(), neg_inf<float>(), kNoIndex, neg_inf<float>(), 0u, 0.0};
+#pragma unroll
+      for (int o = 1; o < kWaves; o <<= 1) {
+        const T os = __shfl_xor(x.bs, o, 64);
+        const int32_t obi = __shfl_xor(x.bi, o, 64);
+        const float oy = __shfl_xor(x.by, o, 64);
+        const float om = __shfl_xor(x.mm, o, 64);
+        const double oz = __shfl_xor(x.zz, o, 64);
+        const uint32_t on = (uint32_t)__shfl_xor((int)x.nv, o, 64);
+        if (beats(os, obi, x.bs, x.bi)) {
+          x.bs = os;
+          x.bi = obi;
+          x.by = oy;
+        }
+        if (om > x.mm) {
+          x.zz = (x.mm == neg_inf<float>() ? 0.0 : x.zz * (double)rel_mass(x.mm, om)) + oz;
+          x.mm = om;
+        } else if (om != neg_inf<float>()) {
+          x.zz += oz * (double)rel_mass(om, x.mm);
+        }
+        x.nv += on;
+      }
+      if (b < B) {
+        FiltRec<T>* rec = reinterpret_cast<FiltRec<T>*>(static_cast<char*>(a.cand) +
+                                                        (b * a.nT + tile) * (int64_t)kFiltRecBytes);
+        if (lane < kFiltList) {
+          rec->ly[lane] = my;
+          rec->li[lane] = mi;
+        }
+        if (lane == 0) {
+          rec->bs = x.bs;
+          rec->by = x.by;
+          rec->bi = x.bi;
+          rec->mm = x.mm;
+          rec->nv = x.nv;
+          rec->zz = x.zz;
+        }
+      }
+    }
+    return;
+  }
 
   if constexpr (kTopK) {
     // Per column, its kTopKMax places among the 8 waves' running places
@@ -1400,6 +1642,304 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   if (tid == 0) clear_counter(a.counters + btile);
 }
 
+// ---------------------------------------------------------------------------
+// Filtered sampling, Stage 2: one wave per row resolves the row's kept set
+// from its tiles' records, with the filtered sampler's rules and arithmetic
+// over the same float32 logits (fs_filter.hip: top-k by value, top-p by
+// 64-bit fixed-point masses exp((y - M) / t) in units of 2^-40, min-p by
+// exp((y - M) / t) >= m, each cut keeping whole classes of equal logits),
+// then draws over the kept tokens.
+//
+// Every token above C (the largest 8th-listed logit among tiles with more
+// valid tokens than their list holds) is listed, so merging the sorted lists
+// (a wave argmax over the tiles' list heads per step) walks the row's logits
+// in exact descending order for as long as they stay above C.  A row is
+// resolved when every cut it needs lies above C, and every tile either lists
+// all its kept tokens (its last listed logit is not kept, or it has no more
+// tokens) or has its best-scoring token kept (then that token is its best
+// kept one).  Other rows are flagged for the exact fallback.  Top-p without
+// top-k takes the total mass from the tiles' float64 sums instead of the
+// filtered sampler's sum of per-token fixed-point masses.
+// ---------------------------------------------------------------------------
+constexpr int kFiltRowsPerBlock = 4;
+
+__device__ __forceinline__ uint32_t filt_order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <typename T>
+__global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(FusedArgs a) {
+  __shared__ float sly[kFiltRowsPerBlock][kMaxFusedTiles][kFiltList];
+  __shared__ int32_t sli[kFiltRowsPerBlock][kMaxFusedTiles][kFiltList];
+  constexpr int kQ = kMaxFusedTiles / 64;  // tiles per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t b = (int64_t)blockIdx.x * kFiltRowsPerBlock + wave;
+  if (b >= a.B) return;  // whole waves; nothing below waits on another wave
+  const int nT = a.nT;
+  const char* rbase = static_cast<const char*>(a.cand) + b * nT * (int64_t)kFiltRecBytes;
+
+  // This lane's tiles t = lane + 64 q: the record fields, the list in LDS.
+  float tm[kQ], tby[kQ];
+  uint32_t tn[kQ];
+  double tz[kQ];
+  T tbs[kQ];
+  int32_t tbi[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int t = lane + 64 * q;
+    tm[q] = neg_inf<float>();
+    tby[q] = neg_inf<float>();
+    tn[q] = 0u;
+    tz[q] = 0.0;
+    tbs[q] = neg_inf<T>();
+    tbi[q] = kNoIndex;
+    if (t < nT) {
+      const FiltRec<T>* r = reinterpret_cast<const FiltRec<T>*>(rbase + (int64_t)t * kFiltRecBytes);
+      tm[q] = r->mm;
+      tn[q] = r->nv;
+      tz[q] = r->zz;
+      tbs[q] = r->bs;
+      tby[q] = r->by;
+      tbi[q] = r->bi;
+#pragma unroll
+      for (int e = 0; e < kFiltList; ++e) {
+        sly[wave][t][e] = r->ly[e];
+        sli[wave][t][e] = r->li[e];
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // The row's largest valid logit, its number of valid logits, and C.
+  float M = neg_inf<float>(), C = neg_inf<float>();
+  uint32_t n_valid = 0u;
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    M = fmaxf(M, tm[q]);
+    n_valid += tn[q];
+    if (tn[q] > (uint32_t)kFiltList) C = fmaxf(C, sly[wave][lane + 64 * q][kFiltList - 1]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    M = fmaxf(M, __shfl_xor(M, o, 64));
+    C = fmaxf(C, __shfl_xor(C, o, 64));
+    n_valid += (uint32_t)__shfl_xor((int)n_valid, o, 64);
+  }
+  if (n_valid == 0u) {
+    if (lane == 0) a.out[b] = -1;
+    return;
+  }
+  const float t = a.temp[b];
+  const bool greedy = !(t > 0.0f);
+  if (greedy) {
+    // the argmax: the smallest index among the tiles whose largest logit is M
+    // (each list holds its tile's smallest such index first)
+    int32_t bi = kNoIndex;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int tt = lane + 64 * q;
+      if (tt < nT && tn[q] > 0u && sly[wave][tt][0] == M) bi = min(bi, sli[wave][tt][0]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) bi = min(bi, __shfl_xor(bi, o, 64));
+    if (lane == 0) a.out[b] = (int64_t)bi;
+    return;
+  }
+  const T inv_t = T(1) / T(t);
+  const float inv_tf = 1.0f / t;
+  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
+  const int32_t top_k = a.top_k ? a.top_k[b] : 0;
+  const float top_p = a.top_p ? a.top_p[b] : 1.0f;
+  const float min_p = a.min_p ? a.min_p[b] : 0.0f;
+  // NaN parameters compare false: their filters are off.
+  const bool use_k = top_k > 0 && (int64_t)top_k < (int64_t)n_valid;
+  const bool use_p = top_p < 1.0f;
+  bool use_m = min_p > 0.0f;
+  auto mass_of = [&](float y) -> float {
+    if (M == __builtin_inff()) return y == M ? 1.0f : 0.0f;
+    return expf((y - M) * inv_tf);
+  };
+  auto mass_fixed = [&](float y) -> unsigned long long {
+    return (unsigned long long)(mass_of(y) * 0x1p40f);
+  };
+
+  // The merge walk: per lane, a cursor into each of its tiles' lists.
+  int cur[kQ];
+  float hy[kQ];
+  int32_t hix[kQ];
+  auto reset = [&]() {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int tt = lane + 64 * q;
+      cur[q] = 0;
+      hy[q] = tt < nT ? sly[wave][tt][0] : neg_inf<float>();
+      hix[q] = tt < nT ? sli[wave][tt][0] : kNoIndex;
+    }
+  };
+  auto peek = [&]() -> Cand<float> {
+    float m = neg_inf<float>();
+    int32_t i = kNoIndex;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const bool take = beats_nb(hy[q], hix[q], m, i);
+      m = take ? hy[q] : m;
+      i = take ? hix[q] : i;
+    }
+    wave_argmax_xor(m, i, 0);
+    return Cand<float>{m, i};
+  };
+  auto advance = [&](const Cand<float>& c) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+      if (hix[q] == c.idx && hy[q] == c.m) {
+        const int tt = lane + 64 * q;
+        ++cur[q];
+        hy[q] = cur[q] < kFiltList ? sly[wave][tt][cur[q]] : neg_inf<float>();
+        hix[q] = cur[q] < kFiltList ? sli[wave][tt][cur[q]] : kNoIndex;
+      }
+  };
+
+  bool unresolved = false;
+  uint32_t key_k = 0u, key_p = 0u;
+  unsigned long long z_k = 0ull;  // fixed-point mass of the top-k survivors
+  if (use_k) {
+    if ((int64_t)top_k > (int64_t)nT * kFiltList) {
+      unresolved = true;
+    } else {
+      reset();
+      float v = neg_inf<float>();
+      for (int j = 0; j < top_k; ++j) {
+        const Cand<float> c = peek();
+        if (!(c.m > C)) {
+          unresolved = true;
+          break;
+        }
+        v = c.m;
+        z_k += mass_fixed(v);
+        advance(c);
+      }
+      if (!unresolved) {
+        // the rest of the k-th value's class (all above C, so all listed)
+        for (;;) {
+          const Cand<float> c = peek();
+          if (!(c.m == v)) break;
+          z_k += mass_fixed(v);
+          advance(c);
+        }
+        key_k = filt_order_key(v);
+      }
+    }
+  }
+  if (use_p && !unresolved) {
+    if (!(top_p > 0.0f)) {
+      key_p = filt_order_key(M);
+    } else {
+      double target;
+      if (use_k) {
+        target = (double)top_p * (double)z_k;
+      } else {
+        double zt = 0.0;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+          if (tn[q] > 0u) zt += tz[q] * (double)mass_of(tm[q]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) zt += __shfl_xor(zt, o, 64);
+        target = (double)top_p * (zt * 0x1p40);
+      }
+      // classes of equal logits in descending order: kept while the mass of
+      // the strictly larger survivors is below the target
+      reset();
+      unsigned long long above = 0ull;
+      float last = M;
+      for (;;) {
+        Cand<float> c = peek();
+        if (c.m == neg_inf<float>()) break;                         // every token walked
+        if (use_k && filt_order_key(c.m) < key_k) break;            // past the survivors
+        if (!(c.m > C)) {
+          unresolved = true;
+          break;
+        }
+        if (!((double)above < target)) break;
+        last = c.m;
+        unsigned long long cls = 0ull;
+        do {
+          cls += mass_fixed(c.m);
+          advance(c);
+          c = peek();
+        } while (c.m == last);
+        above += cls;
+      }
+      key_p = filt_order_key(last);
+    }
+  }
+  uint32_t kappa = key_k > key_p ? key_k : key_p;
+  if (use_m && !(min_p < 1.0f)) {
+    const uint32_t km = filt_order_key(M);
+    kappa = kappa > km ? kappa : km;
+    use_m = false;
+  }
+
+  // The draw over the kept tokens: valid, key >= kappa, and the min-p test.
+  T bm = neg_inf<T>();
+  int32_t bi = kNoIndex;
+  if (!unresolved) {
+    auto kept = [&](float y) -> bool {
+      return (y == y) & (y != neg_inf<float>()) && filt_order_key(y) >= kappa &&
+             (!use_m || mass_of(y) >= min_p);
+    };
+    auto score1 = [&](float y, int32_t i) -> T {
+      if constexpr (std::is_same<T, float>::value) {
+        const Words w = noise_words(a.key, (uint32_t)i >> 2, rid);
+        const uint32_t q = (uint32_t)i & 3u;
+        const uint32_t word = q == 0 ? w.w0 : (q == 1 ? w.w1 : (q == 2 ? w.w2 : w.w3));
+        return T(y * inv_tf) + T(gumbel_f32(word));
+      } else {
+        const Words w = noise_words(a.key, (uint32_t)i >> 1, rid);
+        return (i & 1) ? T(y) * inv_t + T(gumbel_f64(w.w2, w.w3))
+                       : T(y) * inv_t + T(gumbel_f64(w.w0, w.w1));
+      }
+    };
+    bool lost = false;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int tt = lane + 64 * q;
+      if (tt >= nT || tn[q] == 0u) continue;
+      if (tn[q] <= (uint32_t)kFiltList || !kept(sly[wave][tt][kFiltList - 1])) {
+        for (int e = 0; e < kFiltList; ++e) {
+          const float y = sly[wave][tt][e];
+          if (!kept(y)) break;  // the list is sorted: the rest is not kept
+          const int32_t i = sli[wave][tt][e];
+          const T sv = score1(y, i);
+          if (beats(sv, i, bm, bi)) {
+            bm = sv;
+            bi = i;
+          }
+        }
+      } else if (kept(tby[q])) {
+        if (beats(tbs[q], tbi[q], bm, bi)) {
+          bm = tbs[q];
+          bi = tbi[q];
+        }
+      } else {
+        lost = true;
+      }
+    }
+    unresolved = __builtin_amdgcn_ballot_w64(lost) != 0;
+    wave_argmax_xor(bm, bi, 0);
+  }
+  if (lane == 0) {
+    if (unresolved) {
+      a.row_flags[b] = 1u;
+      __hip_atomic_fetch_add(a.flag_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      a.out[b] = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
+    }
+  }
+}
+
 // Kernels that fold the float32 noise fold the bias with it (a bias
 // template); the others read the bias after the k-loop.
 template <int NB, int WF>
@@ -1436,6 +1976,21 @@ hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream)
       if constexpr ((NB == 1 || NB == 4) && BF)
         launch((fused_stage1_kernel<NB, kEpiTopK64, false, kWBf16>), grid,
                            dim3(kThreads), 0, stream, a);
+      else
+        return hipErrorInvalidValue;
+      break;
+    case kEpiFilt32:
+      // Filtered sampling: tiles of at most 64 columns, bf16 weights.
+      if constexpr (NB <= 4 && BF)
+        launch((fused_stage1_kernel<NB, kEpiFilt32, false, kWBf16>), grid, dim3(kThreads), 0,
+               stream, a);
+      else
+        return hipErrorInvalidValue;
+      break;
+    case kEpiFilt64:
+      if constexpr ((NB == 1 || NB == 4) && BF)
+        launch((fused_stage1_kernel<NB, kEpiFilt64, false, kWBf16>), grid, dim3(kThreads), 0,
+               stream, a);
       else
         return hipErrorInvalidValue;
       break;
@@ -1517,6 +2072,35 @@ hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) 
   if (a.W8) return launch_w<kWFp8>(a, epi, grid, nb, stream);
   if (nb > 4) return launch_wide(a, epi, grid, stream);
   return launch_w<kWBf16>(a, epi, grid, nb, stream);
+}
+
+int fused_filtered_column_blocks(int64_t B, bool fp64) {
+  int nb = fused_column_blocks(B, true, false);  // tiles of at most 64 columns
+  if (fp64 && nb > 1) nb = 4;                    // float64 scores: 16 or 64 columns
+  return nb;
+}
+
+hipError_t launch_fused_filtered(const FusedArgs& a, bool fp64, const FilterArgs& fa,
+                                 hipStream_t stream) {
+  const int nb = fused_filtered_column_blocks(a.B, fp64);
+  const dim3 grid((unsigned)a.nT, (unsigned)((a.B + 16 * nb - 1) / (16 * nb)));
+  hipError_t e = launch_w<kWBf16>(a, fp64 ? kEpiFilt64 : kEpiFilt32, grid, nb, stream);
+  if (e != hipSuccess) return e;
+  const dim3 g2((unsigned)((a.B + kFiltRowsPerBlock - 1) / kFiltRowsPerBlock));
+  if (fp64)
+    launch(filt_stage2_kernel<double>, g2, dim3(64 * kFiltRowsPerBlock), 0, stream, a);
+  else
+    launch(filt_stage2_kernel<float>, g2, dim3(64 * kFiltRowsPerBlock), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // The fallback: the same tiles' logits of the flagged rows (the store
+  // epilogue returns at once when none is flagged), then the filtered
+  // sampler over them (one workgroup per row, the others return at once).
+  FusedArgs s = a;
+  s.Y = fa.X == nullptr ? nullptr : const_cast<float*>(fa.X);
+  e = launch_w<kWBf16>(s, kEpiStore, grid, nb, stream);
+  if (e != hipSuccess) return e;
+  return launch_logits_filtered(fa, fp64, stream);
 }
 
 int64_t fused_wave_span_bytes(int64_t V, int64_t D, int nT, int elem_bytes) {

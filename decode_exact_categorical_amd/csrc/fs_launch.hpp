@@ -54,6 +54,16 @@ struct FusedArgs {
   float* Y;    // [B, V] (store epilogue only)
   int bias_vec4;  // bias rows are 16-byte aligned
   int k;          // Gumbel-top-k: places per row (out is [B, k]; cand is [B, nT, kTopKMax])
+  // Filtered sampling (kEpiFilt32/64): per-row filters (each may be null:
+  // off), cand is [B, nT] FiltRec records; rows Stage 2 cannot resolve from
+  // the records get row_flags[b] = 1 and are counted on *flag_count; the
+  // store epilogue then writes only those rows' logits (skipping the whole
+  // launch when *flag_count is 0).
+  const int32_t* top_k;
+  const float* top_p;
+  const float* min_p;
+  uint32_t* row_flags;   // [B], zero between calls
+  uint32_t* flag_count;  // one word, zero between calls
 };
 
 enum FusedEpilogue {
@@ -61,8 +71,39 @@ enum FusedEpilogue {
   kEpiSample64 = 1,  // one draw per row, float64 noise
   kEpiStore = 2,     // logits to Y (test hook)
   kEpiTopK32 = 3,    // Gumbel-top-k, float32 noise
-  kEpiTopK64 = 4     // Gumbel-top-k, float64 noise
+  kEpiTopK64 = 4,    // Gumbel-top-k, float64 noise
+  kEpiFilt32 = 5,    // filtered sampling, float32 noise
+  kEpiFilt64 = 6     // filtered sampling, float64 noise
 };
+
+// What the filtered epilogue keeps of one (row, vocabulary tile) for Stage 2:
+// the tile's kFiltList largest valid logits (larger first, equal logits in
+// increasing index order; -inf / kNoIndex past the tile's valid tokens), its
+// best perturbed score over all its valid tokens with that token's index and
+// logit, its largest valid logit mm with zz = sum of exp((y - mm) / t) over
+// its valid tokens, and its number of valid tokens.
+constexpr int kFiltList = 8;
+template <typename T>
+struct FiltRec {
+  float ly[kFiltList];
+  int32_t li[kFiltList];
+  T bs;
+  float by;
+  int32_t bi;
+  float mm;
+  uint32_t nv;
+  double zz;
+};
+constexpr int kFiltRecBytes = 128;  // record stride in the workspace
+static_assert(sizeof(FiltRec<double>) <= kFiltRecBytes, "a record fits its stride");
+// Fused filtered sampling: Stage 1 with the filtered epilogue, Stage 2 (one
+// wave per row), then the exact fallback for the rows Stage 2 flags: the same
+// matmul storing those rows' logits to Y, and the filtered sampler over them
+// (`fa` carries its arguments; its X is Y).
+hipError_t launch_fused_filtered(const FusedArgs& a, bool fp64, const struct FilterArgs& fa,
+                                 hipStream_t stream);
+// Column blocks the filtered epilogue runs with for a batch of B rows.
+int fused_filtered_column_blocks(int64_t B, bool fp64);
 
 // Number of vocabulary tiles (workgroups along x) the fused kernel uses: one
 // per CU, at most kMaxFusedTiles (Stage 2 reads a row's candidates in
@@ -122,6 +163,10 @@ struct FilterArgs {
   // Filtered logits (launch_filter_logits): [B, V] out; vec4 then also
   // covers this buffer.
   float* Y;
+  // Only the rows with row_flags[b] != 0 (null: every row), each clearing its
+  // flag when done; workgroup 0 clears *flag_count.  One workgroup per row.
+  uint32_t* row_flags;
+  uint32_t* flag_count;
 };
 // Split rows up to this many run chunks and merge in one launch (the merge in
 // each row's last workgroup): at B <= 8 that saves the second launch's gap;

@@ -259,6 +259,42 @@ fs_status fs_sample_logits_filtered(const float *logits, int64_t B, int64_t V,
                                     size_t workspace_bytes, fs_stream_t stream);
 
 /*
+ * Filtered exact sampling fused into the LM head [SD sample pipeline,
+ * "Semantics"; FS "core method", "algorithm details"]: per row, exactly the
+ * draw fs_sample_logits_filtered makes over the float32 logits y = H W^T that
+ * the fused kernels form (fs_debug_logits), without writing those logits:
+ *   H, W, B, D, V  as for fs_sample_fused (bf16, no bias), B <= 65535
+ *   temp, top_k, top_p, min_p, seed, offset, out_idx, row_ids  as for
+ *            fs_sample_logits_filtered (each filter array may be NULL: off)
+ *   flags    host: 0 or FS_FP64_NOISE
+ *   workspace, workspace_bytes  device, 256-byte aligned, at least
+ *            fs_workspace_bytes_fused_filtered(B, V) bytes, zeroed once before
+ *            first use (every call leaves its counters and flags at zero;
+ *            calls sharing one workspace are serialised by their stream)
+ * Stage 1 keeps, per row and vocabulary tile, the tile's 8 largest logits,
+ * its best perturbed score, its mass sum exp((y - m) / t) relative to its
+ * largest logit m and its count of valid logits [FS Stage 1; the grouped
+ * form's per-group masses, "technical novelty"].  Stage 2 walks the tiles'
+ * sorted lists in descending order to place the top-k, top-p and min-p cuts
+ * and draws over the kept tokens.  A row whose cuts or draw reach below what
+ * the lists hold (kept sets wider than the tiles' lists, e.g. top-p alone
+ * over a flat row) is resolved exactly by a fallback in the same call: the
+ * fused matmul again, storing only those rows' logits into the workspace,
+ * and the filtered sampler over them.  Rows with top-k resolve with the
+ * filtered sampler's fixed-point masses, so they draw what it draws bit for
+ * bit; rows with top-p but no top-k take the total mass from the tiles'
+ * float64 sums (a decision within about 1e-6 relative of its boundary may
+ * differ).  Four launches on `stream`.
+ */
+size_t fs_workspace_bytes_fused_filtered(int64_t B, int64_t V);
+fs_status fs_sample_fused_filtered(const fs_bf16 *H, const fs_bf16 *W, int64_t B, int64_t D,
+                                   int64_t V, const float *temp, const int32_t *top_k,
+                                   const float *top_p, const float *min_p, uint64_t seed,
+                                   uint64_t offset, int64_t *out_idx, const uint32_t *row_ids,
+                                   uint32_t flags, void *workspace, size_t workspace_bytes,
+                                   fs_stream_t stream);
+
+/*
  * Repetition penalty [SD sample pipeline and Semantics: the penalty comes
  * before the temperature]: out_logits = logits, except that every token
  * occurring in row b's previous tokens has its logit y replaced by

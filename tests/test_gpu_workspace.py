@@ -146,3 +146,30 @@ def test_one_workspace_serves_every_entry_point(dev):
     torch.cuda.synchronize()
     ref, gap, _ = oracle.sample_fused(H, W, t2.numpy(), seed=7, offset=8)
     check_index_parity(got.cpu().numpy(), ref, gap, "fused after the other entry points")
+
+
+def test_fused_filtered_shares_the_workspace(dev):
+    """The fused filtered sampler keeps its fallback flags in the counter region
+    (word 0 their count, words 1 .. B the rows') and its records and fallback
+    logits after it: after it runs (fallback rows included) the counters are
+    zero and the other entry points draw what the oracle draws; and after them
+    it still matches the materialised path."""
+    say("fused filtered (with fallback rows) -> fused -> fused filtered, one workspace")
+    B, D, V = 12, 256, 6000
+    H = synthetic.hidden(B, D, seed=90)
+    W = synthetic.weight(V, D, std=0.004, seed=91)       # flat rows: top-p alone falls back
+    t = torch.full((B,), 1.0)
+    Hd, Wd, td = H.to(dev), W.to(dev), t.to(dev)
+    fs.sample_fused_filtered(Hd, Wd, td, top_p=0.9, seed=1, offset=1)
+    torch.cuda.synchronize()
+    ws = fs._workspace(dev, 0)
+    assert int(ws[:4 * (B + 1)].view(torch.int32).abs().sum().item()) == 0
+    t2 = synthetic.temperatures(B, seed=92)
+    got = fs.sample_fused(Hd, Wd, t2.to(dev), seed=7, offset=8)
+    torch.cuda.synchronize()
+    ref, gap, _ = oracle.sample_fused(H, W, t2.numpy(), seed=7, offset=8)
+    check_index_parity(got.cpu().numpy(), ref, gap, "fused after the fused filtered sampler")
+    a = fs.sample_fused_filtered(Hd, Wd, td, top_p=0.9, seed=2, offset=3)
+    Y = fs.debug_logits(Hd, Wd)
+    b = fs.sample_logits_filtered(Y, td, top_p=0.9, seed=2, offset=3)
+    assert torch.equal(a, b)
