@@ -160,7 +160,7 @@ def _need(t: torch.Tensor, name: str, dtype, device, shape=None):
 
 def _temp_tensor(temp, B: int, device) -> torch.Tensor:
     if isinstance(temp, (int, float)):
-        return torch.full((B,), float(temp), dtype=torch.float32, device=device)
+        return _constant(float(temp), torch.float32, B, device)
     _need(temp, "temp", torch.float32, device, (B,))
     return temp
 
@@ -353,13 +353,30 @@ def sample_logits(logits: torch.Tensor, temp, *, seed: int, offset: int,
     return out
 
 
+_constants: dict = {}
+
+
+def _constant(v, dtype, B: int, device) -> torch.Tensor:
+    """A [B] tensor holding the scalar v on `device`, made once per (value,
+    dtype, B, device) and reused (the library only reads it), so a scalar
+    parameter costs no fill kernel per call."""
+    key = (float(v), dtype, B, device.index)
+    t = _constants.get(key)
+    if t is None:
+        if len(_constants) > 256:
+            _constants.clear()
+        t = torch.full((B,), v, dtype=dtype, device=device)
+        _constants[key] = t
+    return t
+
+
 def _filter_param(v, name: str, dtype, B: int, device):
     """A per-row filter parameter: None (off), a Python scalar for every row, or
     a [B] tensor of `dtype` on the device."""
     if v is None:
         return None
     if isinstance(v, (int, float)):
-        return torch.full((B,), v, dtype=dtype, device=device)
+        return _constant(v, dtype, B, device)
     _need(v, name, dtype, device, (B,))
     return v
 

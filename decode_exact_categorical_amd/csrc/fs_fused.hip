@@ -160,7 +160,7 @@ struct Pipeline {
   static constexpr bool late_noise = EPI == kEpiSample64 || EPI == kEpiTopK32 || EPI == kEpiTopK64 ||
                                      EPI == kEpiFilt32 || EPI == kEpiFilt64;
   static constexpr bool wide = NB > 4;
-  static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || late_noise);
+  static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || (late_noise && EPI != kEpiFilt32));
   static constexpr bool ring1 = !narrow && !wide && NB >= 3 && !wide_extra;
   static constexpr int row_blocks = wide ? 2 : ((NB <= 2 || ring1) ? 5 : 3);
   static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || late_noise);
@@ -1650,16 +1650,20 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 // exp((y - M) / t) >= m, each cut keeping whole classes of equal logits),
 // then draws over the kept tokens.
 //
-// Every token above C (the largest 8th-listed logit among tiles with more
-// valid tokens than their list holds) is listed, so merging the sorted lists
-// (a wave argmax over the tiles' list heads per step) walks the row's logits
-// in exact descending order for as long as they stay above C.  A row is
-// resolved when every cut it needs lies above C, and every tile either lists
-// all its kept tokens (its last listed logit is not kept, or it has no more
-// tokens) or has its best-scoring token kept (then that token is its best
-// kept one).  Other rows are flagged for the exact fallback.  Top-p without
-// top-k takes the total mass from the tiles' float64 sums instead of the
-// filtered sampler's sum of per-token fixed-point masses.
+// The lists hold every token above C (the largest last-listed logit among
+// tiles with more valid tokens than their list), so any count or mass over
+// "the tokens above x" is exact for x >= C.  Each lane holds its tiles' list
+// entries as order-preserving keys.  The k-th largest key is found bit by bit
+// from the top (the largest x with at least k keys >= x: a count per step),
+// and the top-p cut likewise (the largest x whose strictly larger survivors
+// carry at least p of the mass: a 64-bit mass sum per step; the lowest kept
+// class is the smallest survivor key above it).  A row is resolved when each
+// cut it needs lies above C, and every tile either lists all its kept tokens
+// (its last listed logit is not kept, or it has no more tokens) or has its
+// best-scoring token kept (then that token is its best kept one).  Other rows
+// are flagged for the exact fallback.  Top-p without top-k takes the total
+// mass from the tiles' float64 sums instead of the filtered sampler's sum of
+// per-token fixed-point masses.
 // ---------------------------------------------------------------------------
 constexpr int kFiltRowsPerBlock = 4;
 
@@ -1668,18 +1672,116 @@ __device__ __forceinline__ uint32_t filt_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Sums over a whole wave64 by DPP exchanges inside each row of 16 lanes
+// (xor 1, xor 2, then the half-row and row mirrors, each pairing groups that
+// already hold their sums) and the four rows' sums read back with readlane:
+// no LDS round trip.  The result is wave-uniform.
+template <int kCtrl>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  return (unsigned long long)dpp_u32<kCtrl>((uint32_t)v) |
+         ((unsigned long long)dpp_u32<kCtrl>((uint32_t)(v >> 32)) << 32);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp_u32<0xb1>(v);
+  v += dpp_u32<0x4e>(v);
+  v += dpp_u32<0x141>(v);
+  v += dpp_u32<0x140>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+  v += dpp_u64<0xb1>(v);
+  v += dpp_u64<0x4e>(v);
+  v += dpp_u64<0x141>(v);
+  v += dpp_u64<0x140>(v);
+  unsigned long long r = 0ull;
+#pragma unroll
+  for (int row = 0; row < 4; ++row)
+    r += (unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row) |
+         ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row) << 32);
+  return r;
+}
+
+// Wave-wide max / min by the same DPP pattern (float max, int32 min).
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_val<0xb1>(v));
+  v = fmaxf(v, dpp_val<0x4e>(v));
+  v = fmaxf(v, dpp_val<0x141>(v));
+  v = fmaxf(v, dpp_val<0x140>(v));
+  return fmaxf(fmaxf(lane_val(v, 0), lane_val(v, 16)), fmaxf(lane_val(v, 32), lane_val(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0xb1>(v));
+  v = min(v, dpp_u32<0x4e>(v));
+  v = min(v, dpp_u32<0x141>(v));
+  v = min(v, dpp_u32<0x140>(v));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
+  v = min(v, (int32_t)dpp_u32<0xb1>((uint32_t)v));
+  v = min(v, (int32_t)dpp_u32<0x4e>((uint32_t)v));
+  v = min(v, (int32_t)dpp_u32<0x141>((uint32_t)v));
+  v = min(v, (int32_t)dpp_u32<0x140>((uint32_t)v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// The largest x with at least k of the wave's keys >= x (0 if fewer than k
+// valid keys), found bit by bit from the top with ballot counts.
+template <int N>
+__device__ __forceinline__ uint32_t filt_kth_key(const uint32_t (&k_)[N], uint32_t k) {
+  uint32_t x = 0u;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t tx = x | (1u << bit);
+    uint32_t c = 0u;  // wave-uniform
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      c += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(k_[e] >= tx));
+    if (c >= k) x = tx;
+  }
+  return x;
+}
+
+// The largest x whose strictly larger keys of the wave carry a mass sum that
+// is not below target (as float64), found bit by bit from the top.
+template <int N>
+__device__ __forceinline__ uint32_t filt_mass_cut(const uint32_t (&k_)[N],
+                                                  const unsigned long long (&m_)[N],
+                                                  double target) {
+  uint32_t x = 0u;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t tx = x | (1u << bit);
+    unsigned long long g = 0ull;
+#pragma unroll
+    for (int e = 0; e < N; ++e) g += k_[e] > tx ? m_[e] : 0ull;
+    if (!((double)wave_sum_u64(g) < target)) x = tx;
+  }
+  return x;
+}
+
 template <typename T>
 __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(FusedArgs a) {
-  __shared__ float sly[kFiltRowsPerBlock][kMaxFusedTiles][kFiltList];
-  __shared__ int32_t sli[kFiltRowsPerBlock][kMaxFusedTiles][kFiltList];
   constexpr int kQ = kMaxFusedTiles / 64;  // tiles per lane
+  constexpr int kE = kQ * kFiltList;       // list entries per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t b = (int64_t)blockIdx.x * kFiltRowsPerBlock + wave;
   if (b >= a.B) return;  // whole waves; nothing below waits on another wave
   const int nT = a.nT;
   const char* rbase = static_cast<const char*>(a.cand) + b * nT * (int64_t)kFiltRecBytes;
+  // the row's parameters, requested with the records (one round trip)
+  const float t = a.temp[b];
+  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
+  const int32_t top_k = a.top_k ? a.top_k[b] : 0;
+  const float top_p = a.top_p ? a.top_p[b] : 1.0f;
+  const float min_p = a.min_p ? a.min_p[b] : 0.0f;
 
-  // This lane's tiles t = lane + 64 q: the record fields, the list in LDS.
+  // This lane's tiles t = lane + 64 q: list entries (entry q * 8 + e) and
+  // the record fields.  Tiles past nT hold nothing (-inf entries).
+  float ey[kE];
+  int32_t ei[kE];
   float tm[kQ], tby[kQ];
   uint32_t tn[kQ];
   double tz[kQ];
@@ -1688,30 +1790,27 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     const int t = lane + 64 * q;
-    tm[q] = neg_inf<float>();
-    tby[q] = neg_inf<float>();
-    tn[q] = 0u;
-    tz[q] = 0.0;
-    tbs[q] = neg_inf<T>();
-    tbi[q] = kNoIndex;
-    if (t < nT) {
-      const FiltRec<T>* r = reinterpret_cast<const FiltRec<T>*>(rbase + (int64_t)t * kFiltRecBytes);
-      tm[q] = r->mm;
-      tn[q] = r->nv;
-      tz[q] = r->zz;
-      tbs[q] = r->bs;
-      tby[q] = r->by;
-      tbi[q] = r->bi;
+    const bool live = t < nT;
+    const FiltRec<T>* r =
+        reinterpret_cast<const FiltRec<T>*>(rbase + (int64_t)(live ? t : 0) * kFiltRecBytes);
+    const float4 y0 = *reinterpret_cast<const float4*>(&r->ly[0]);
+    const float4 y1 = *reinterpret_cast<const float4*>(&r->ly[4]);
+    const int4 i0 = *reinterpret_cast<const int4*>(&r->li[0]);
+    const int4 i1 = *reinterpret_cast<const int4*>(&r->li[4]);
+    const float yy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+    const int32_t ii[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-      for (int e = 0; e < kFiltList; ++e) {
-        sly[wave][t][e] = r->ly[e];
-        sli[wave][t][e] = r->li[e];
-      }
+    for (int e = 0; e < kFiltList; ++e) {
+      ey[q * kFiltList + e] = live ? yy[e] : neg_inf<float>();
+      ei[q * kFiltList + e] = live ? ii[e] : kNoIndex;
     }
+    tm[q] = live ? r->mm : neg_inf<float>();
+    tn[q] = live ? r->nv : 0u;
+    tz[q] = live ? r->zz : 0.0;
+    tbs[q] = live ? r->bs : neg_inf<T>();
+    tby[q] = live ? r->by : neg_inf<float>();
+    tbi[q] = live ? r->bi : kNoIndex;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // The row's largest valid logit, its number of valid logits, and C.
   float M = neg_inf<float>(), C = neg_inf<float>();
@@ -1720,40 +1819,28 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
   for (int q = 0; q < kQ; ++q) {
     M = fmaxf(M, tm[q]);
     n_valid += tn[q];
-    if (tn[q] > (uint32_t)kFiltList) C = fmaxf(C, sly[wave][lane + 64 * q][kFiltList - 1]);
+    if (tn[q] > (uint32_t)kFiltList) C = fmaxf(C, ey[q * kFiltList + kFiltList - 1]);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    M = fmaxf(M, __shfl_xor(M, o, 64));
-    C = fmaxf(C, __shfl_xor(C, o, 64));
-    n_valid += (uint32_t)__shfl_xor((int)n_valid, o, 64);
-  }
+  M = wave_max_f32(M);
+  C = wave_max_f32(C);
+  n_valid = wave_sum_u32(n_valid);
   if (n_valid == 0u) {
     if (lane == 0) a.out[b] = -1;
     return;
   }
-  const float t = a.temp[b];
-  const bool greedy = !(t > 0.0f);
-  if (greedy) {
-    // the argmax: the smallest index among the tiles whose largest logit is M
+  if (!(t > 0.0f)) {
+    // greedy: the smallest index among the tiles whose largest logit is M
     // (each list holds its tile's smallest such index first)
     int32_t bi = kNoIndex;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int tt = lane + 64 * q;
-      if (tt < nT && tn[q] > 0u && sly[wave][tt][0] == M) bi = min(bi, sli[wave][tt][0]);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) bi = min(bi, __shfl_xor(bi, o, 64));
+    for (int q = 0; q < kQ; ++q)
+      if (tn[q] > 0u && ey[q * kFiltList] == M) bi = min(bi, ei[q * kFiltList]);
+    bi = wave_min_i32(bi);
     if (lane == 0) a.out[b] = (int64_t)bi;
     return;
   }
   const T inv_t = T(1) / T(t);
   const float inv_tf = 1.0f / t;
-  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
-  const int32_t top_k = a.top_k ? a.top_k[b] : 0;
-  const float top_p = a.top_p ? a.top_p[b] : 1.0f;
-  const float min_p = a.min_p ? a.min_p[b] : 0.0f;
   // NaN parameters compare false: their filters are off.
   const bool use_k = top_k > 0 && (int64_t)top_k < (int64_t)n_valid;
   const bool use_p = top_p < 1.0f;
@@ -1765,115 +1852,122 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
   auto mass_fixed = [&](float y) -> unsigned long long {
     return (unsigned long long)(mass_of(y) * 0x1p40f);
   };
-
-  // The merge walk: per lane, a cursor into each of its tiles' lists.
-  int cur[kQ];
-  float hy[kQ];
-  int32_t hix[kQ];
-  auto reset = [&]() {
+  // Keys of the entries (invalid entries: 0, below every valid key).
+  uint32_t ek[kE];
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int tt = lane + 64 * q;
-      cur[q] = 0;
-      hy[q] = tt < nT ? sly[wave][tt][0] : neg_inf<float>();
-      hix[q] = tt < nT ? sli[wave][tt][0] : kNoIndex;
-    }
-  };
-  auto peek = [&]() -> Cand<float> {
-    float m = neg_inf<float>();
-    int32_t i = kNoIndex;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const bool take = beats_nb(hy[q], hix[q], m, i);
-      m = take ? hy[q] : m;
-      i = take ? hix[q] : i;
-    }
-    wave_argmax_xor(m, i, 0);
-    return Cand<float>{m, i};
-  };
-  auto advance = [&](const Cand<float>& c) {
-#pragma unroll
-    for (int q = 0; q < kQ; ++q)
-      if (hix[q] == c.idx && hy[q] == c.m) {
-        const int tt = lane + 64 * q;
-        ++cur[q];
-        hy[q] = cur[q] < kFiltList ? sly[wave][tt][cur[q]] : neg_inf<float>();
-        hix[q] = cur[q] < kFiltList ? sli[wave][tt][cur[q]] : kNoIndex;
-      }
-  };
+  for (int e = 0; e < kE; ++e)
+    ek[e] = (ey[e] == ey[e]) & (ey[e] != neg_inf<float>()) ? filt_order_key(ey[e]) : 0u;
+  const uint32_t keyC = C == neg_inf<float>() ? 0u : filt_order_key(C);
 
   bool unresolved = false;
   uint32_t key_k = 0u, key_p = 0u;
-  unsigned long long z_k = 0ull;  // fixed-point mass of the top-k survivors
-  if (use_k) {
-    if ((int64_t)top_k > (int64_t)nT * kFiltList) {
-      unresolved = true;
-    } else {
-      reset();
-      float v = neg_inf<float>();
-      for (int j = 0; j < top_k; ++j) {
-        const Cand<float> c = peek();
-        if (!(c.m > C)) {
-          unresolved = true;
-          break;
-        }
-        v = c.m;
-        z_k += mass_fixed(v);
-        advance(c);
-      }
-      if (!unresolved) {
-        // the rest of the k-th value's class (all above C, so all listed)
-        for (;;) {
-          const Cand<float> c = peek();
-          if (!(c.m == v)) break;
-          z_k += mass_fixed(v);
-          advance(c);
-        }
-        key_k = filt_order_key(v);
-      }
+  // Candidates: the entries the cuts can involve.  With top-k, every entry at
+  // or above the k-th largest tile maximum (at least k tokens reach it, so
+  // the k-th largest logit does); without it, every entry above C (a top-p cut
+  // below C is not resolved anyway).  Up to kCand of them go to this wave's
+  // LDS, kCand / 64 a lane; more run the descents over all the entries.
+  constexpr int kCand = 256;
+  constexpr int kCL = kCand / 64;
+  __shared__ uint32_t cks[kFiltRowsPerBlock][kCand];
+  __shared__ unsigned long long cms[kFiltRowsPerBlock][kCand];
+  const bool need_cut = use_k || (use_p && top_p > 0.0f);
+  if (need_cut) {
+    uint32_t lo = keyC + 1u;
+    if (use_k) {
+      uint32_t tk[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) tk[q] = ek[q * kFiltList];
+      lo = filt_kth_key(tk, (uint32_t)top_k);
     }
-  }
-  if (use_p && !unresolved) {
-    if (!(top_p > 0.0f)) {
-      key_p = filt_order_key(M);
-    } else {
-      double target;
-      if (use_k) {
-        target = (double)top_p * (double)z_k;
+    uint32_t count = 0u;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const bool c = ek[e] != 0u && ek[e] >= lo;
+      const unsigned long long bal = __builtin_amdgcn_ballot_w64(c);
+      const uint32_t pos = count + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+      if (c && pos < (uint32_t)kCand) {
+        cks[wave][pos] = ek[e];
+        cms[wave][pos] = use_p ? mass_fixed(ey[e]) : 0ull;
+      }
+      count += (uint32_t)__builtin_popcountll(bal);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // The cuts over N candidate keys a lane (and their masses).
+    auto cuts = [&](auto NC) {
+      constexpr int N = decltype(NC)::value;
+      uint32_t ck[N];
+      unsigned long long cm[N];
+      if constexpr (N == kCL) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          const uint32_t slot = (uint32_t)(lane + 64 * j);
+          ck[j] = slot < count ? cks[wave][slot] : 0u;
+          cm[j] = slot < count ? cms[wave][slot] : 0ull;
+        }
       } else {
-        double zt = 0.0;
 #pragma unroll
-        for (int q = 0; q < kQ; ++q)
-          if (tn[q] > 0u) zt += tz[q] * (double)mass_of(tm[q]);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) zt += __shfl_xor(zt, o, 64);
-        target = (double)top_p * (zt * 0x1p40);
-      }
-      // classes of equal logits in descending order: kept while the mass of
-      // the strictly larger survivors is below the target
-      reset();
-      unsigned long long above = 0ull;
-      float last = M;
-      for (;;) {
-        Cand<float> c = peek();
-        if (c.m == neg_inf<float>()) break;                         // every token walked
-        if (use_k && filt_order_key(c.m) < key_k) break;            // past the survivors
-        if (!(c.m > C)) {
-          unresolved = true;
-          break;
+        for (int e = 0; e < N; ++e) {
+          ck[e] = (ek[e] >= lo) ? ek[e] : 0u;
+          cm[e] = (use_p && ck[e] != 0u) ? mass_fixed(ey[e]) : 0ull;
         }
-        if (!((double)above < target)) break;
-        last = c.m;
-        unsigned long long cls = 0ull;
-        do {
-          cls += mass_fixed(c.m);
-          advance(c);
-          c = peek();
-        } while (c.m == last);
-        above += cls;
       }
-      key_p = filt_order_key(last);
-    }
+      if (use_k) {
+        key_k = filt_kth_key(ck, (uint32_t)top_k);
+        if (key_k <= keyC) unresolved = true;  // also when fewer than k keys are listed
+      }
+      if (use_p && !unresolved) {
+        if (!(top_p > 0.0f)) {
+          key_p = filt_order_key(M);
+          return;
+        }
+        // survivors: the candidates at or above key_k (every valid candidate
+        // without top-k); the others get key 0 and mass 0
+        unsigned long long zs = 0ull;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const bool sv = ck[e] != 0u && ck[e] >= key_k;
+          ck[e] = sv ? ck[e] : 0u;
+          cm[e] = sv ? cm[e] : 0ull;
+          zs += cm[e];
+        }
+        double target;
+        if (use_k) {
+          target = (double)top_p * (double)wave_sum_u64(zs);
+        } else {
+          double zt = 0.0;
+#pragma unroll
+          for (int q = 0; q < kQ; ++q)
+            if (tn[q] > 0u) zt += tz[q] * (double)mass_of(tm[q]);
+          zt += dpp_val<0xb1>(zt);
+          zt += dpp_val<0x4e>(zt);
+          zt += dpp_val<0x141>(zt);
+          zt += dpp_val<0x140>(zt);
+          zt = (lane_val(zt, 0) + lane_val(zt, 16)) + (lane_val(zt, 32) + lane_val(zt, 48));
+          target = (double)top_p * (zt * 0x1p40);
+        }
+        // the largest x whose strictly larger survivors carry at least the
+        // target; the lowest kept class is the smallest survivor key above it
+        const uint32_t x = filt_mass_cut(ck, cm, target);
+        uint32_t kp = 0xffffffffu;
+#pragma unroll
+        for (int e = 0; e < N; ++e)
+          if (ck[e] != 0u) kp = (ck[e] > x && ck[e] < kp) ? ck[e] : kp;
+        kp = wave_min_u32(kp);
+        // Without top-k the survivors held are the tokens above C: the masses
+        // above any x >= C are exact, so the cut is resolved when x >= C (the
+        // class at x + 1 and below is then decided on exact sums); x < C means
+        // the tokens above C carry less than the target and the cut lies at or
+        // below C.
+        if (!use_k && x < keyC) unresolved = true;
+        key_p = kp;
+      }
+    };
+    if (count <= (uint32_t)kCand)
+      cuts(std::integral_constant<int, kCL>{});
+    else
+      cuts(std::integral_constant<int, kE>{});
   }
   uint32_t kappa = key_k > key_p ? key_k : key_p;
   if (use_m && !(min_p < 1.0f)) {
@@ -1890,38 +1984,39 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
       return (y == y) & (y != neg_inf<float>()) && filt_order_key(y) >= kappa &&
              (!use_m || mass_of(y) >= min_p);
     };
-    auto score1 = [&](float y, int32_t i) -> T {
-      if constexpr (std::is_same<T, float>::value) {
-        const Words w = noise_words(a.key, (uint32_t)i >> 2, rid);
-        const uint32_t q = (uint32_t)i & 3u;
-        const uint32_t word = q == 0 ? w.w0 : (q == 1 ? w.w1 : (q == 2 ? w.w2 : w.w3));
-        return T(y * inv_tf) + T(gumbel_f32(word));
-      } else {
-        const Words w = noise_words(a.key, (uint32_t)i >> 1, rid);
-        return (i & 1) ? T(y) * inv_t + T(gumbel_f64(w.w2, w.w3))
-                       : T(y) * inv_t + T(gumbel_f64(w.w0, w.w1));
-      }
-    };
+    // Per tile: its best-scoring token when that token is kept (it is then
+    // the tile's best kept token, no noise to compute), else the kept tokens
+    // of its list when the list holds all of them, else the row is lost.
     bool lost = false;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      const int tt = lane + 64 * q;
-      if (tt >= nT || tn[q] == 0u) continue;
-      if (tn[q] <= (uint32_t)kFiltList || !kept(sly[wave][tt][kFiltList - 1])) {
+      if (tn[q] == 0u) continue;
+      if (kept(tby[q])) {
+        if (beats(tbs[q], tbi[q], bm, bi)) {
+          bm = tbs[q];
+          bi = tbi[q];
+        }
+      } else if (tn[q] <= (uint32_t)kFiltList || !kept(ey[q * kFiltList + kFiltList - 1])) {
+#pragma unroll
         for (int e = 0; e < kFiltList; ++e) {
-          const float y = sly[wave][tt][e];
-          if (!kept(y)) break;  // the list is sorted: the rest is not kept
-          const int32_t i = sli[wave][tt][e];
-          const T sv = score1(y, i);
+          const float y = ey[q * kFiltList + e];
+          const int32_t i = ei[q * kFiltList + e];
+          if (!kept(y)) continue;
+          T sv;
+          if constexpr (std::is_same<T, float>::value) {
+            const Words w = noise_words(a.key, (uint32_t)i >> 2, rid);
+            const uint32_t qq = (uint32_t)i & 3u;
+            const uint32_t word = qq == 0 ? w.w0 : (qq == 1 ? w.w1 : (qq == 2 ? w.w2 : w.w3));
+            sv = T(y * inv_tf) + T(gumbel_f32(word));
+          } else {
+            const Words w = noise_words(a.key, (uint32_t)i >> 1, rid);
+            sv = (i & 1) ? T(y) * inv_t + T(gumbel_f64(w.w2, w.w3))
+                         : T(y) * inv_t + T(gumbel_f64(w.w0, w.w1));
+          }
           if (beats(sv, i, bm, bi)) {
             bm = sv;
             bi = i;
           }
-        }
-      } else if (kept(tby[q])) {
-        if (beats(tbs[q], tbi[q], bm, bi)) {
-          bm = tbs[q];
-          bi = tbi[q];
         }
       } else {
         lost = true;
