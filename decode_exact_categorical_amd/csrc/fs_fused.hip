@@ -67,7 +67,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kHPad = 8;          // bf16 padding per LDS column row (16 bytes)
 constexpr float kInfTemp = 0x1p60f;  // at or above this, t * g is not kept in the accumulator
 
-enum ColMode { kGreedy = 0, kSample = 1, kInfT = 2 };
+enum ColMode { kGreedy = 0, kSample = 1, kInfT = 2, kModeMask = 3, kFiltMass = 4 };
 
 // Weight formats: bf16, OCP FP8 E4M3 with a float32 scale per row, MXFP4
 // (E2M1 elements, an E8M0 scale per block of 32 along k).
@@ -405,6 +405,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     ci.t = t;
     ci.inv_t = ci.mode == kGreedy ? 1.0f : 1.0f / t;
     ci.rid = a.row_ids ? a.row_ids[bc] : (uint32_t)bc;
+    if constexpr (kFilt) {
+      // Filtered sampling: the tile mass serves only a row whose top-p is on
+      // without top-k (kFiltMass); others skip its exponentials.
+      const float p = a.top_p ? a.top_p[bc] : 1.0f;
+      const int32_t k = a.top_k ? a.top_k[bc] : 0;
+      if (p < 1.0f && p > 0.0f && !(k > 0)) ci.mode |= kFiltMass;
+    }
     cols[tid] = ci;
   }
   bool col_ok[NB];
@@ -1174,9 +1181,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         float mm = neg_inf<float>(), mz = 0.0f;
         uint32_t nv = 0u;
         const ColInfo ci = cols[16 * cb + col];
-        const bool greedy = ci.mode == kGreedy;
+        const bool greedy = (ci.mode & kModeMask) == kGreedy;
         const float inv_tf = greedy ? 1.0f : 1.0f / ci.t;
         const T inv_t = greedy ? T(1) : T(1) / T(ci.t);
+        // whether any column of the wave needs the tile mass (wave-uniform)
+        const bool any_mass = __builtin_amdgcn_ballot_w64((ci.mode & kFiltMass) != 0) != 0ull;
         // mass of logit y relative to a larger-or-equal logit m
         auto rel_mass = [&](float y, float m) -> float {
           if (m == __builtin_inff()) return y == m ? 1.0f : 0.0f;
@@ -1220,9 +1229,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
             if (ok[j]) {
               ++nv;
               if (y[j] > mm) {
-                mz = mm == neg_inf<float>() ? 1.0f : mz * rel_mass(mm, y[j]) + 1.0f;
+                if (any_mass) mz = mm == neg_inf<float>() ? 1.0f : mz * rel_mass(mm, y[j]) + 1.0f;
                 mm = y[j];
-              } else {
+              } else if (any_mass) {
                 mz += rel_mass(y[j], mm);
               }
               if (sc[j] > bs) {  // increasing index order: ties keep the smaller
@@ -1486,7 +1495,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         }
       }
       const ColInfo ci = cols[c];
-      const float inv_tf = ci.mode == kGreedy ? 1.0f : 1.0f / ci.t;
+      const float inv_tf = (ci.mode & kModeMask) == kGreedy ? 1.0f : 1.0f / ci.t;
       auto rel_mass = [&](float y, float m) -> float {
         if (m == __builtin_inff()) return y == m ? 1.0f : 0.0f;
         return expf((y - m) * inv_tf);
@@ -1527,7 +1536,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           rec->bi = x.bi;
           rec->mm = x.mm;
           rec->nv = x.nv;
-          rec->zz = x.zz;
+          rec->zz = (ci.mode & kFiltMass) != 0 ? x.zz : -1.0;  // -1: not summed
         }
       }
     }
@@ -1727,13 +1736,28 @@ __device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
-// The largest x with at least k of the wave's keys >= x (0 if fewer than k
-// valid keys), found bit by bit from the top with ballot counts.
+// The first bit at which keys in [lo, hi] can differ, and their common
+// prefix above it: the descents below need only decide the bits from there.
+__device__ __forceinline__ int filt_top_bit(uint32_t lo, uint32_t hi, uint32_t* prefix) {
+  const uint32_t d = lo ^ hi;
+  if (d == 0u) {
+    *prefix = hi;
+    return -1;
+  }
+  const int top = 31 - __builtin_clz(d);
+  *prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
+  return top;
+}
+
+// The largest x with at least k of the wave's keys >= x, found bit by bit
+// from the top with ballot counts, knowing that it lies in [lo, hi] (lo: the
+// smallest, hi: the largest valid key; at least k valid keys).
 template <int N>
-__device__ __forceinline__ uint32_t filt_kth_key(const uint32_t (&k_)[N], uint32_t k) {
-  uint32_t x = 0u;
+__device__ __forceinline__ uint32_t filt_kth_key(const uint32_t (&k_)[N], uint32_t k, uint32_t lo,
+                                                 uint32_t hi) {
+  uint32_t x;
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = filt_top_bit(lo, hi, &x); bit >= 0; --bit) {
     const uint32_t tx = x | (1u << bit);
     uint32_t c = 0u;  // wave-uniform
 #pragma unroll
@@ -1745,14 +1769,15 @@ __device__ __forceinline__ uint32_t filt_kth_key(const uint32_t (&k_)[N], uint32
 }
 
 // The largest x whose strictly larger keys of the wave carry a mass sum that
-// is not below target (as float64), found bit by bit from the top.
+// is not below target (as float64), found bit by bit from the top, knowing
+// that it lies in [lo, hi] (the caller checks the sum above lo first).
 template <int N>
 __device__ __forceinline__ uint32_t filt_mass_cut(const uint32_t (&k_)[N],
                                                   const unsigned long long (&m_)[N],
-                                                  double target) {
-  uint32_t x = 0u;
+                                                  double target, uint32_t lo, uint32_t hi) {
+  uint32_t x;
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = filt_top_bit(lo, hi, &x); bit >= 0; --bit) {
     const uint32_t tx = x | (1u << bit);
     unsigned long long g = 0ull;
 #pragma unroll
@@ -1762,10 +1787,32 @@ __device__ __forceinline__ uint32_t filt_mass_cut(const uint32_t (&k_)[N],
   return x;
 }
 
+// The smallest and largest of the wave's nonzero keys (0xffffffff, 0 when none).
+template <int N>
+__device__ __forceinline__ void filt_key_range(const uint32_t (&k_)[N], uint32_t* lo, uint32_t* hi) {
+  uint32_t l = 0xffffffffu, h = 0u;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    l = (k_[e] != 0u && k_[e] < l) ? k_[e] : l;
+    h = k_[e] > h ? k_[e] : h;
+  }
+  *lo = wave_min_u32(l);
+  *hi = ~wave_min_u32(~h);
+}
+
 template <typename T>
 __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(FusedArgs a) {
   constexpr int kQ = kMaxFusedTiles / 64;  // tiles per lane
-  constexpr int kE = kQ * kFiltList;       // list entries per lane
+  constexpr int kCand = 512;               // candidate slots of a row (kCL a lane)
+  constexpr int kCL = kCand / 64;
+  // The row's lists (tile t's entries at [t][e]), its candidates and the
+  // listed tokens its draw scores, per wave.  The loops over them stay rolled:
+  // one wave works a row alone, so its instruction stream must stay in cache.
+  __shared__ float sly[kFiltRowsPerBlock][kMaxFusedTiles][kFiltList];
+  __shared__ int32_t sli[kFiltRowsPerBlock][kMaxFusedTiles][kFiltList];
+  __shared__ uint32_t cks[kFiltRowsPerBlock][kCand];
+  __shared__ float cys[kFiltRowsPerBlock][kCand];
+  __shared__ int32_t cis[kFiltRowsPerBlock][kCand];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t b = (int64_t)blockIdx.x * kFiltRowsPerBlock + wave;
   if (b >= a.B) return;  // whole waves; nothing below waits on another wave
@@ -1778,37 +1825,35 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
   const float top_p = a.top_p ? a.top_p[b] : 1.0f;
   const float min_p = a.min_p ? a.min_p[b] : 0.0f;
 
-  // This lane's tiles t = lane + 64 q: list entries (entry q * 8 + e) and
-  // the record fields.  Tiles past nT hold nothing (-inf entries).
-  float ey[kE];
-  int32_t ei[kE];
-  float tm[kQ], tby[kQ];
+  // This lane's tiles t = lane + 64 q: the record fields in registers, the
+  // lists in LDS.  Tiles past nT hold nothing (-inf entries).
+  float tm[kQ], tby[kQ], tl7[kQ];
   uint32_t tn[kQ];
   double tz[kQ];
   T tbs[kQ];
   int32_t tbi[kQ];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    const int t = lane + 64 * q;
-    const bool live = t < nT;
+    const int tt = lane + 64 * q;
+    const bool live = tt < nT;
     const FiltRec<T>* r =
-        reinterpret_cast<const FiltRec<T>*>(rbase + (int64_t)(live ? t : 0) * kFiltRecBytes);
-    const float4 y0 = *reinterpret_cast<const float4*>(&r->ly[0]);
-    const float4 y1 = *reinterpret_cast<const float4*>(&r->ly[4]);
+        reinterpret_cast<const FiltRec<T>*>(rbase + (int64_t)(live ? tt : 0) * kFiltRecBytes);
+    float4 y0 = *reinterpret_cast<const float4*>(&r->ly[0]);
+    float4 y1 = *reinterpret_cast<const float4*>(&r->ly[4]);
     const int4 i0 = *reinterpret_cast<const int4*>(&r->li[0]);
     const int4 i1 = *reinterpret_cast<const int4*>(&r->li[4]);
-    const float yy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-    const int32_t ii[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-#pragma unroll
-    for (int e = 0; e < kFiltList; ++e) {
-      ey[q * kFiltList + e] = live ? yy[e] : neg_inf<float>();
-      ei[q * kFiltList + e] = live ? ii[e] : kNoIndex;
-    }
-    tm[q] = live ? r->mm : neg_inf<float>();
+    const float ninf = neg_inf<float>();
+    if (!live) y0 = y1 = make_float4(ninf, ninf, ninf, ninf);
+    *reinterpret_cast<float4*>(&sly[wave][tt][0]) = y0;
+    *reinterpret_cast<float4*>(&sly[wave][tt][4]) = y1;
+    *reinterpret_cast<int4*>(&sli[wave][tt][0]) = i0;
+    *reinterpret_cast<int4*>(&sli[wave][tt][4]) = i1;
+    tl7[q] = y1.w;
+    tm[q] = live ? r->mm : ninf;
     tn[q] = live ? r->nv : 0u;
     tz[q] = live ? r->zz : 0.0;
     tbs[q] = live ? r->bs : neg_inf<T>();
-    tby[q] = live ? r->by : neg_inf<float>();
+    tby[q] = live ? r->by : ninf;
     tbi[q] = live ? r->bi : kNoIndex;
   }
 
@@ -1819,7 +1864,7 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
   for (int q = 0; q < kQ; ++q) {
     M = fmaxf(M, tm[q]);
     n_valid += tn[q];
-    if (tn[q] > (uint32_t)kFiltList) C = fmaxf(C, ey[q * kFiltList + kFiltList - 1]);
+    if (tn[q] > (uint32_t)kFiltList) C = fmaxf(C, tl7[q]);
   }
   M = wave_max_f32(M);
   C = wave_max_f32(C);
@@ -1828,13 +1873,16 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
     if (lane == 0) a.out[b] = -1;
     return;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (!(t > 0.0f)) {
     // greedy: the smallest index among the tiles whose largest logit is M
     // (each list holds its tile's smallest such index first)
     int32_t bi = kNoIndex;
 #pragma unroll
     for (int q = 0; q < kQ; ++q)
-      if (tn[q] > 0u && ey[q * kFiltList] == M) bi = min(bi, ei[q * kFiltList]);
+      if (tm[q] == M && tn[q] > 0u) bi = min(bi, sli[wave][lane + 64 * q][0]);
     bi = wave_min_i32(bi);
     if (lane == 0) a.out[b] = (int64_t)bi;
     return;
@@ -1849,125 +1897,212 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
     if (M == __builtin_inff()) return y == M ? 1.0f : 0.0f;
     return expf((y - M) * inv_tf);
   };
-  auto mass_fixed = [&](float y) -> unsigned long long {
-    return (unsigned long long)(mass_of(y) * 0x1p40f);
+  auto key_of = [&](float y) -> uint32_t {  // 0 for invalid logits
+    return (y == y) & (y != neg_inf<float>()) ? filt_order_key(y) : 0u;
   };
-  // Keys of the entries (invalid entries: 0, below every valid key).
-  uint32_t ek[kE];
-#pragma unroll
-  for (int e = 0; e < kE; ++e)
-    ek[e] = (ey[e] == ey[e]) & (ey[e] != neg_inf<float>()) ? filt_order_key(ey[e]) : 0u;
   const uint32_t keyC = C == neg_inf<float>() ? 0u : filt_order_key(C);
 
   bool unresolved = false;
   uint32_t key_k = 0u, key_p = 0u;
-  // Candidates: the entries the cuts can involve.  With top-k, every entry at
-  // or above the k-th largest tile maximum (at least k tokens reach it, so
-  // the k-th largest logit does); without it, every entry above C (a top-p cut
-  // below C is not resolved anyway).  Up to kCand of them go to this wave's
-  // LDS, kCand / 64 a lane; more run the descents over all the entries.
-  constexpr int kCand = 256;
-  constexpr int kCL = kCand / 64;
-  __shared__ uint32_t cks[kFiltRowsPerBlock][kCand];
-  __shared__ unsigned long long cms[kFiltRowsPerBlock][kCand];
-  const bool need_cut = use_k || (use_p && top_p > 0.0f);
-  if (need_cut) {
+  if (use_k || (use_p && top_p > 0.0f)) {
+    // Candidates: the entries the cuts can involve.  With top-k, every entry
+    // at or above the k-th largest tile maximum (at least k tokens reach it,
+    // so the k-th largest logit does); without it, every entry above C (a
+    // top-p cut at or below C is not resolved here).  More than kCand
+    // candidates: the fallback.
     uint32_t lo = keyC + 1u;
     if (use_k) {
       uint32_t tk[kQ];
+      uint32_t nmax = 0u;
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) tk[q] = ek[q * kFiltList];
-      lo = filt_kth_key(tk, (uint32_t)top_k);
+      for (int q = 0; q < kQ; ++q) {
+        tk[q] = tn[q] > 0u ? filt_order_key(tm[q]) : 0u;
+        nmax += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(tk[q] != 0u));
+      }
+      lo = 0u;  // fewer than k tiles with a valid logit: every entry
+      if (nmax >= (uint32_t)top_k) {
+        uint32_t l, h;
+        filt_key_range(tk, &l, &h);
+        lo = filt_kth_key(tk, (uint32_t)top_k, l, h);
+      }
+      lo = lo < 1u ? 1u : lo;
     }
     uint32_t count = 0u;
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll 1
+    for (int q = 0; q < kQ; ++q) {
+      const int tt = lane + 64 * q;
+      const float4 v0 = *reinterpret_cast<const float4*>(&sly[wave][tt][0]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&sly[wave][tt][4]);
+      const float yv[kFiltList] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      const bool c = ek[e] != 0u && ek[e] >= lo;
-      const unsigned long long bal = __builtin_amdgcn_ballot_w64(c);
-      const uint32_t pos = count + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
-      if (c && pos < (uint32_t)kCand) {
-        cks[wave][pos] = ek[e];
-        cms[wave][pos] = use_p ? mass_fixed(ey[e]) : 0ull;
+      for (int e = 0; e < kFiltList; ++e) {
+        const uint32_t k = key_of(yv[e]);
+        const bool c = k >= lo;
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(c);
+        const uint32_t pos = count + (uint32_t)__builtin_popcountll(bal & below);
+        if (c && pos < (uint32_t)kCand) {
+          cks[wave][pos] = k;
+          cys[wave][pos] = yv[e];
+        }
+        count += (uint32_t)__builtin_popcountll(bal);
       }
-      count += (uint32_t)__builtin_popcountll(bal);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // The cuts over N candidate keys a lane (and their masses).
-    auto cuts = [&](auto NC) {
-      constexpr int N = decltype(NC)::value;
-      uint32_t ck[N];
-      unsigned long long cm[N];
-      if constexpr (N == kCL) {
+    if (count > (uint32_t)kCand) {
+      unresolved = true;
+    } else if (count <= 64u) {
+      // Few candidates (the common case with top-k): one a lane, sorted by
+      // key, largest first (bitonic; equal keys end up adjacent); the k-th
+      // key is then lane k - 1's, and top-p is a prefix sum of the masses.
+      uint32_t sk = (uint32_t)lane < count ? cks[wave][lane] : 0u;
+      float sy = (uint32_t)lane < count ? cys[wave][lane] : neg_inf<float>();
 #pragma unroll
-        for (int j = 0; j < N; ++j) {
-          const uint32_t slot = (uint32_t)(lane + 64 * j);
-          ck[j] = slot < count ? cks[wave][slot] : 0u;
-          cm[j] = slot < count ? cms[wave][slot] : 0ull;
-        }
-      } else {
+      for (int kk = 2; kk <= 64; kk <<= 1)
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-          ck[e] = (ek[e] >= lo) ? ek[e] : 0u;
-          cm[e] = (use_p && ck[e] != 0u) ? mass_fixed(ey[e]) : 0ull;
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+          const uint32_t ok = (uint32_t)__shfl_xor((int)sk, jj, 64);
+          const float oy = __shfl_xor(sy, jj, 64);
+          // descending blocks keep the larger key in the lower lane
+          const bool larger = ((lane & kk) == 0) == ((lane & jj) == 0);
+          const bool take = larger ? (ok > sk) : (ok < sk);
+          sk = take ? ok : sk;
+          sy = take ? oy : sy;
         }
-      }
       if (use_k) {
-        key_k = filt_kth_key(ck, (uint32_t)top_k);
+        if ((uint32_t)top_k <= count) key_k = (uint32_t)__builtin_amdgcn_readlane((int)sk, top_k - 1);
         if (key_k <= keyC) unresolved = true;  // also when fewer than k keys are listed
       }
       if (use_p && !unresolved) {
         if (!(top_p > 0.0f)) {
           key_p = filt_order_key(M);
-          return;
-        }
-        // survivors: the candidates at or above key_k (every valid candidate
-        // without top-k); the others get key 0 and mass 0
-        unsigned long long zs = 0ull;
-#pragma unroll
-        for (int e = 0; e < N; ++e) {
-          const bool sv = ck[e] != 0u && ck[e] >= key_k;
-          ck[e] = sv ? ck[e] : 0u;
-          cm[e] = sv ? cm[e] : 0ull;
-          zs += cm[e];
-        }
-        double target;
-        if (use_k) {
-          target = (double)top_p * (double)wave_sum_u64(zs);
         } else {
-          double zt = 0.0;
+          const bool sv = sk != 0u && sk >= key_k;
+          const unsigned long long m = sv ? (unsigned long long)(mass_of(sy) * 0x1p40f) : 0ull;
+          unsigned long long incl = m;
 #pragma unroll
-          for (int q = 0; q < kQ; ++q)
-            if (tn[q] > 0u) zt += tz[q] * (double)mass_of(tm[q]);
-          zt += dpp_val<0xb1>(zt);
-          zt += dpp_val<0x4e>(zt);
-          zt += dpp_val<0x141>(zt);
-          zt += dpp_val<0x140>(zt);
-          zt = (lane_val(zt, 0) + lane_val(zt, 16)) + (lane_val(zt, 32) + lane_val(zt, 48));
-          target = (double)top_p * (zt * 0x1p40);
+          for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long u = (unsigned long long)__shfl_up((long long)incl, o, 64);
+            incl += lane >= o ? u : 0ull;
+          }
+          const unsigned long long total =
+              (unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63) |
+              ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), 63) << 32);
+          double target;
+          if (use_k) {
+            target = (double)top_p * (double)total;
+          } else {
+            // (a tile mass of -1 was not summed: this row's top-k is set but
+            // not below its count of valid logits; the fallback decides it)
+            double zt = 0.0;
+            bool missing = false;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+              if (tn[q] > 0u) {
+                zt += tz[q] * (double)mass_of(tm[q]);
+                missing |= tz[q] < 0.0;
+              }
+            zt += dpp_val<0xb1>(zt);
+            zt += dpp_val<0x4e>(zt);
+            zt += dpp_val<0x141>(zt);
+            zt += dpp_val<0x140>(zt);
+            zt = (lane_val(zt, 0) + lane_val(zt, 16)) + (lane_val(zt, 32) + lane_val(zt, 48));
+            target = (double)top_p * (zt * 0x1p40);
+            if (__builtin_amdgcn_ballot_w64(missing) != 0ull) target = __builtin_inf();
+          }
+          if ((double)total < target) {
+            unresolved = true;  // the cut lies at or below C
+          } else {
+            // a class's mass above is the prefix before its first member; the
+            // kept classes are those whose mass above is below the target
+            const uint32_t prev = (uint32_t)__shfl_up((int)sk, 1, 64);
+            const bool start = sv && (lane == 0 || prev != sk);
+            const unsigned long long kb = __builtin_amdgcn_ballot_w64(start && (double)(incl - m) < target);
+            key_p = (uint32_t)__builtin_amdgcn_readlane((int)sk, 63 - __builtin_clzll(kb));
+          }
         }
-        // the largest x whose strictly larger survivors carry at least the
-        // target; the lowest kept class is the smallest survivor key above it
-        const uint32_t x = filt_mass_cut(ck, cm, target);
-        uint32_t kp = 0xffffffffu;
-#pragma unroll
-        for (int e = 0; e < N; ++e)
-          if (ck[e] != 0u) kp = (ck[e] > x && ck[e] < kp) ? ck[e] : kp;
-        kp = wave_min_u32(kp);
-        // Without top-k the survivors held are the tokens above C: the masses
-        // above any x >= C are exact, so the cut is resolved when x >= C (the
-        // class at x + 1 and below is then decided on exact sums); x < C means
-        // the tokens above C carry less than the target and the cut lies at or
-        // below C.
-        if (!use_k && x < keyC) unresolved = true;
-        key_p = kp;
       }
-    };
-    if (count <= (uint32_t)kCand)
-      cuts(std::integral_constant<int, kCL>{});
-    else
-      cuts(std::integral_constant<int, kE>{});
+    } else {
+      uint32_t ck[kCL];
+      unsigned long long cm[kCL];
+#pragma unroll
+      for (int j = 0; j < kCL; ++j) {
+        const uint32_t slot = (uint32_t)(lane + 64 * j);
+        ck[j] = slot < count ? cks[wave][slot] : 0u;
+      }
+      if (use_k) {
+        uint32_t nk = 0u;
+#pragma unroll
+        for (int j = 0; j < kCL; ++j)
+          nk += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(ck[j] != 0u));
+        if (nk >= (uint32_t)top_k) {
+          uint32_t l, h;
+          filt_key_range(ck, &l, &h);
+          key_k = filt_kth_key(ck, (uint32_t)top_k, l, h);
+        }
+        if (key_k <= keyC) unresolved = true;  // also when fewer than k keys are listed
+      }
+      if (use_p && !unresolved) {
+        if (!(top_p > 0.0f)) {
+          key_p = filt_order_key(M);
+        } else {
+          // survivors: the candidates at or above key_k (every candidate
+          // without top-k), with their fixed-point masses; the others get key
+          // 0 and mass 0
+          unsigned long long zs = 0ull;
+#pragma unroll 1
+          for (int j = 0; j < kCL; ++j) {
+            const bool sv = ck[j] != 0u && ck[j] >= key_k;
+            const uint32_t slot = (uint32_t)(lane + 64 * j);
+            const float y = sv ? cys[wave][slot] : M;
+            cm[j] = sv ? (unsigned long long)(mass_of(y) * 0x1p40f) : 0ull;
+            ck[j] = sv ? ck[j] : 0u;
+            zs += cm[j];
+          }
+          double target;
+          if (use_k) {
+            target = (double)top_p * (double)wave_sum_u64(zs);
+          } else {
+            double zt = 0.0;
+            bool missing = false;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+              if (tn[q] > 0u) {
+                zt += tz[q] * (double)mass_of(tm[q]);
+                missing |= tz[q] < 0.0;
+              }
+            zt += dpp_val<0xb1>(zt);
+            zt += dpp_val<0x4e>(zt);
+            zt += dpp_val<0x141>(zt);
+            zt += dpp_val<0x140>(zt);
+            zt = (lane_val(zt, 0) + lane_val(zt, 16)) + (lane_val(zt, 32) + lane_val(zt, 48));
+            target = (double)top_p * (zt * 0x1p40);
+            if (__builtin_amdgcn_ballot_w64(missing) != 0ull) target = __builtin_inf();
+          }
+          // The largest x whose strictly larger survivors carry at least the
+          // target; the lowest kept class is the smallest survivor key above
+          // it.  Below the smallest survivor key l the sum is every
+          // survivor's mass: when that is short of the target (possible only
+          // without top-k: the survivors held are the tokens above C) the cut
+          // lies at or below C and is not resolved here; otherwise x lies in
+          // [l - 1, the largest key].
+          if ((double)wave_sum_u64(zs) < target) {
+            unresolved = true;
+          } else {
+            uint32_t l, h;
+            filt_key_range(ck, &l, &h);
+            const uint32_t x = filt_mass_cut(ck, cm, target, l - 1u, h);
+            uint32_t kp = 0xffffffffu;
+#pragma unroll
+            for (int j = 0; j < kCL; ++j)
+              if (ck[j] != 0u) kp = (ck[j] > x && ck[j] < kp) ? ck[j] : kp;
+            key_p = wave_min_u32(kp);
+          }
+        }
+      }
+    }
   }
   uint32_t kappa = key_k > key_p ? key_k : key_p;
   if (use_m && !(min_p < 1.0f)) {
@@ -1981,13 +2116,16 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
   int32_t bi = kNoIndex;
   if (!unresolved) {
     auto kept = [&](float y) -> bool {
-      return (y == y) & (y != neg_inf<float>()) && filt_order_key(y) >= kappa &&
-             (!use_m || mass_of(y) >= min_p);
+      const uint32_t k = key_of(y);
+      return k != 0u && k >= kappa && (!use_m || mass_of(y) >= min_p);
     };
     // Per tile: its best-scoring token when that token is kept (it is then
     // the tile's best kept token, no noise to compute), else the kept tokens
     // of its list when the list holds all of them, else the row is lost.
+    // The listed tokens to score are gathered first, so that the lanes
+    // compute their noise side by side rather than one tile at a time.
     bool lost = false;
+    uint32_t lmask = 0u;  // bit q: tile q's kept tokens come from its list
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       if (tn[q] == 0u) continue;
@@ -1996,30 +2134,59 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
           bm = tbs[q];
           bi = tbi[q];
         }
-      } else if (tn[q] <= (uint32_t)kFiltList || !kept(ey[q * kFiltList + kFiltList - 1])) {
-#pragma unroll
-        for (int e = 0; e < kFiltList; ++e) {
-          const float y = ey[q * kFiltList + e];
-          const int32_t i = ei[q * kFiltList + e];
-          if (!kept(y)) continue;
-          T sv;
-          if constexpr (std::is_same<T, float>::value) {
-            const Words w = noise_words(a.key, (uint32_t)i >> 2, rid);
-            const uint32_t qq = (uint32_t)i & 3u;
-            const uint32_t word = qq == 0 ? w.w0 : (qq == 1 ? w.w1 : (qq == 2 ? w.w2 : w.w3));
-            sv = T(y * inv_tf) + T(gumbel_f32(word));
-          } else {
-            const Words w = noise_words(a.key, (uint32_t)i >> 1, rid);
-            sv = (i & 1) ? T(y) * inv_t + T(gumbel_f64(w.w2, w.w3))
-                         : T(y) * inv_t + T(gumbel_f64(w.w0, w.w1));
-          }
-          if (beats(sv, i, bm, bi)) {
-            bm = sv;
-            bi = i;
-          }
-        }
+      } else if (tn[q] <= (uint32_t)kFiltList || !kept(tl7[q])) {
+        lmask |= 1u << q;
       } else {
         lost = true;
+      }
+    }
+    uint32_t nd = 0u;
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll 1
+    for (int q = 0; q < kQ; ++q) {
+      // (a wave-uniform skip when no lane takes this tile slot from its list)
+      if (__builtin_amdgcn_ballot_w64(((lmask >> q) & 1u) != 0u) == 0ull) continue;
+      const int tt = lane + 64 * q;
+      const float4 v0 = *reinterpret_cast<const float4*>(&sly[wave][tt][0]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&sly[wave][tt][4]);
+      const int4 j0 = *reinterpret_cast<const int4*>(&sli[wave][tt][0]);
+      const int4 j1 = *reinterpret_cast<const int4*>(&sli[wave][tt][4]);
+      const float yv[kFiltList] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const int32_t iv[kFiltList] = {j0.x, j0.y, j0.z, j0.w, j1.x, j1.y, j1.z, j1.w};
+#pragma unroll
+      for (int e = 0; e < kFiltList; ++e) {
+        const bool d = ((lmask >> q) & 1u) != 0u && kept(yv[e]);
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(d);
+        const uint32_t pos = nd + (uint32_t)__builtin_popcountll(bal & below);
+        if (d && pos < (uint32_t)kCand) {
+          cys[wave][pos] = yv[e];
+          cis[wave][pos] = iv[e];
+        }
+        nd += (uint32_t)__builtin_popcountll(bal);
+      }
+    }
+    if (nd > (uint32_t)kCand) lost = true;  // (more listed kept tokens than slots: the fallback)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 1
+    for (uint32_t slot = (uint32_t)lane; slot < nd && slot < (uint32_t)kCand; slot += 64u) {
+      const float y = cys[wave][slot];
+      const int32_t i = cis[wave][slot];
+      T sv;
+      if constexpr (std::is_same<T, float>::value) {
+        const Words w = noise_words(a.key, (uint32_t)i >> 2, rid);
+        const uint32_t qq = (uint32_t)i & 3u;
+        const uint32_t word = qq == 0 ? w.w0 : (qq == 1 ? w.w1 : (qq == 2 ? w.w2 : w.w3));
+        sv = T(y * inv_tf) + T(gumbel_f32(word));
+      } else {
+        const Words w = noise_words(a.key, (uint32_t)i >> 1, rid);
+        sv = (i & 1) ? T(y) * inv_t + T(gumbel_f64(w.w2, w.w3))
+                     : T(y) * inv_t + T(gumbel_f64(w.w0, w.w1));
+      }
+      if (beats(sv, i, bm, bi)) {
+        bm = sv;
+        bi = i;
       }
     }
     unresolved = __builtin_amdgcn_ballot_w64(lost) != 0;
