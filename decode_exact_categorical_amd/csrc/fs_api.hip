@@ -225,8 +225,9 @@ fs_status sample_fused(const fs_bf16* H, const void* W, int fmt, const void* sca
   int cus = 0;
   s = device_cus(&cus);
   if (s != FS_OK) return s;
-  // (128-column tiles stream W in passes of 32 rows, which 256 tiles divide evenly)
-  const int nT = fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, fmt) : 0);
+  // (Gumbel-top-k runs the narrow kernel at every batch size)
+  const int nT = k > 0 ? fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, fmt) : 0)
+                       : fs::fused_call_tiles(B, D, V, fmt == kFmtBf16, cus, row_bytes(D, fmt));
   s = check_span(V, D, nT, fmt);
   if (s != FS_OK) return s;
   return launch_sampling(H, W, fmt, scale, B, D, V, temp, bias, seed, offset, out_idx, row_ids,
@@ -279,7 +280,7 @@ fs_status debug_logits(const fs_bf16* H, const void* W, int fmt, const void* sca
   s = device_cus(&cus);
   if (s != FS_OK) return s;
   // (128-column tiles stream W in passes of 32 rows, which 256 tiles divide evenly)
-  const int nT = fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, fmt) : 0);
+  const int nT = fs::fused_call_tiles(B, D, V, fmt == kFmtBf16, cus, row_bytes(D, fmt));
   s = check_span(V, D, nT, fmt);
   if (s != FS_OK) return s;
   fs::FusedArgs a;
@@ -360,7 +361,7 @@ fs_status fs_sample_fused_noalloc(const fs_bf16* H, const fs_bf16* W, int64_t B,
   int cus = 0;
   s = device_cus(&cus);
   if (s != FS_OK) return s;
-  const int nT = fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, kFmtBf16) : 0);
+  const int nT = fs::fused_call_tiles(B, D, V, true, cus, row_bytes(D, kFmtBf16));
   s = check_span(V, D, nT, kFmtBf16);
   if (s != FS_OK) return s;
   if ((size_t)B * (size_t)nT * cand_bytes(flags) > kNoAllocCandBytes)
@@ -848,7 +849,7 @@ int fs_fused_tiles(int64_t B, int64_t D, int64_t V, int weight_format) {
   }
   int cus = 0;
   if (device_cus(&cus) != FS_OK) return -1;
-  return fs::fused_num_tiles(V, cus, B <= 64 ? row_bytes(D, weight_format) : 0);
+  return fs::fused_call_tiles(B, D, V, weight_format == kFmtBf16, cus, row_bytes(D, weight_format));
 }
 
 fs_status fs_debug_stream_read(const void* buf, size_t bytes, uint64_t* out, fs_stream_t stream) {

@@ -2323,6 +2323,7 @@ hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) 
       launch(topk_stage2_kernel<float>, g2, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
+  if (fused_wide_applies(a, epi)) return launch_fused_wide(a, epi, stream);
   const bool narrow = a.W8 != nullptr || a.W4 != nullptr;
   const int nb = fused_column_blocks(a.B, narrow, epi == kEpiSample64);
   const int64_t tile = 16 * nb;

@@ -119,6 +119,16 @@ int fused_column_blocks(int64_t B, bool fp8_weights, bool fp64_noise);
 // Largest byte span of W rows one wave addresses through 32-bit offsets.
 int64_t fused_wave_span_bytes(int64_t V, int64_t D, int nT, int elem_bytes);
 hipError_t launch_fused_stage1(const FusedArgs& a, int epilogue, hipStream_t stream);
+// The wide-batch kernel (fs_wide.hip): bf16 weights, more than 64 rows,
+// D % 32 == 0, one draw per row (float32 or float64 noise) or the logits.
+bool fused_wide_applies(const FusedArgs& a, int epilogue);
+bool fused_wide_shape(int64_t B, int64_t D, bool bf16_weights);
+// Vocabulary tiles of the wide kernel (its batch tiles of 128 columns share
+// the chip).
+int fused_wide_tiles(int64_t B, int64_t V, int num_cus);
+// Vocabulary tiles of a fused sampling or logits call of this shape.
+int fused_call_tiles(int64_t B, int64_t D, int64_t V, bool bf16_weights, int num_cus, int64_t row_bytes);
+hipError_t launch_fused_wide(const FusedArgs& a, int epilogue, hipStream_t stream);
 
 // Standalone sampler over float32 logits (Stage 1, Stage 2 in the last
 // workgroup of each row).
