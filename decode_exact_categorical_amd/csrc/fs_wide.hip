@@ -47,7 +47,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kXRB = 4;                    // row blocks of a wave pass: 64 rows
+#ifndef FS_WIDE_RB
+#define FS_WIDE_RB 4
+#endif
+constexpr int kXRB = FS_WIDE_RB;           // row blocks of a wave pass
 constexpr int kXKC = 128;                  // k per H chunk (four k-steps)
 constexpr int kXCS = kXKC / 32;            // k-steps per chunk
 constexpr int kXCP = kXKC / 8;             // 16-byte pieces of one column's chunk
@@ -305,27 +308,13 @@ __global__ __launch_bounds__(64 * NW) void fused_wide_kernel(FusedArgs a) {
 #pragma unroll
           for (int cb = 0; cb < kXNB; ++cb) hf[j & 1][cb] = h_frag(buf, cb, j % kXCS);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // The MFMAs of k-step j: each H fragment meets the wave's 4 row blocks,
-        // while the next k-step's fragments (same chunk) are read.
-#pragma unroll
-        for (int cb = 0; cb < kXNB; ++cb) {
-          if constexpr (j % kXCS != kXCS - 1) hf[(j + 1) & 1][cb] = h_frag(buf, cb, (j + 1) % kXCS);
-#pragma unroll
-          for (int rb = 0; rb < kXRB; ++rb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(wb[j % kXAhead][rb]), hf[j & 1][cb],
-                                                                  acc[rb][cb], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // Refill the ring: after every second k-step, the two slots just used
-        // take k-steps j + 3 and j + 4, the two 64-byte halves of each row's
-        // 128-byte segment requested back to back (HBM streams markedly
-        // faster so).  Past the pass's end: step 0 against zero H, never used.
-        if constexpr (j % 2 == 1)
-          w_load_pair(wb[(j - 1) % kXAhead], wb[j % kXAhead], wo, it * kXBody + j - 1 + kXAhead);
-        if constexpr (F && j < kXNB) {
-          // Fold slot j: its bias, loaded four k-steps ago, then the bias of
-          // the fold slot four k-steps ahead.
+        constexpr bool kFoldStep = F && j < kXNB;
+        // Fold slot j (fold iterations): the noise of fragment (row block FI,
+        // column block j), bias + t * g, computed in the MFMAs' scheduling
+        // region so its VALU work interleaves with them; its bias was loaded
+        // four k-steps ago.
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kFoldStep) {
           const f32x4 beta = bring[j % kXAhead];
           if constexpr (kLoadBias) {
             constexpr int g4 = (F ? FI : 0) * kXBody + j + kXAhead;  // the slot four k-steps on
@@ -336,19 +325,45 @@ __global__ __launch_bounds__(64 * NW) void fused_wide_kernel(FusedArgs a) {
           const ColInfo ci = cols[wcol0 + 16 * j + col];
           const bool ok = wcol0 + 16 * j + col < ncol;
           const int i0 = pr0 + 16 * FI + 4 * grp;
-          f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (ok && i0 < r1) {
-            if (HAS_BIAS) v = beta;
-            if (ci.mode == kXSample) {
-              const Words w = noise_words(a.key, (uint32_t)i0 >> 2, ci.rid);
-              v[0] += ci.t * gumbel_f32(w.w0);
-              v[1] += ci.t * gumbel_f32(w.w1);
-              v[2] += ci.t * gumbel_f32(w.w2);
-              v[3] += ci.t * gumbel_f32(w.w3);
-            }
+          // (branch-free: every lane computes the noise, selects apply it)
+          const Words w = noise_words(a.key, (uint32_t)i0 >> 2, ci.rid);
+          const bool use = ok && i0 < r1;
+          const float tn = use && ci.mode == kXSample ? ci.t : 0.0f;
+          const float g[4] = {gumbel_f32(w.w0), gumbel_f32(w.w1), gumbel_f32(w.w2), gumbel_f32(w.w3)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float b = HAS_BIAS && use ? beta[e] : 0.0f;
+            v[e] = tn == 0.0f ? b : b + tn * g[e];
           }
-          acc[F ? FI : 0][j < kXNB ? j : 0] += v;
+        } else {
+          __builtin_amdgcn_sched_barrier(0);
         }
+        // The MFMAs of k-step j: each H fragment meets the wave's 4 row blocks,
+        // while the next k-step's fragments (same chunk) are read.
+#pragma unroll
+        for (int cb = 0; cb < kXNB; ++cb) {
+          if constexpr (j % kXCS != kXCS - 1) hf[(j + 1) & 1][cb] = h_frag(buf, cb, (j + 1) % kXCS);
+#pragma unroll
+          for (int rb = 0; rb < kXRB; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(wb[j % kXAhead][rb]), hf[j & 1][cb],
+                                                                  acc[rb][cb], 0, 0, 0);
+        }
+        if constexpr (kFoldStep) {
+          // one MFMA, then up to three VALU instructions of the noise
+#pragma unroll
+          for (int q = 0; q < kXRB * kXNB; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kFoldStep) acc[F ? FI : 0][j < kXNB ? j : 0] += v;
+        // Refill the ring: after every second k-step, the two slots just used
+        // take k-steps j + 3 and j + 4, the two 64-byte halves of each row's
+        // 128-byte segment requested back to back (HBM streams markedly
+        // faster so).  Past the pass's end: step 0 against zero H, never used.
+        if constexpr (j % 2 == 1)
+          w_load_pair(wb[(j - 1) % kXAhead], wb[j % kXAhead], wo, it * kXBody + j - 1 + kXAhead);
         if (j % kXCS == kXCS - 1) {
           __builtin_amdgcn_sched_barrier(0);
           h_store(buf ^ 1);
@@ -358,11 +373,7 @@ __global__ __launch_bounds__(64 * NW) void fused_wide_kernel(FusedArgs a) {
     };
     // (Each fold iteration is its own copy: it folds into fixed registers.)
     if constexpr (kFold) {
-      static_assert(kXRB == 4, "one fold iteration per row block");
-      body(std::integral_constant<int, 0>(), 0);
-      body(std::integral_constant<int, 1>(), 1);
-      body(std::integral_constant<int, 2>(), 2);
-      body(std::integral_constant<int, 3>(), 3);
+      static_for<kXRB>([&](auto ftag) { body(ftag, decltype(ftag)::value); });
     }
 #pragma unroll 1
     for (int it = kFold ? kXRB : 0; it < NI; ++it) body(std::integral_constant<int, -1>(), it);
