@@ -230,6 +230,10 @@ def main() -> int:
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="only time the plain streaming read (fs_debug_stream_read) of the headline "
                          "step's algorithmic byte count, --steps times")
+    ap.add_argument("--large-batch", action="store_true",
+                    help="only time the large-batch head (B = 256, D = 4096, V = 128256, fp32 bias "
+                         "with 10%% of each row masked), --steps times: the command profiled for "
+                         "the wide kernel's MFMA counters")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB, --steps times (the known-size "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -269,6 +273,25 @@ def main() -> int:
         gbs = buf.numel() / (kms * 1e-3) / 1e9
         print(json.dumps({"stream_ceiling_bytes": buf.numel(), "avg_launch_us": round(kms * 1e3, 2),
                           "achieved_gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                          "steps": args.steps}), flush=True)
+        return 0
+
+    if args.large_batch:
+        dev = torch.device("cuda:0")
+        gl = torch.Generator(device=dev).manual_seed(7)
+        VL, BL = 128256, 256
+        WL = (torch.randn(VL, D_MODEL, generator=gl, device=dev) * 0.02).to(torch.bfloat16)
+        HL = torch.randn(BL, D_MODEL, generator=gl, device=dev).to(torch.bfloat16)
+        TL = 0.5 + 0.7 * torch.rand(BL, generator=gl, device=dev)
+        biasL = torch.randn(BL, VL, generator=gl, device=dev)
+        biasL.masked_fill_(torch.rand(BL, VL, generator=gl, device=dev) < 0.1, float("-inf"))
+        ms, kms, pc = time_calls(
+            torch, fs, lambda s: fs.sample_fused(HL, WL, TL, biasL, seed=77, offset=s),
+            args.steps, args.warmup)
+        flops = 2 * BL * VL * D_MODEL
+        print(json.dumps({"large_batch_us": round(ms * 1e3, 2), "kernel_us": round(kms * 1e3, 2),
+                          "tflops": round(flops / (kms * 1e-3) / 1e12, 1),
+                          "mfma_frac": round(flops / (kms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
                           "steps": args.steps}), flush=True)
         return 0
 
