@@ -552,7 +552,7 @@ def main() -> int:
                 fl[key]["speedup_vs_eager"] = round(
                     fl[key]["eager_transformers_chain_us"] / fl[key]["us_per_call"], 2)
             if bl == 64 and not name:
-                # the chain's masked, temperature-scaled logits (filter_logits)
+                # the filter chain's output logits (filter_logits)
                 Y = torch.empty_like(X)
                 fms, fkms, _ = time_calls(
                     torch, fs, lambda s: fs.filter_logits(X, Tl, out=Y, **kw),

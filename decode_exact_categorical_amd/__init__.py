@@ -494,8 +494,8 @@ def sample(logits: torch.Tensor, temperature, *, top_k=None, top_p=None, min_p=N
 
 def filter_logits(logits: torch.Tensor, temp, *, top_k=None, top_p=None, min_p=None,
                   out: torch.Tensor | None = None) -> torch.Tensor:
-    """The masked, temperature-scaled logits of the filter chain top-k, top-p, min-p over
-    float32 logits [B, V]: y / temp on the kept tokens, -inf elsewhere."""
+    """The filter chain's output over float32 logits [B, V] (top-k, top-p, min-p after
+    temperature): y / temp where the chain keeps a token, -inf where it drops one."""
     lib = load_library()
     dev = logits.device
     if dev.type != "cuda":

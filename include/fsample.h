@@ -316,7 +316,7 @@ fs_status fs_repetition_penalty(const float *logits, int64_t B, int64_t V,
 
 /*
  * The filter chain's output [SD API table, filter_logits; Semantics]: the
- * masked, temperature-scaled logits of fs_sample_logits_filtered's kept set,
+ * logits scaled by 1/t on fs_sample_logits_filtered's kept set, -inf off it,
  *   out_logits[b, i] = logits[b, i] * (1 / t)   for the kept tokens,
  *                      -inf                      elsewhere (NaN included);
  * greedy rows (t <= 0 or NaN) keep the largest valid logit's tie class,

@@ -1,5 +1,5 @@
-"""GPU parity of fs_filter_logits (the filter chain's masked, temperature-scaled
-logits) against the oracle, through the C ABI, and of filtered speculative
+"""GPU parity of fs_filter_logits (the filter chain's output: y / t on the kept
+tokens, -inf elsewhere) against the oracle, through the C ABI, and of filtered speculative
 decoding composed from it.
 
 * -inf exactly at the oracle's dropped tokens and y / t at its kept tokens

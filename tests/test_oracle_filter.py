@@ -215,7 +215,7 @@ def test_law_chi_square(fp64):
 
 @pytest.mark.parametrize("setting", SETTINGS[:6] + [dict()])
 def test_filter_logits_match_processor_output(setting):
-    """The processors return the masked, temperature-scaled logits themselves."""
+    """The processors' own output: y / t on the tokens they keep, -inf elsewhere."""
     rng = np.random.default_rng(16)
     B, V = 40, 300
     x = (rng.standard_normal((B, V)) * rng.uniform(0.5, 4.0, size=(B, 1))).astype(np.float32)
