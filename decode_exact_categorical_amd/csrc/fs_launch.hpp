@@ -133,7 +133,7 @@ hipError_t launch_fused_wide(const FusedArgs& a, int epilogue, hipStream_t strea
 // Standalone sampler over float32 logits (Stage 1, Stage 2 in the last
 // workgroup of each row).
 constexpr int kLogitsChunk = 2048;      // fewest logits per workgroup (sizes the workspace)
-constexpr int kLogitsChunkMax = 32768;  // most logits per workgroup
+constexpr int kLogitsChunkMax = 131072;  // most logits per workgroup
 int logits_chunk(int64_t B, int64_t V);  // logits per workgroup for a launch
 struct LogitsArgs {
   const float* X;  // [B, V]
