@@ -67,7 +67,15 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kHPad = 8;          // bf16 padding per LDS column row (16 bytes)
 constexpr float kInfTemp = 0x1p60f;  // at or above this, t * g is not kept in the accumulator
 
-enum ColMode { kGreedy = 0, kSample = 1, kInfT = 2, kModeMask = 3, kFiltMass = 4 };
+enum ColMode { kGreedy = 0, kSample = 1, kInfT = 2, kModeMask = 3, kFiltMass = 4, kFiltStore = 8 };
+
+// Filtered sampling: rows whose cuts the tiles' lists are likely not to hold
+// (top-p or min-p without top-k, a sampled row) get their logits written by
+// Stage 1 itself, so that a row Stage 2 cannot settle needs no second matmul.
+// Stage 1 and Stage 2 both decide with this function, on the same parameters.
+__device__ __forceinline__ bool filt_store_row(float t, int32_t k, float p, float m) {
+  return (t > 0.0f) && !(k > 0) && ((p < 1.0f) || (m > 0.0f));
+}
 
 // Weight formats: bf16, OCP FP8 E4M3 with a float32 scale per row, MXFP4
 // (E2M1 elements, an E8M0 scale per block of 32 along k).
@@ -410,7 +418,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       // without top-k (kFiltMass); others skip its exponentials.
       const float p = a.top_p ? a.top_p[bc] : 1.0f;
       const int32_t k = a.top_k ? a.top_k[bc] : 0;
+      const float m = a.min_p ? a.min_p[bc] : 0.0f;
       if (p < 1.0f && p > 0.0f && !(k > 0)) ci.mode |= kFiltMass;
+      if (a.Y != nullptr && filt_store_row(t, k, p, m)) ci.mode |= kFiltStore;
     }
     cols[tid] = ci;
   }
@@ -1199,6 +1209,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           for (int c2 = 0; c2 < NB; ++c2)
             if (c2 == cb) y = acc[rb][c2];
           const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+          if ((ci.mode & kFiltStore) != 0 && bt0 + 16 * cb + col < B) {
+            float* yr = a.Y + (bt0 + 16 * cb + col) * V;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (i0 + j < r1) yr[i0 + j] = y[j];
+          }
           bool ok[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) ok[j] = (i0 + j < r1) & (y[j] == y[j]) & (y[j] != neg_inf<float>());
@@ -1320,7 +1336,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           if (EPI == kEpiStore) {
             if (!col_ok[cb]) continue;
             const int64_t b = bt0 + 16 * cb + col;
-            if (a.row_flags != nullptr && a.row_flags[b] == 0u) continue;
+            if (a.row_flags != nullptr && a.row_flags[b] != 1u) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               if (i0 + j < r1) a.Y[b * V + i0 + j] = W8 ? y[j] * wsc[rb][j] : y[j];
@@ -2193,8 +2209,10 @@ __global__ __launch_bounds__(64 * kFiltRowsPerBlock) void filt_stage2_kernel(Fus
     wave_argmax_xor(bm, bi, 0);
   }
   if (lane == 0) {
-    if (unresolved) {
-      a.row_flags[b] = 1u;
+    if (unresolved && filt_store_row(t, top_k, top_p, min_p)) {
+      a.row_flags[b] = 2u;  // its logits are in Y already (Stage 1 wrote them)
+    } else if (unresolved) {
+      a.row_flags[b] = 1u;  // the store launch writes its logits
       __hip_atomic_fetch_add(a.flag_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       a.out[b] = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
@@ -2347,7 +2365,11 @@ hipError_t launch_fused_filtered(const FusedArgs& a, bool fp64, const FilterArgs
                                  hipStream_t stream) {
   const int nb = fused_filtered_column_blocks(a.B, fp64);
   const dim3 grid((unsigned)a.nT, (unsigned)((a.B + 16 * nb - 1) / (16 * nb)));
-  hipError_t e = launch_w<kWBf16>(a, fp64 ? kEpiFilt64 : kEpiFilt32, grid, nb, stream);
+  // Stage 1 writes the logits of the rows filt_store_row picks into the
+  // fallback's buffer as it goes.
+  FusedArgs s1 = a;
+  s1.Y = fa.X == nullptr ? nullptr : const_cast<float*>(fa.X);
+  hipError_t e = launch_w<kWBf16>(s1, fp64 ? kEpiFilt64 : kEpiFilt32, grid, nb, stream);
   if (e != hipSuccess) return e;
   const dim3 g2((unsigned)((a.B + kFiltRowsPerBlock - 1) / kFiltRowsPerBlock));
   if (fp64)
@@ -2356,9 +2378,10 @@ hipError_t launch_fused_filtered(const FusedArgs& a, bool fp64, const FilterArgs
     launch(filt_stage2_kernel<float>, g2, dim3(64 * kFiltRowsPerBlock), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // The fallback: the same tiles' logits of the flagged rows (the store
-  // epilogue returns at once when none is flagged), then the filtered
-  // sampler over them (one workgroup per row, the others return at once).
+  // The fallback: the same tiles' logits of the flagged rows whose logits
+  // Stage 1 did not write (flag 1; the store epilogue returns at once when
+  // there is none), then the filtered sampler over every flagged row (one
+  // workgroup per row, the others return at once).
   FusedArgs s = a;
   s.Y = fa.X == nullptr ? nullptr : const_cast<float*>(fa.X);
   e = launch_w<kWBf16>(s, kEpiStore, grid, nb, stream);

@@ -55,10 +55,11 @@ struct FusedArgs {
   int bias_vec4;  // bias rows are 16-byte aligned
   int k;          // Gumbel-top-k: places per row (out is [B, k]; cand is [B, nT, kTopKMax])
   // Filtered sampling (kEpiFilt32/64): per-row filters (each may be null:
-  // off), cand is [B, nT] FiltRec records; rows Stage 2 cannot resolve from
-  // the records get row_flags[b] = 1 and are counted on *flag_count; the
-  // store epilogue then writes only those rows' logits (skipping the whole
-  // launch when *flag_count is 0).
+  // off), cand is [B, nT] FiltRec records; Stage 1 also writes to Y the
+  // logits of the rows filt_store_row picks.  Rows Stage 2 cannot resolve
+  // from the records get row_flags[b] = 2 when their logits are in Y, else 1
+  // (counted on *flag_count); the store epilogue then writes only the rows
+  // flagged 1 (skipping the whole launch when *flag_count is 0).
   const int32_t* top_k;
   const float* top_p;
   const float* min_p;

@@ -279,8 +279,10 @@ fs_status fs_sample_logits_filtered(const float *logits, int64_t B, int64_t V,
  * and draws over the kept tokens.  A row whose cuts or draw reach below what
  * the lists hold (kept sets wider than the tiles' lists, e.g. top-p alone
  * over a flat row) is resolved exactly by a fallback in the same call: the
- * fused matmul again, storing only those rows' logits into the workspace,
- * and the filtered sampler over them.  Rows with top-k resolve with the
+ * filtered sampler over that row's logits in the workspace.  Stage 1 writes
+ * them there as it goes for sampled rows with top-p or min-p but no top-k
+ * (the rows whose cuts usually lie below the lists); any other such row gets
+ * them from a second pass of the fused matmul that stores only its logits.  Rows with top-k resolve with the
  * filtered sampler's fixed-point masses, so they draw what it draws bit for
  * bit; rows with top-p but no top-k take the total mass from the tiles'
  * float64 sums (a decision within about 1e-6 relative of its boundary may
