@@ -163,9 +163,10 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
 template <int NB, int EPI, bool HAS_BIAS, int WF>
 struct Pipeline {
   static constexpr bool narrow = WF != kWBf16;  // FP8 or MXFP4 weights
-  // Noise added after the k-loop (float64 noise, Gumbel-top-k): the same
-  // register budget as float64 noise.
-  static constexpr bool late_noise = EPI == kEpiSample64 || EPI == kEpiTopK32 || EPI == kEpiTopK64 ||
+  // Noise added after the k-loop (float64 noise, filtered sampling): the same
+  // register budget as float64 noise.  (Gumbel-top-k with float32 noise folds
+  // it, as the single draw does.)
+  static constexpr bool late_noise = EPI == kEpiSample64 || EPI == kEpiTopK64 ||
                                      EPI == kEpiFilt32 || EPI == kEpiFilt64;
   static constexpr bool wide = NB > 4;
   static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || (late_noise && EPI != kEpiFilt32));
@@ -197,7 +198,8 @@ struct Pipeline {
 // k-loop.
 template <int NB, int EPI, bool HAS_BIAS, int WF>
 struct FoldNoise {
-  static constexpr bool value = EPI == kEpiSample32 && (WF != kWFp8 || (NB & 1) != 0);
+  static constexpr bool value =
+      (EPI == kEpiSample32 || EPI == kEpiTopK32) && (WF != kWFp8 || (NB & 1) != 0);
 };
 
 // An FP8 row scale the fold can divide by: nonzero and finite.
@@ -1099,9 +1101,26 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
           for (int c2 = 0; c2 < NB; ++c2)
             if (c2 == cb) y = acc[rb][c2];
           const int64_t i0 = r0 + 16 * (rb_first + rb) + 4 * grp;
+          T s[4];
+          if constexpr (kFold) {
+            // The noise and the bias are in the sums already: acc / t (greedy
+            // columns carry 1 / t = 1), infinite temperatures add g after it.
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] = T(y[j] * ci.inv_t);
+            if (__builtin_amdgcn_ballot_w64(ci.mode == kInfT) != 0ull && ci.mode == kInfT) {
+              const Words w = noise_words(a.key, (uint32_t)(i0 >> 2), ci.rid);
+              s[0] += gumbel_f32(w.w0);
+              s[1] += gumbel_f32(w.w1);
+              s[2] += gumbel_f32(w.w2);
+              s[3] += gumbel_f32(w.w3);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              topk_insert(lm, li, i0 + j < r1 ? s[j] : neg_inf<T>(), (int32_t)(i0 + j));
+            continue;
+          }
           float beta[4];
           load_bias4(a, bcol, i0, beta);
-          T s[4];
           if (greedy) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) s[j] = T(y[j]) + T(beta[j]);
@@ -2243,12 +2262,22 @@ hipError_t launch_nb(const FusedArgs& a, int epi, dim3 grid, hipStream_t stream)
                          stream, a);
       break;
     case kEpiTopK32:
-      // Gumbel-top-k: tiles of at most 64 columns, bf16 weights.
-      if constexpr (NB <= 4 && BF)
-        launch((fused_stage1_kernel<NB, kEpiTopK32, false, kWBf16>), grid,
-                           dim3(kThreads), 0, stream, a);
-      else
+      // Gumbel-top-k: tiles of at most 64 columns, bf16 weights; the float32
+      // noise and the bias are folded as for one draw.
+      if constexpr (NB <= 4 && BF) {
+        constexpr bool FT = FoldNoise<NB, kEpiTopK32, false, kWBf16>::value;
+        if (a.bias && FT && a.bias_vec4)
+          launch((fused_stage1_kernel<NB, kEpiTopK32, FT, kWBf16, FT>), grid, dim3(kThreads), 0,
+                 stream, a);
+        else if (a.bias && FT)
+          launch((fused_stage1_kernel<NB, kEpiTopK32, FT, kWBf16>), grid, dim3(kThreads), 0,
+                 stream, a);
+        else
+          launch((fused_stage1_kernel<NB, kEpiTopK32, false, kWBf16>), grid, dim3(kThreads), 0,
+                 stream, a);
+      } else {
         return hipErrorInvalidValue;
+      }
       break;
     case kEpiTopK64:
       // Float64 scores: tiles of 16 or 64 columns (the 32- and 48-column
