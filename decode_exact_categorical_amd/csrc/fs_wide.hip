@@ -18,9 +18,8 @@
 //    read the same W rows at the same time (the second read is served by the
 //    CU's cache).  At two waves per SIMD (256 registers) this tile spills.
 //  * W goes straight from HBM into VGPRs in the bf16 MFMA A-operand layout,
-//    four k-steps ahead; the stream runs on across passes (the last k-steps
-//    of a pass prefetch the first of the next).  Each W fragment feeds 8
-//    MFMAs.
+//    three to four k-steps ahead (each pass requests its own first k-steps).
+//    Each W fragment feeds 8 MFMAs.
 //  * H is the B operand, staged through LDS in double-buffered chunks of 128 k
 //    for all the workgroup's columns; each H fragment read from LDS feeds the
 //    wave's 4 row blocks.
