@@ -1580,21 +1580,41 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
 
   if constexpr (kTopK) {
     // Per column, its kTopKMax places among the 8 waves' running places
-    // (one candidate a lane): wave w takes columns w, w + 8, ...
+    // (each sorted best first): wave w takes columns w, w + 8, ..., one group
+    // of 8 lanes a column, whose lane l holds wave l's list; three
+    // xor-exchanges and bitonic merges of sorted lists leave the column's
+    // places in every lane of the group, and lane l stores place l.
     __syncthreads();
-    static_assert(kWaves * kTopKMax == 64, "one candidate per lane");
-#pragma unroll 1
-    for (int c = wave; c < 16 * NB; c += kWaves) {
-      Cand<T> it[1];
-      it[0] = tkc[lane / kTopKMax][c][lane % kTopKMax];
-      const int64_t b = bt0 + c;
-      Cand<T>* dst = reinterpret_cast<Cand<T>*>(a.cand) + (b * a.nT + tile) * kTopKMax;
-      Cand<T> pl = Cand<T>{neg_inf<T>(), kNoIndex};
-#pragma unroll 1
-      for (int r = 0; r < kTopKMax; ++r) {
-        pl = next_place(it, r == 0, pl.m, pl.idx);
-        if (lane == 0 && b < B) store_cand(dst + r, pl);
+    static_assert(kWaves == kTopKMax && kWaves * kWaves == 64, "a group of 8 lanes per column");
+    {
+      const int src = lane % kWaves;
+      const int c = wave + kWaves * (lane / kWaves);
+      const bool cv = c < 16 * NB;
+      T lm[kTopKMax];
+      int32_t li[kTopKMax];
+#pragma unroll
+      for (int j = 0; j < kTopKMax; ++j) {
+        const Cand<T> o = tkc[src][cv ? c : 0][j];
+        lm[j] = cv ? o.m : neg_inf<T>();
+        li[j] = cv ? o.idx : kNoIndex;
       }
+#pragma unroll
+      for (int x = 1; x < kWaves; x <<= 1) {
+        T om[kTopKMax];
+        int32_t oi[kTopKMax];
+#pragma unroll
+        for (int j = 0; j < kTopKMax; ++j) {
+          om[j] = __shfl_xor(lm[j], x, 64);
+          oi[j] = __shfl_xor(li[j], x, 64);
+        }
+        merge_top(lm, li, om, oi);
+      }
+      Cand<T> mine = Cand<T>{lm[0], li[0]};
+#pragma unroll
+      for (int j = 1; j < kTopKMax; ++j)
+        if (src == j) mine = Cand<T>{lm[j], li[j]};
+      const int64_t b = bt0 + c;
+      if (cv && b < B) store_cand(reinterpret_cast<Cand<T>*>(a.cand) + (b * a.nT + tile) * kTopKMax + src, mine);
     }
     wait_stores_complete();
 
