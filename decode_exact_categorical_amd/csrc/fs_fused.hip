@@ -153,8 +153,12 @@ __device__ __forceinline__ void load_bias4(const FusedArgs& a, int64_t b, int64_
 //  * 64 columns with a bias or float64 noise: 3 row blocks, two pairs in
 //    flight, each pair reloaded after all its MFMAs (no room for more).
 // Passes of 4 row blocks (64 rows) stream W markedly slower than 3 or 5.
-// FP8 weights (W8) take the simplest of these: two pairs in flight, 5 row
-// blocks up to 32 columns and 3 beyond, each pair reloaded after its MFMAs.
+// FP8 weights (W8) and MXFP4 weights up to 32 columns: two pairs in flight,
+// 5 row blocks, each pair reloaded after its MFMAs; at 48 and 64 columns the
+// ring of one (5 row blocks, one pass), except 64 columns with a bias or
+// float64 noise: 3 row blocks and two pairs in flight.  (The ring of one took
+// FP8 at 48 / 64 columns from 137 / 160 to 122 / 149 us at the Qwen head and
+// MXFP4 from 122 / 136 to 105 / 116.)
 // Batch tiles wider than 64 columns (8 column blocks: the large-batch end,
 // where the contraction approaches the MFMA roofline) use every W fragment
 // for 8 MFMAs: 2 row blocks a pass (64 accumulators a lane), two pairs in
@@ -170,9 +174,9 @@ struct Pipeline {
                                      EPI == kEpiFilt32 || EPI == kEpiFilt64;
   static constexpr bool wide = NB > 4;
   static constexpr bool wide_extra = NB == 4 && (HAS_BIAS || (late_noise && EPI != kEpiFilt32));
-  static constexpr bool ring1 = !narrow && !wide && NB >= 3 && !wide_extra;
+  static constexpr bool ring1 = !wide && NB >= 3 && !wide_extra;
   static constexpr int row_blocks = wide ? 2 : ((NB <= 2 || ring1) ? 5 : 3);
-  static constexpr bool half_h = ring1 && (NB == 4 || HAS_BIAS || late_noise);
+  static constexpr bool half_h = ring1 && !narrow && (NB == 4 || HAS_BIAS || late_noise);
   static constexpr bool interleave = !narrow && !wide && !wide_extra;
   // k per H chunk in LDS.  MXFP4 at 16 and 32 columns takes chunks of two
   // load-step pairs (512 k), as FP8's 256-k chunks are: one barrier per four
@@ -842,6 +846,81 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       }
     };
 
+    // FP8 and MXFP4 with one load-step pair in flight (48 and 64 columns):
+    // the pair's MFMAs load step by load step over every row block, and in
+    // the last one each row block's W (and MXFP4 scale words) is reloaded
+    // with pair q as soon as its MFMAs have issued.
+    auto mma8_reload = [&](u32x4 (&w)[2][kRB], int buf, int kk, int q) {
+      const WElem* w0 = step_base(2 * q);
+      const WElem* w1 = step_base(2 * q + 1);
+      // Per load step, the first 8 values of every row block, then the next
+      // 8 (each accumulator still takes its MFMAs in mma8's order), so one
+      // H fragment per column block is live at a time.
+#pragma unroll
+      for (int ls = 0; ls < 2; ++ls)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 hf[NB];
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb)
+            hf[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 64 * ls + 16 * grp + 8 * h]);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) {
+            u32x4 lo, hi;
+            e4m3x16_to_bf16(w[ls][rb], lo, hi);
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(h == 0 ? lo : hi), hf[cb], acc[rb][cb],
+                                                                    0, 0, 0);
+            if (ls == 1 && h == 1) {
+              w[0][rb] = load_frag(w0 + woff[rb]);
+              w[1][rb] = load_frag(w1 + woff[rb]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto mma4_reload = [&](u32x4 (&w)[2][kRB], uint32_t (&sw)[2][kRB], int buf, int kk, int q) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const WElem* w0 = step_base(2 * q);
+      const WElem* w1 = step_base(2 * q + 1);
+      const uint8_t* sp = swave + 4 * (phys_step(2 * q) & ~1);
+#pragma unroll
+      for (int ls = 0; ls < 2; ++ls)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x8 hf[NB];
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb)
+            hf[cb] = *reinterpret_cast<const bf16x8*>(&hs[buf][16 * cb + col][kk + 128 * ls + 32 * grp + 8 * i]);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) {
+            const uint32_t e = (sw[ls][rb] >> (8 * grp)) & 255u;
+            const float sc = __builtin_bit_cast(
+                float, e == 0u ? 0x00400000u : (e == 255u ? 0x7fc00000u : e << 23));
+            const uint32_t d = w[ls][rb][i];
+            const u32x4 v = u32x4{
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3))};
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(v), hf[cb], acc[rb][cb], 0, 0, 0);
+            if (ls == 1 && i == 3) {
+              w[0][rb] = load_frag(w0 + woff[rb]);
+              w[1][rb] = load_frag(w1 + woff[rb]);
+              const u32x2 sv = *reinterpret_cast<const u32x2*>(sp + soff[rb]);
+              sw[0][rb] = sv[0];
+              sw[1][rb] = sv[1];
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          if (ls == 1 && i == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     // The k-loop is straight-line: every k-step pair issues the same loads in
     // the same order (2 x kRB W fragments, then the biases of the slots folded
     // four steps later), every chunk the same NB H loads, and every pass runs
@@ -873,9 +952,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     bias_slot_load(ba0, 0);
     bias_slot_load(ba1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (W4)
+    if constexpr (W4 && !kRing1)
       load_pair4(pb, sb, 1);
-    else if constexpr (!kRing1)
+    else if constexpr (!W4 && !kRing1)
       load_pair(pb, 1);
     bias_slot_load(bb0, 2);
     bias_slot_load(bb1, 3);
@@ -900,6 +979,34 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         h_load(c + 1, Half0{});
         h_load(c + 1, Half1{});
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kRing1) {
+          // One pair in flight (48 and 64 columns): both chunks' pairs run
+          // through pa, each reloaded with the next chunk's as it is used.
+          mma4_reload(pa, sa, 0, 0, c + 1);
+          FS_FOLD_SLOT(2 * c, ba0);
+          FS_FOLD_SLOT(2 * c + 1, ba1);
+          __builtin_amdgcn_sched_barrier(0);
+          bias_slot_load(ba0, 2 * c + 4);
+          bias_slot_load(ba1, 2 * c + 5);
+          __builtin_amdgcn_sched_barrier(0);
+          h_store(1, Half0{});
+          h_store(1, Half1{});
+          __syncthreads();
+          h_load(c + 2, Half0{});
+          h_load(c + 2, Half1{});
+          __builtin_amdgcn_sched_barrier(0);
+          mma4_reload(pa, sa, 1, 0, c + 2);
+          FS_FOLD_SLOT(2 * c + 2, bb0);
+          FS_FOLD_SLOT(2 * c + 3, bb1);
+          __builtin_amdgcn_sched_barrier(0);
+          bias_slot_load(bb0, 2 * c + 6);
+          bias_slot_load(bb1, 2 * c + 7);
+          __builtin_amdgcn_sched_barrier(0);
+          h_store(0, Half0{});
+          h_store(0, Half1{});
+          __syncthreads();
+          continue;
+        }
         mma4(pa, sa, 0, 0);
         FS_FOLD_SLOT(2 * c, ba0);
         FS_FOLD_SLOT(2 * c + 1, ba1);
@@ -942,6 +1049,27 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
         // chunk ahead.
         h_load(cn, Half1{});
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kRing1) {
+          // One pair in flight: the chunk's two pairs both run through pa.
+          mma8_reload(pa, buf, 0, 2 * c + 1);
+          FS_FOLD_SLOT(4 * c, ba0);
+          FS_FOLD_SLOT(4 * c + 1, ba1);
+          __builtin_amdgcn_sched_barrier(0);
+          bias_slot_load(ba0, 4 * c + 4);
+          bias_slot_load(ba1, 4 * c + 5);
+          __builtin_amdgcn_sched_barrier(0);
+          mma8_reload(pa, buf, 128, 2 * c + 2);
+          FS_FOLD_SLOT(4 * c + 2, bb0);
+          FS_FOLD_SLOT(4 * c + 3, bb1);
+          __builtin_amdgcn_sched_barrier(0);
+          bias_slot_load(bb0, 4 * c + 6);
+          bias_slot_load(bb1, 4 * c + 7);
+          __builtin_amdgcn_sched_barrier(0);
+          h_store(buf ^ 1, Half0{});
+          h_store(buf ^ 1, Half1{});
+          __syncthreads();
+          continue;
+        }
         mma8(pa, buf, 0);
         FS_FOLD_SLOT(4 * c, ba0);
         FS_FOLD_SLOT(4 * c + 1, ba1);
