@@ -78,8 +78,13 @@ __device__ __forceinline__ bool filt_store_row(float t, int32_t k, float p, floa
 }
 
 // Weight formats: bf16, OCP FP8 E4M3 with a float32 scale per row, MXFP4
-// (E2M1 elements, an E8M0 scale per block of 32 along k).
-enum WeightFormat { kWBf16 = 0, kWFp8 = 1, kWFp4 = 2 };
+// (E2M1 elements, an E8M0 scale per block of 32 along k).  MXFP4 kernels
+// stage each wave's rows of block scales in LDS for a pass while a row's
+// scales fit the LDS row (D <= kS4MaxD); kWFp4Wide, for larger D, reads them
+// from memory with each load-step pair's W.
+enum WeightFormat { kWBf16 = 0, kWFp8 = 1, kWFp4 = 2, kWFp4Wide = 3 };
+constexpr int kS4MaxD = 4096;
+constexpr int kS4Row = kS4MaxD / 32 + 8;  // LDS bytes of a row's scales (8 of padding)
 
 template <int EPI>
 struct ScoreType {
@@ -183,7 +188,8 @@ struct Pipeline {
   // 16-byte loads of a row (measured 5 us faster there; with 3-row-block
   // passes, and at 32 columns with a bias or float64 noise, whose registers
   // it overflows, 256-k chunks of one pair each are faster).
-  static constexpr bool w4_long = WF == kWFp4 && (NB == 1 || (NB == 2 && !HAS_BIAS && !late_noise));
+  static constexpr bool w4_long =
+      (WF == kWFp4 || WF == kWFp4Wide) && (NB == 1 || (NB == 2 && !HAS_BIAS && !late_noise));
   static constexpr int chunk_k = wide ? 128 : (w4_long ? 512 : 256);
   // Fragment (rb, cb) gets its noise at k-step noise_slots * rb + cb.
   static constexpr int noise_slots = wide ? NB : 4;
@@ -321,7 +327,8 @@ __global__ __launch_bounds__(256) void topk_stage2_kernel(FusedArgs a) {
 template <int NB, int EPI, bool HAS_BIAS, int WF, bool BV4 = false>
 __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) {
   typedef typename ScoreType<EPI>::type T;
-  constexpr bool W8 = WF == kWFp8, W4 = WF == kWFp4;
+  constexpr bool W8 = WF == kWFp8, W4 = WF == kWFp4 || WF == kWFp4Wide;
+  constexpr bool kS4L = WF == kWFp4;  // MXFP4 scales staged in LDS
   constexpr bool kFold = FoldNoise<NB, EPI, HAS_BIAS, WF>::value;
   constexpr bool kTopK = EPI == kEpiTopK32 || EPI == kEpiTopK64;
   constexpr bool kFilt = EPI == kEpiFilt32 || EPI == kEpiFilt64;
@@ -480,6 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
   }
 
   __shared__ __attribute__((aligned(16))) uint16_t hs[2][16 * NB][kHRow];
+  // MXFP4 block scales of each wave's rows in the current pass (kS4L).
+  __shared__ __attribute__((aligned(8))) uint8_t s4l[kS4L ? kWaves : 1][kS4L ? 16 * kRB : 1][kS4L ? kS4Row : 8];
 
   // H chunk staging.  A chunk is 16*NB columns x kKC k = 16*NB*kKC/8 pieces of
   // 16 bytes; thread t stages pieces t + 512*q, q < kHQ, so every thread
@@ -545,7 +554,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       woff[rb] = (uint32_t)((row - rbase) * row_units + kLaneUnits * grp);
     }
     // MXFP4: each lane's row's E8M0 scales, D/32 bytes a row; a lane reads the
-    // 4 bytes of a load step's 4 blocks (one per lane of the row).
+    // 4 bytes of a load step's 4 blocks (one per lane of the row) with each
+    // load-step pair.  With kS4L the wave's rows of scales for the pass are
+    // first copied to its own LDS area (8-byte pieces, rows past the wave's
+    // last repeat it) and read from there: read from memory a pair at a
+    // time, a row's 128-byte line of scales is fetched again from HBM most
+    // of the times it is used (the W stream evicts it from L2 in between),
+    // about half as many bytes again as the weights.
     const uint8_t* swave = W4 ? a.w4_scale + rbase * (D / 32) : nullptr;
     uint32_t soff[kRB];
 #pragma unroll
@@ -553,6 +568,21 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       int64_t row = r0 + 16 * (rb_first + rb) + col;
       if (row > rlast) row = rlast;
       soff[rb] = W4 ? (uint32_t)((row - rbase) * (D / 32)) : 0u;
+    }
+    if constexpr (kS4L) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const int ppr = (int)(D / 256);  // 8-byte pieces of a row (D is a multiple of 256)
+      for (int pc = lane; pc < 16 * kRB * ppr; pc += 64) {
+        const int i = pc / ppr, o = (pc - i * ppr) * 8;
+        int64_t row = r0 + 16 * rb_first + i;
+        if (row > rlast) row = rlast;
+        *reinterpret_cast<u32x2*>(&s4l[wave][i][o]) =
+            *reinterpret_cast<const u32x2*>(swave + (row - rbase) * (D / 32) + o);
+      }
+      // (The area is the wave's own: its LDS operations complete in order.)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     f32x4 acc[kRB][NB];
@@ -694,7 +724,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       for (int rb = 0; rb < kRB; ++rb) {
         dst[0][rb] = load_frag(w0 + woff[rb]);
         dst[1][rb] = load_frag(w1 + woff[rb]);
-        const u32x2 v = *reinterpret_cast<const u32x2*>(sp + soff[rb]);
+        const u32x2 v = kS4L ? *reinterpret_cast<const u32x2*>(&s4l[wave][16 * rb + col][sp - swave])
+                             : *reinterpret_cast<const u32x2*>(sp + soff[rb]);
         sw[0][rb] = v[0];
         sw[1][rb] = v[1];
       }
@@ -911,7 +942,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
             if (ls == 1 && i == 3) {
               w[0][rb] = load_frag(w0 + woff[rb]);
               w[1][rb] = load_frag(w1 + woff[rb]);
-              const u32x2 sv = *reinterpret_cast<const u32x2*>(sp + soff[rb]);
+              const u32x2 sv = kS4L ? *reinterpret_cast<const u32x2*>(&s4l[wave][16 * rb + col][sp - swave])
+                                    : *reinterpret_cast<const u32x2*>(sp + soff[rb]);
               sw[0][rb] = sv[0];
               sw[1][rb] = sv[1];
               __builtin_amdgcn_sched_barrier(0);
@@ -2526,7 +2558,8 @@ hipError_t launch_fused_stage1(const FusedArgs& a, int epi, hipStream_t stream) 
   const dim3 grid((unsigned)a.nT, (unsigned)nbt);
   // Each column's logits come from its own MFMA column, so the tile width
   // does not change any row's arithmetic.
-  if (a.W4) return launch_w<kWFp4>(a, epi, grid, nb, stream);
+  if (a.W4)
+    return a.D <= kS4MaxD ? launch_w<kWFp4>(a, epi, grid, nb, stream) : launch_w<kWFp4Wide>(a, epi, grid, nb, stream);
   if (a.W8) return launch_w<kWFp8>(a, epi, grid, nb, stream);
   if (nb > 4) return launch_wide(a, epi, grid, stream);
   return launch_w<kWBf16>(a, epi, grid, nb, stream);

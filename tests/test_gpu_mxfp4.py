@@ -62,6 +62,8 @@ LOGIT_SHAPES = [
     (16, 4096, 2000),
     (1, 256, 5),
     (32, 768, 3000),       # 32 columns in 512-k chunks, the last one half past D
+    (3, 4352, 1500),       # scales read per pair (past 4096 k)
+    (64, 4352, 700),
 ]
 
 
@@ -102,6 +104,9 @@ MXFP4_CASES = [
     dict(B=20, D=256, V=170001, bias=True),
     dict(B=30, D=768, V=4099, greedy_rows=(4,)),    # 512-k chunks, the last one half past D
     dict(B=9, D=1280, V=2048, bias=True),           # 16 columns, bias, 512-k chunks
+    # past 4096 k a row's scales no longer fit the LDS row: read per pair
+    dict(B=5, D=4352, V=3001, greedy_rows=(2,)),
+    dict(B=50, D=4352, V=2001, bias=True),
 ]
 
 
