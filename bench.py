@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("µs/decode-step & achieved HBM GB/s (fused LM-head+sample), "
           "D=4096 V=151936 B=1–64")
 D_MODEL, VOCAB = 4096, 151936
-LOGITS_CHUNK = 2048             # logits per workgroup of the standalone sampler
+LOGITS_CHUNK = 2048             # smallest chunk of the standalone sampler (bounds its candidate count)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_stage1_qwen3_8b_b64_traffic.txt")

@@ -470,7 +470,7 @@ fs_status fs_sample_logits(const float* logits, int64_t B, int64_t V, const floa
     a.rid_base = (uint32_t)b0;
     a.key = fs::make_key(seed, offset);
     a.cand = candidates_of(workspace);
-    a.chunk = fs::logits_chunk(nb, V);
+    a.chunk = fs::logits_sample_chunk(nb, V);
     a.nT = (int)((V + a.chunk - 1) / a.chunk);  // <= nT at the smallest chunk
     a.counters = counters_of(workspace);
     a.out = out_idx + b0;

@@ -135,7 +135,8 @@ hipError_t launch_fused_wide(const FusedArgs& a, int epilogue, hipStream_t strea
 // workgroup of each row).
 constexpr int kLogitsChunk = 2048;      // fewest logits per workgroup (sizes the workspace)
 constexpr int kLogitsChunkMax = 131072;  // most logits per workgroup
-int logits_chunk(int64_t B, int64_t V);  // logits per workgroup for a launch
+int logits_chunk(int64_t B, int64_t V);         // logits per workgroup, top-k launches
+int logits_sample_chunk(int64_t B, int64_t V);  // logits per workgroup, one-draw launches
 struct LogitsArgs {
   const float* X;  // [B, V]
   int64_t B, V;

@@ -278,11 +278,29 @@ __global__ __launch_bounds__(kThreads) void logits_stage1_kernel(LogitsArgs a) {
 
 }  // namespace
 
-int logits_chunk(int64_t B, int64_t V) {
-  constexpr int64_t kTargetWorkgroups = 2048;  // 8 per CU
+namespace {
+// The largest chunk (kLogitsChunk 2^k <= kLogitsChunkMax) that leaves at least
+// `target` workgroups.
+int64_t largest_chunk(int64_t B, int64_t V, int64_t target) {
   int64_t chunk = kLogitsChunk;
-  while (chunk < kLogitsChunkMax && B * ((V + 2 * chunk - 1) / (2 * chunk)) >= kTargetWorkgroups)
-    chunk *= 2;
+  while (chunk < kLogitsChunkMax && B * ((V + 2 * chunk - 1) / (2 * chunk)) >= target) chunk *= 2;
+  return chunk;
+}
+}  // namespace
+
+int logits_chunk(int64_t B, int64_t V) {
+  return (int)largest_chunk(B, V, 2048);  // 8 workgroups per CU
+}
+
+int logits_sample_chunk(int64_t B, int64_t V) {
+  // Longer chunks let a wave's running best skip more transforms (bound then
+  // refine); more workgroups hide more latency.  Measured at V = 131072: the
+  // largest chunk that leaves 1024 workgroups (4 a CU), unless that chunk is
+  // under 32768 logits (B < 256), where the largest that leaves 512 is
+  // faster (float32 noise, us: B = 64 29 -> 21, B = 128 38 -> 33, B = 256 71
+  // -> 50, B = 512 -> 75, B = 4096 unchanged).
+  int64_t chunk = largest_chunk(B, V, 1024);
+  if (chunk < 32768) chunk = largest_chunk(B, V, 512);
   return (int)chunk;
 }
 
