@@ -144,6 +144,30 @@ def test_logits_sampling_parity(dev, B, V, misalign, fp64):
     check_index_parity(got, ref, gap, f"logits B={B} V={V} fp64={fp64}")
 
 
+@pytest.mark.parametrize("fp64", [False, True])
+def test_logits_draws_independent_of_chunking(dev, fp64):
+    # The standalone sampler splits a row into chunks whose length follows the
+    # batch size (2048 logits at B = 8, 32768 at B = 320 and V = 131072), and
+    # each chunk skips the noise of logits its running best rules out.  The
+    # draw is the exhaustive argmax either way: the same rows with the same
+    # ids give the same tokens bit for bit in a batch of 320 and in batches
+    # of 8.
+    say(f"logits sampler chunking invariance fp64={fp64}")
+    B, V = 320, 131072
+    g = torch.Generator(device=dev).manual_seed(41)
+    x = torch.randn((B, V), generator=g, device=dev) * 3.0
+    temp = (0.5 + torch.rand(B, generator=g, device=dev))
+    temp[3] = 0.0
+    rid = torch.arange(7000, 7000 + B, dtype=torch.int32, device=dev)
+    whole = fs.sample_logits(x, temp, seed=5, offset=11, row_ids=rid, fp64_noise=fp64)
+    parts = torch.cat([fs.sample_logits(x[r:r + 8].contiguous(), temp[r:r + 8].contiguous(), seed=5,
+                                        offset=11, row_ids=rid[r:r + 8].contiguous(), fp64_noise=fp64)
+                       for r in range(0, B, 8)])
+    torch.cuda.synchronize()
+    assert torch.equal(whole.cpu(), parts.cpu())
+    assert (whole >= 0).all()
+
+
 def test_greedy_logits_exact_with_ties(dev):
     say("greedy logits with ties")
     rng = np.random.default_rng(5)
