@@ -67,9 +67,20 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
     acc.z ^= v.z;
     acc.w ^= v.w;
   }
+  // One atomic per workgroup: device-scope atomics on one address are
+  // serialised where the memory is, so one per wave (2048 over the chip) would
+  // add a tail of tens of microseconds.
+  __shared__ uint64_t part[kStreamThreads / 64];
   uint64_t x = ((uint64_t)(acc.x ^ acc.z) << 32) | (uint64_t)(acc.y ^ acc.w);
   for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o, 64);
-  if ((threadIdx.x & 63) == 0 && x != 0) atomicXor((unsigned long long*)out, (unsigned long long)x);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x / 64] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    x = 0;
+#pragma unroll
+    for (int w = 0; w < kStreamThreads / 64; ++w) x ^= part[w];
+    if (x != 0) atomicXor((unsigned long long*)out, (unsigned long long)x);
+  }
 }
 
 }  // namespace
