@@ -85,6 +85,7 @@ __device__ __forceinline__ bool filt_store_row(float t, int32_t k, float p, floa
 enum WeightFormat { kWBf16 = 0, kWFp8 = 1, kWFp4 = 2, kWFp4Wide = 3 };
 constexpr int kS4MaxD = 4096;
 constexpr int kS4Row = kS4MaxD / 32 + 8;  // LDS bytes of a row's scales (8 of padding)
+static_assert(kS4MaxD / 256 <= 16, "a row's scales in LDS are at most 16 pieces of 8 bytes");
 
 template <int EPI>
 struct ScoreType {
@@ -569,20 +570,31 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
       if (row > rlast) row = rlast;
       soff[rb] = W4 ? (uint32_t)((row - rbase) * (D / 32)) : 0u;
     }
+    // A lane copies 8-byte piece lane % 16 of rows lane / 16 + 4 j: its loads
+    // go out here, all of them before the first store waits (a load, a wait
+    // and a store per piece in turn would start every pass with some twenty
+    // HBM round trips one after the other), and the stores come after the
+    // first W loads of the pass have been issued, so that the two round trips
+    // overlap.  Lanes past a row's D / 256 pieces repeat its last one.
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 sv[kS4L ? 4 * kRB : 1];
+    int s4o = 0, s4r = 0;  // the lane's piece offset and first row
     if constexpr (kS4L) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const int ppr = (int)(D / 256);  // 8-byte pieces of a row (D is a multiple of 256)
-      for (int pc = lane; pc < 16 * kRB * ppr; pc += 64) {
-        const int i = pc / ppr, o = (pc - i * ppr) * 8;
-        int64_t row = r0 + 16 * rb_first + i;
+      const int ppr = (int)(D / 256);  // 8-byte pieces of a row: 1 .. kS4MaxD / 256
+      // (An opaque copy of the lane index: computed from it, the addresses
+      // are not hoisted out of the pass loop to occupy registers through the
+      // k-loop.)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      s4o = (ln % 16 < ppr ? ln % 16 : ppr - 1) * 8;
+      s4r = ln / 16;
+#pragma unroll
+      for (int j = 0; j < 4 * kRB; ++j) {
+        int64_t row = r0 + 16 * rb_first + s4r + 4 * j;
         if (row > rlast) row = rlast;
-        *reinterpret_cast<u32x2*>(&s4l[wave][i][o]) =
-            *reinterpret_cast<const u32x2*>(swave + (row - rbase) * (D / 32) + o);
+        sv[j] = *reinterpret_cast<const u32x2*>(swave + (row - rbase) * (D / 32) + s4o);
       }
-      // (The area is the wave's own: its LDS operations complete in order.)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     f32x4 acc[kRB][NB];
@@ -715,8 +727,17 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // one 8-byte load for the pair (a pair's 256 k are 8 blocks of a row; D is
     // a multiple of 256, so a pair inside D starts at an even step, and a pair
     // past D re-reads the last pair's scales, against zero H).
+    auto scale_words = [&](uint32_t (&sw)[2][kRB], int q) {
+      const uint8_t* sp = swave + 4 * (phys_step(2 * q) & ~1);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const u32x2 v = kS4L ? *reinterpret_cast<const u32x2*>(&s4l[wave][16 * rb + col][sp - swave])
+                             : *reinterpret_cast<const u32x2*>(sp + soff[rb]);
+        sw[0][rb] = v[0];
+        sw[1][rb] = v[1];
+      }
+    };
     auto load_pair4 = [&](u32x4 (&dst)[2][kRB], uint32_t (&sw)[2][kRB], int q) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       const WElem* w0 = step_base(2 * q);
       const WElem* w1 = step_base(2 * q + 1);
       const uint8_t* sp = swave + 4 * (phys_step(2 * q) & ~1);
@@ -976,21 +997,34 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     // scheduler to swap them, the first pass through the loop head would see
     // pair 0 as the newest loads, and the compiler would wait for nearly all
     // loads there on every pass.
+    // With the MXFP4 scales in LDS, the first pairs' scale words are read once
+    // the staged scales are stored (after the pairs' W loads).
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (W4)
+    if constexpr (W4 && !kS4L)
       load_pair4(pa, sa, 0);
     else
       load_pair(pa, 0);
     bias_slot_load(ba0, 0);
     bias_slot_load(ba1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (W4 && !kRing1)
+    if constexpr (W4 && !kS4L && !kRing1)
       load_pair4(pb, sb, 1);
-    else if constexpr (!W4 && !kRing1)
+    else if constexpr (!kRing1)
       load_pair(pb, 1);
     bias_slot_load(bb0, 2);
     bias_slot_load(bb1, 3);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kS4L) {
+#pragma unroll
+      for (int j = 0; j < 4 * kRB; ++j) *reinterpret_cast<u32x2*>(&s4l[wave][s4r + 4 * j][s4o]) = sv[j];
+      // (The area is the wave's own: its LDS operations complete in order.)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      scale_words(sa, 0);
+      if constexpr (!kRing1) scale_words(sb, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     h_store(0, Half0{});
     h_store(0, Half1{});
     __syncthreads();
