@@ -225,6 +225,26 @@ __device__ __forceinline__ void wave_argmax_xor(T& m, int32_t& i, int lo_bit) {
   }
 }
 
+// Reduce (m, i) over each aligned group of kWidth consecutive lanes (8, 16 or
+// 32; a group's lanes are all active or all inactive): DPP exchanges within 16
+// lanes, one xor-shuffle between the halves of 32.  Every lane of a group ends
+// with the group's best (unique under the total order, so the pairing does not
+// matter).
+template <int kWidth, typename T>
+__device__ __forceinline__ void group_argmax(T& m, int32_t& i) {
+  static_assert(kWidth == 8 || kWidth == 16 || kWidth == 32, "groups of 8, 16 or 32 lanes");
+  auto step = [&](T om, int32_t oi) {
+    const bool take = beats_nb(om, oi, m, i);
+    m = take ? om : m;
+    i = take ? oi : i;
+  };
+  step(dpp_val<0xb1>(m), (int32_t)dpp_u32<0xb1>((uint32_t)i));
+  step(dpp_val<0x4e>(m), (int32_t)dpp_u32<0x4e>((uint32_t)i));
+  step(dpp_val<0x141>(m), (int32_t)dpp_u32<0x141>((uint32_t)i));
+  if constexpr (kWidth >= 16) step(dpp_val<0x140>(m), (int32_t)dpp_u32<0x140>((uint32_t)i));
+  if constexpr (kWidth == 32) step(__shfl_xor(m, 16, 64), __shfl_xor(i, 16, 64));
+}
+
 // ---------------------------------------------------------------------------
 // Stage 2 inside the sampling kernel [FlashSampling, "algorithm details",
 // Stage 2].  The workgroups of one group (a batch tile of the fused kernel, a

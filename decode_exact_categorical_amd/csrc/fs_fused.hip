@@ -1857,44 +1857,56 @@ __global__ __launch_bounds__(kThreads, 1) void fused_stage1_kernel(FusedArgs a) 
     }
   }
 
-  // Stage 2 of this batch tile, in the workgroup that finishes it last.  Wave
-  // w takes rows w, w + 8, ... of the tile and issues every candidate load of
-  // 8 of its rows at a time (clamped, always valid addresses) before reducing
-  // any, so the tail costs one round trip to the coherence point per 8 rows
-  // of a wave, not one per row.
+  // Stage 2 of this batch tile, in the workgroup that finishes it last.  Row r
+  // of the tile goes to kTPR consecutive threads (8 to 32, so a row's threads
+  // share a wave), thread q of them taking the row's candidates q, q + kTPR,
+  // ...: every thread issues all its candidate loads (clamped, always valid
+  // addresses) before it compares any, and the rows reduce side by side, so
+  // the tail costs one round trip to the coherence point and a few lane
+  // exchanges.  (A wave per row in turn, each across its 64 lanes, cost about
+  // 4 us more at 64 rows.)
   if (!finish_last(a.counters + btile, (uint32_t)nT)) return;
-  constexpr int kRowsPerWave = kTile / kWaves;
-  constexpr int kRowGroup = kRowsPerWave < 8 ? kRowsPerWave : 8;
-  constexpr int kLoadsPerRow = kMaxFusedTiles / 64;
-  const Cand<T>* cand = reinterpret_cast<const Cand<T>*>(a.cand);
+  {
+    constexpr int kTPR = kTile <= 16 ? 32 : (kTile <= 32 ? 16 : 8);
+    constexpr int kPerThread = kMaxFusedTiles / kTPR;
+    static_assert(64 % kTPR == 0, "a row's threads lie in one wave");
+    const Cand<T>* cand = reinterpret_cast<const Cand<T>*>(a.cand);
+    const int q = tid % kTPR;
+    // (Tiles of 128 rows: two rows a group of threads, one after the other.)
 #pragma unroll 1
-  for (int i0 = 0; i0 < kRowsPerWave; i0 += kRowGroup) {
-    if (bt0 + wave + kWaves * i0 >= B) break;
-    Cand<T> c[kRowGroup][kLoadsPerRow];
-#pragma unroll
-    for (int i = 0; i < kRowGroup; ++i) {
-      int64_t b = bt0 + wave + kWaves * (i0 + i);
-      if (b > B - 1) b = B - 1;
-#pragma unroll
-      for (int j = 0; j < kLoadsPerRow; ++j) {
-        const int t = lane + 64 * j < a.nT ? lane + 64 * j : a.nT - 1;
-        c[i][j] = load_cand(cand + b * a.nT + t);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kRowGroup; ++i) {
-      const int64_t b = bt0 + wave + kWaves * (i0 + i);
+    for (int r = tid / kTPR; r < kTile; r += kThreads / kTPR) {
+      const int64_t b = bt0 + r;
       if (b >= B) break;
-      T bm = neg_inf<T>();
-      int32_t bi = kNoIndex;
+      Cand<T> c[kPerThread];
 #pragma unroll
-      for (int j = 0; j < kLoadsPerRow; ++j)
-        if (lane + 64 * j < a.nT && beats(c[i][j].m, c[i][j].idx, bm, bi)) {
-          bm = c[i][j].m;
-          bi = c[i][j].idx;
-        }
-      wave_argmax_xor(bm, bi, 0);
-      if (lane == 0) a.out[b] = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
+      for (int j = 0; j < kPerThread; ++j) {
+        const int t = q + kTPR * j < a.nT ? q + kTPR * j : a.nT - 1;
+        c[j] = load_cand(cand + b * a.nT + t);
+      }
+      // Four independent chains (candidate j in chain j % 4), then the four.
+      T cm[4];
+      int32_t ci[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cm[k] = neg_inf<T>();
+        ci[k] = kNoIndex;
+      }
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const bool take = q + kTPR * j < a.nT && beats_nb(c[j].m, c[j].idx, cm[j % 4], ci[j % 4]);
+        cm[j % 4] = take ? c[j].m : cm[j % 4];
+        ci[j % 4] = take ? c[j].idx : ci[j % 4];
+      }
+      T bm = cm[0];
+      int32_t bi = ci[0];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) {
+        const bool take = beats_nb(cm[k], ci[k], bm, bi);
+        bm = take ? cm[k] : bm;
+        bi = take ? ci[k] : bi;
+      }
+      group_argmax<kTPR>(bm, bi);
+      if (q == 0) a.out[b] = bm == neg_inf<T>() ? (int64_t)-1 : (int64_t)bi;
     }
   }
   if (tid == 0) clear_counter(a.counters + btile);
